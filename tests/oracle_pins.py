@@ -1,0 +1,236 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` raises AssertionError when the oracle disagrees. They are
+called by tests/test_oracle.py directly and again under planted mistakes
+(mutations of the oracle, on the CPU) to show that each pin can fail.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import mla as om
+import mla_synth as ms
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# page values
+# --------------------------------------------------------------------------
+
+def pin_page_dims():
+    g = json.load(open(os.path.join(GOLDEN, "page_values.json")))
+    d = g["deepseek_dims"]
+    dims = ms.DIMS["decode_bf16"]
+    assert d["kv_lora_rank"] + d["qk_rope_head_dim"] == d["cache_entry_dim"]
+    assert dims.kv_lora_rank == d["kv_lora_rank"] and dims.qk_rope_head_dim == d["qk_rope_head_dim"]
+    # the oracle's cache entries have the printed width, q heads are nope+rope
+    w = ms.make_workload("tiny_f32", dims=ms.ModelDims(
+        hidden_size=64, num_heads=2, q_lora_rank=0, kv_lora_rank=d["kv_lora_rank"],
+        qk_nope_head_dim=8, qk_rope_head_dim=d["qk_rope_head_dim"], v_head_dim=8, dtype="f32"),
+        q_lens=[3], prefix_lens=[0])
+    q, ent, _ = om.project_tokens(w.dims, w.weights, w.x, np.arange(3))
+    assert ent.shape == (3, d["cache_entry_dim"])
+    assert q.shape == (3, 2, 8 + d["qk_rope_head_dim"])
+    # paged cache layout: [num_blocks, block_size, 576], page bytes have no x2
+    pb = g["page_bytes"]
+    cache_shape = (w.num_blocks, w.dims.page_size, w.dims.entry_dim)
+    assert len(cache_shape) == g["cache_shape"]["rank"] and cache_shape[-1] == g["cache_shape"]["last_dim"]
+    bf16_page = pb["mla_factor"] * 64 * g["identities"]["num_kv_heads"] * 576 * 2
+    assert bf16_page == 73728
+    assert pb["full_attention_factor"] * 64 * 1 * 576 * 2 == 2 * bf16_page
+    assert pb["fp8_ds_mla_bytes_per_token"] > 576  # packed fp8 entry carries more than one byte per dim
+
+
+# --------------------------------------------------------------------------
+# RMSNorm: library routine and closed forms
+# --------------------------------------------------------------------------
+
+def pin_rms_norm():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((7, 33))
+    g = 1 + 0.1 * rng.standard_normal(33)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (33,), torch.from_numpy(g), eps=1e-6).numpy()
+    assert np.max(np.abs(om.rms_norm(x, g, 1e-6) - ref)) < 1e-13
+    # constant row c -> gamma * c / sqrt(c^2 + eps)
+    c = 3.0
+    y = om.rms_norm(np.full((1, 5), c), np.ones(5), 1e-6)
+    assert np.allclose(y, c / math.sqrt(c * c + 1e-6), rtol=0, atol=1e-15)
+    # with eps = 0 it is scale invariant and has unit RMS
+    y1, y2 = om.rms_norm(x, np.ones(33), 0.0), om.rms_norm(5.0 * x, np.ones(33), 0.0)
+    assert np.max(np.abs(y1 - y2)) < 1e-13
+    assert np.allclose(np.sqrt(np.mean(y1 ** 2, axis=-1)), 1.0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# RoPE: complex-rotation form, identities
+# --------------------------------------------------------------------------
+
+def _rope_complex(x, pos, theta, style):
+    """RoPE as multiplication of the complex pairs by exp(i * p * w_j)."""
+    r = x.shape[-1]
+    w = theta ** (-2.0 * np.arange(r // 2) / r)
+    if style == om.ROPE_NEOX:
+        z = x[..., : r // 2] + 1j * x[..., r // 2:]
+    else:
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+    z = z * np.exp(1j * np.asarray(pos, np.float64)[:, None] * w[None, :])
+    out = np.empty_like(x)
+    if style == om.ROPE_NEOX:
+        out[..., : r // 2], out[..., r // 2:] = z.real, z.imag
+    else:
+        out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    return out
+
+
+def pin_rope():
+    rng = np.random.default_rng(12)
+    for style in (om.ROPE_NEOX, om.ROPE_INTERLEAVED):
+        x = rng.standard_normal((9, 16))
+        pos = rng.integers(0, 40000, size=9)
+        y = om.apply_rope(x, pos, 10000.0, style)
+        assert np.max(np.abs(y - _rope_complex(x, pos, 10000.0, style))) < 1e-9
+        assert np.max(np.abs(om.apply_rope(x, np.zeros(9), 1e4, style) - x)) == 0.0  # p=0: identity
+        assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+        # relative position: <R(p)q, R(t)k> depends on p - t only
+        q, k = rng.standard_normal((1, 16)), rng.standard_normal((1, 16))
+        a = om.apply_rope(q, [1000], 1e4, style) @ om.apply_rope(k, [990], 1e4, style).T
+        b = om.apply_rope(q, [10], 1e4, style) @ om.apply_rope(k, [0], 1e4, style).T
+        assert abs(float((a - b).item())) < 1e-10
+        # first pair rotates by exactly p radians (theta^0 = 1)
+        e0 = np.zeros((1, 16))
+        a_idx, b_idx = om.rope_pairs(16, style)
+        e0[0, a_idx[0]] = 1.0
+        z = om.apply_rope(e0, [3], 1e4, style)
+        assert abs(z[0, a_idx[0]] - math.cos(3)) < 1e-15 and abs(z[0, b_idx[0]] - math.sin(3)) < 1e-15
+    # interleaved == NeoX under the fixed permutation that de-interleaves pairs
+    x = rng.standard_normal((5, 16))
+    pos = np.arange(5) * 77
+    perm = np.concatenate([np.arange(0, 16, 2), np.arange(1, 16, 2)])
+    yi = om.apply_rope(x, pos, 1e4, om.ROPE_INTERLEAVED)
+    yn = om.apply_rope(x[:, perm], pos, 1e4, om.ROPE_NEOX)
+    assert np.max(np.abs(yi[:, perm] - yn)) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# attention core: library routine, softmax properties, empty rows
+# --------------------------------------------------------------------------
+
+def pin_attention_core():
+    rng = np.random.default_rng(13)
+    S, L, H, d, dv = 11, 29, 3, 12, 7
+    q = rng.standard_normal((S, H, d))
+    k = rng.standard_normal((L, H, d))
+    v = rng.standard_normal((L, H, dv))
+    lo = rng.integers(0, 20, size=S)
+    hi = lo + rng.integers(1, 10, size=S)
+    hi = np.minimum(hi, L)
+    lo[3], hi[3] = 5, 5  # one empty row
+    o, lse, P = om.attention_core(q, k, v, lo, hi, 0.3, return_probs=True)
+    j = np.arange(L)
+    mask = torch.from_numpy((j[None, :] >= lo[:, None]) & (j[None, :] < hi[:, None]))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), torch.from_numpy(k).permute(1, 0, 2),
+        torch.from_numpy(v).permute(1, 0, 2), attn_mask=mask, scale=0.3).permute(1, 0, 2).numpy()
+    rows = np.array([i for i in range(S) if hi[i] > lo[i]])
+    assert np.max(np.abs(o[rows] - ref[rows])) < 1e-13
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P[rows].sum(-1) - 1.0)) < 1e-14
+    assert np.all(P[~mask.numpy()[:, None, :].repeat(H, 1)] == 0)
+    # empty row: exact zeros, lse = -inf
+    assert np.all(o[3] == 0.0) and np.all(np.isneginf(lse[3]))
+    # a single visible key gets probability 1 and returns its value
+    o1, _ = om.attention_core(q, k, v, [4] * S, [5] * S, 0.3)
+    assert np.max(np.abs(o1 - v[4][None])) < 1e-15
+    # lse is the log of the partition function
+    i = 0
+    s = 0.3 * (k[lo[i]:hi[i], 0, :] @ q[i, 0])
+    assert abs(lse[i, 0] - math.log(np.exp(s).sum())) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+def tiny_dims(**kw):
+    base = dict(hidden_size=48, num_heads=3, q_lora_rank=0, kv_lora_rank=16, qk_nope_head_dim=8,
+                qk_rope_head_dim=6, v_head_dim=5, rope_style=om.ROPE_NEOX, dtype="f32", page_size=4)
+    base.update(kw)
+    return ms.ModelDims(**base)
+
+
+def pin_brute_force(w):
+    """Vectorised oracle == scalar-loop brute force (one sequence)."""
+    assert w.batch == 1
+    ref_out, ref_ent = om.brute_force_forward(w.dims, w.weights, w.x, w.prefix_rows[0],
+                                              w.mask_kind, w.window)
+    out, ent, _ = om.forward_sequence(w.dims, w.weights, w.x, w.prefix_rows[0], w.mask_kind, w.window)
+    assert np.max(np.abs(ent - ref_ent)) <= 1e-12 * max(1.0, np.max(np.abs(ref_ent)))
+    assert np.max(np.abs(out - ref_out)) <= 1e-12 * max(1.0, np.max(np.abs(ref_out))), \
+        np.max(np.abs(out - ref_out))
+
+
+def pin_absorbed_equals_expanded(w, seqs=None):
+    """The absorbed (decode) form equals the expanded (prefill) form in fp64
+    up to reassociation: the two are one computation regrouped."""
+    e = om.mla_forward(w.dims, w.weights, w.x, w.q_lens, w.prefix_rows, w.mask_kind, w.window,
+                       w.row_lo, w.row_hi, form="expanded", seqs=seqs)
+    a = om.mla_forward(w.dims, w.weights, w.x, w.q_lens, w.prefix_rows, w.mask_kind, w.window,
+                       w.row_lo, w.row_hi, form="absorbed", seqs=seqs)
+    for b in e:
+        ref = e[b][0]
+        assert _rel(a[b][0], ref) < 1e-12, (b, _rel(a[b][0], ref))
+        assert np.max(np.abs(a[b][0] - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def pin_masks(w):
+    """Special cases of the masks on one sequence of w (prefill)."""
+    x, pre = w.x, w.prefix_rows[0]
+    S, P = x.shape[0], pre.shape[0]
+    # window >= L is the causal mask
+    c = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_CAUSAL)
+    s = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_SLIDING, window=P + S + 3)
+    assert np.max(np.abs(c[0] - s[0])) == 0.0
+    # window 1: each query sees only its own entry -> attention output = own v
+    _, ent, attn = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_SLIDING, window=1)
+    _, v = om.expand_kv(w.dims, w.weights, ent)
+    gate = om.project_tokens(w.dims, w.weights, x, P + np.arange(S))[2]
+    own = v.reshape(S, -1) * (gate if gate is not None else 1.0)
+    assert np.max(np.abs(attn - own)) < 1e-12
+    # window 0 or an empty explicit interval: the whole output row is exactly 0
+    out0, _, _ = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_SLIDING, window=0)
+    assert np.all(out0 == 0.0)
+    lo = np.arange(S) + P
+    hi = lo.copy()
+    hi[::2] += 1  # odd rows dropped
+    o, _, _ = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_CAUSAL, row_lo=lo, row_hi=hi)
+    assert np.all(o[1::2] == 0.0) and np.all(np.abs(o[0::2]).max(axis=1) > 0)
+
+
+def pin_cache_consistency(w, split: int):
+    """prefill(S) == prefill(k) then prefill(S-k) over the cached prefix ==
+    successive one-token decodes (causal mask)."""
+    x, pre = w.x, w.prefix_rows[0]
+    S = x.shape[0]
+    full, ent, _ = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_CAUSAL)
+    a, ent_a, _ = om.forward_sequence(w.dims, w.weights, x[:split], pre, om.MASK_CAUSAL)
+    b, ent_b, _ = om.forward_sequence(w.dims, w.weights, x[split:], np.concatenate([pre, ent_a]),
+                                      om.MASK_CAUSAL)
+    assert np.max(np.abs(np.concatenate([a, b]) - full)) < 1e-12 * max(1, np.abs(full).max())
+    assert np.max(np.abs(np.concatenate([ent_a, ent_b]) - ent)) < 1e-12
+    cache = pre
+    for i in range(S):
+        o, e, _ = om.forward_sequence(w.dims, w.weights, x[i:i + 1], cache, om.MASK_CAUSAL)
+        assert np.max(np.abs(o[0] - full[i])) < 1e-12 * max(1, np.abs(full).max())
+        cache = np.concatenate([cache, e])

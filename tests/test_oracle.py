@@ -1,0 +1,188 @@
+"""CPU pins of the fp64 oracle (no GPU), plus planted mistakes that each pin
+must catch (mutation check, as in the SpecForge refactor-parity test that
+scales Q by 1+1e-6 and drops empty-row zeroing)."""
+import numpy as np
+import pytest
+
+import mla_synth as ms
+from oracle import mla as om
+from tests import oracle_pins as P
+
+
+def _tiny(mask=ms.MASK_CAUSAL, window=0, **dims_kw):
+    dims = P.tiny_dims(**dims_kw)
+    return ms.make_workload("tiny", dims=dims, seed=5, q_lens=[9], prefix_lens=[6],
+                            mask_kind=mask, window=window)
+
+
+def test_page_dims():
+    P.pin_page_dims()
+
+
+def test_rms_norm():
+    P.pin_rms_norm()
+
+
+def test_rope():
+    P.pin_rope()
+
+
+def test_attention_core():
+    P.pin_attention_core()
+
+
+@pytest.mark.parametrize("variant", [
+    dict(),
+    dict(q_lora_rank=12, rope_style=om.ROPE_INTERLEAVED),
+    dict(use_output_gate=True, rope_style=om.ROPE_INTERLEAVED),
+])
+@pytest.mark.parametrize("mask,window", [(ms.MASK_CAUSAL, 0), (ms.MASK_FULL, 0), (ms.MASK_SLIDING, 4)])
+def test_brute_force(variant, mask, window):
+    P.pin_brute_force(_tiny(mask, window, **variant))
+
+
+def test_brute_force_tiny_config():
+    """The tiny fp32 workload itself (hidden 256, 4 heads, 16 causal tokens)."""
+    P.pin_brute_force(ms.make_workload("tiny_f32"))
+
+
+def test_brute_force_gamma():
+    dims = P.tiny_dims(q_lora_rank=10)
+    w = ms.make_workload("tiny", dims=dims, seed=6, q_lens=[5], prefix_lens=[3], gamma_noise=True)
+    P.pin_brute_force(w)
+
+
+@pytest.mark.parametrize("variant", [dict(), dict(q_lora_rank=12, use_output_gate=True)])
+def test_masks(variant):
+    P.pin_masks(_tiny(**variant))
+
+
+def test_cache_consistency():
+    P.pin_cache_consistency(_tiny(q_lora_rank=12), split=4)
+
+
+def _small(name, **kw):
+    """A named workload's model dims with a handful of short sequences."""
+    return ms.make_workload(name, **kw)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", dict()),
+    ("draft_block_bf16", dict(q_lens=[16, 16], prefix_lens=[40, 3])),
+    ("decode_bf16", dict(batch=3, len_range=(1, 70))),
+    ("prefill_bf16", dict(q_lens=[37], prefix_lens=[0])),
+    ("long_decode_bf16", dict(batch=2, len_range=(30, 90), window=16)),
+])
+def test_absorbed_equals_expanded(name, kw, workload_cache):
+    key = ("abs", name)
+    if key not in workload_cache:
+        workload_cache[key] = _small(name, **kw)
+    P.pin_absorbed_equals_expanded(workload_cache[key])
+
+
+def test_dropped_block_rows():
+    """Explicit empty intervals (a dropped draft block) give exact-zero rows
+    through the batched entry too."""
+    w = _tiny()
+    S = w.total_tokens
+    lo = np.zeros(S, np.int32)
+    hi = np.full(S, 6 + S, np.int32)
+    hi[2:5] = 0
+    res = om.mla_forward(w.dims, w.weights, w.x, w.q_lens, w.prefix_rows, w.mask_kind,
+                         row_lo=lo, row_hi=hi)
+    out = res[0][0]
+    assert np.all(out[2:5] == 0) and np.all(np.abs(out[5:]).max(1) > 0)
+
+
+# --------------------------------------------------------------------------
+# mutations: each planted mistake must make some pin fail
+# --------------------------------------------------------------------------
+
+def _expect_fail(fn, *a):
+    with pytest.raises(AssertionError):
+        fn(*a)
+
+
+def test_mutation_scale_q(monkeypatch):
+    orig = om.project_tokens
+
+    def bad(*a, **k):
+        q, e, g = orig(*a, **k)
+        return q * (1 + 1e-6), e, g
+    monkeypatch.setattr(om, "project_tokens", bad)
+    _expect_fail(P.pin_brute_force, _tiny())
+
+
+def test_mutation_drop_zeroing(monkeypatch):
+    orig = om.attention_core
+
+    def bad(q, k, v, lo, hi, scale, return_probs=False):
+        lo = np.asarray(lo).copy()
+        hi = np.asarray(hi).copy()
+        empty = hi <= lo
+        lo[empty], hi[empty] = 0, k.shape[0]  # an empty row silently attends to everything
+        return orig(q, k, v, lo, hi, scale, return_probs)
+    monkeypatch.setattr(om, "attention_core", bad)
+    _expect_fail(P.pin_attention_core)
+    _expect_fail(P.pin_masks, _tiny())
+
+
+def test_mutation_rope_style(monkeypatch):
+    orig = om.rope_pairs
+    monkeypatch.setattr(om, "rope_pairs", lambda r, s: orig(r, 1 - s))
+    _expect_fail(P.pin_rope)
+    _expect_fail(P.pin_brute_force, _tiny())
+
+
+def test_mutation_rope_sign(monkeypatch):
+    orig = om.rope_angles
+    monkeypatch.setattr(om, "rope_angles", lambda p, r, t: -orig(p, r, t))
+    _expect_fail(P.pin_rope)
+
+
+def test_mutation_window_off_by_one(monkeypatch):
+    def bad(p, kv_len, kind, window):
+        if kind == om.MASK_SLIDING:
+            return max(0, p - window), min(p + 1, kv_len)
+        return orig(p, kv_len, kind, window)
+    orig = om.visible_interval
+    monkeypatch.setattr(om, "visible_interval", bad)
+    _expect_fail(P.pin_masks, _tiny())
+    _expect_fail(P.pin_brute_force, _tiny(ms.MASK_SLIDING, 4))
+
+
+def test_mutation_transposed_absorption(monkeypatch):
+    """W_UV taken from the k_nope rows instead of the v rows (a swapped split)."""
+    orig = om._absorbed_attention
+
+    def bad(dims, W, q, entries, lo, hi, scale):
+        W2 = dict(W)
+        H, n, dv, c = dims.num_heads, dims.qk_nope_head_dim, dims.v_head_dim, dims.kv_lora_rank
+        wk = np.asarray(W["kv_b_proj"]).reshape(H, n + dv, c)
+        W2["kv_b_proj"] = np.concatenate([wk[:, :n], wk[:, n:][:, ::-1]], axis=1).reshape(-1, c)
+        return orig(dims, W2, q, entries, lo, hi, scale)
+    monkeypatch.setattr(om, "_absorbed_attention", bad)
+    _expect_fail(P.pin_absorbed_equals_expanded, _tiny())
+
+
+def test_mutation_cache_raw_latent(monkeypatch):
+    """Caching the raw kv_c instead of the RMSNorm'd latent."""
+    orig = om.rms_norm
+    calls = {"n": 0}
+
+    def bad(x, g, eps):
+        calls["n"] += 1
+        y = orig(x, g, eps)
+        return np.asarray(x, np.float64) if x.shape[-1] == 16 else y
+    monkeypatch.setattr(om, "rms_norm", bad)
+    _expect_fail(P.pin_brute_force, _tiny())
+
+
+def test_mutation_gate_dropped(monkeypatch):
+    orig = om.project_tokens
+
+    def bad(*a, **k):
+        q, e, g = orig(*a, **k)
+        return q, e, None
+    monkeypatch.setattr(om, "project_tokens", bad)
+    _expect_fail(P.pin_brute_force, _tiny(use_output_gate=True))
