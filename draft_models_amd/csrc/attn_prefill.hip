@@ -1,0 +1,301 @@
+// Expanded-form MLA attention for prefill (MLA blog, forward_mha listing):
+// per head, K = [k_nope (from the kv_b expansion) | k_pe (the one shared rope
+// key, read from the latent cache)], V = the expanded v. Flash-style: the key
+// axis is streamed through LDS in 64-key tiles with an online softmax, so the
+// score matrix never reaches HBM. Queries of a sequence see the cached prefix
+// and the new tokens in one pass over [lo, hi), which equals attending to the
+// prefix and to the new tokens separately and merging the two results by
+// their log-sum-exp (the listing's merge_attn_states step).
+//
+// Work split: one workgroup = 4 wavefronts x (16 * QB) queries of one head of
+// one sequence. Scores are computed transposed (S^T = K Q^T) so that each
+// lane ends up holding the probabilities of one query for 8 keys -- exactly
+// the B-operand layout of the P V product -- and no LDS round trip of P is
+// needed. V is stored transposed in LDS ([d][key]) for the A operand of P V.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void visible(const MaskArgs& m, int t, int p, int L, int& lo, int& hi) {
+  if (m.row_lo != nullptr && m.row_hi != nullptr) {
+    lo = min(max(m.row_lo[t], 0), L);
+    hi = min(max(m.row_hi[t], 0), L);
+    return;
+  }
+  if (m.kind == 0) { lo = 0; hi = L; }
+  else if (m.kind == 1) { lo = 0; hi = min(p + 1, L); }
+  else { lo = max(0, p - m.window + 1); hi = min(p + 1, L); }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_frag_g(Frag<T>& f, const T* p, bool ok);
+template <>
+__device__ __forceinline__ void load_frag_g(Frag<bf16>& f, const bf16* p, bool ok) {
+  f.v = ok ? *reinterpret_cast<const bf16x8*>(p) : bf16x8{};
+}
+template <>
+__device__ __forceinline__ void load_frag_g(Frag<float>& f, const float* p, bool ok) {
+  floatx4 lo = ok ? *reinterpret_cast<const floatx4*>(p) : floatx4{};
+  floatx4 hi = ok ? *reinterpret_cast<const floatx4*>(p + 4) : floatx4{};
+  f.v = floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 4 consecutive elements from LDS into fragment slots [o, o+4)
+__device__ __forceinline__ void lds4(Frag<bf16>& f, int o, const bf16* p) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  f.v[o] = v[0]; f.v[o + 1] = v[1]; f.v[o + 2] = v[2]; f.v[o + 3] = v[3];
+}
+__device__ __forceinline__ void lds4(Frag<float>& f, int o, const float* p) {
+  floatx4 v = *reinterpret_cast<const floatx4*>(p);
+  f.v[o] = v[0]; f.v[o + 1] = v[1]; f.v[o + 2] = v[2]; f.v[o + 3] = v[3];
+}
+__device__ __forceinline__ void lds_frag(Frag<bf16>& f, const bf16* p) { f.v = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void lds_frag(Frag<float>& f, const float* p) {
+  floatx4 lo = *reinterpret_cast<const floatx4*>(p), hi = *reinterpret_cast<const floatx4*>(p + 4);
+  f.v = floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename T, int DQK, int DV, int QB>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
+  using V16 = typename Vec16<T>::type;
+  constexpr int BKEY = 64;
+  constexpr int BQ = 64 * QB;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int KROW = DQK + VEC;
+  constexpr int VROW = BKEY + VEC;
+  constexpr int KS = DQK / 32;   // contraction steps of Q K^T
+  constexpr int DB = DV / 16;    // 16-row blocks of O^T
+  static_assert(DQK % 32 == 0 && DV % 16 == 0, "padded head dims");
+  __shared__ __attribute__((aligned(16))) T Ks[BKEY * KROW];
+  __shared__ __attribute__((aligned(16))) T Vt[DV * VROW];
+  __shared__ int kmin_s, kmax_s;
+
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ql = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+  ql = min(max(ql, 0), a.max_q_len);
+  if (qt * BQ >= ql) return;
+  const int pl = min(max(a.prefix_lens[b], 0), a.max_kv_len - ql);
+  const int L = pl + ql;
+  const int t0 = a.cu_seqlens[b];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, g = lane >> 4;
+  const float sl2 = a.scale * kLog2e;
+
+  if (tid == 0) { kmin_s = 0x7fffffff; kmax_s = 0; }
+  __syncthreads();
+  int lo[QB], hi[QB], qi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qi[qb] = qt * BQ + wave * 16 * QB + qb * 16 + lr;
+    lo[qb] = 0; hi[qb] = 0;
+    if (qi[qb] < ql && t0 + qi[qb] < a.total_tokens) visible(a.mask, t0 + qi[qb], pl + qi[qb], L, lo[qb], hi[qb]);
+    if (g == 0 && lo[qb] < hi[qb]) {
+      atomicMin(&kmin_s, lo[qb]);
+      atomicMax(&kmax_s, hi[qb]);
+    }
+  }
+  __syncthreads();
+  const int kbeg = (kmin_s / BKEY) * BKEY, kend = kmax_s;
+
+  // queries in registers (B operand: column = query, 8 contraction elements)
+  Frag<T> qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool qok = qi[qb] < ql && t0 + qi[qb] < a.total_tokens;
+    const T* qrow = reinterpret_cast<const T*>(a.q) + (int64_t)(t0 + (qok ? qi[qb] : 0)) * a.ldq + (int64_t)h * a.qk_head;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int e = ks * 32 + g * 8;
+      load_frag_g(qf[qb][ks], qrow + e, qok && e < a.n + a.r);
+    }
+  }
+
+  floatx4 o[DB][QB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY; l[qb] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const T* kvb = reinterpret_cast<const T*>(a.kv) + (int64_t)b * a.max_kv_len * a.ldkv + (int64_t)h * (a.n + a.dv);
+  const T* cache = reinterpret_cast<const T*>(a.cache);
+  const int E = a.c + a.r;
+  constexpr int KVPR = DQK / VEC;   // vectors per K row
+  constexpr int VVPR = DV / VEC;    // vectors per V row
+
+  for (int k0 = kbeg; k0 < kend; k0 += BKEY) {
+    // ---- stage K (rows = keys) and V^T (rows = value dims) in LDS
+    for (int v = tid; v < BKEY * KVPR; v += 256) {
+      const int jj = v / KVPR, col = (v % KVPR) * VEC;
+      const int key = k0 + jj;
+      V16 val = {};
+      if (key < kend) {
+        if (col < a.n) {
+          val = *reinterpret_cast<const V16*>(kvb + (int64_t)key * a.ldkv + col);
+        } else if (col < a.n + a.r) {
+          const int blk = a.block_table[(int64_t)b * a.max_blocks + key / a.page];
+          if (blk >= 0 && blk < a.num_blocks)
+            val = *reinterpret_cast<const V16*>(cache + ((int64_t)blk * a.page + key % a.page) * E + a.c + (col - a.n));
+        }
+      }
+      *reinterpret_cast<V16*>(&Ks[jj * KROW + col]) = val;
+    }
+    for (int v = tid; v < BKEY * VVPR; v += 256) {
+      const int jj = v / VVPR, d0 = (v % VVPR) * VEC;
+      const int key = k0 + jj;
+      V16 val = {};
+      if (key < kend && d0 < a.dv) val = *reinterpret_cast<const V16*>(kvb + (int64_t)key * a.ldkv + a.n + d0);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) Vt[(d0 + e) * VROW + jj] = val[e];
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T : s[kb][qb][i] is key k0 + 16 kb + 4 g + i, query lr of block qb
+    floatx4 s[4][QB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        Frag<T> kf;
+        lds_frag(kf, &Ks[(kb * 16 + lr) * KROW + ks * 32 + g * 8]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16(kf, qf[qb][ks], s[kb][qb]);
+      }
+    }
+
+    // ---- online softmax (log2 domain), per query
+    Frag<T> pf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + kb * 16 + g * 4 + i;
+          const bool vis = key >= lo[qb] && key < hi[qb];
+          const float x = vis ? s[kb][qb][i] * sl2 : -INFINITY;
+          s[kb][qb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[qb], mx);
+      float alpha = 1.f, sum = 0.f;
+      if (mnew != -INFINITY) {
+        alpha = exp2f(m[qb] - mnew);  // m = -inf -> 0
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = exp2f(s[kb][qb][i] - mnew);  // masked -> 0
+            s[kb][qb][i] = p;
+            sum += p;
+          }
+        m[qb] = mnew;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l[qb] = l[qb] * alpha + sum;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d][qb] *= alpha;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[qb][k2].v[e] = from_f32<T>(s[2 * k2][qb][e]);
+          pf[qb][k2].v[4 + e] = from_f32<T>(s[2 * k2 + 1][qb][e]);
+        }
+    }
+
+    // ---- O^T += V^T P^T  (keys of step k2 for lane group g: 32k2 + 4g + {0..3}, 32k2 + 16 + 4g + {0..3})
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        Frag<T> vf;
+        const T* row = &Vt[(d * 16 + lr) * VROW + k2 * 32 + g * 4];
+        lds4(vf, 0, row);
+        lds4(vf, 4, row + 16);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma16(vf, pf[qb][k2], o[d][qb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds O[query lr][d .. d+3], d = 16 db + 4 g
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qi[qb] >= ql) continue;
+    const int t = t0 + qi[qb];
+    if (t >= a.total_tokens) continue;
+    const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+    T* orow = reinterpret_cast<T*>(a.out) + (int64_t)t * a.ldo + (int64_t)h * a.dv;
+    const T* grow = a.gate ? reinterpret_cast<const T*>(a.gate) + (int64_t)t * a.ldg + (int64_t)h * a.dv : nullptr;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const int d0 = d * 16 + g * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (d0 + i >= a.dv) break;
+        float v = o[d][qb][i] * inv;
+        if (grow) v *= sigmoidf(to_f32(grow[d0 + i]));
+        orow[d0 + i] = from_f32<T>(v);
+      }
+    }
+  }
+}
+
+template <typename T, int DQK, int DV>
+hipError_t launch_dims(const PrefillAttnArgs& a, hipStream_t s) {
+  // one 16-query block per wave for short query runs (draft blocks), two otherwise
+  const int QB = a.max_q_len <= 64 ? 1 : 2;
+  const int BQ = 64 * QB;
+  dim3 grid((a.max_q_len + BQ - 1) / BQ, a.H, a.batch);
+  if (QB == 1) hipLaunchKernelGGL((prefill_attn_kernel<T, DQK, DV, 1>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((prefill_attn_kernel<T, DQK, DV, 2>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const PrefillAttnArgs& a, hipStream_t s) {
+  const int dqk = a.n + a.r, dv = a.dv;
+  if (dqk <= 32 && dv <= 16) return launch_dims<T, 32, 16>(a, s);
+  if (dqk <= 64 && dv <= 32) return launch_dims<T, 64, 32>(a, s);
+  if (dqk <= 192 && dv <= 128) return launch_dims<T, 192, 128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16) {
+  const int vec = is_bf16 ? 8 : 4;
+  if (a.n + a.r > 192 || a.dv > 128) return "prefill attention: head dims above 192 (q/k) or 128 (v) are not supported";
+  if (a.n % vec || a.r % vec || a.dv % vec || a.c % vec) return "prefill attention: n, r, dv and c must be 16-byte multiples";
+  if ((a.n + a.r) % 8) return "prefill attention: n + r must be a multiple of 8";
+  if (a.ldq % vec || a.qk_head % vec || a.ldkv % vec) return "prefill attention: row strides must be 16-byte multiples";
+  return nullptr;
+}
+
+hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s) {
+  if (a.batch <= 0 || a.max_q_len <= 0) return hipSuccess;
+  return is_bf16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace mla

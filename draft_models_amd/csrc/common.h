@@ -1,0 +1,69 @@
+// Shared device-side definitions for the gfx950 MLA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// 8-element MFMA operand fragment of one lane: 8 consecutive elements of the
+// contraction axis. bf16: one 16-byte register quad; fp32: two.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { floatx8 v; };
+
+__device__ __forceinline__ void load_frag(Frag<bf16>& f, const bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load_frag(Frag<float>& f, const float* p) {
+  f.v = *reinterpret_cast<const floatx8*>(p);
+}
+
+// acc[16x16] += A(16 rows x 32) * B(32 x 16 cols). Lane l supplies row/col
+// (l % 16) and contraction elements 8 * (l / 16) .. + 7 of both operands; the
+// result holds rows 4 * (l / 16) + i, column l % 16 in acc[i]. The hardware's
+// own order of the contraction elements does not matter as long as A and B
+// use the same lane/element -> k assignment, which they do.
+__device__ __forceinline__ floatx4 mfma16(const Frag<bf16>& a, const Frag<bf16>& b, floatx4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(const Frag<float>& a, const Frag<float>& b, floatx4 acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// 16-byte vector of T.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct Vec16<float> { typedef floatx4 type; static constexpr int n = 4; };
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace mla

@@ -1,0 +1,71 @@
+// Host-side interface of the non-GEMM kernels of the MLA forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct RopeCacheArgs {
+  void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // q [T, H, n + r] rows of stride ldq
+  const void* kv = nullptr; int64_t ldkv = 0;            // [T, c + r] rows of stride ldkv
+  const void* gamma_kv = nullptr;                         // [c]
+  void* cache = nullptr;
+  const int32_t* block_table = nullptr;
+  int num_blocks = 0, max_blocks = 0, page = 0;
+  const float* rope_cos = nullptr; const float* rope_sin = nullptr;  // [max_seq_len, r/2]
+  int H = 0, n = 0, r = 0, c = 0;
+  int interleaved = 0;
+  float eps = 0.f;
+  // token -> (sequence, position)
+  int decode = 0;
+  const int32_t* seq_lens = nullptr;     // decode
+  const int32_t* cu_seqlens = nullptr;   // prefill
+  const int32_t* prefix_lens = nullptr;  // prefill
+  int max_q_len = 0, max_kv_len = 0, max_seq_len = 0, total_tokens = 0;
+};
+hipError_t rope_cache_launch(const RopeCacheArgs& a, bool is_bf16, int grid_x, int batch, hipStream_t s);
+
+// Visible-key rule shared by the attention kernels.
+struct MaskArgs {
+  int kind = 0, window = 0;
+  const int32_t* row_lo = nullptr; const int32_t* row_hi = nullptr;  // prefill, optional
+};
+
+struct PrefillAttnArgs {
+  const void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // roped q [T, H, n + r]
+  const void* kv = nullptr; int64_t ldkv = 0;                  // expanded [B * max_kv_len, H, n + dv]
+  const void* cache = nullptr;                                  // k_pe from the paged cache
+  const int32_t* block_table = nullptr;
+  int num_blocks = 0, max_blocks = 0, page = 0;
+  const int32_t* cu_seqlens = nullptr; const int32_t* prefix_lens = nullptr;
+  int batch = 0, max_q_len = 0, max_kv_len = 0, total_tokens = 0;
+  int H = 0, n = 0, r = 0, c = 0, dv = 0;
+  float scale = 0.f;
+  MaskArgs mask;
+  void* out = nullptr; int64_t ldo = 0;             // [T, H * dv]
+  const void* gate = nullptr; int64_t ldg = 0;      // raw gate pre-activation [T, H * dv] or null
+};
+hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s);
+const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16);
+
+struct DecodeAttnArgs {
+  const void* ql = nullptr; int64_t ldql = 0;       // latent query q_nope W_UK [B, H, c], row stride ldql
+  const void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // roped q (rope part at offset n)
+  const void* cache = nullptr;
+  const int32_t* block_table = nullptr;
+  int num_blocks = 0, max_blocks = 0, page = 0;
+  const int32_t* seq_lens = nullptr;
+  int max_seq_len = 0, batch = 0;
+  int H = 0, n = 0, r = 0, c = 0;
+  float scale = 0.f;
+  MaskArgs mask;
+  int chunk = 0, splits = 0;                        // keys per split, splits per sequence
+  float* part_o = nullptr;                          // [B, splits, H, c]
+  float* part_lse = nullptr;                        // [B, splits, H]
+  void* o_lat = nullptr;                            // [B, H, c] combined latent output
+};
+hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
+const char* decode_attn_check(const DecodeAttnArgs& a, bool is_bf16);
+
+}  // namespace mla

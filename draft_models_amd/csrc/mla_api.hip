@@ -1,0 +1,483 @@
+// C ABI of the MLA forward: context creation (validation, weight repacking,
+// workspaces) and the stream-ordered launch sequences of the expanded prefill
+// and the absorbed decode.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mla.h"
+#include "common.h"
+#include "gemm.h"
+#include "kernels.h"
+
+using namespace mla;
+
+struct mla_ctx {
+  mla_config cfg;
+  bool bf16 = true;
+  int esz = 2;
+  int H = 0, n = 0, r = 0, c = 0, dv = 0, ql = 0, hid = 0, E = 0, qkh = 0;
+  float scale = 0.f;
+  int device = 0;
+  // owned, repacked weights
+  void* W1 = nullptr;  // fused first projection [N1, hid] = [q_a | q ; kv_a ; g]
+  int N1 = 0, off_q = 0, off_kv = 0, off_g = -1;
+  void* Wqb = nullptr;     // q_b_proj with the q_a_layernorm gain folded into its columns
+  void* Wkvb = nullptr;    // kv_b_proj [H (n + dv), c]
+  void* Wuk_t = nullptr;   // per head W_UK^T [H][c][n]
+  void* Wo = nullptr;      // o_proj [hid, H dv]
+  void* gamma_kv = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  // workspaces
+  void* buf1 = nullptr;    // [max_tokens, N1]
+  void* qbuf = nullptr;    // [max_tokens, H (n + r)]  (low-rank Q path)
+  void* kvexp = nullptr;   // [max_prefill_kv, H (n + dv)]
+  void* attn = nullptr;    // [max_tokens, H dv]
+  void* qlat = nullptr;    // [max_batch, H, c]
+  void* olat = nullptr;    // [max_batch, H, c]
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  int max_splits = 32;
+  float* gemm_ws = nullptr;
+  int64_t gemm_ws_elems = 0;
+  std::vector<void*> allocs;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t _e = (expr);                                                        \
+    if (_e != hipSuccess)                                                          \
+      return fail(MLA_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
+  } while (0)
+
+__global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst, int64_t rows, int cols, int bf) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * cols) return;
+  const int col = (int)(i % cols);
+  if (bf) {
+    const bf16* s = reinterpret_cast<const bf16*>(src);
+    const bf16* g = reinterpret_cast<const bf16*>(gamma);
+    reinterpret_cast<bf16*>(dst)[i] = (bf16)((float)s[i] * (float)g[col]);
+  } else {
+    const float* s = reinterpret_cast<const float*>(src);
+    const float* g = reinterpret_cast<const float*>(gamma);
+    reinterpret_cast<float*>(dst)[i] = s[i] * g[col];
+  }
+}
+
+// Wuk_t[h][cc][nn] = kv_b_proj[h (n + dv) + nn][cc]
+__global__ void wuk_transpose_kernel(const void* wkvb, void* out, int H, int n, int dv, int c, int bf) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)H * c * n;
+  if (i >= total) return;
+  const int nn = (int)(i % n);
+  const int cc = (int)((i / n) % c);
+  const int h = (int)(i / ((int64_t)n * c));
+  const int64_t src = ((int64_t)h * (n + dv) + nn) * c + cc;
+  if (bf) reinterpret_cast<bf16*>(out)[i] = reinterpret_cast<const bf16*>(wkvb)[src];
+  else reinterpret_cast<float*>(out)[i] = reinterpret_cast<const float*>(wkvb)[src];
+}
+
+int dev_alloc(mla_ctx* ctx, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return MLA_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(MLA_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  ctx->allocs.push_back(*p);
+  return MLA_OK;
+}
+
+void free_all(mla_ctx* ctx) {
+  for (void* p : ctx->allocs) (void)hipFree(p);
+  ctx->allocs.clear();
+}
+
+int validate_config(const mla_config* c, const mla_weights* w) {
+  if (!c || !w) return fail(MLA_ERR_INVALID_ARG, "config and weights must not be NULL");
+  if (c->hidden_size <= 0 || c->num_heads <= 0 || c->kv_lora_rank <= 0 || c->qk_nope_head_dim <= 0 ||
+      c->qk_rope_head_dim <= 0 || c->v_head_dim <= 0 || c->q_lora_rank < 0)
+    return fail(MLA_ERR_DIMS, "every model dimension must be positive (q_lora_rank >= 0)");
+  if (c->qk_rope_head_dim % 2) return fail(MLA_ERR_DIMS, "qk_rope_head_dim must be even (RoPE rotates pairs)");
+  if (c->dtype != MLA_DTYPE_F32 && c->dtype != MLA_DTYPE_BF16) return fail(MLA_ERR_INVALID_ARG, "unknown dtype");
+  if (c->rope_style != MLA_ROPE_NEOX && c->rope_style != MLA_ROPE_INTERLEAVED)
+    return fail(MLA_ERR_INVALID_ARG, "unknown rope_style");
+  if (!(c->rope_theta > 1.0) || !std::isfinite(c->rope_theta)) return fail(MLA_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!(c->rms_norm_eps >= 0.0) || !std::isfinite(c->rms_norm_eps)) return fail(MLA_ERR_INVALID_ARG, "rms_norm_eps must be >= 0");
+  if (!std::isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (c->use_output_gate != 0 && c->use_output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "use_output_gate must be 0 or 1");
+  if (c->page_size <= 0 || c->max_batch <= 0 || c->max_tokens <= 0 || c->max_seq_len <= 0 || c->max_prefill_kv < 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_size, max_batch, max_tokens, max_seq_len must be positive, max_prefill_kv >= 0");
+  const int vec = c->dtype == MLA_DTYPE_BF16 ? 8 : 4;
+  const int n = c->qk_nope_head_dim, r = c->qk_rope_head_dim, kc = c->kv_lora_rank, dv = c->v_head_dim;
+  if (n % vec || r % vec || kc % vec || dv % vec || c->hidden_size % vec || (c->q_lora_rank % vec))
+    return fail(MLA_ERR_UNSUPPORTED, "every dimension must be a multiple of 16 bytes of the dtype");
+  if ((n + r) % 8 || (kc + r) % 8 || kc % 8)
+    return fail(MLA_ERR_UNSUPPORTED, "n + r, c + r and c must be multiples of 8");
+  if (n + r > 192 || dv > 128 || kc > 512 || kc + r > 576)
+    return fail(MLA_ERR_UNSUPPORTED, "head dims above n + r = 192, dv = 128, c = 512, c + r = 576 are not supported");
+  if (!w->kv_a_proj_with_mqa || !w->kv_a_layernorm || !w->kv_b_proj || !w->o_proj)
+    return fail(MLA_ERR_INVALID_ARG, "kv_a_proj_with_mqa, kv_a_layernorm, kv_b_proj and o_proj are required");
+  if (c->q_lora_rank > 0 && (!w->q_a_proj || !w->q_a_layernorm || !w->q_b_proj))
+    return fail(MLA_ERR_INVALID_ARG, "q_lora_rank > 0 needs q_a_proj, q_a_layernorm and q_b_proj");
+  if (c->q_lora_rank == 0 && !w->q_proj) return fail(MLA_ERR_INVALID_ARG, "q_lora_rank == 0 needs q_proj");
+  if (c->use_output_gate && !w->g_proj) return fail(MLA_ERR_INVALID_ARG, "use_output_gate needs g_proj");
+  return MLA_OK;
+}
+
+int check_mask(int kind, int window) {
+  if (kind != MLA_MASK_FULL && kind != MLA_MASK_CAUSAL && kind != MLA_MASK_SLIDING)
+    return fail(MLA_ERR_INVALID_ARG, "unknown mask kind");
+  if (kind == MLA_MASK_SLIDING && window < 0) return fail(MLA_ERR_INVALID_ARG, "window must be >= 0");
+  return MLA_OK;
+}
+
+int run_gemm(mla_ctx* ctx, const GemmArgs& g, hipStream_t s) {
+  if (const char* m = gemm_check(g, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
+  HIP_TRY(gemm_launch(g, ctx->bf16, ctx->gemm_ws, ctx->gemm_ws_elems, s));
+  return MLA_OK;
+}
+
+// fused first projection and (low-rank path) the q_b projection with the
+// q_a RMSNorm folded into its epilogue; fills q / ldq
+int project(mla_ctx* ctx, const void* x, int T, hipStream_t s, void** q, int64_t* ldq) {
+  GemmArgs g1;
+  g1.A = x; g1.lda = ctx->hid;
+  g1.W = ctx->W1; g1.ldw = ctx->hid;
+  g1.C = ctx->buf1; g1.ldc = ctx->N1;
+  g1.M = T; g1.N = ctx->N1; g1.K = ctx->hid;
+  if (int e = run_gemm(ctx, g1, s)) return e;
+  if (ctx->ql > 0) {
+    GemmArgs g2;
+    g2.A = ctx->buf1; g2.lda = ctx->N1;
+    g2.W = ctx->Wqb; g2.ldw = ctx->ql;
+    g2.C = ctx->qbuf; g2.ldc = (int64_t)ctx->H * ctx->qkh;
+    g2.M = T; g2.N = ctx->H * ctx->qkh; g2.K = ctx->ql;
+    g2.epi = EPI_ROWNORM; g2.eps = (float)ctx->cfg.rms_norm_eps;
+    if (int e = run_gemm(ctx, g2, s)) return e;
+    *q = ctx->qbuf;
+    *ldq = (int64_t)ctx->H * ctx->qkh;
+  } else {
+    *q = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_q * ctx->esz;
+    *ldq = ctx->N1;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_err.c_str(); }
+
+int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, mla_ctx** out) {
+  if (!out) return fail(MLA_ERR_INVALID_ARG, "out must not be NULL");
+  *out = nullptr;
+  if (int e = validate_config(cfg, w)) return e;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  mla_ctx* ctx = new mla_ctx();
+  ctx->cfg = *cfg;
+  ctx->bf16 = cfg->dtype == MLA_DTYPE_BF16;
+  ctx->esz = ctx->bf16 ? 2 : 4;
+  ctx->H = cfg->num_heads; ctx->n = cfg->qk_nope_head_dim; ctx->r = cfg->qk_rope_head_dim;
+  ctx->c = cfg->kv_lora_rank; ctx->dv = cfg->v_head_dim; ctx->ql = cfg->q_lora_rank;
+  ctx->hid = cfg->hidden_size; ctx->E = ctx->c + ctx->r; ctx->qkh = ctx->n + ctx->r;
+  ctx->scale = cfg->softmax_scale > 0 ? (float)cfg->softmax_scale : (float)(1.0 / std::sqrt((double)ctx->qkh));
+  const int H = ctx->H, esz = ctx->esz;
+  const int64_t hid = ctx->hid;
+
+  auto bail = [&](int e) {
+    free_all(ctx);
+    delete ctx;
+    return e;
+  };
+  if (hipGetDevice(&ctx->device) != hipSuccess) return bail(fail(MLA_ERR_HIP, "hipGetDevice failed"));
+
+  // fused first projection rows: [q_a_proj | q_proj] ; kv_a_proj_with_mqa ; g_proj
+  const int nq = ctx->ql > 0 ? ctx->ql : H * ctx->qkh;
+  ctx->off_q = 0;
+  ctx->off_kv = nq;
+  ctx->N1 = nq + ctx->E;
+  if (cfg->use_output_gate) {
+    ctx->off_g = ctx->N1;
+    ctx->N1 += H * ctx->dv;
+  }
+  int e;
+  if ((e = dev_alloc(ctx, &ctx->W1, (size_t)ctx->N1 * hid * esz))) return bail(e);
+  {
+    char* dst = static_cast<char*>(ctx->W1);
+    const void* qsrc = ctx->ql > 0 ? w->q_a_proj : w->q_proj;
+    if (hipMemcpyAsync(dst, qsrc, (size_t)nq * hid * esz, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(dst + (size_t)ctx->off_kv * hid * esz, w->kv_a_proj_with_mqa, (size_t)ctx->E * hid * esz,
+                       hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        (cfg->use_output_gate &&
+         hipMemcpyAsync(dst + (size_t)ctx->off_g * hid * esz, w->g_proj, (size_t)H * ctx->dv * hid * esz,
+                        hipMemcpyDeviceToDevice, s) != hipSuccess))
+      return bail(fail(MLA_ERR_HIP, "copy of the first projection weights failed"));
+  }
+  if (ctx->ql > 0) {
+    const int64_t rows = (int64_t)H * ctx->qkh;
+    if ((e = dev_alloc(ctx, &ctx->Wqb, (size_t)rows * ctx->ql * esz))) return bail(e);
+    const int64_t tot = rows * ctx->ql;
+    hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->q_b_proj,
+                       w->q_a_layernorm, ctx->Wqb, rows, ctx->ql, (int)ctx->bf16);
+    if (hipGetLastError() != hipSuccess) return bail(fail(MLA_ERR_HIP, "q_b_proj repack failed"));
+  }
+  const int64_t kvb_rows = (int64_t)H * (ctx->n + ctx->dv);
+  if ((e = dev_alloc(ctx, &ctx->Wkvb, (size_t)kvb_rows * ctx->c * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->Wuk_t, (size_t)H * ctx->c * ctx->n * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->Wo, (size_t)hid * H * ctx->dv * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->gamma_kv, (size_t)ctx->c * esz))) return bail(e);
+  if (hipMemcpyAsync(ctx->Wkvb, w->kv_b_proj, (size_t)kvb_rows * ctx->c * esz, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(ctx->Wo, w->o_proj, (size_t)hid * H * ctx->dv * esz, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(ctx->gamma_kv, w->kv_a_layernorm, (size_t)ctx->c * esz, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return bail(fail(MLA_ERR_HIP, "weight copy failed"));
+  {
+    const int64_t tot = (int64_t)H * ctx->c * ctx->n;
+    hipLaunchKernelGGL(wuk_transpose_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->kv_b_proj,
+                       ctx->Wuk_t, H, ctx->n, ctx->dv, ctx->c, (int)ctx->bf16);
+    if (hipGetLastError() != hipSuccess) return bail(fail(MLA_ERR_HIP, "W_UK repack failed"));
+  }
+
+  // RoPE table: fp64 angles rounded once to fp32 cos/sin
+  {
+    const int half = ctx->r / 2;
+    const size_t cnt = (size_t)cfg->max_seq_len * half;
+    std::vector<float> hc(cnt), hs(cnt);
+    for (int p = 0; p < cfg->max_seq_len; ++p)
+      for (int j = 0; j < half; ++j) {
+        const double ang = (double)p * std::pow(cfg->rope_theta, -2.0 * j / (double)ctx->r);
+        hc[(size_t)p * half + j] = (float)std::cos(ang);
+        hs[(size_t)p * half + j] = (float)std::sin(ang);
+      }
+    void *pc, *ps;
+    if ((e = dev_alloc(ctx, &pc, cnt * sizeof(float)))) return bail(e);
+    if ((e = dev_alloc(ctx, &ps, cnt * sizeof(float)))) return bail(e);
+    ctx->rope_cos = static_cast<float*>(pc);
+    ctx->rope_sin = static_cast<float*>(ps);
+    if (hipMemcpyAsync(pc, hc.data(), cnt * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(ps, hs.data(), cnt * sizeof(float), hipMemcpyHostToDevice, s) != hipSuccess)
+      return bail(fail(MLA_ERR_HIP, "RoPE table upload failed"));
+    // the host vectors must outlive the asynchronous copies
+    if (hipStreamSynchronize(s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "stream synchronize failed"));
+  }
+
+  // workspaces
+  const int64_t T = cfg->max_tokens, B = cfg->max_batch;
+  if ((e = dev_alloc(ctx, &ctx->buf1, (size_t)T * ctx->N1 * esz))) return bail(e);
+  if (ctx->ql > 0 && (e = dev_alloc(ctx, &ctx->qbuf, (size_t)T * H * ctx->qkh * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->kvexp, (size_t)cfg->max_prefill_kv * kvb_rows * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->attn, (size_t)T * H * ctx->dv * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->qlat, (size_t)B * H * ctx->c * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->olat, (size_t)B * H * ctx->c * esz))) return bail(e);
+  void* p;
+  if ((e = dev_alloc(ctx, &p, (size_t)B * ctx->max_splits * H * ctx->c * sizeof(float)))) return bail(e);
+  ctx->part_o = static_cast<float*>(p);
+  if ((e = dev_alloc(ctx, &p, (size_t)B * ctx->max_splits * H * sizeof(float)))) return bail(e);
+  ctx->part_lse = static_cast<float*>(p);
+  ctx->gemm_ws_elems = (int64_t)16 << 20;
+  if ((e = dev_alloc(ctx, &p, (size_t)ctx->gemm_ws_elems * sizeof(float)))) return bail(e);
+  ctx->gemm_ws = static_cast<float*>(p);
+
+  if (hipStreamSynchronize(s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "stream synchronize failed"));
+  *out = ctx;
+  return MLA_OK;
+}
+
+int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t total_tokens,
+                         const int32_t* cu_seqlens_q, const int32_t* prefix_lens, int32_t max_q_len,
+                         int32_t max_kv_len, void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks, int32_t mask_kind, int32_t window, const int32_t* row_lo,
+                         const int32_t* row_hi, void* out, void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (!x || !cu_seqlens_q || !prefix_lens || !kv_cache || !block_table || !out)
+    return fail(MLA_ERR_INVALID_ARG, "x, cu_seqlens_q, prefix_lens, kv_cache, block_table and out must not be NULL");
+  if (batch <= 0 || total_tokens <= 0 || max_q_len <= 0 || max_kv_len <= 0 || num_blocks <= 0 || max_blocks <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch, total_tokens, max_q_len, max_kv_len, num_blocks, max_blocks must be positive");
+  if ((row_lo == nullptr) != (row_hi == nullptr)) return fail(MLA_ERR_INVALID_ARG, "row_lo and row_hi go together");
+  if (int e = check_mask(mask_kind, window)) return e;
+  const mla_config& c = ctx->cfg;
+  if (max_q_len > total_tokens || max_kv_len < max_q_len)
+    return fail(MLA_ERR_INVALID_ARG, "need max_q_len <= total_tokens and max_kv_len >= max_q_len");
+  if (batch > c.max_batch || total_tokens > c.max_tokens || max_kv_len > c.max_seq_len)
+    return fail(MLA_ERR_CAPACITY, "batch, total_tokens or max_kv_len above the init limits");
+  if ((int64_t)batch * max_kv_len > c.max_prefill_kv)
+    return fail(MLA_ERR_CAPACITY, "batch * max_kv_len exceeds max_prefill_kv");
+  if ((int64_t)max_blocks * c.page_size < max_kv_len)
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks * page_size must cover max_kv_len");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  void* q;
+  int64_t ldq;
+  if (int e = project(ctx, x, total_tokens, s, &q, &ldq)) return e;
+
+  RopeCacheArgs rc;
+  rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
+  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.gamma_kv = ctx->gamma_kv;
+  rc.cache = kv_cache; rc.block_table = block_table;
+  rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
+  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
+  rc.H = ctx->H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
+  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  rc.eps = (float)c.rms_norm_eps;
+  rc.decode = 0; rc.cu_seqlens = cu_seqlens_q; rc.prefix_lens = prefix_lens;
+  rc.max_q_len = max_q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
+  rc.total_tokens = total_tokens;
+  HIP_TRY(rope_cache_launch(rc, ctx->bf16, max_q_len, batch, s));
+
+  // expand every visible latent (prefix and new) through kv_b_proj
+  GemmArgs gk;
+  gk.gather = true;
+  gk.ga.cache = kv_cache; gk.ga.block_table = block_table; gk.ga.cu_seqlens = cu_seqlens_q;
+  gk.ga.prefix_lens = prefix_lens; gk.ga.batch = batch; gk.ga.max_kv_len = max_kv_len;
+  gk.ga.page = c.page_size; gk.ga.max_blocks = max_blocks; gk.ga.num_blocks = num_blocks;
+  gk.ga.entry = ctx->E; gk.ga.max_q_len = max_q_len;
+  gk.A = kv_cache; gk.lda = ctx->E;
+  gk.W = ctx->Wkvb; gk.ldw = ctx->c;
+  gk.C = ctx->kvexp; gk.ldc = (int64_t)ctx->H * (ctx->n + ctx->dv);
+  gk.M = batch * max_kv_len; gk.N = ctx->H * (ctx->n + ctx->dv); gk.K = ctx->c;
+  if (int e = run_gemm(ctx, gk, s)) return e;
+
+  PrefillAttnArgs pa;
+  pa.q = q; pa.ldq = ldq; pa.qk_head = ctx->qkh;
+  pa.kv = ctx->kvexp; pa.ldkv = (int64_t)ctx->H * (ctx->n + ctx->dv);
+  pa.cache = kv_cache; pa.block_table = block_table;
+  pa.num_blocks = num_blocks; pa.max_blocks = max_blocks; pa.page = c.page_size;
+  pa.cu_seqlens = cu_seqlens_q; pa.prefix_lens = prefix_lens;
+  pa.batch = batch; pa.max_q_len = max_q_len; pa.max_kv_len = max_kv_len; pa.total_tokens = total_tokens;
+  pa.H = ctx->H; pa.n = ctx->n; pa.r = ctx->r; pa.c = ctx->c; pa.dv = ctx->dv;
+  pa.scale = ctx->scale;
+  pa.mask.kind = mask_kind; pa.mask.window = window; pa.mask.row_lo = row_lo; pa.mask.row_hi = row_hi;
+  pa.out = ctx->attn; pa.ldo = (int64_t)ctx->H * ctx->dv;
+  if (ctx->off_g >= 0) {
+    pa.gate = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    pa.ldg = ctx->N1;
+  }
+  if (const char* m = prefill_attn_check(pa, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
+  HIP_TRY(prefill_attn_launch(pa, ctx->bf16, s));
+
+  GemmArgs go;
+  go.A = ctx->attn; go.lda = (int64_t)ctx->H * ctx->dv;
+  go.W = ctx->Wo; go.ldw = (int64_t)ctx->H * ctx->dv;
+  go.C = out; go.ldc = ctx->hid;
+  go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
+  return run_gemm(ctx, go, s);
+}
+
+int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+                        const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t mask_kind, int32_t window, void* out, void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (!kv_cache) return fail(MLA_ERR_INVALID_ARG, "kv_cache must not be NULL (decode reads the latent cache)");
+  if (!x || !block_table || !seq_lens || !out)
+    return fail(MLA_ERR_INVALID_ARG, "x, block_table, seq_lens and out must not be NULL");
+  if (batch <= 0 || num_blocks <= 0 || max_blocks <= 0 || max_seq_len <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch, num_blocks, max_blocks and max_seq_len must be positive");
+  if (int e = check_mask(mask_kind, window)) return e;
+  const mla_config& c = ctx->cfg;
+  if (batch > c.max_batch || batch > c.max_tokens || max_seq_len > c.max_seq_len)
+    return fail(MLA_ERR_CAPACITY, "batch or max_seq_len above the init limits");
+  if ((int64_t)max_blocks * c.page_size < max_seq_len)
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks * page_size must cover max_seq_len");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int H = ctx->H;
+
+  void* q;
+  int64_t ldq;
+  if (int e = project(ctx, x, batch, s, &q, &ldq)) return e;
+
+  RopeCacheArgs rc;
+  rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
+  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.gamma_kv = ctx->gamma_kv;
+  rc.cache = kv_cache; rc.block_table = block_table;
+  rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
+  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
+  rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
+  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  rc.eps = (float)c.rms_norm_eps;
+  rc.decode = 1; rc.seq_lens = seq_lens; rc.max_seq_len = max_seq_len; rc.total_tokens = batch;
+  HIP_TRY(rope_cache_launch(rc, ctx->bf16, 1, batch, s));
+
+  // W_UK absorption: ql_nope[b, h] = q_nope[b, h] . W_UK^T[h]   (per head: [B, n] x [n, c])
+  GemmArgs ga;
+  ga.A = q; ga.lda = ldq; ga.sA = ctx->qkh;
+  ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
+  ga.C = ctx->qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
+  ga.M = batch; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
+  if (int e = run_gemm(ctx, ga, s)) return e;
+
+  // split-KV sizing from the longest visible range (keys per split a multiple of 32)
+  const int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+  const int groups = (H + 63) / 64;
+  int want = (512 + batch * groups - 1) / (batch * groups);
+  want = std::max(1, std::min(want, ctx->max_splits));
+  int chunk = std::max(1, (max_vis + want - 1) / want);
+  chunk = std::max(64, ((chunk + 31) / 32) * 32);
+  const int splits = std::max(1, std::min(ctx->max_splits, (max_vis + chunk - 1) / chunk));
+  if ((int64_t)splits * chunk < max_vis) chunk = ((max_vis + splits - 1) / splits + 31) / 32 * 32;
+
+  DecodeAttnArgs da;
+  da.ql = ctx->qlat; da.ldql = (int64_t)H * ctx->c;
+  da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
+  da.cache = kv_cache; da.block_table = block_table;
+  da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
+  da.seq_lens = seq_lens; da.max_seq_len = max_seq_len; da.batch = batch;
+  da.H = H; da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
+  da.scale = ctx->scale;
+  da.mask.kind = mask_kind; da.mask.window = window;
+  da.chunk = chunk; da.splits = splits;
+  da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
+  da.o_lat = ctx->olat;
+  if (const char* m = decode_attn_check(da, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
+  HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
+
+  // W_UV: out_v[b, h] = o_lat[b, h] . W_UV[h]^T (per head: [B, c] x [c, dv]), gated
+  GemmArgs gv;
+  gv.A = ctx->olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
+  gv.W = static_cast<char*>(ctx->Wkvb) + (size_t)ctx->n * ctx->c * ctx->esz;
+  gv.ldw = ctx->c; gv.sW = (int64_t)(ctx->n + ctx->dv) * ctx->c;
+  gv.C = ctx->attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
+  gv.M = batch; gv.N = ctx->dv; gv.K = ctx->c; gv.batch = H;
+  if (ctx->off_g >= 0) {
+    gv.epi = EPI_GATE;
+    gv.G = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    gv.ldg = ctx->N1; gv.sG = ctx->dv;
+  }
+  if (int e = run_gemm(ctx, gv, s)) return e;
+
+  GemmArgs go;
+  go.A = ctx->attn; go.lda = (int64_t)H * ctx->dv;
+  go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
+  go.C = out; go.ldc = ctx->hid;
+  go.M = batch; go.N = ctx->hid; go.K = H * ctx->dv;
+  return run_gemm(ctx, go, s);
+}
+
+void mla_free(mla_ctx* ctx) {
+  if (!ctx) return;
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  free_all(ctx);
+  (void)hipSetDevice(cur);
+  delete ctx;
+}
+
+}  // extern "C"

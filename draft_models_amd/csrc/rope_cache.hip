@@ -1,0 +1,97 @@
+// Latent RMSNorm, partial RoPE and the cache write of the new tokens.
+//
+// For each new token (MLA blog, MultiHeadLatentAttentionWrapper.forward and
+// do_kv_cache_update listings): the latent kv_c is RMS-normalised with the
+// kv_a_layernorm gain, k_pe and the rope part q[..., n:] of every head are
+// rotated at the token's logical position, and the entry
+// [RMSNorm(kv_c) | RoPE(k_pe)] is stored into its paged-cache slot. The write
+// happens before any attention kernel of the same call runs (stream order),
+// so each query sees its own entry.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
+  const int b = blockIdx.y, i = blockIdx.x;
+  int t, pos;
+  if (a.decode) {
+    if (i != 0) return;
+    const int L = a.seq_lens[b];
+    if (L < 1) return;
+    t = b;
+    pos = min(L, a.max_seq_len) - 1;
+  } else {
+    int ql = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    ql = min(max(ql, 0), a.max_q_len);
+    if (i >= ql) return;
+    t = a.cu_seqlens[b] + i;
+    if (t < 0 || t >= a.total_tokens) return;
+    const int pl = min(max(a.prefix_lens[b], 0), a.max_kv_len - ql);
+    pos = pl + i;
+  }
+  const int half = a.r / 2;
+  const float* cs = a.rope_cos + (int64_t)pos * half;
+  const float* sn = a.rope_sin + (int64_t)pos * half;
+  auto pair = [&](int j, int& ia, int& ib) {
+    if (a.interleaved) { ia = 2 * j; ib = 2 * j + 1; }
+    else { ia = j; ib = j + half; }
+  };
+
+  // rotate q[t, h, n:] for every head, in place
+  T* q = reinterpret_cast<T*>(a.q) + (int64_t)t * a.ldq;
+  for (int p = threadIdx.x; p < a.H * half; p += 256) {
+    const int h = p / half, j = p % half;
+    int ia, ib;
+    pair(j, ia, ib);
+    T* qh = q + (int64_t)h * a.qk_head + a.n;
+    const float xa = to_f32(qh[ia]), xb = to_f32(qh[ib]);
+    qh[ia] = from_f32<T>(xa * cs[j] - xb * sn[j]);
+    qh[ib] = from_f32<T>(xa * sn[j] + xb * cs[j]);
+  }
+
+  // RMSNorm of the latent
+  const T* kv = reinterpret_cast<const T*>(a.kv) + (int64_t)t * a.ldkv;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < a.c; e += 256) {
+    const float f = to_f32(kv[e]);
+    ss += f * f;
+  }
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float scale = rsqrtf(tot / (float)a.c + a.eps);
+
+  // slot of logical position pos
+  if (pos / a.page >= a.max_blocks) return;
+  const int blk = a.block_table[(int64_t)b * a.max_blocks + pos / a.page];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  T* dst = reinterpret_cast<T*>(a.cache) + ((int64_t)blk * a.page + pos % a.page) * (a.c + a.r);
+  const T* gamma = reinterpret_cast<const T*>(a.gamma_kv);
+  for (int e = threadIdx.x; e < a.c; e += 256) dst[e] = from_f32<T>(to_f32(kv[e]) * scale * to_f32(gamma[e]));
+  const T* kpe = kv + a.c;
+  for (int j = threadIdx.x; j < half; j += 256) {
+    int ia, ib;
+    pair(j, ia, ib);
+    const float xa = to_f32(kpe[ia]), xb = to_f32(kpe[ib]);
+    dst[a.c + ia] = from_f32<T>(xa * cs[j] - xb * sn[j]);
+    dst[a.c + ib] = from_f32<T>(xa * sn[j] + xb * cs[j]);
+  }
+}
+
+}  // namespace
+
+hipError_t rope_cache_launch(const RopeCacheArgs& a, bool is_bf16, int grid_x, int batch, hipStream_t s) {
+  if (grid_x <= 0 || batch <= 0) return hipSuccess;
+  dim3 grid(grid_x, batch);
+  if (is_bf16) hipLaunchKernelGGL(rope_cache_kernel<bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(rope_cache_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

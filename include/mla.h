@@ -1,0 +1,190 @@
+/*
+ * mla.h — C ABI of the MI355X (gfx950) Multi-head Latent Attention forward.
+ *
+ * The operation is the MLA layer described by the "MLA(Multi-Head Latent
+ * Attention)" blog walk-through of vLLM's MLA code (the DeepseekV2MLAAttention,
+ * MultiHeadLatentAttentionWrapper.forward, MLAAttention.forward,
+ * do_kv_cache_update, forward_mha and forward_mqa listings) with the options of
+ * SpecForge PR "Add config-selectable MLA draft attention" (Summary: optional
+ * low-rank Q, shared compressed KV latent, partial interleaved or NeoX RoPE,
+ * optional output gate, full/sliding masks; Structure: fully-masked-query
+ * zeroing and o_proj):
+ *
+ *   q     = (q_lora ? RMSNorm(x W_qa^T) W_qb^T : x W_q^T)      viewed [T, H, n + r]
+ *   kv    = x W_kva^T = [kv_c (c) | k_pe (r)]
+ *   entry = [RMSNorm(kv_c) | RoPE(k_pe)]                        written to the cache first
+ *   q[..., n:] = RoPE(q[..., n:])
+ *   attention per head over the visible cache entries, then optional gate
+ *   sigma(x W_g^T), then o_proj.
+ *
+ * Notation: H heads, n = qk_nope_head_dim, r = qk_rope_head_dim,
+ * c = kv_lora_rank, dv = v_head_dim, E = c + r (one cache entry, 576 for the
+ * DeepSeek dims 512 + 64).
+ *
+ * Conventions shared by every entry point
+ *  - "device" pointers are HIP device memory on the current device; "host"
+ *    arguments are plain values. Element type of every floating-point array is
+ *    the context's dtype (fp32 or bf16, row-major, contiguous).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
+ *    stream) and never synchronises, except mla_init_weights (once, at the end).
+ *  - Host-side validation of every host argument happens before any HIP call;
+ *    on failure the function returns a nonzero mla_status, launches nothing and
+ *    mla_last_error() describes the problem. Contents of device arrays are not
+ *    validated on the host (that would need a synchronisation): kernels clamp
+ *    lengths, positions and intervals into range and ignore block-table entries
+ *    outside [0, num_blocks), so bad indices cannot address outside the buffers.
+ *  - A context may be used by one stream at a time (its workspaces are shared
+ *    between calls). Errors inside kernels surface at the caller's next
+ *    synchronisation, as HIP reports them.
+ *  - The paged latent cache is [num_blocks, page_size, E] (one KV head, no
+ *    separate K and V planes; get_kv_cache_shape and MLAAttentionSpec listings).
+ *    Entry j of sequence b (its logical position j) lives at
+ *    cache[block_table[b * max_blocks + j / page_size]][j % page_size].
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_API __attribute__((visibility("default")))
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, negative or zero size, bad enum */
+  MLA_ERR_DIMS = 2,        /* inconsistent model dimensions */
+  MLA_ERR_UNSUPPORTED = 3, /* valid but not supported by these kernels (alignment, sizes) */
+  MLA_ERR_CAPACITY = 4,    /* call exceeds the limits given at init */
+  MLA_ERR_HIP = 5,         /* a HIP runtime call failed */
+  MLA_ERR_OOM = 6          /* device allocation failed */
+} mla_status;
+
+typedef enum mla_dtype { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* NeoX rotates pairs (j, j + r/2); interleaved rotates pairs (2j, 2j + 1);
+ * both by angle pos * theta^(-2j/r). Rotated pairs stay in place. */
+typedef enum mla_rope_style { MLA_ROPE_NEOX = 0, MLA_ROPE_INTERLEAVED = 1 } mla_rope_style;
+
+/* Visible keys of a query at logical position p in a sequence of L entries:
+ * FULL [0, L); CAUSAL [0, p + 1); SLIDING [max(0, p - window + 1), p + 1)
+ * (exactly `window` keys including itself). A query with no visible key gets
+ * an attention output of exactly zero. */
+typedef enum mla_mask_kind { MLA_MASK_FULL = 0, MLA_MASK_CAUSAL = 1, MLA_MASK_SLIDING = 2 } mla_mask_kind;
+
+typedef struct mla_config {
+  int32_t hidden_size;
+  int32_t num_heads;
+  int32_t q_lora_rank;      /* 0 = no low-rank Q path (q_proj is used) */
+  int32_t kv_lora_rank;     /* c */
+  int32_t qk_nope_head_dim; /* n */
+  int32_t qk_rope_head_dim; /* r (even) */
+  int32_t v_head_dim;       /* dv */
+  int32_t rope_style;       /* mla_rope_style */
+  double rope_theta;        /* > 1 */
+  double rms_norm_eps;      /* >= 0, both RMSNorms */
+  double softmax_scale;     /* <= 0 selects 1 / sqrt(n + r) */
+  int32_t use_output_gate;  /* 0 or 1: out = o_proj(attn * sigmoid(x W_g^T)) */
+  int32_t dtype;            /* mla_dtype of weights, activations and cache */
+  int32_t page_size;        /* tokens per cache block */
+  /* capacity limits; workspaces are allocated once at init from these */
+  int32_t max_batch;        /* sequences per call */
+  int32_t max_tokens;       /* new tokens per call (decode: = batch) */
+  int32_t max_seq_len;      /* cache entries per sequence (positions < max_seq_len) */
+  int32_t max_prefill_kv;   /* prefill: batch * max_kv_len rows of expanded K/V; 0 = no prefill */
+} mla_config;
+
+/* Layer weights, device pointers in nn.Linear [out, in] row-major layout with
+ * the names used on the pages. Unused entries may be NULL. */
+typedef struct mla_weights {
+  const void* q_a_proj;           /* [q_lora_rank, hidden]        (q_lora_rank > 0) */
+  const void* q_a_layernorm;      /* [q_lora_rank]                (q_lora_rank > 0) */
+  const void* q_b_proj;           /* [H * (n + r), q_lora_rank]   (q_lora_rank > 0) */
+  const void* q_proj;             /* [H * (n + r), hidden]        (q_lora_rank == 0) */
+  const void* kv_a_proj_with_mqa; /* [c + r, hidden] */
+  const void* kv_a_layernorm;     /* [c] */
+  const void* kv_b_proj;          /* [H * (n + dv), c], per head [k_nope rows | v rows] */
+  const void* o_proj;             /* [hidden, H * dv] */
+  const void* g_proj;             /* [H * dv, hidden]             (use_output_gate) */
+} mla_weights;
+
+typedef struct mla_ctx mla_ctx;
+
+/*
+ * mla_init_weights — validate the configuration and create a context.
+ * Dimension identities checked here (MLA blog, dimension summary and
+ * MLAAttention.__init__): q head dim = n + r, cache entry = c + r, one KV
+ * head; r even; every size > 0. The library copies and repacks the weights
+ * into device memory it owns (fused first projection, the q_a RMSNorm gain
+ * folded into q_b_proj, the per-head W_UK^T blocks of kv_b_proj for the
+ * absorbed decode); the caller may free its weight tensors after return.
+ * Workspaces are sized from the capacity fields. Synchronises `stream` once.
+ * On success *out receives the context; on failure *out is NULL.
+ */
+MLA_API int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, mla_ctx** out);
+
+/*
+ * mla_prefill_expanded — MLA forward of `total_tokens` new tokens in expanded
+ * form (MLA blog, forward_mha listing: the latent is expanded through kv_b_proj
+ * into per-head k_nope and v, K = [k_nope, k_pe]).
+ *   x            device [total_tokens, hidden]; sequence b owns rows
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   cu_seqlens_q device int32 [batch + 1], nondecreasing, cu[0] = 0, cu[batch] = total_tokens
+ *   prefix_lens  device int32 [batch]: entries already cached for sequence b
+ *                (its latent prefix); new token i is at logical position prefix_len + i
+ *   max_q_len    host: >= every q_len; max_kv_len host: >= every prefix_len + q_len
+ *   kv_cache     device [num_blocks, page_size, E]; the new entries
+ *                [RMSNorm(kv_c) | RoPE(k_pe)] are written at their positions
+ *                before attention, so each query sees its own entry
+ *   block_table  device int32 [batch, max_blocks]
+ *   mask_kind, window  mla_mask_kind and its window (SLIDING only)
+ *   row_lo, row_hi     optional device int32 [total_tokens]: when both are
+ *                non-NULL they replace the mask with the visible interval
+ *                [row_lo, row_hi) of positions (clamped to [0, L)); lo >= hi
+ *                drops the row (its output is zero)
+ *   out          device [total_tokens, hidden]
+ * Limits: batch <= max_batch, total_tokens <= max_tokens, max_kv_len <=
+ * max_seq_len, batch * max_kv_len <= max_prefill_kv (else MLA_ERR_CAPACITY).
+ */
+MLA_API int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t total_tokens,
+                         const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
+                         int32_t max_q_len, int32_t max_kv_len,
+                         void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                         int32_t max_blocks, int32_t mask_kind, int32_t window,
+                         const int32_t* row_lo, const int32_t* row_hi,
+                         void* out, void* stream);
+
+/*
+ * mla_decode_absorbed — one new token per sequence in absorbed form (MLA blog,
+ * the decode branch and forward_mqa listing: q_nope is projected into latent
+ * space through W_UK, attention runs over the whole E-wide cache entries as
+ * MQA with one shared latent head, the latent output is projected back through
+ * W_UV).
+ *   x            device [batch, hidden]
+ *   seq_lens     device int32 [batch]: cache length INCLUDING the new token,
+ *                which is written at position seq_len - 1 before attention
+ *   max_seq_len  host: >= every seq_len (sizes the split-KV grid)
+ *   out          device [batch, hidden]
+ * kv_cache must not be NULL (the listing asserts a non-empty cache).
+ * Limits: batch <= max_batch and <= max_tokens, max_seq_len <= the init max_seq_len.
+ */
+MLA_API int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch,
+                        void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                        int32_t mask_kind, int32_t window, void* out, void* stream);
+
+/* mla_free — release everything the context owns (waits for its device work
+ * to finish on the device). NULL is a no-op. */
+MLA_API void mla_free(mla_ctx* ctx);
+
+/* mla_last_error — message of the last failure on the calling thread
+ * (thread-local, valid until the next call on that thread). */
+MLA_API const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

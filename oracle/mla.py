@@ -210,23 +210,28 @@ def _absorbed_attention(dims, W, q, entries, lo, hi, scale):
 
 def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
                      rows: Optional[Sequence[int]] = None, row_lo=None, row_hi=None,
-                     form: str = "expanded", softmax_scale: Optional[float] = None):
+                     form: str = "expanded", softmax_scale: Optional[float] = None,
+                     first_position: int = 0):
     """One sequence: S new tokens at logical positions P..P+S-1 after P cached
     prefix entries. The new entries are appended to the cache before attention,
     so each query sees its own entry (MLAAttention.forward listing: cache update
     first, then attention).
 
     rows: indices (within the sequence) of the queries to compute outputs for
-    (default all). row_lo/row_hi: explicit visible intervals [lo, hi) per new
-    token, replacing the mask (clamped to [0, P+S)).
+    (default all). row_lo/row_hi: explicit visible intervals [lo, hi) of
+    positions per new token, replacing the mask (clamped to [0, L)).
+    first_position: the given prefix rows are the cache entries at positions
+    first_position .. first_position + P - 1 (a window of a longer cache); every
+    selected query must then see no key before first_position.
     Returns (out [len(rows), hidden], new entries [S, E], attn [len(rows), H*dv])."""
     x = _f64(x)
     prefix_rows = _f64(prefix_rows).reshape(-1, dims.kv_lora_rank + dims.qk_rope_head_dim)
     S, P = x.shape[0], prefix_rows.shape[0]
-    L = P + S
+    f0 = int(first_position)
+    L = f0 + P + S  # absolute length of the sequence
     H, dv = dims.num_heads, dims.v_head_dim
     scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(dims.qk_nope_head_dim + dims.qk_rope_head_dim)
-    positions = P + np.arange(S)
+    positions = f0 + P + np.arange(S)
     q, new_entries, gate = project_tokens(dims, W, x, positions)
     entries = np.concatenate([prefix_rows, new_entries], axis=0)
     sel = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -237,6 +242,10 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
         iv = [visible_interval(int(positions[i]), L, mask_kind, window) for i in sel]
         lo = np.array([a for a, _ in iv], dtype=np.int64)
         hi = np.array([b for _, b in iv], dtype=np.int64)
+    if f0:
+        if np.any((lo < f0) & (hi > lo)):
+            raise ValueError("a query sees keys before first_position")
+        lo, hi = np.maximum(lo - f0, 0), np.maximum(hi - f0, 0)
     if form == "expanded":
         k, v = expand_kv(dims, W, entries)
         o, _ = attention_core(q[sel], k, v, lo, hi, scale)
@@ -254,11 +263,12 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
 def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: int,
                 window: int = 0, row_lo=None, row_hi=None, form: str = "expanded",
                 seqs: Optional[Sequence[int]] = None, rows_per_seq: Optional[dict] = None,
-                softmax_scale: Optional[float] = None):
+                softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None):
     """A batch of sequences packed along the token axis (x is [sum q_lens, hidden]).
 
     seqs: the sequences to evaluate (default all); rows_per_seq: optional
-    {seq: [row indices]} subset of queries. Returns dict seq -> (out, entries, attn)."""
+    {seq: [row indices]} subset of queries; first_positions: optional
+    {seq: position of its first given prefix row}. Returns dict seq -> (out, entries, attn)."""
     q_lens = np.asarray(q_lens, dtype=np.int64)
     cu = np.concatenate([[0], np.cumsum(q_lens)])
     res = {}
@@ -270,7 +280,8 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
         rows = None if rows_per_seq is None else rows_per_seq.get(b)
         res[b] = forward_sequence(dims, W, np.asarray(x)[s0:s1], prefix_rows[b], mask_kind, window,
                                   rows=rows, row_lo=lo, row_hi=hi, form=form,
-                                  softmax_scale=softmax_scale)
+                                  softmax_scale=softmax_scale,
+                                  first_position=0 if first_positions is None else first_positions.get(b, 0))
     return res
 
 

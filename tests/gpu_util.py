@@ -1,0 +1,105 @@
+"""Helpers of the GPU parity tests: run a workload through the C ABI and
+compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import mla_synth as ms
+from mla_synth.device import from_torch, upload
+from draft_models_amd import binding as B
+from oracle import mla as om
+
+TOL_BF16 = dict(max_abs=2e-2, rel_l2=5e-3)
+TOL_F32 = dict(max_abs=1e-4, rel_l2=None)
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool = False):
+    """One call of the workload's entry point. Returns (out [T, hidden], cache
+    [num_blocks, page, E]) as float32 numpy."""
+    say(f"[gpu] {w.name} mode={w.mode} B={w.batch} T={w.total_tokens} "
+        f"max_kv={int(w.kv_lens.max())} mask={w.mask_kind} window={w.window} seed={w.seed}")
+    t = upload(w)
+    d = w.dims
+    max_kv = int(w.kv_lens.max())
+    prefill = w.mode == "prefill"
+    cfg = B.make_config(d, max_batch=w.batch + (3 if extra_capacity else 0),
+                        max_tokens=w.total_tokens + (5 if extra_capacity else 0),
+                        max_seq_len=max_kv + (7 if extra_capacity else 0),
+                        max_prefill_kv=w.batch * max_kv if prefill else 0,
+                        softmax_scale=softmax_scale)
+    m = B.MLA(cfg, t["weights"])
+    dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    out = torch.full((w.total_tokens, d.hidden_size), float("nan"), dtype=dt, device="cuda")
+    if prefill:
+        m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], int(w.q_lens.max()), max_kv, t["cache"],
+                  t["block_table"], w.mask_kind, w.window, out, row_lo=t.get("row_lo"), row_hi=t.get("row_hi"))
+    else:
+        m.decode(t["x"], t["cache"], t["block_table"], t["seq_lens"], max_kv, w.mask_kind, w.window, out)
+    torch.cuda.synchronize()
+    m.close()
+    return from_torch(out), from_torch(t["cache"])
+
+
+def oracle(w: ms.Workload, seqs=None, rows_per_seq=None, form="expanded", first_positions=None,
+           softmax_scale=None):
+    return om.mla_forward(w.dims, w.weights, w.x, w.q_lens, w.prefix_rows, w.mask_kind, w.window,
+                          w.row_lo, w.row_hi, form=form, seqs=seqs, rows_per_seq=rows_per_seq,
+                          softmax_scale=softmax_scale, first_positions=first_positions)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    max_abs = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got - ref))
+    return max_abs, rel
+
+
+def assert_close(got, ref, dtype: str, what: str, magnitude_scaled: bool = False):
+    """max |got - ref| <= max_abs and ||got - ref|| / ||ref|| <= rel_l2.
+
+    magnitude_scaled: the max-abs bar is applied to |got - ref| / max(1, |ref|).
+    Used for stored cache entries: a bf16 value is only representable to within
+    2^-9 |v| (0.0156 at |v| = 8, above 2e-2 beyond), and the unnormalised rope
+    key reaches |v| of about 8, so an absolute bar cannot hold for any bf16
+    storage of it; the relative L2 bar is unchanged."""
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    max_abs, rel = errors(got, ref)
+    worst = max_abs
+    if magnitude_scaled and got.size:
+        d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+        worst = float(np.max(d / np.maximum(1.0, np.abs(np.asarray(ref, np.float64)))))
+    say(f"  {what}: max_abs={max_abs:.3e} scaled_max={worst:.3e} rel_l2={rel:.3e}")
+    assert worst <= tol["max_abs"], f"{what}: max error {worst} > {tol['max_abs']}"
+    if tol["rel_l2"] is not None:
+        assert rel <= tol["rel_l2"], f"{what}: relative L2 error {rel} > {tol['rel_l2']}"
+
+
+def check(w: ms.Workload, out, cache, res, rows_per_seq=None):
+    """Compare the GPU output rows and written cache entries of the sequences
+    in `res` (oracle results) and check the prefix entries are untouched."""
+    cu = w.cu_seqlens
+    got_o, ref_o, got_e, ref_e = [], [], [], []
+    for b, (o_ref, e_ref, _) in res.items():
+        rows = np.arange(w.q_lens[b]) if rows_per_seq is None else np.asarray(rows_per_seq[b])
+        got_o.append(out[cu[b] + rows])
+        ref_o.append(o_ref)
+        P = int(w.prefix_lens[b])
+        got_e.append(ms.gather_entries(w, cache, b, P, P + int(w.q_lens[b])))
+        ref_e.append(e_ref)
+        if P:
+            kept = ms.gather_entries(w, cache, b, 0, P)
+            assert np.array_equal(kept, w.prefix_rows[b]), f"prefix entries of sequence {b} changed"
+    assert_close(np.concatenate(got_e), np.concatenate(ref_e), w.dims.dtype, "cache entries",
+                 magnitude_scaled=True)
+    assert_close(np.concatenate(got_o), np.concatenate(ref_o), w.dims.dtype, "out")

@@ -234,3 +234,15 @@ def pin_cache_consistency(w, split: int):
         o, e, _ = om.forward_sequence(w.dims, w.weights, x[i:i + 1], cache, om.MASK_CAUSAL)
         assert np.max(np.abs(o[0] - full[i])) < 1e-12 * max(1, np.abs(full).max())
         cache = np.concatenate([cache, e])
+
+
+def pin_window_trim(w, window: int):
+    """Under a sliding window, dropping the prefix rows no query can see (and
+    giving the position of the first kept row) leaves every output unchanged."""
+    x, pre = w.x, w.prefix_rows[0]
+    P, S = pre.shape[0], x.shape[0]
+    full = om.forward_sequence(w.dims, w.weights, x, pre, om.MASK_SLIDING, window)
+    f0 = max(0, P + 1 - window)  # first key the earliest new query can see
+    trim = om.forward_sequence(w.dims, w.weights, x, pre[f0:], om.MASK_SLIDING, window, first_position=f0)
+    assert np.max(np.abs(full[0] - trim[0])) == 0.0
+    assert np.max(np.abs(full[1] - trim[1])) == 0.0

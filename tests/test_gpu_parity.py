@@ -1,0 +1,167 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs. bf16: max |err| <= 2e-2 and relative L2 <= 5e-3; fp32:
+max |err| <= 1e-4. Small cases compare every output row and every written
+cache entry; full-size workloads compare sampled sequences / rows that the
+oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import mla_synth as ms
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts only with -m gpu
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _run_and_check(w, **kw):
+    out, cache = U.run_gpu(w, **kw)
+    res = U.oracle(w)
+    U.check(w, out, cache, res)
+    return out
+
+
+# ---------------------------------------------------------------- tiny fp32
+
+def test_tiny_f32_prefill():
+    """The tiny fp32 model: 16 causal tokens, hidden 256, 4 heads, no low-rank Q."""
+    _run_and_check(ms.make_workload("tiny_f32"))
+
+
+def test_tiny_f32_decode():
+    w = ms.make_workload("tiny_f32", mode="decode", seq_lens=[1, 17, 40, 64, 65, 200], mask_kind=ms.MASK_CAUSAL)
+    _run_and_check(w)
+
+
+@pytest.mark.parametrize("variant", [
+    dict(q_lora_rank=64, rope_style=ms.ROPE_INTERLEAVED),
+    dict(use_output_gate=True),
+])
+@pytest.mark.parametrize("mask,window", [(ms.MASK_FULL, 0), (ms.MASK_SLIDING, 5)])
+def test_tiny_f32_variants_prefill(variant, mask, window):
+    w = ms.make_workload("tiny_f32", dims_override=variant, q_lens=[7, 70, 1], prefix_lens=[3, 60, 130],
+                         mask_kind=mask, window=window, seed=10)
+    _run_and_check(w)
+
+
+@pytest.mark.parametrize("variant", [
+    dict(q_lora_rank=64, rope_style=ms.ROPE_INTERLEAVED, use_output_gate=True),
+])
+def test_tiny_f32_variants_decode(variant):
+    w = ms.make_workload("tiny_f32", dims_override=variant, mode="decode", seq_lens=[3, 90, 129],
+                         mask_kind=ms.MASK_SLIDING, window=33, seed=11)
+    _run_and_check(w)
+
+
+def test_tiny_gamma_noise_bf16():
+    """Nonunit RMSNorm gains (the q_a gain is folded into q_b_proj) in bf16."""
+    w = ms.make_workload("tiny_f32", dims_override=dict(q_lora_rank=64, dtype="bf16"), q_lens=[20, 9],
+                         prefix_lens=[5, 40], gamma_noise=True, seed=12)
+    _run_and_check(w)
+
+
+# ---------------------------------------------------- model dims, short runs
+
+def test_draft_block_small():
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 16, 16], prefix_lens=[100, 37, 300])
+    _run_and_check(w)
+
+
+def test_decode_small():
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 65, 700, 333, 64])
+    _run_and_check(w)
+
+
+def test_prefill_small():
+    w = ms.make_workload("prefill_bf16", q_lens=[300, 129], prefix_lens=[0, 0])
+    _run_and_check(w)
+
+
+def test_long_decode_small():
+    w = ms.make_workload("long_decode_bf16", seq_lens=[1500, 2999, 1024, 1025, 7])
+    _run_and_check(w)
+
+
+def test_prefill_chunked_sliding():
+    """Causal prefill of a chunk after a cached prefix under a sliding window."""
+    w = ms.make_workload("prefill_bf16", q_lens=[77, 200], prefix_lens=[300, 5], mask_kind=ms.MASK_SLIDING,
+                         window=128, seed=13)
+    _run_and_check(w)
+
+
+def test_dropped_rows_are_exact_zero():
+    """Explicit visible intervals with lo >= hi (a dropped draft block) give
+    output rows that are exactly zero; the other rows match the oracle."""
+    q_lens, prefix = [16, 16], [50, 20]
+    T = sum(q_lens)
+    lo = np.zeros(T, np.int32)
+    hi = np.array([p + q for p, q in zip(prefix, q_lens) for _ in range(q)], np.int32)
+    hi[3:9] = 0
+    lo[20:24] = 30
+    hi[20:24] = 30
+    w = ms.make_workload("draft_block_bf16", q_lens=q_lens, prefix_lens=prefix, row_interval=(lo, hi), seed=14)
+    out = _run_and_check(w)
+    assert np.all(out[3:9] == 0) and np.all(out[20:24] == 0)
+
+
+def test_window_zero_gives_zero_output():
+    w = ms.make_workload("tiny_f32", mask_kind=ms.MASK_SLIDING, window=0, q_lens=[9], prefix_lens=[4], seed=15)
+    out, _ = U.run_gpu(w)
+    assert np.all(out == 0)
+
+
+def test_softmax_scale_override():
+    w = ms.make_workload("tiny_f32", q_lens=[12], prefix_lens=[30], seed=16)
+    out, cache = U.run_gpu(w, softmax_scale=0.05)
+    U.check(w, out, cache, U.oracle(w, softmax_scale=0.05))
+
+
+def test_capacity_above_call():
+    """Context limits larger than the call (workspace rows beyond the batch)."""
+    w = ms.make_workload("decode_bf16", seq_lens=[100, 3000], seed=17)
+    out, cache = U.run_gpu(w, extra_capacity=True)
+    U.check(w, out, cache, U.oracle(w))
+
+
+# ------------------------------------------------ full sizes, sampled checks
+
+def test_full_draft_block():
+    """8 sequences x 16 fully visible tokens over a 2048-entry latent prefix."""
+    w = ms.make_workload("draft_block_bf16")
+    out, cache = U.run_gpu(w)
+    U.check(w, out, cache, U.oracle(w, seqs=[0, 5]))
+
+
+def test_full_decode():
+    """64 sequences, cache lengths uniform in [1024, 8192]; sampled sequences
+    checked against the oracle's absorbed form (pinned equal to the expanded
+    form in fp64 by the CPU tests)."""
+    w = ms.make_workload("decode_bf16")
+    out, cache = U.run_gpu(w)
+    L = w.kv_lens
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 17, 40})
+    U.check(w, out, cache, U.oracle(w, seqs=seqs, form="absorbed"))
+
+
+def test_full_prefill():
+    """4 x 4096 causal tokens; sampled rows (tile edges, the first and last)."""
+    w = ms.make_workload("prefill_bf16")
+    out, cache = U.run_gpu(w)
+    rows = [0, 1, 15, 16, 63, 64, 127, 128, 1000, 2047, 4095]
+    rps = {0: rows, 3: rows}
+    U.check(w, out, cache, U.oracle(w, seqs=[0, 3], rows_per_seq=rps), rows_per_seq=rps)
+
+
+def test_full_long_decode():
+    """16 sequences with 16k-32k cached entries under a 1024-token sliding
+    window and the output gate; the oracle sees only the visible window."""
+    w = ms.make_workload("long_decode_bf16")
+    out, cache = U.run_gpu(w)
+    seqs = [0, int(np.argmax(w.kv_lens)), 9]
+    first = {b: int(w.kv_lens[b]) - w.window for b in seqs}
+    trimmed = ms.Workload(**{**w.__dict__})
+    trimmed.prefix_rows = [r[first.get(b, 0):] if b in first else r for b, r in enumerate(w.prefix_rows)]
+    res = U.oracle(trimmed, seqs=seqs, form="absorbed", first_positions=first)
+    U.check(w, out, cache, res)

@@ -57,6 +57,15 @@ def test_masks(variant):
     P.pin_masks(_tiny(**variant))
 
 
+def test_window_trim():
+    w = ms.make_workload("tiny", dims=P.tiny_dims(q_lora_rank=12, use_output_gate=True), seed=7,
+                         q_lens=[3], prefix_lens=[40])
+    P.pin_window_trim(w, window=5)
+    with pytest.raises(ValueError):  # a query that would see a trimmed key
+        om.forward_sequence(w.dims, w.weights, w.x, w.prefix_rows[0][10:], om.MASK_SLIDING, 40,
+                            first_position=10)
+
+
 def test_cache_consistency():
     P.pin_cache_consistency(_tiny(q_lora_rank=12), split=4)
 
