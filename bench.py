@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""MLA forward benchmark on one MI355X.
+
+Default workload: the draft-block MLA layer -- 8 sequences, each a 16-token
+block that sees all of itself and a 2048-entry latent prefix (FULL mask),
+hidden 4096, 32 heads, q_lora_rank 1536, kv_lora_rank 512, qk_nope 128,
+qk_rope 64, v_head 128, interleaved RoPE, bf16, through mla_prefill_expanded.
+One step = one call of the entry point = the whole hot path (projections,
+latent RMSNorm + RoPE + cache write, expansion of every visible latent, flash
+attention, o_proj). Inputs are synthetic (seeded), resident in HBM before the
+timed region.
+
+Prints one JSON line: value = algorithmic work of the step / step time
+(TFLOP/s for prefill workloads, latent-cache GB/s for decode workloads),
+plus the roofline of the dominant kernel (timed live with HIP events on the
+library's stream) and the fp64 oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "MLA decode latent-cache GB/s + prefill TFLOP/s (% of MI355X roofline)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+DESCR = {
+    "tiny_f32": "tiny MLA fp32: 1 x 16 causal tokens, hidden 256, 4 heads, no q_lora, kv_lora 32, "
+                "nope 16, rope 8, v 16, NeoX RoPE",
+    "draft_block_bf16": "draft-block MLA bf16: 8 x 16-token fully visible block over a 2048-entry latent "
+                        "prefix, hidden 4096, 32 heads, q_lora 1536, kv_lora 512, nope 128, rope 64, v 128, "
+                        "interleaved RoPE",
+    "decode_bf16": "DeepSeek-V3-shaped absorbed decode bf16: 64 sequences x 1 query, cache length "
+                   "uniform in [1024, 8192], hidden 7168, 128 heads, q_lora 1536, kv_lora 512, nope 128, "
+                   "rope 64, v 128",
+    "prefill_bf16": "expanded prefill bf16: 4 x 4096 causal tokens, hidden 4096, 32 heads, q_lora 1536, "
+                    "kv_lora 512, nope 128, rope 64, v 128, NeoX RoPE",
+    "long_decode_bf16": "long-context decode bf16: 16 sequences, cache length uniform in [16384, 32768], "
+                        "1024-token sliding window, sigmoid output gate, 128 heads, kv_lora 512, nope 128, "
+                        "rope 64, v 128, hidden 7168, no q_lora",
+}
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (from shapes only)
+# ----------------------------------------------------------------------------
+
+def visible_counts(w):
+    """Visible keys of every query (same rule as the library's masks)."""
+    counts = []
+    for b in range(w.batch):
+        P, S = int(w.prefix_lens[b]), int(w.q_lens[b])
+        L = P + S
+        for i in range(S):
+            p = P + i
+            if w.row_lo is not None:
+                t = int(w.cu_seqlens[b]) + i
+                lo, hi = max(0, min(int(w.row_lo[t]), L)), max(0, min(int(w.row_hi[t]), L))
+            elif w.mask_kind == 0:
+                lo, hi = 0, L
+            elif w.mask_kind == 1:
+                lo, hi = 0, min(p + 1, L)
+            else:
+                lo, hi = max(0, p - w.window + 1), min(p + 1, L)
+            counts.append(max(0, hi - lo))
+    return np.asarray(counts, dtype=np.int64)
+
+
+def stage_work(w, seqs=None):
+    """Algorithmic flops and bytes of each stage of one step (optionally for a
+    subset of the sequences)."""
+    d = w.dims
+    esz = 2 if d.dtype == "bf16" else 4
+    H, n, r, c, dv, hid, ql = (d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank,
+                              d.v_head_dim, d.hidden_size, d.q_lora_rank)
+    E = c + r
+    sel = np.arange(w.batch) if seqs is None else np.asarray(seqs)
+    T = int(w.q_lens[sel].sum())
+    kv = int(w.kv_lens[sel].sum())
+    vis_all = visible_counts(w)
+    cu = w.cu_seqlens
+    pairs = int(sum(vis_all[cu[b]:cu[b + 1]].sum() for b in sel))
+    n1 = (ql if ql else H * (n + r)) + E + (H * dv if d.use_output_gate else 0)
+    work = {}
+    work["qkv_a_gemm"] = dict(flops=2 * T * hid * n1, bytes=(n1 * hid + T * (hid + n1)) * esz)
+    if ql:
+        work["q_b_gemm"] = dict(flops=2 * T * ql * H * (n + r), bytes=(H * (n + r) * ql + T * (ql + H * (n + r))) * esz)
+    work["o_proj_gemm"] = dict(flops=2 * T * H * dv * hid, bytes=(hid * H * dv + T * (H * dv + hid)) * esz)
+    if w.mode == "prefill":
+        work["kv_b_expand"] = dict(flops=2 * kv * c * H * (n + dv),
+                                   bytes=(H * (n + dv) * c + kv * (c + H * (n + dv))) * esz)
+        work["prefill_attn"] = dict(flops=2 * pairs * H * (n + r + dv), bytes=None)
+    else:
+        work["wuk_absorb"] = dict(flops=2 * T * H * n * c, bytes=(H * n * c + T * H * (n + c)) * esz)
+        work["decode_attn"] = dict(flops=2 * pairs * H * (E + c), bytes=pairs * E * esz)
+        work["wuv_gemm"] = dict(flops=2 * T * H * c * dv, bytes=(H * dv * c + T * H * (c + dv)) * esz)
+    work["_step"] = dict(flops=sum(v["flops"] for v in work.values()),
+                         cache_bytes=pairs * E * esz,
+                         bytes=sum((v["bytes"] or 0) for v in work.values()))
+    return work
+
+
+def step_value(w, work):
+    """(value per step, unit): TFLOP for prefill, latent-cache GB for decode."""
+    if w.mode == "prefill":
+        return work["_step"]["flops"] / 1e12, "TFLOP/s"
+    return work["_step"]["cache_bytes"] / 1e9, "GB/s"
+
+
+# ----------------------------------------------------------------------------
+# measured HBM traffic (committed rocprofv3 counter summaries)
+# ----------------------------------------------------------------------------
+
+def kernel_source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "draft_models_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+STAGE_SOURCES = {
+    "kv_b_expand": ["gemm.hip", "common.h"], "qkv_a_gemm": ["gemm.hip", "common.h"],
+    "q_b_gemm": ["gemm.hip", "common.h"], "o_proj_gemm": ["gemm.hip", "common.h"],
+    "wuk_absorb": ["gemm.hip", "common.h"], "wuv_gemm": ["gemm.hip", "common.h"],
+    "prefill_attn": ["attn_prefill.hip", "common.h"], "decode_attn": ["attn_decode.hip", "common.h"],
+    "decode_merge": ["attn_decode.hip", "common.h"], "rope_cache": ["rope_cache.hip", "common.h"],
+}
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from profiles/traffic_<stage>_<workload>.json, or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != kernel_source_sha(STAGE_SOURCES[stage]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w, budget_s: float):
+    from threadpoolctl import threadpool_info
+    from oracle import mla as om
+    order = list(np.argsort(w.kv_lens))  # shortest first keeps the sample bounded
+    done, t0 = [], time.perf_counter()
+    first = {}
+    for b in order:
+        b = int(b)
+        if w.mode == "decode" and w.mask_kind == 2:
+            # only the visible window of a sliding-window decode enters the computation
+            first[b] = max(0, int(w.kv_lens[b]) - w.window)
+        pre = w.prefix_rows[b][first.get(b, 0):]
+        cu = w.cu_seqlens
+        om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
+                            first_position=first.get(b, 0))
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    work = stage_work(w, seqs=done)
+    per, unit = step_value(w, work)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": per / el, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch} sequences (ids {sorted(done)}), expanded fp64 oracle, "
+                      f"{el:.1f} s wall", "wall_s": round(el, 3)}
+
+
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="draft_block_bf16", choices=sorted(DESCR))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true", help="no per-stage events in the timed region")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each GPU would run its own sequences with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_synth as ms
+    from mla_synth.device import upload
+    from draft_models_amd import binding as B
+
+    w = ms.make_workload(args.workload)
+    t = upload(w)
+    d = w.dims
+    max_kv = int(w.kv_lens.max())
+    prefill = w.mode == "prefill"
+    cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_kv,
+                        max_prefill_kv=w.batch * max_kv if prefill else 0)
+    m = B.MLA(cfg, t["weights"])
+    dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    out = torch.empty((w.total_tokens, d.hidden_size), dtype=dt, device="cuda")
+    max_q = int(w.q_lens.max())
+
+    def step():
+        if prefill:
+            m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], max_q, max_kv, t["cache"], t["block_table"],
+                      w.mask_kind, w.window, out)
+        else:
+            m.decode(t["x"], t["cache"], t["block_table"], t["seq_lens"], max_kv, w.mask_kind, w.window, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    m.profile(not args.no_profile)
+    m.profile_read()  # clear
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    stages = m.profile_read()
+    m.profile(False)
+    ms_step = total_ms / args.steps
+
+    work = stage_work(w)
+    per_step, unit = step_value(w, work)
+    value = per_step / (ms_step / 1e3)
+
+    # dominant kernel: the stage with the largest total time
+    timed = {k: v for k, v in stages.items() if v[1] > 0}
+    roofline = None
+    if timed:
+        dom = max(timed, key=lambda k: timed[k][0])
+        dom_ms = timed[dom][0] / timed[dom][1]
+        wk = work.get(dom, {})
+        if dom in ("decode_attn", "rope_cache", "decode_merge") or (w.mode == "decode" and wk.get("bytes")):
+            bound, peak, unit_r = "hbm", HBM_PEAK_GBS, "GB/s"
+            achieved = (wk.get("bytes") or 0) / (dom_ms / 1e3) / 1e9
+        else:
+            bound, peak, unit_r = "mfma", MFMA_PEAK_TFLOPS[d.dtype], "TFLOP/s"
+            achieved = wk.get("flops", 0) / (dom_ms / 1e3) / 1e12
+        roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": unit_r, "frac": round(achieved / peak, 4),
+                    "traffic": measured_traffic(dom, args.workload), "kernel_ms": round(dom_ms, 5)}
+
+    res = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": d.dtype, "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": args.workload, "description": DESCR[args.workload], "batch": w.batch,
+                   "new_tokens": w.total_tokens, "max_kv_len": max_kv, "entry_point":
+                       "mla_prefill_expanded" if prefill else "mla_decode_absorbed",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in timed.items()},
+        "step_work": {"tflop": round(work["_step"]["flops"] / 1e12, 4),
+                      "latent_cache_gb": round(work["_step"]["cache_bytes"] / 1e9, 4)},
+    }
+    if not prefill:
+        res["whole_call_gbps"] = round(work["_step"]["bytes"] / (ms_step / 1e3) / 1e9, 2)
+    m.close()
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,9 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 
-EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_free", "mla_last_error")
+EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_free", "mla_last_error",
+           "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
+NUM_STAGES = 10
 
 
 class MLAError(RuntimeError):
@@ -71,6 +73,12 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.mla_free.restype = None
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = C.c_char_p
+    lib.mla_profile_enable.argtypes = [vp, i32]
+    lib.mla_profile_enable.restype = C.c_int
+    lib.mla_profile_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+    lib.mla_profile_read.restype = C.c_int
+    lib.mla_profile_stage_name.argtypes = [i32]
+    lib.mla_profile_stage_name.restype = C.c_char_p
     _lib = lib
     return lib
 
@@ -131,6 +139,16 @@ class MLA:
         _check(self._lib.mla_decode_absorbed(
             self.ctx, _ptr(x), x.shape[0], _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), max_seq_len, mask_kind, window, _ptr(out), _stream(stream)))
+
+    def profile(self, enable: bool):
+        _check(self._lib.mla_profile_enable(self.ctx, int(enable)))
+
+    def profile_read(self) -> Dict[str, tuple]:
+        """{stage name: (total ms, launches)} since the last read (synchronises)."""
+        ms = (C.c_double * NUM_STAGES)()
+        cnt = (C.c_int32 * NUM_STAGES)()
+        _check(self._lib.mla_profile_read(self.ctx, ms, cnt))
+        return {self._lib.mla_profile_stage_name(i).decode(): (ms[i], cnt[i]) for i in range(NUM_STAGES)}
 
     def close(self):
         if self.ctx:

@@ -6,6 +6,8 @@
 
 namespace mla {
 
+using bf16_t = __bf16;
+
 struct RopeCacheArgs {
   void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // q [T, H, n + r] rows of stride ldq
   const void* kv = nullptr; int64_t ldkv = 0;            // [T, c + r] rows of stride ldkv
@@ -64,8 +66,12 @@ struct DecodeAttnArgs {
   float* part_o = nullptr;                          // [B, splits, H, c]
   float* part_lse = nullptr;                        // [B, splits, H]
   void* o_lat = nullptr;                            // [B, H, c] combined latent output
+  const bf16_t* zeros = nullptr;                    // >= 16 zero bytes (tile padding source)
 };
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
+hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
+// heads handled by one workgroup of the decode kernel chosen for `a`
+int decode_heads_per_group(const DecodeAttnArgs& a, bool is_bf16);
 const char* decode_attn_check(const DecodeAttnArgs& a, bool is_bf16);
 
 }  // namespace mla

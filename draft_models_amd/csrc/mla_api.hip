@@ -43,7 +43,13 @@ struct mla_ctx {
   int max_splits = 32;
   float* gemm_ws = nullptr;
   int64_t gemm_ws_elems = 0;
+  void* zeros = nullptr;   // 256 zero bytes: source of padding chunks in streamed tiles
   std::vector<void*> allocs;
+  // stage timing (mla_profile_*)
+  bool profiling = false;
+  struct Mark { int stage; hipEvent_t start, stop; };
+  std::vector<Mark> marks;
+  std::vector<hipEvent_t> event_pool;
 };
 
 namespace {
@@ -146,6 +152,41 @@ int check_mask(int kind, int window) {
   return MLA_OK;
 }
 
+enum Stage { ST_QKV_A = 0, ST_Q_B, ST_ROPE_CACHE, ST_KV_B, ST_PREFILL_ATTN, ST_WUK, ST_DECODE_ATTN,
+             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"qkv_a_gemm", "q_b_gemm", "rope_cache", "kv_b_expand", "prefill_attn",
+                                     "wuk_absorb", "decode_attn", "decode_merge", "wuv_gemm", "o_proj_gemm"};
+
+hipEvent_t pool_event(mla_ctx* ctx) {
+  if (!ctx->event_pool.empty()) {
+    hipEvent_t e = ctx->event_pool.back();
+    ctx->event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event now and the stop event when it goes out of scope
+// (only while profiling is on).
+struct StageTimer {
+  mla_ctx* ctx;
+  hipStream_t s;
+  int stage;
+  hipEvent_t start = nullptr;
+  StageTimer(mla_ctx* c, hipStream_t st, int sg) : ctx(c), s(st), stage(sg) {
+    if (ctx->profiling && (start = pool_event(ctx)) != nullptr) (void)hipEventRecord(start, s);
+  }
+  ~StageTimer() {
+    if (!start) return;
+    hipEvent_t stop = pool_event(ctx);
+    if (!stop) return;
+    (void)hipEventRecord(stop, s);
+    ctx->marks.push_back({stage, start, stop});
+  }
+};
+
 int run_gemm(mla_ctx* ctx, const GemmArgs& g, hipStream_t s) {
   if (const char* m = gemm_check(g, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
   HIP_TRY(gemm_launch(g, ctx->bf16, ctx->gemm_ws, ctx->gemm_ws_elems, s));
@@ -160,7 +201,10 @@ int project(mla_ctx* ctx, const void* x, int T, hipStream_t s, void** q, int64_t
   g1.W = ctx->W1; g1.ldw = ctx->hid;
   g1.C = ctx->buf1; g1.ldc = ctx->N1;
   g1.M = T; g1.N = ctx->N1; g1.K = ctx->hid;
-  if (int e = run_gemm(ctx, g1, s)) return e;
+  {
+    StageTimer st(ctx, s, ST_QKV_A);
+    if (int e = run_gemm(ctx, g1, s)) return e;
+  }
   if (ctx->ql > 0) {
     GemmArgs g2;
     g2.A = ctx->buf1; g2.lda = ctx->N1;
@@ -168,6 +212,7 @@ int project(mla_ctx* ctx, const void* x, int T, hipStream_t s, void** q, int64_t
     g2.C = ctx->qbuf; g2.ldc = (int64_t)ctx->H * ctx->qkh;
     g2.M = T; g2.N = ctx->H * ctx->qkh; g2.K = ctx->ql;
     g2.epi = EPI_ROWNORM; g2.eps = (float)ctx->cfg.rms_norm_eps;
+    StageTimer st(ctx, s, ST_Q_B);
     if (int e = run_gemm(ctx, g2, s)) return e;
     *q = ctx->qbuf;
     *ldq = (int64_t)ctx->H * ctx->qkh;
@@ -292,6 +337,8 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   ctx->gemm_ws_elems = (int64_t)16 << 20;
   if ((e = dev_alloc(ctx, &p, (size_t)ctx->gemm_ws_elems * sizeof(float)))) return bail(e);
   ctx->gemm_ws = static_cast<float*>(p);
+  if ((e = dev_alloc(ctx, &ctx->zeros, 256))) return bail(e);
+  if (hipMemsetAsync(ctx->zeros, 0, 256, s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "zero page init failed"));
 
   if (hipStreamSynchronize(s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "stream synchronize failed"));
   *out = ctx;
@@ -338,7 +385,10 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   rc.decode = 0; rc.cu_seqlens = cu_seqlens_q; rc.prefix_lens = prefix_lens;
   rc.max_q_len = max_q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = total_tokens;
-  HIP_TRY(rope_cache_launch(rc, ctx->bf16, max_q_len, batch, s));
+  {
+    StageTimer st(ctx, s, ST_ROPE_CACHE);
+    HIP_TRY(rope_cache_launch(rc, ctx->bf16, max_q_len, batch, s));
+  }
 
   // expand every visible latent (prefix and new) through kv_b_proj
   GemmArgs gk;
@@ -351,7 +401,10 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   gk.W = ctx->Wkvb; gk.ldw = ctx->c;
   gk.C = ctx->kvexp; gk.ldc = (int64_t)ctx->H * (ctx->n + ctx->dv);
   gk.M = batch * max_kv_len; gk.N = ctx->H * (ctx->n + ctx->dv); gk.K = ctx->c;
-  if (int e = run_gemm(ctx, gk, s)) return e;
+  {
+    StageTimer st(ctx, s, ST_KV_B);
+    if (int e = run_gemm(ctx, gk, s)) return e;
+  }
 
   PrefillAttnArgs pa;
   pa.q = q; pa.ldq = ldq; pa.qk_head = ctx->qkh;
@@ -369,13 +422,17 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
     pa.ldg = ctx->N1;
   }
   if (const char* m = prefill_attn_check(pa, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
-  HIP_TRY(prefill_attn_launch(pa, ctx->bf16, s));
+  {
+    StageTimer st(ctx, s, ST_PREFILL_ATTN);
+    HIP_TRY(prefill_attn_launch(pa, ctx->bf16, s));
+  }
 
   GemmArgs go;
   go.A = ctx->attn; go.lda = (int64_t)ctx->H * ctx->dv;
   go.W = ctx->Wo; go.ldw = (int64_t)ctx->H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
+  StageTimer st(ctx, s, ST_O_PROJ);
   return run_gemm(ctx, go, s);
 }
 
@@ -412,7 +469,10 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
   rc.decode = 1; rc.seq_lens = seq_lens; rc.max_seq_len = max_seq_len; rc.total_tokens = batch;
-  HIP_TRY(rope_cache_launch(rc, ctx->bf16, 1, batch, s));
+  {
+    StageTimer st(ctx, s, ST_ROPE_CACHE);
+    HIP_TRY(rope_cache_launch(rc, ctx->bf16, 1, batch, s));
+  }
 
   // W_UK absorption: ql_nope[b, h] = q_nope[b, h] . W_UK^T[h]   (per head: [B, n] x [n, c])
   GemmArgs ga;
@@ -420,11 +480,17 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
   ga.C = ctx->qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
   ga.M = batch; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
-  if (int e = run_gemm(ctx, ga, s)) return e;
+  {
+    StageTimer st(ctx, s, ST_WUK);
+    if (int e = run_gemm(ctx, ga, s)) return e;
+  }
 
   // split-KV sizing from the longest visible range (keys per split a multiple of 32)
+  DecodeAttnArgs da;
+  da.c = ctx->c; da.r = ctx->r; da.page = c.page_size; da.H = H;
   const int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
-  const int groups = (H + 63) / 64;
+  const int hpg = decode_heads_per_group(da, ctx->bf16);
+  const int groups = (H + hpg - 1) / hpg;
   int want = (512 + batch * groups - 1) / (batch * groups);
   want = std::max(1, std::min(want, ctx->max_splits));
   int chunk = std::max(1, (max_vis + want - 1) / want);
@@ -432,7 +498,6 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   const int splits = std::max(1, std::min(ctx->max_splits, (max_vis + chunk - 1) / chunk));
   if ((int64_t)splits * chunk < max_vis) chunk = ((max_vis + splits - 1) / splits + 31) / 32 * 32;
 
-  DecodeAttnArgs da;
   da.ql = ctx->qlat; da.ldql = (int64_t)H * ctx->c;
   da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
   da.cache = kv_cache; da.block_table = block_table;
@@ -444,8 +509,16 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   da.chunk = chunk; da.splits = splits;
   da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
   da.o_lat = ctx->olat;
+  da.zeros = static_cast<const bf16_t*>(ctx->zeros);
   if (const char* m = decode_attn_check(da, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
-  HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
+  {
+    StageTimer st(ctx, s, ST_DECODE_ATTN);
+    HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_DECODE_MERGE);
+    HIP_TRY(decode_merge_launch(da, ctx->bf16, s));
+  }
 
   // W_UV: out_v[b, h] = o_lat[b, h] . W_UV[h]^T (per head: [B, c] x [c, dv]), gated
   GemmArgs gv;
@@ -459,14 +532,48 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
     gv.G = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
     gv.ldg = ctx->N1; gv.sG = ctx->dv;
   }
-  if (int e = run_gemm(ctx, gv, s)) return e;
+  {
+    StageTimer st(ctx, s, ST_WUV);
+    if (int e = run_gemm(ctx, gv, s)) return e;
+  }
 
   GemmArgs go;
   go.A = ctx->attn; go.lda = (int64_t)H * ctx->dv;
   go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = batch; go.N = ctx->hid; go.K = H * ctx->dv;
+  StageTimer st(ctx, s, ST_O_PROJ);
   return run_gemm(ctx, go, s);
+}
+
+int mla_profile_enable(mla_ctx* ctx, int32_t enable) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  ctx->profiling = enable != 0;
+  return MLA_OK;
+}
+
+int mla_profile_read(mla_ctx* ctx, double* ms, int32_t* count) {
+  if (!ctx || !ms) return fail(MLA_ERR_INVALID_ARG, "ctx and ms must not be NULL");
+  for (int i = 0; i < ST_COUNT; ++i) {
+    ms[i] = 0.0;
+    if (count) count[i] = 0;
+  }
+  int rc = MLA_OK;
+  for (auto& mk : ctx->marks) {
+    float t = 0.f;
+    if (hipEventSynchronize(mk.stop) != hipSuccess || hipEventElapsedTime(&t, mk.start, mk.stop) != hipSuccess)
+      rc = fail(MLA_ERR_HIP, "reading a stage event failed");
+    ms[mk.stage] += t;
+    if (count) count[mk.stage] += 1;
+    ctx->event_pool.push_back(mk.start);
+    ctx->event_pool.push_back(mk.stop);
+  }
+  ctx->marks.clear();
+  return rc;
+}
+
+const char* mla_profile_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : nullptr;
 }
 
 void mla_free(mla_ctx* ctx) {
@@ -475,6 +582,11 @@ void mla_free(mla_ctx* ctx) {
   (void)hipGetDevice(&cur);
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
+  for (auto& mk : ctx->marks) {
+    (void)hipEventDestroy(mk.start);
+    (void)hipEventDestroy(mk.stop);
+  }
+  for (hipEvent_t e : ctx->event_pool) (void)hipEventDestroy(e);
   free_all(ctx);
   (void)hipSetDevice(cur);
   delete ctx;

@@ -175,6 +175,30 @@ MLA_API int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch,
                         int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
                         int32_t mask_kind, int32_t window, void* out, void* stream);
 
+/*
+ * Stage timing, for measurement. When enabled, every launch sequence of the
+ * context records a pair of HIP events around each stage on the call's own
+ * stream (the stream the stage's kernels run on); mla_profile_read waits for
+ * them, returns per-stage totals and clears the record. Stages (index: name):
+ *   0 qkv_a_gemm   fused first projection (x -> [q_c | q], kv_c, k_pe, gate)
+ *   1 q_b_gemm     q_b projection with the q_a RMSNorm folded in
+ *   2 rope_cache   latent RMSNorm, RoPE of q_pe and k_pe, cache write
+ *   3 kv_b_expand  prefill: expansion of every visible latent through kv_b_proj
+ *   4 prefill_attn prefill: flash attention over the expanded keys/values
+ *   5 wuk_absorb   decode: q_nope -> latent space through W_UK
+ *   6 decode_attn  decode: split-KV latent attention over the paged cache
+ *   7 decode_merge decode: log-sum-exp merge of the splits
+ *   8 wuv_gemm     decode: latent output -> v_head_dim through W_UV (+ gate)
+ *   9 o_proj_gemm  output projection
+ * A stage may be more than one kernel (a split-K GEMM adds its reduction).
+ */
+#define MLA_NUM_STAGES 10
+MLA_API int mla_profile_enable(mla_ctx* ctx, int32_t enable);
+/* ms[i]: total elapsed milliseconds of stage i; count[i]: times it ran. Both
+ * host arrays of MLA_NUM_STAGES entries (count may be NULL). Synchronises. */
+MLA_API int mla_profile_read(mla_ctx* ctx, double* ms, int32_t* count);
+MLA_API const char* mla_profile_stage_name(int32_t stage);
+
 /* mla_free — release everything the context owns (waits for its device work
  * to finish on the device). NULL is a no-op. */
 MLA_API void mla_free(mla_ctx* ctx);
