@@ -64,6 +64,44 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS address lds_base + 16 l. Issued through inline
+// asm so that the compiler does not treat later LDS reads as aliasing the
+// in-flight copy; completion is tracked by the caller with an explicit
+// vmcnt wait followed by a workgroup barrier.
+__device__ __forceinline__ void dma16(const void* gptr, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
+}
+
+// Same copy with a scalar base address and a 32-bit per-lane byte offset
+// (the saddr form: no 64-bit vector address per lane); lds_addr is the
+// wave-uniform LDS byte address of the destination.
+__device__ __forceinline__ void dma16_sbase(uint32_t voff_bytes, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff_bytes), "s"(sbase),
+               "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across,
+// without the vmcnt(0) that __syncthreads implies (prefetches stay in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS accesses are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// vmcnt(n) with expcnt / lgkmcnt unconstrained (gfx9 s_waitcnt encoding)
+#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// logistic sigmoid with the hardware reciprocal (v_rcp_f32, ~1 ulp)
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 }  // namespace mla

@@ -36,12 +36,17 @@ struct GemmArgs {
   float eps = 0.f;
   bool gather = false;
   GatherA ga;
+  const void* zeros = nullptr;  // >= 16 zero bytes (source of absent rows for streamed tiles)
 };
 
 // Launch (choosing tile shape and split-K). `ws` is an fp32 workspace of
 // `ws_elems` floats used for split-K partial sums (may be null: no split-K).
 // Returns hipSuccess or the launch error. bf16 == true selects bf16 operands.
 hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_elems, hipStream_t s);
+
+// The 256 x 256 LDS-streaming kernel (gemm_big.hip) and when it applies.
+bool gemm_big_eligible(const GemmArgs& g, bool is_bf16);
+hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s);
 
 // Validation of the alignment and size assumptions of gemm_launch; returns
 // nullptr when fine, else a static message.

@@ -298,6 +298,7 @@ const char* gemm_check(const GemmArgs& g, bool is_bf16) {
 
 hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_elems, hipStream_t s) {
   if (g.M == 0) return hipSuccess;
+  if (g.zeros != nullptr && gemm_big_eligible(g, is_bf16)) return gemm_big_launch(g, g.zeros, s);
   return is_bf16 ? launch_t<bf16>(g, ws, ws_elems, s) : launch_t<float>(g, ws, ws_elems, s);
 }
 

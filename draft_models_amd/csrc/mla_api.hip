@@ -187,7 +187,9 @@ struct StageTimer {
   }
 };
 
-int run_gemm(mla_ctx* ctx, const GemmArgs& g, hipStream_t s) {
+int run_gemm(mla_ctx* ctx, const GemmArgs& g0, hipStream_t s) {
+  GemmArgs g = g0;
+  g.zeros = ctx->zeros;
   if (const char* m = gemm_check(g, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
   HIP_TRY(gemm_launch(g, ctx->bf16, ctx->gemm_ws, ctx->gemm_ws_elems, s));
   return MLA_OK;
