@@ -148,14 +148,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);  // finite: every tile has a visible key
-    const float alpha = exp2f(m - mnew);
+    const float alpha = fast_exp2(m - mnew);
     float sum = 0.f;
     Frag<T> pf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[kb][i] - mnew);
+        const float p = fast_exp2(s[kb][i] - mnew);
         sum += p;
         pf.v[kb * 4 + i] = from_f32<T>(p);
       }
@@ -431,14 +431,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(DecodeAttnArgs
     // it by more than 2^8 (probabilities stay <= 256, exact after the final
     // division by l); rescaling the accumulators is then rare
     const float mnew = (mx > m + 8.f) ? mx : m;
-    const float alpha = exp2f(m - mnew);
+    const float alpha = fast_exp2(m - mnew);
     float sum = 0.f;
     Frag<bf16> pf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[kb][i] - mnew);
+        const float p = fast_exp2(s[kb][i] - mnew);
         sum += p;
         pf.v[kb * 4 + i] = (bf16)p;
       }
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
   float den = 0.f;
   for (int s = 0; s < a.splits; ++s) {
     const float ls = a.part_lse[base + (int64_t)s * a.H];
-    if (ls != -INFINITY) den += exp2f(ls - mx);
+    if (ls != -INFINITY) den += fast_exp2(ls - mx);
   }
   const float inv = 1.f / den;
   for (int d = threadIdx.x; d < a.c; d += 256) {
@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
     for (int s = 0; s < a.splits; ++s) {
       const float ls = a.part_lse[base + (int64_t)s * a.H];
       if (ls == -INFINITY) continue;
-      acc += exp2f(ls - mx) * a.part_o[(base + (int64_t)s * a.H) * a.c + d];
+      acc += fast_exp2(ls - mx) * a.part_o[(base + (int64_t)s * a.H) * a.c + d];
     }
     dst[d] = from_f32<T>(acc * inv);
   }

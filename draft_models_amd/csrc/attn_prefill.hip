@@ -195,12 +195,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
       const float mnew = fmaxf(m[qb], mx);
       float alpha = 1.f, sum = 0.f;
       if (mnew != -INFINITY) {
-        alpha = exp2f(m[qb] - mnew);  // m = -inf -> 0
+        alpha = fast_exp2(m[qb] - mnew);  // m = -inf -> 0
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float p = exp2f(s[kb][qb][i] - mnew);  // masked -> 0
+            const float p = fast_exp2(s[kb][qb][i] - mnew);  // masked -> 0
             s[kb][qb][i] = p;
             sum += p;
           }
@@ -262,6 +262,313 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel for the DeepSeek head shape (n = 128, r = 64, dv = 128). One
+// workgroup = 4 wavefronts x 32 queries (two 16-query MFMA blocks each, so
+// every LDS fragment feeds two MFMAs) of one head. 64-key tiles stream from
+// HBM straight into LDS (global_load_lds_dwordx4), double-buffered: k_nope
+// and v rows of the expanded buffer through the scalar-base form, the shared
+// rope key from the paged cache. Rows are unpadded with XOR-swizzled 16-byte
+// chunks: by (row & 7) for the key tiles (conflict-free 16-byte score operand
+// reads) and by 2 (row & 7) for the value tile (chunk pairs stay adjacent;
+// the 8 rows read together by 32 lanes of transposing reads hit distinct banks). Tiles inside every query's visible interval skip the masking.
+// ---------------------------------------------------------------------------
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 tr_pair(const bf16* p0, const bf16* p1) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+namespace big {
+constexpr int KT = 64;                  // keys per tile
+constexpr int QB = 2;                   // 16-query blocks per wavefront
+constexpr int NW = 8;                   // wavefronts per workgroup (two per SIMD)
+constexpr int BQ = NW * 16 * QB;        // queries per workgroup
+constexpr int NOPE_CH = 16, PE_CH = 8, V_CH = 16;   // 16-byte chunks per key row
+__device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch + (c ^ (row & 7)); }
+__device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 7) << 1)); }
+}  // namespace big
+
+__global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnArgs a) {
+  using namespace big;
+  __shared__ __attribute__((aligned(16))) bf16x8 knope[2][KT * NOPE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 kpe[2][KT * PE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 vt[2][KT * V_CH];
+  __shared__ int iv[4];  // union lo, union hi, intersection lo, intersection hi
+
+  // heaviest (latest, for causal masks) query tiles first
+  const int qt = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int ql = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+  ql = min(max(ql, 0), a.max_q_len);
+  if (qt * BQ >= ql) return;
+  const int pl = min(max(a.prefix_lens[b], 0), a.max_kv_len - ql);
+  const int L = pl + ql;
+  const int t0 = a.cu_seqlens[b];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, g = lane >> 4;
+  const float sl2 = a.scale * kLog2e;
+
+  if (tid == 0) { iv[0] = 0x7fffffff; iv[1] = 0; iv[2] = 0; iv[3] = 0x7fffffff; }
+  __syncthreads();
+  int lo[QB], hi[QB], qi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qi[qb] = qt * BQ + wave * 16 * QB + qb * 16 + lr;
+    lo[qb] = 0; hi[qb] = 0;
+    if (qi[qb] < ql && t0 + qi[qb] < a.total_tokens) visible(a.mask, t0 + qi[qb], pl + qi[qb], L, lo[qb], hi[qb]);
+    if (g == 0 && lo[qb] < hi[qb]) {
+      atomicMin(&iv[0], lo[qb]);
+      atomicMax(&iv[1], hi[qb]);
+      atomicMax(&iv[2], lo[qb]);
+      atomicMin(&iv[3], hi[qb]);
+    }
+    if (g == 0 && qi[qb] < ql && lo[qb] >= hi[qb]) {  // an empty row: no tile is unmasked for it
+      atomicMax(&iv[2], 0x7fffffff);
+    }
+  }
+  __syncthreads();
+  const int kbeg = (iv[0] / KT) * KT, kend = iv[1];
+  const int in_lo = iv[2], in_hi = iv[3];  // tiles inside [in_lo, in_hi) need no mask
+
+  // queries in registers (B operand: column = query, 8 contraction elements)
+  Frag<bf16> qf[QB][6];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool qok = qi[qb] < ql && t0 + qi[qb] < a.total_tokens;
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + (int64_t)(t0 + (qok ? qi[qb] : 0)) * a.ldq +
+                       (int64_t)h * a.qk_head;
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
+      qf[qb][ks].v = qok ? v : bf16x8{};
+    }
+  }
+
+  // DMA geometry. k_nope / v: 16 chunks per key row, 4 instructions per wave
+  // each (rows 4 (4 j + wave) .. + 3); byte offsets relative to the tile's
+  // first key row of this head in the expanded buffer. k_pe: 8 chunks per row,
+  // 2 instructions per wave, per-lane 64-bit addresses (the rows of one tile
+  // may lie in two pages).
+  const bf16* kvb = reinterpret_cast<const bf16*>(a.kv) + (int64_t)b * a.max_kv_len * a.ldkv + (int64_t)h * (a.n + a.dv);
+  const int64_t row_bytes = a.ldkv * 2;
+  uint32_t noff[2], voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sl = (j * NW + wave) * 64 + lane;
+    const int row = sl / NOPE_CH, cs = sl % NOPE_CH;
+    noff[j] = (uint32_t)(row * row_bytes) + (uint32_t)((cs ^ (row & 7)) * 16);
+    const int cv = cs ^ ((row & 7) << 1);
+    voff[j] = (uint32_t)(row * row_bytes) + 256u + (uint32_t)(cv * 16);
+  }
+  const bf16* cache = reinterpret_cast<const bf16*>(a.cache);
+  const int E = a.c + a.r;
+  const int32_t* __restrict__ btab = a.block_table + (int64_t)b * a.max_blocks;
+  const uint32_t knope_lds = lds_addr(&knope[0][0]), vt_lds = lds_addr(&vt[0][0]), kpe_lds = lds_addr(&kpe[0][0]);
+  // k_pe: 8 chunks per row, 2 instructions per wave; byte offsets relative to
+  // the tile's first entry in its cache page (tiles never cross a page: they
+  // start at multiples of 64 keys and the page size is a multiple of 64)
+  uint32_t poff[1];
+#pragma unroll
+  for (int j = 0; j < 1; ++j) {
+    const int sl = (j * NW + wave) * 64 + lane;
+    const int row = sl / PE_CH, cs = sl % PE_CH;
+    poff[j] = (uint32_t)(row * E * 2) + (uint32_t)(a.c * 2) + (uint32_t)((cs ^ (row & 7)) * 16);
+  }
+  // block-table entries of the key range live in a register, one page per lane
+  int pbase = kbeg / a.page;
+  int btreg = (pbase + lane < a.max_blocks) ? btab[pbase + lane] : -1;
+
+  auto issue = [&](int k0, int buf) {
+    // rows past the last key re-read the last key (their scores are masked)
+    const int last = min(kend, L) - 1;
+    const int rows_valid = last - k0 + 1;
+    const bf16* base = kvb + (int64_t)k0 * a.ldkv;
+    const int pg = k0 / a.page;
+    if (pg - pbase >= 64) {
+      pbase = pg;
+      btreg = (pbase + lane < a.max_blocks) ? btab[pbase + lane] : -1;
+    }
+    int blk = __builtin_amdgcn_readlane(btreg, pg - pbase);
+    if (blk < 0 || blk >= a.num_blocks) blk = 0;  // unmapped page: any valid memory (output is garbage-in)
+    const bf16* pbase_ptr = cache + ((int64_t)blk * a.page + (k0 - pg * a.page)) * E;
+    const uint32_t nb = knope_lds + (uint32_t)(buf * KT * NOPE_CH * 16);
+    const uint32_t vb = vt_lds + (uint32_t)(buf * KT * V_CH * 16);
+    const uint32_t pb = kpe_lds + (uint32_t)(buf * KT * PE_CH * 16);
+    if (rows_valid >= KT) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dma16_sbase(noff[j], base, nb + (uint32_t)(j * NW + wave) * 1024u);
+        dma16_sbase(voff[j], base, vb + (uint32_t)(j * NW + wave) * 1024u);
+      }
+      dma16_sbase(poff[0], pbase_ptr, pb + (uint32_t)wave * 1024u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sl = (j * NW + wave) * 64 + lane;
+        const int row = sl / NOPE_CH;
+        const uint32_t back = row >= rows_valid ? (uint32_t)((row - rows_valid + 1) * row_bytes) : 0u;
+        dma16_sbase(noff[j] - back, base, nb + (uint32_t)(j * NW + wave) * 1024u);
+        dma16_sbase(voff[j] - back, base, vb + (uint32_t)(j * NW + wave) * 1024u);
+      }
+      {
+        const int row = (wave * 64 + lane) / PE_CH;
+        const uint32_t back = row >= rows_valid ? (uint32_t)((row - rows_valid + 1) * E * 2) : 0u;
+        dma16_sbase(poff[0] - back, pbase_ptr, pb + (uint32_t)wave * 1024u);
+      }
+    }
+  };
+
+  floatx4 o[8][QB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY; l[qb] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int ra = lr >> 2, rb = lr & 3;
+  const bool active = qt * BQ + wave * 16 * QB < ql;
+
+  MLA_WAIT_VMCNT(0);  // query fragments landed: in the loop only tile copies are outstanding
+  if (kbeg < kend) issue(kbeg, 0);
+  int buf = 0;
+  for (int k0 = kbeg; k0 < kend; k0 += KT, buf ^= 1) {
+    if (k0 + KT < kend) {
+      issue(k0 + KT, buf ^ 1);
+      MLA_WAIT_VMCNT(5);  // 2 + 2 + 1 copies per wave of the next tile may stay in flight
+    } else {
+      MLA_WAIT_VMCNT(0);
+    }
+    lds_barrier();
+    const bf16x8* KN = knope[buf];
+    const bf16x8* KP = kpe[buf];
+    const bf16x8* VT = vt[buf];
+    if (!active) {  // no query of this wavefront exists: it only helps stream tiles
+      lds_barrier();
+      continue;
+    }
+
+    // ---- S^T = K Q^T: s[kb][qb][i] = key k0 + 16 kb + 4 g + i, query lr of block qb
+    floatx4 s[4][QB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 6; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        Frag<bf16> kf;
+        const int row = kb * 16 + lr;
+        kf.v = ks < 4 ? KN[kslot(row, ks * 4 + g, NOPE_CH)] : KP[kslot(row, (ks - 4) * 4 + g, PE_CH)];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16(kf, qf[qb][ks], s[kb][qb]);
+      }
+    }
+
+    // ---- online softmax (log2 domain) with lazy rescaling
+    const bool needmask = !(k0 >= in_lo && k0 + KT <= in_hi);
+    Frag<bf16> pf[QB][2];
+    float alpha[QB];
+    bool rescale = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[kb][qb][i] * sl2;
+          if (needmask) {
+            const int key = k0 + kb * 16 + g * 4 + i;
+            if (key < lo[qb] || key >= hi[qb]) x = -INFINITY;
+          }
+          s[kb][qb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = (mx > m[qb] + 8.f) ? mx : m[qb];
+      // rows with nothing visible so far keep m = -inf and p = 0
+      alpha[qb] = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
+      rescale |= mnew != m[qb];
+      float sum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (mnew == -INFINITY) ? 0.f : fast_exp2(s[kb][qb][i] - mnew);
+          s[kb][qb][i] = p;
+          sum += p;
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      l[qb] = l[qb] * alpha[qb] + sum;
+      m[qb] = mnew;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pf[qb][k2].v[e] = (bf16)s[2 * k2][qb][e];
+          pf[qb][k2].v[4 + e] = (bf16)s[2 * k2 + 1][qb][e];
+        }
+    }
+    if (__any(rescale)) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[d][qb] *= alpha[qb];
+    }
+
+    // ---- O^T += V^T P^T; transposed V operand from the row-major tile: lane
+    // k = 4 a + b' of a 16-lane group points at key row 32 k2 + 4 g + a [+16],
+    // dims 16 d + 4 b' .. + 3, and receives keys 32 k2 + 4 g + {0..3} [+16] of dim 16 d + lr
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int el = d * 16 + rb * 4;
+      const int c = el >> 3, half = (el >> 2) & 1;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int r0 = k2 * 32 + g * 4 + ra;
+        Frag<bf16> vf;
+        vf.v = tr_pair(reinterpret_cast<const bf16*>(&VT[vslot(r0, c)]) + half * 4,
+                       reinterpret_cast<const bf16*>(&VT[vslot(r0 + 16, c)]) + half * 4);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma16(vf, pf[qb][k2], o[d][qb]);
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- epilogue: lane holds O[query lr][d .. d+3], d = 16 db + 4 g
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (qi[qb] >= ql) continue;
+    const int t = t0 + qi[qb];
+    if (t >= a.total_tokens) continue;
+    const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+    bf16* orow = reinterpret_cast<bf16*>(a.out) + (int64_t)t * a.ldo + (int64_t)h * a.dv;
+    const bf16* grow = a.gate ? reinterpret_cast<const bf16*>(a.gate) + (int64_t)t * a.ldg + (int64_t)h * a.dv : nullptr;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int d0 = d * 16 + g * 4;
+      floatx4 v = o[d][qb] * inv;
+      if (grow) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= sigmoidf((float)grow[d0 + i]);
+      }
+      *reinterpret_cast<bf16x4*>(orow + d0) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    }
+  }
+}
+
 template <typename T, int DQK, int DV>
 hipError_t launch_dims(const PrefillAttnArgs& a, hipStream_t s) {
   // one 16-query block per wave for short query runs (draft blocks), two otherwise
@@ -295,6 +602,11 @@ const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16) {
 
 hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s) {
   if (a.batch <= 0 || a.max_q_len <= 0) return hipSuccess;
+  if (is_bf16 && a.n == 128 && a.r == 64 && a.dv == 128 && a.c % 8 == 0 && a.page % big::KT == 0) {
+    dim3 grid((a.max_q_len + big::BQ - 1) / big::BQ, a.H, a.batch);
+    hipLaunchKernelGGL(prefill_attn_bf16_kernel, grid, dim3(64 * big::NW), 0, s, a);
+    return hipGetLastError();
+  }
   return is_bf16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
 }
 

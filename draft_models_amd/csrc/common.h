@@ -101,6 +101,10 @@ __device__ __forceinline__ void lds_barrier() {
 // vmcnt(n) with expcnt / lgkmcnt unconstrained (gfx9 s_waitcnt encoding)
 #define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
+// 2^x with the hardware instruction (v_exp_f32; results below 2^-126 flush to
+// zero, which is harmless for softmax weights)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // logistic sigmoid with the hardware reciprocal (v_rcp_f32, ~1 ulp)
 __device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
