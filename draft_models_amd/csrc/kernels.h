@@ -67,11 +67,23 @@ struct DecodeAttnArgs {
   float* part_lse = nullptr;                        // [B, splits, H]
   void* o_lat = nullptr;                            // [B, H, c] combined latent output
   const bf16_t* zeros = nullptr;                    // >= 16 zero bytes (tile padding source)
+  // stream-K partition (512 + 64 bf16 latent): `ranges` workgroup ranges,
+  // pieces in part_o [2 ranges, H, c] / part_lse [2 ranges, H]
+  int ranges = 0;
+  int32_t* tstart = nullptr;                        // [batch + 1] first tile of every sequence
 };
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
-// heads handled by one workgroup of the decode kernel chosen for `a`
-int decode_heads_per_group(const DecodeAttnArgs& a, bool is_bf16);
 const char* decode_attn_check(const DecodeAttnArgs& a, bool is_bf16);
+
+// Stream-K decode of the 512 + 64 bf16 latent (attn_decode_sk.hip).
+constexpr int kDecodeMaxTiles = 256;   // 32-key tiles per workgroup range
+constexpr int kDecodeMaxBatch = 1024;  // sequences per call
+// nullptr when `a` (with ranges / workspaces filled in) can take this path
+const char* decode_sk_check(const DecodeAttnArgs& a);
+// ranges for `batch` sequences of at most `max_visible` visible keys on `cus` compute units
+int decode_sk_ranges(int batch, int max_visible, int cus);
+hipError_t decode_sk_launch(const DecodeAttnArgs& a, hipStream_t s);
+hipError_t decode_sk_merge_launch(const DecodeAttnArgs& a, hipStream_t s);
 
 }  // namespace mla

@@ -1,6 +1,7 @@
 // C ABI of the MLA forward: context creation (validation, weight repacking,
 // workspaces) and the stream-ordered launch sequences of the expanded prefill
 // and the absorbed decode.
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -41,6 +42,10 @@ struct mla_ctx {
   float* part_o = nullptr;
   float* part_lse = nullptr;
   int max_splits = 32;
+  int cus = 256;            // compute units of the device
+  bool sk_shape = false;    // bf16 512 + 64 latent: stream-K decode
+  int sk_max_ranges = 0;
+  int32_t* sk_tstart = nullptr;
   float* gemm_ws = nullptr;
   int64_t gemm_ws_elems = 0;
   void* zeros = nullptr;   // 256 zero bytes: source of padding chunks in streamed tiles
@@ -332,9 +337,24 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   if ((e = dev_alloc(ctx, &ctx->qlat, (size_t)B * H * ctx->c * esz))) return bail(e);
   if ((e = dev_alloc(ctx, &ctx->olat, (size_t)B * H * ctx->c * esz))) return bail(e);
   void* p;
-  if ((e = dev_alloc(ctx, &p, (size_t)B * ctx->max_splits * H * ctx->c * sizeof(float)))) return bail(e);
+  if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess ||
+      ctx->cus <= 0)
+    return bail(fail(MLA_ERR_HIP, "querying the compute-unit count failed"));
+  ctx->sk_shape = ctx->bf16 && ctx->c == 512 && ctx->r == 64 && H <= 128 && cfg->page_size % 32 == 0;
+  // decode partials: stream-K pieces [2 ranges, H, c] for batches it covers,
+  // per-split partials [B, splits, H, c] otherwise
+  int64_t part_rows = 0;
+  if (ctx->sk_shape) {
+    const int skb = (int)std::min<int64_t>(B, kDecodeMaxBatch);
+    ctx->sk_max_ranges = decode_sk_ranges(skb, cfg->max_seq_len, ctx->cus);
+    part_rows = 2 * (int64_t)ctx->sk_max_ranges;
+    if ((e = dev_alloc(ctx, &p, (size_t)(skb + 1) * sizeof(int32_t)))) return bail(e);
+    ctx->sk_tstart = static_cast<int32_t*>(p);
+  }
+  if (!ctx->sk_shape || B > kDecodeMaxBatch) part_rows = std::max<int64_t>(part_rows, B * ctx->max_splits);
+  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * H * ctx->c * sizeof(float)))) return bail(e);
   ctx->part_o = static_cast<float*>(p);
-  if ((e = dev_alloc(ctx, &p, (size_t)B * ctx->max_splits * H * sizeof(float)))) return bail(e);
+  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * H * sizeof(float)))) return bail(e);
   ctx->part_lse = static_cast<float*>(p);
   ctx->gemm_ws_elems = (int64_t)16 << 20;
   if ((e = dev_alloc(ctx, &p, (size_t)ctx->gemm_ws_elems * sizeof(float)))) return bail(e);
@@ -487,19 +507,7 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
     if (int e = run_gemm(ctx, ga, s)) return e;
   }
 
-  // split-KV sizing from the longest visible range (keys per split a multiple of 32)
   DecodeAttnArgs da;
-  da.c = ctx->c; da.r = ctx->r; da.page = c.page_size; da.H = H;
-  const int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
-  const int hpg = decode_heads_per_group(da, ctx->bf16);
-  const int groups = (H + hpg - 1) / hpg;
-  int want = (512 + batch * groups - 1) / (batch * groups);
-  want = std::max(1, std::min(want, ctx->max_splits));
-  int chunk = std::max(1, (max_vis + want - 1) / want);
-  chunk = std::max(64, ((chunk + 31) / 32) * 32);
-  const int splits = std::max(1, std::min(ctx->max_splits, (max_vis + chunk - 1) / chunk));
-  if ((int64_t)splits * chunk < max_vis) chunk = ((max_vis + splits - 1) / splits + 31) / 32 * 32;
-
   da.ql = ctx->qlat; da.ldql = (int64_t)H * ctx->c;
   da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
   da.cache = kv_cache; da.block_table = block_table;
@@ -508,18 +516,43 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   da.H = H; da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
   da.scale = ctx->scale;
   da.mask.kind = mask_kind; da.mask.window = window;
-  da.chunk = chunk; da.splits = splits;
   da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
   da.o_lat = ctx->olat;
   da.zeros = static_cast<const bf16_t*>(ctx->zeros);
-  if (const char* m = decode_attn_check(da, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
-  {
-    StageTimer st(ctx, s, ST_DECODE_ATTN);
-    HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
-  }
-  {
-    StageTimer st(ctx, s, ST_DECODE_MERGE);
-    HIP_TRY(decode_merge_launch(da, ctx->bf16, s));
+  const int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+  if (ctx->sk_shape && batch <= kDecodeMaxBatch) {
+    // stream-K: equal tile ranges over all sequences, pieces merged afterwards
+    da.ranges = decode_sk_ranges(batch, max_vis, ctx->cus);
+    da.tstart = ctx->sk_tstart;
+    if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
+    if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
+    {
+      StageTimer st(ctx, s, ST_DECODE_ATTN);
+      HIP_TRY(decode_sk_launch(da, s));
+    }
+    {
+      StageTimer st(ctx, s, ST_DECODE_MERGE);
+      HIP_TRY(decode_sk_merge_launch(da, s));
+    }
+  } else {
+    // split-KV sizing from the longest visible range (keys per split a multiple of 32)
+    const int groups = (H + 63) / 64;
+    int want = (512 + batch * groups - 1) / (batch * groups);
+    want = std::max(1, std::min(want, ctx->max_splits));
+    int chunk = std::max(1, (max_vis + want - 1) / want);
+    chunk = std::max(64, ((chunk + 31) / 32) * 32);
+    const int splits = std::max(1, std::min(ctx->max_splits, (max_vis + chunk - 1) / chunk));
+    if ((int64_t)splits * chunk < max_vis) chunk = ((max_vis + splits - 1) / splits + 31) / 32 * 32;
+    da.chunk = chunk; da.splits = splits;
+    if (const char* m = decode_attn_check(da, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
+    {
+      StageTimer st(ctx, s, ST_DECODE_ATTN);
+      HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
+    }
+    {
+      StageTimer st(ctx, s, ST_DECODE_MERGE);
+      HIP_TRY(decode_merge_launch(da, ctx->bf16, s));
+    }
   }
 
   // W_UV: out_v[b, h] = o_lat[b, h] . W_UV[h]^T (per head: [B, c] x [c, dv]), gated

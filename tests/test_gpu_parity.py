@@ -74,6 +74,22 @@ def test_decode_small():
     _run_and_check(w)
 
 
+def test_decode_window_edges():
+    """Sliding windows whose first visible key is not a multiple of the
+    32-key tile, lengths around tile and page edges."""
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 31, 32, 33, 95, 130, 700], mask_kind=ms.MASK_SLIDING,
+                         window=33, seed=18)
+    _run_and_check(w)
+
+
+def test_decode_window_zero_bf16():
+    """No visible key (window 0): the attention output, hence the layer
+    output, is exactly zero for every sequence."""
+    w = ms.make_workload("decode_bf16", seq_lens=[5, 64, 300], mask_kind=ms.MASK_SLIDING, window=0, seed=19)
+    out, _ = U.run_gpu(w)
+    assert np.all(out == 0)
+
+
 def test_prefill_small():
     w = ms.make_workload("prefill_bf16", q_lens=[300, 129], prefix_lens=[0, 0])
     _run_and_check(w)
