@@ -22,13 +22,20 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hi
          "-I", os.path.join(PKG, "..", "include")]
 
 
+# Per-file code-generation options. The stream-K decode keeps its latent
+# output accumulators in VGPRs (its rare rescale multiplies them there) and its
+# queries in AGPRs; with the VGPR form of MFMA the accumulators are not moved
+# between the two register files every tile.
+FILE_FLAGS = {"attn_decode_sk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the gfx950 target feature; that warning is expected
     noise = "is not a recognized feature for this target"

@@ -12,16 +12,22 @@
 // sequence are written as partial outputs with their log-sum-exp and merged
 // by a second kernel with log-sum-exp weights.
 //
-// Inside a workgroup: 8 wavefronts, wavefront w owns heads 16 w .. 16 w + 15
-// of the (at most 128) heads, so each workgroup reads every tile once from
-// HBM for all heads. A wavefront keeps its latent queries in registers (the
-// B operand of S^T = C q^T: 16 heads x 576 dims, 72 VGPRs) and its latent
-// output O^T (512 dims x 16 heads, fp32, 128 VGPRs); two wavefronts share a
-// SIMD. Tiles stream from HBM straight into LDS (global_load_lds_dwordx4)
-// through a ring of NBUF buffers; the scores read 16-byte key-row fragments
-// and the value product reads the same rows through the transposing LDS read
-// (ds_read_b64_tr_b16), so the tile is stored once, row-major, with a swizzle
-// that keeps both access patterns free of bank conflicts.
+// Inside a workgroup: 8 wavefronts and all (at most 128) heads, so each
+// workgroup reads every tile once from HBM. The score product is split by
+// head: wavefront w computes the scores and the online softmax of heads
+// 16 w .. 16 w + 15 over all 576 dims, its latent queries held in registers.
+// The value product is split by latent dim: wavefront w accumulates
+// O^T = C^T P^T for latent dims 64 w .. 64 w + 63 and all heads, reading the
+// probabilities of every head block (bf16, 1 KB per block) and the rare
+// rescale factors that the other wavefronts shared through LDS. So the
+// transposing reads of the values touch each tile byte once per workgroup,
+// and the queries (72 VGPRs) plus outputs (128 VGPRs) of a wavefront fit two
+// wavefronts per SIMD. Tiles stream from HBM straight into LDS
+// (global_load_lds_dwordx4) through a ring of NBUF buffers; the scores read
+// 16-byte key-row fragments and the value product reads the same rows through
+// the transposing LDS read (ds_read_b64_tr_b16), so the tile is stored once,
+// row-major, with a swizzle that keeps both access patterns free of bank
+// conflicts.
 #include <algorithm>
 
 #include "common.h"
@@ -34,20 +40,24 @@ namespace {
 constexpr int KT = 32;              // keys per tile
 constexpr int ECH = 72;             // 16-byte chunks per 576-wide bf16 entry
 constexpr int SLOTS = KT * ECH;     // 16-byte chunks per tile
-constexpr int NW = 8;               // wavefronts per workgroup, 16 heads each
+constexpr int NW = 8;               // wavefronts per workgroup
 constexpr int NT = NW * 64;         // threads per workgroup
 constexpr int DMA_N = (SLOTS + NT - 1) / NT;  // DMA instructions per lane per tile (the last one partial)
 constexpr int KS = 18;              // 32-dim steps of the score product
 constexpr int DB = 32;              // 16-dim blocks of the 512 value dims
+constexpr int DBW = DB / NW;        // value blocks of one wavefront (64 latent dims)
+constexpr int HBW = NW;             // 16-head blocks of a workgroup (128 heads)
+static_assert(HBW == 8, "the rescale flags of the head blocks are read as one 8-byte word");
 constexpr int ROWB = ECH * 16;      // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
-static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots");
+static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane DMA instructions");
 
-// Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ f(row))
-// of the row. f maps 8 consecutive rows to 8 distinct values (16-byte score
-// reads: 8 rows, one chunk) and any 4 rows 4a .. 4a + 3 to distinct pairs
-// {2k, 2k + 1} (transposing reads: 4 rows x 2 adjacent chunks).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ (row & 7))
+// of the row (rows are 72 chunks = 1152 bytes). Measured on gfx950 with the
+// LDS bank-conflict counter, this XOR keeps both access patterns of the tile
+// conflict free: 16-byte score reads (16 rows, one chunk) and transposing
+// value reads (4 rows x 2 adjacent chunks per 16 lanes).
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -87,6 +97,10 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   __shared__ int t_lo[kDecodeMaxTiles], t_hi[kDecodeMaxTiles];
   __shared__ int t_end[kDecodeMaxTiles];  // end (local index) of the tile's piece
   __shared__ int wsum[NW];
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[HBW][64];  // probabilities of every head block
+  __shared__ float abuf[HBW][16];                                // rescale factors of every head
+  __shared__ __attribute__((aligned(8))) unsigned char aflag[HBW];  // head block needs a rescale
+  __shared__ float mbuf[HBW][16], lbuf[HBW][16];                 // softmax state at a piece's end
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,18 +178,18 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
 
   // ---- DMA geometry: instruction j of this wavefront fills tile slots
   // [(NW j + wave) 64, +64) (the last instruction only on the first waves);
-  // the lane's slot holds chunk c of row `row`
-  uint32_t voff[DMA_N];
-#pragma unroll
-  for (int j = 0; j < DMA_N; ++j) {
-    const int p = min((j * NW + wave) * 64 + lane, SLOTS - 1);
-    const int row = p / ECH, pc = p % ECH;
-    const int c = (pc & ~7) | ((pc & 7) ^ swz(row));
-    voff[j] = (uint32_t)(row * ROWB + c * 16);
-  }
+  // the lane's slot holds chunk c of row `row`. The byte offsets are derived
+  // at every issue from an opaque zero, so that they are not hoisted into
+  // registers that would stay live across the whole loop.
   const bool last_dma = (DMA_N - 1) * NW * 64 + wave * 64 < SLOTS;  // this wave issues instruction DMA_N - 1
   const char* cache = reinterpret_cast<const char*>(a.cache);
   const uint32_t tile_lds = lds_addr(&tile[0][0]);
+  auto slot_offset = [&](int j, uint32_t z) {
+    const uint32_t p = min((uint32_t)((j * NW + wave) * 64 + lane) + z, (uint32_t)(SLOTS - 1));
+    const uint32_t row = p / ECH, pc = p % ECH;
+    const uint32_t c = (pc & ~7u) | ((pc & 7u) ^ (uint32_t)swz((int)row));
+    return row * ROWB + c * 16u;
+  };
 
   auto issue = [&](int i, int buf) {
     const int ent = __builtin_amdgcn_readfirstlane(t_ent[i]);
@@ -183,23 +197,20 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     const int lo = __builtin_amdgcn_readfirstlane(t_lo[i]);
     const int hi = __builtin_amdgcn_readfirstlane(t_hi[i]);
     const uint32_t dst = tile_lds + (uint32_t)buf * (SLOTS * 16) + (uint32_t)wave * 1024u;
+    uint32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
     if (ent >= 0 && k0 >= lo && k0 + KT <= hi) {
       const char* base = cache + (int64_t)ent * ROWB;
 #pragma unroll
       for (int j = 0; j < DMA_N; ++j)
-        if (j < DMA_N - 1 || last_dma) dma16_sbase(voff[j], base, dst + (uint32_t)j * (NW * 1024u));
+        if (j < DMA_N - 1 || last_dma) dma16_sbase(slot_offset(j, z), base, dst + (uint32_t)j * (NW * 1024u));
     } else {
-      // edge tile: rows outside [lo, hi) and unmapped pages read the zero page.
-      // The row is re-derived here from the slot offset (through an opaque
-      // zero, so that nothing of this rare path is hoisted into registers
-      // that stay live across the loop).
-      uint32_t z;
-      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      // edge tile: rows outside [lo, hi) and unmapped pages read the zero page
       const char* base = cache + (int64_t)(ent < 0 ? 0 : ent) * ROWB;
 #pragma unroll
       for (int j = 0; j < DMA_N; ++j) {
         if (j == DMA_N - 1 && !last_dma) continue;
-        const uint32_t off = voff[j] + z;
+        const uint32_t off = slot_offset(j, z);
         const int key = k0 + (int)(off / ROWB);
         const bool ok = ent >= 0 && key >= lo && key < hi;
         const void* src = ok ? (const void*)(base + off) : (const void*)a.zeros;
@@ -207,21 +218,23 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       }
     }
   };
+
   // ---- per-lane LDS read bases (bytes). Scores: rows lr and 16 + lr, chunk
-  // 4 s + g. Values (transposing reads): lane k = 4 qa + qb of its 16-lane
-  // group points at rows 4 g + qa (and 16 + 4 g + qa), dims 16 d + 4 qb .. + 3.
-  int kbase[2], vbase[4];
+  // 4 s + g. Values (transposing reads) of this wavefront's 64 latent dims:
+  // lane k = 4 qa + qb of its 16-lane group points at rows 4 g + qa (and
+  // 16 + 4 g + qa), dims 64 wave + 16 d + 4 qb .. + 3.
+  int kbase[2], vrow, vx;
 #pragma unroll
   for (int x = 0; x < 2; ++x) kbase[x] = (lr * ECH + ((4 * x + g) ^ swz(lr))) * 16;
   {
+    // chunk 8 wave + (2 d + (qb >> 1)) of the row, the low 3 bits XOR-ed with swz(row)
     const int qa = lr >> 2, qb = lr & 3;
     const int row = 4 * g + qa;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) vbase[x] = (row * ECH + ((2 * x + (qb >> 1)) ^ swz(row))) * 16 + (qb & 1) * 8;
+    vrow = (row * ECH + 8 * wave) * 16 + (qb & 1) * 8;
+    vx = (qb >> 1) ^ swz(row);
   }
 
-  const int h = wave * 16 + lr;  // this lane's head
-  const bool active = wave * 16 < a.H;
+  const int h = wave * 16 + lr;  // head of this lane's scores and softmax
   const bool hok = h < a.H;
   const float sl2 = a.scale * kLog2e;
 
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     const int hi = __builtin_amdgcn_readfirstlane(t_hi[i]);
     const bool piece_start = __builtin_amdgcn_readfirstlane(t_k0[i]) == (lo / KT) * KT;
 
-    // latent query of this lane's head: B operand of S^T, dims 32 s + 8 g .. + 7
+    // latent query of head h: B operand of S^T, dims 32 s + 8 g .. + 7
     Frag<bf16> q[KS];
     {
       const bf16* ql = reinterpret_cast<const bf16*>(a.ql) + (int64_t)b * a.ldql + (int64_t)(hok ? h : 0) * a.c;
@@ -253,9 +266,12 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     // the queries, and the outputs stored by the previous piece (stores may
     // complete out of order with loads): wait for everything
     MLA_WAIT_VMCNT(0);
-    floatx4 o[DB];
+    // O^T blocks: latent dims 64 wave + 16 d + 4 g + {0..3}, head 16 hb + lr
+    floatx4 o[DBW][HBW];
 #pragma unroll
-    for (int d = 0; d < DB; ++d) o[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < DBW; ++d)
+#pragma unroll
+      for (int hb = 0; hb < HBW; ++hb) o[d][hb] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.f;
 
     for (; i < iend; ++i) {
@@ -264,13 +280,12 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       if (later <= 0) MLA_WAIT_VMCNT(0);
       else if (later == 1) { if (last_dma) MLA_WAIT_VMCNT(DMA_N); else MLA_WAIT_VMCNT(DMA_N - 1); }
       else { if (last_dma) MLA_WAIT_VMCNT(2 * DMA_N); else MLA_WAIT_VMCNT(2 * DMA_N - 2); }
-      lds_barrier();  // tile i is in LDS for every wavefront; tile i - 1 is no longer read
+      lds_barrier();  // tile i is in LDS for every wavefront; tile i - 1 and the shared probabilities are no longer read
       if (i + NBUF - 1 < n) issue(i + NBUF - 1, (i + NBUF - 1) % NBUF);
-      if (!active) continue;
       const int k0 = __builtin_amdgcn_readfirstlane(t_k0[i]);
       const char* Tb = reinterpret_cast<const char*>(&tile[buf][0]);
 
-      // ---- S^T (32 keys x 16 heads) = C q^T over the 576 dims
+      // ---- S^T (32 keys x the 16 heads of this wavefront) = C q^T over the 576 dims
       floatx4 sc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         sc[1] = mfma16(k1f, q[s], sc[1]);
       }
 
-      // ---- online softmax (log2 domain); lane holds keys 16 kb + 4 g + e of head h
+      // ---- online softmax of head h (log2 domain); lane holds keys 16 kb + 4 g + e
       const bool edge = k0 < lo || k0 + KT > hi;
       float mx = -INFINITY;
 #pragma unroll
@@ -315,54 +330,94 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         }
       l = l * alpha + sum;
       m = mnew;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int d = 0; d < DB; ++d) o[d] *= alpha;
-      }
+      // share the probabilities (the B operand of head block `wave`) and the
+      // rescale factors with the wavefronts that own the other latent dims
+      pbuf[wave][lane] = pf.v;
+      const bool resc = __any(alpha != 1.f);
+      if (resc && g == 0) abuf[wave][lr] = alpha;
+      if (lane == 0) aflag[wave] = resc ? 1 : 0;
+      lds_barrier();
 
-      // ---- O^T (512 dims x 16 heads) += C^T P^T; operand element e of lane
-      // (g, lr) is key 16 (e / 4) + 4 g + e % 4, the order the scores came in
+      // ---- O^T (this wavefront's 64 latent dims x 128 heads) += C^T P^T;
+      // operand element e of lane (g, lr) is key 16 (e / 4) + 4 g + e % 4,
+      // the order the scores came in
+      // one 8-byte read of all the rescale flags (rare: lazy rescaling)
+      const uint64_t flags = *reinterpret_cast<const uint64_t*>(aflag);
+      if (__builtin_amdgcn_readfirstlane((uint32_t)flags) | __builtin_amdgcn_readfirstlane((uint32_t)(flags >> 32))) {
 #pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const char* p = Tb + vbase[d & 3] + (d >> 2) * 128;
-        Frag<bf16> vf;
-        vf.v = tr_pair(p, p + 16 * ROWB);
-        o[d] = mfma16(vf, pf, o[d]);
+        for (int hb = 0; hb < HBW; ++hb) {
+          if ((flags >> (8 * hb)) & 0xff) {
+            const float al = abuf[hb][lr];
+#pragma unroll
+            for (int d = 0; d < DBW; ++d) o[d][hb] *= al;
+          }
+        }
+      }
+      Frag<bf16> vf[DBW];
+#pragma unroll
+      for (int d = 0; d < DBW; ++d) {
+        const char* p = Tb + vrow + ((2 * d) ^ vx) * 16;
+        vf[d].v = tr_pair(p, p + 16 * ROWB);
+      }
+#pragma unroll
+      for (int hb = 0; hb < HBW; ++hb) {
+        Frag<bf16> ph;
+        ph.v = pbuf[hb][lane];
+#pragma unroll
+        for (int d = 0; d < DBW; ++d) o[d][hb] = mfma16(vf[d], ph, o[d][hb]);
       }
     }
-    if (active) {
-      // ---- finish this piece of sequence b: whole sequence -> normalised
-      // latent output; a cut piece -> partial output + log-sum-exp in slot 1
-      // (piece starts the sequence, range ends inside it) or slot 0 (the
-      // range starts inside the sequence)
-      const int klast = __builtin_amdgcn_readfirstlane(t_k0[iend - 1]);
-      const bool whole = piece_start && klast + KT >= hi;
-      const int64_t slot = 2 * (int64_t)r + (piece_start ? 1 : 0);
+
+    // ---- finish this piece of sequence b: whole sequence -> normalised latent
+    // output; a cut piece -> partial output + log-sum-exp in slot 1 (piece
+    // starts the sequence, range ends inside it) or slot 0 (the range starts
+    // inside the sequence). Each head's softmax state comes from the
+    // wavefront that owns its scores.
+    {
       float lsum = l;
       lsum += __shfl_xor(lsum, 16);
       lsum += __shfl_xor(lsum, 32);
-      const float inv = 1.f / lsum;
-      if (hok) {
-        if (whole) {
-          bf16* dst = reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + h) * a.c + g * 4;
+      if (g == 0) {
+        mbuf[wave][lr] = m;
+        lbuf[wave][lr] = lsum;
+      }
+      lds_barrier();
+      const int klast = __builtin_amdgcn_readfirstlane(t_k0[iend - 1]);
+      const bool whole = piece_start && klast + KT >= hi;
+      const int64_t slot = 2 * (int64_t)r + (piece_start ? 1 : 0);
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const floatx4 v = o[d] * inv;
+      for (int hb = 0; hb < HBW; ++hb) {
+        const int hh = hb * 16 + lr;
+        if (hh >= a.H) continue;
+        const float inv = 1.f / lbuf[hb][lr];
+        if (whole) {
+          bf16* dst = reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + hh) * a.c + wave * 64 + g * 4;
+#pragma unroll
+          for (int d = 0; d < DBW; ++d) {
+            const floatx4 v = o[d][hb] * inv;
             *reinterpret_cast<bf16x4*>(dst + d * 16) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
           }
         } else {
-          float* dst = a.part_o + (slot * a.H + h) * a.c + g * 4;
+          // partial output, normalised by its own sum, stored as bf16 (the
+          // merged latent output is rounded to bf16 in any case)
+          bf16* dst = reinterpret_cast<bf16*>(a.part_o) + (slot * a.H + hh) * a.c + wave * 64 + g * 4;
 #pragma unroll
-          for (int d = 0; d < DB; ++d) *reinterpret_cast<floatx4*>(dst + d * 16) = o[d] * inv;
-          if (g == 0) a.part_lse[slot * a.H + h] = m + __log2f(lsum);
+          for (int d = 0; d < DBW; ++d) {
+            const floatx4 v = o[d][hb] * inv;
+            *reinterpret_cast<bf16x4*>(dst + d * 16) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+          }
         }
       }
+      if (!whole && g == 0 && hok) a.part_lse[slot * a.H + h] = m + __log2f(lsum);
     }
   }
 }
 
 // o_lat of the sequences that were cut between ranges: log-sum-exp weighted
 // sum of the pieces' normalised outputs; sequences with no visible key get 0.
+// Tile-to-range arithmetic in double: exact for the integer sizes involved.
+__device__ __forceinline__ int range_start_d(int r, int R, int T) { return (int)floor((double)r * T / R); }
+
 __global__ __launch_bounds__(256) void decode_sk_merge_kernel(DecodeAttnArgs a) {
   const int b = blockIdx.y;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -376,30 +431,26 @@ __global__ __launch_bounds__(256) void decode_sk_merge_kernel(DecodeAttnArgs a) 
     return;
   }
   // range holding tile x: the largest g with range_start(g) <= x
-  auto range_of = [&](int x) { return (int)((((int64_t)x + 1) * R + T - 1) / T) - 1; };
+  auto range_of = [&](int x) { return (int)ceil((double)(x + 1) * R / T) - 1; };
   const int gs = range_of(ts), ge = range_of(te - 1);
   if (gs == ge) return;  // finished inside one range
+  const bf16* po = reinterpret_cast<const bf16*>(a.part_o);
   float mx = -INFINITY;
   for (int gg = gs; gg <= ge; ++gg) {
-    if (gg > gs && range_start(gg + 1, R, T) == range_start(gg, R, T)) continue;  // empty range
+    if (gg > gs && range_start_d(gg + 1, R, T) == range_start_d(gg, R, T)) continue;  // empty range
     const int64_t slot = 2 * (int64_t)gg + (gg == gs ? 1 : 0);
     mx = fmaxf(mx, a.part_lse[slot * a.H + h]);
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   for (int gg = gs; gg <= ge; ++gg) {
-    if (gg > gs && range_start(gg + 1, R, T) == range_start(gg, R, T)) continue;
+    if (gg > gs && range_start_d(gg + 1, R, T) == range_start_d(gg, R, T)) continue;
     const int64_t slot = 2 * (int64_t)gg + (gg == gs ? 1 : 0);
     const float w = fast_exp2(a.part_lse[slot * a.H + h] - mx);
     den += w;
-    const float* src = a.part_o + (slot * a.H + h) * a.c + t * 8;
-    const floatx4 x0 = *reinterpret_cast<const floatx4*>(src);
-    const floatx4 x1 = *reinterpret_cast<const floatx4*>(src + 4);
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(po + (slot * a.H + h) * a.c + t * 8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += w * x0[e];
-      acc[4 + e] += w * x1[e];
-    }
+    for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[e];
   }
   const float inv = 1.f / den;
   bf16x8 v;
@@ -423,15 +474,16 @@ const char* decode_sk_check(const DecodeAttnArgs& a) {
 }
 
 int decode_sk_ranges(int batch, int max_visible, int cus) {
+  // one workgroup per range: cus ranges fill the device once
   const int64_t tiles_upper = (int64_t)batch * ((max_visible + KT - 1) / KT + 1);
-  int64_t r = std::max<int64_t>(cus, (tiles_upper + kDecodeMaxTiles - 1) / kDecodeMaxTiles);
+  int64_t r = std::max<int64_t>(std::max(cus, 8), (tiles_upper + kDecodeMaxTiles - 1) / kDecodeMaxTiles);
   r = (r + 7) / 8 * 8;
   return (int)r;
 }
 
 hipError_t decode_sk_launch(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_sk_kernel<4>, dim3(a.ranges), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(decode_sk_kernel<3>, dim3(a.ranges), dim3(NT), 0, s, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   return hipSuccess;
 }
