@@ -8,9 +8,10 @@
 // MFMAs. LDS rows are unpadded; the 16-byte chunk index of a row is XOR-ed
 // with (row & 7), so the fragment reads (8 consecutive rows, one chunk) hit
 // distinct banks. Rows that do not exist (past M or N, or absent gathered
-// rows) read a zero page. Tiles are ordered so that each XCD (workgroup id
-// mod 8) walks a contiguous range of M-tiles with all of their N-tiles,
-// keeping the activation rows in that XCD's L2.
+// rows) read a zero page. Tiles are placed on XCDs in 2-D blocks (see
+// TileMap) so that each XCD's L2 keeps its band of weight rows.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -26,19 +27,32 @@ constexpr int DMA_PER_WAVE = TILE_SLOTS / 256;   // per operand per wave per k s
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ (row & 7)); }
 
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int mtiles, int ntiles) {
-  __shared__ __attribute__((aligned(16))) bf16x8 tw[2][TILE_SLOTS];  // weight rows (n)
-  __shared__ __attribute__((aligned(16))) bf16x8 ta[2][TILE_SLOTS];  // activation rows (m)
-  __shared__ float rowscale[BM];
+// Tile placement: the 8 XCDs (workgroup id mod 8) form an xm x xn grid; XCD
+// (xi, xj) owns the block of M-tile band xi and N-tile band xj and walks it
+// M-major (all N-tiles of its band for one M-tile, then the next M-tile), so
+// the weight rows of its N band stay in that XCD's L2 while the activation
+// rows stream through once per N band.
+struct TileMap {
+  int mtiles, ntiles, xm, xn;
+};
 
-  // XCD-aware tile order: ids with the same (id % 8) share an XCD and take a
-  // contiguous range of the M-major tile sequence
-  const int total = mtiles * ntiles;
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm) {
+  // operand rings (weight rows, then activation rows); after the k loop the
+  // same 128 KB stage the output tile for coalesced stores
+  __shared__ __attribute__((aligned(16))) bf16x8 lds[4 * TILE_SLOTS];
+  bf16x8 (*tw)[TILE_SLOTS] = reinterpret_cast<bf16x8(*)[TILE_SLOTS]>(&lds[0]);
+  bf16x8 (*ta)[TILE_SLOTS] = reinterpret_cast<bf16x8(*)[TILE_SLOTS]>(&lds[2 * TILE_SLOTS]);
+  __shared__ float rowscale[BM];
+  __shared__ int rowok[BM];  // output row exists (inside M, gathered row present)
+
   const int id = blockIdx.x;
-  const int per_xcd = (total + 7) / 8;
-  const int t = (id & 7) * per_xcd + (id >> 3);
-  if (t >= total) return;
-  const int mt = t / ntiles, nt = t % ntiles;
+  const int xcd = id & 7, u = id >> 3;
+  const int xi = xcd / tm.xn, xj = xcd % tm.xn;
+  const int mb0 = xi * tm.mtiles / tm.xm, mb1 = (xi + 1) * tm.mtiles / tm.xm;
+  const int nb0 = xj * tm.ntiles / tm.xn, nb1 = (xj + 1) * tm.ntiles / tm.xn;
+  const int bw = nb1 - nb0;
+  if (bw <= 0 || u >= (mb1 - mb0) * bw) return;
+  const int mt = mb0 + u / bw, nt = nb0 + u % bw;
   const int m0 = mt * BM, n0 = nt * BN;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -79,6 +93,19 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int mtiles
     aoff[j] = (uint32_t)(off * 2) + colb;
   }
 
+  {
+    const int m = m0 + tid;  // 256 threads, one output row each
+    bool ok = m < g.M;
+    if (ok && g.gather) {
+      const GatherA& ga = g.ga;
+      const int bb = m / ga.max_kv_len, jj = m % ga.max_kv_len;
+      int ql = ga.cu_seqlens[bb + 1] - ga.cu_seqlens[bb];
+      ql = min(max(ql, 0), ga.max_q_len);
+      const int pl = min(max(ga.prefix_lens[bb], 0), ga.max_kv_len - ql);
+      ok = jj < pl + ql;  // absent gathered rows are not stored
+    }
+    rowok[tid] = ok;
+  }
   const uint32_t tw_lds = lds_addr(&tw[0][0]), ta_lds = lds_addr(&ta[0][0]);
   auto issue = [&](int kt, int buf) {
     const bf16* wb = W + kt * BK;
@@ -155,42 +182,46 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int mtiles
     __syncthreads();
   }
 
-  // epilogue: lane holds C[m][n .. n + 3], m = m0 + 128 wm + 16 b + lr, n = n0 + 128 wn + 16 a + 4 g4
-  bf16* C = reinterpret_cast<bf16*>(g.C);
-  const bf16* G = reinterpret_cast<const bf16*>(g.G);
+  // epilogue, staged through LDS: lane holds C[m][n .. n + 3] for
+  // m = 128 wm + 16 b + lr, n = 128 wn + 16 a + 4 g4 (tile-local). The bf16
+  // tile is written as 256 rows of 32 16-byte chunks, chunk c of row r at
+  // position c ^ (r & 31) (the 16 rows of one write land on distinct chunks),
+  // then stored to C with 16 contiguous bytes per lane, 512 bytes per row.
+  char* cst = reinterpret_cast<char*>(&lds[0]);
 #pragma unroll
   for (int b = 0; b < 8; ++b) {
     const int ml = wm * 128 + b * 16 + lr;
-    const int m = m0 + ml;
-    if (m >= g.M) continue;
-    if (g.gather) {
-      // absent gathered rows are not stored
-      const GatherA& ga = g.ga;
-      const int bb = m / ga.max_kv_len, jj = m % ga.max_kv_len;
-      int ql = ga.cu_seqlens[bb + 1] - ga.cu_seqlens[bb];
-      ql = min(max(ql, 0), ga.max_q_len);
-      const int pl = min(max(ga.prefix_lens[bb], 0), ga.max_kv_len - ql);
-      if (jj >= pl + ql) continue;
-    }
     const float rs = rownorm ? rowscale[ml] : 1.f;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-      const int n = n0 + wn * 128 + a * 16 + g4 * 4;
-      if (n >= g.N) continue;
-      floatx4 v = acc[a][b];
-      if (rownorm) v = v * rs;
-      if (g.epi == EPI_GATE) {
-        const bf16* gp = G + (int64_t)m * g.ldg + n;
+      const floatx4 v = acc[a][b] * rs;
+      const int c = wn * 16 + a * 2 + (g4 >> 1);
+      *reinterpret_cast<bf16x4*>(cst + (ml * 32 + (c ^ (ml & 31))) * 16 + (g4 & 1) * 8) =
+          bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    }
+  }
+  __syncthreads();
+  bf16* C = reinterpret_cast<bf16*>(g.C);
+  const bf16* G = reinterpret_cast<const bf16*>(g.G);
+  const int c = tid & 31;
+  const int n = n0 + c * 8;
+#pragma unroll 4
+  for (int it = 0; it < BM / 8; ++it) {
+    const int ml = it * 8 + (tid >> 5);
+    const int m = m0 + ml;
+    if (!rowok[ml] || n >= g.N) continue;
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(cst + (ml * 32 + (c ^ (ml & 31))) * 16);
+    if (g.epi == EPI_GATE) {
+      const bf16* gp = G + (int64_t)m * g.ldg + n;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (n + e < g.N) v[e] *= sigmoidf((float)gp[e]);
-      }
-      bf16* dst = C + (int64_t)m * g.ldc + n;
-      if (n + 3 < g.N) {
-        *reinterpret_cast<bf16x4*>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-      } else {
-        for (int e = 0; e < 4 && n + e < g.N; ++e) dst[e] = (bf16)v[e];
-      }
+      for (int e = 0; e < 8; ++e)
+        if (n + e < g.N) v[e] = (bf16)((float)v[e] * sigmoidf((float)gp[e]));
+    }
+    bf16* dst = C + (int64_t)m * g.ldc + n;
+    if (n + 7 < g.N) {
+      *reinterpret_cast<bf16x8*>(dst) = v;
+    } else {
+      for (int e = 0; e < 8 && n + e < g.N; ++e) dst[e] = v[e];
     }
   }
 }
@@ -199,6 +230,9 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, int mtiles
 
 bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) {
   if (!is_bf16 || g.batch != 1 || g.K % BK != 0 || g.M < 512 || g.N < 256) return false;
+  // 16-byte output stores (and gate loads)
+  if (g.ldc % 8 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
+  if (g.epi == EPI_GATE && (g.ldg % 8 || (reinterpret_cast<uintptr_t>(g.G) & 15))) return false;
   // per-slot source offsets are 32-bit byte offsets
   const int64_t lim = (int64_t)1 << 31;  // elements (2 bytes each)
   if ((int64_t)g.N * g.ldw >= lim) return false;
@@ -208,11 +242,32 @@ bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) {
 }
 
 hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s) {
-  const int mtiles = (g.M + BM - 1) / BM, ntiles = (g.N + BN - 1) / BN;
-  const int total = mtiles * ntiles;
-  const int grid = ((total + 7) / 8) * 8;
   (void)zeros;
-  hipLaunchKernelGGL(gemm_big_kernel, dim3(grid), dim3(256), 0, s, g, mtiles, ntiles);
+  TileMap tm;
+  tm.mtiles = (g.M + BM - 1) / BM;
+  tm.ntiles = (g.N + BN - 1) / BN;
+  // XCD grid: estimated Infinity-Cache traffic xn |A| + xm |W| (each XCD reads
+  // its A band once per N band and its W band once); with a short k loop the W
+  // band must also stay resident in the 4 MB L2 of the XCD
+  const double a_bytes = (double)g.M * g.K * 2, w_bytes = (double)g.N * g.K * 2;
+  const int opts[4][2] = {{1, 8}, {2, 4}, {4, 2}, {8, 1}};
+  double best = 1e300;
+  tm.xm = 2; tm.xn = 4;
+  for (const auto& o : opts) {
+    if (o[0] > tm.mtiles || o[1] > tm.ntiles) continue;
+    if (g.K <= 1024 && w_bytes / o[1] > 3.0 * 1024 * 1024 && o[1] < 8) continue;
+    const double cost = o[1] * a_bytes + o[0] * w_bytes;
+    if (cost < best) { best = cost; tm.xm = o[0]; tm.xn = o[1]; }
+  }
+  // workgroups per XCD: the largest block
+  int per = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int xi = x / tm.xn, xj = x % tm.xn;
+    const int mb = (xi + 1) * tm.mtiles / tm.xm - xi * tm.mtiles / tm.xm;
+    const int nb = (xj + 1) * tm.ntiles / tm.xn - xj * tm.ntiles / tm.xn;
+    per = std::max(per, mb * nb);
+  }
+  hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8), dim3(256), 0, s, g, tm);
   return hipGetLastError();
 }
 
