@@ -312,8 +312,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
           sc[kb][e] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = red4_max(mx);
       // lazy rescaling: the reference max moves only when exceeded by more
       // than 2^8 (probabilities stay <= 256; exact after the division by l)
       const float mnew = (mx > m + 8.f) ? mx : m;
@@ -374,9 +373,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     // inside the sequence). Each head's softmax state comes from the
     // wavefront that owns its scores.
     {
-      float lsum = l;
-      lsum += __shfl_xor(lsum, 16);
-      lsum += __shfl_xor(lsum, 32);
+      const float lsum = red4_sum(l);
       if (g == 0) {
         mbuf[wave][lr] = m;
         lbuf[wave][lr] = lsum;

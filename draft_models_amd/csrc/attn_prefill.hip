@@ -12,6 +12,8 @@
 // lane ends up holding the probabilities of one query for 8 keys -- exactly
 // the B-operand layout of the P V product -- and no LDS round trip of P is
 // needed. V is stored transposed in LDS ([d][key]) for the A operand of P V.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -190,8 +192,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
           s[kb][qb][i] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = red4_max(mx);
       const float mnew = fmaxf(m[qb], mx);
       float alpha = 1.f, sum = 0.f;
       if (mnew != -INFINITY) {
@@ -209,8 +210,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = red4_sum(sum);
       l[qb] = l[qb] * alpha + sum;
 #pragma unroll
       for (int d = 0; d < DB; ++d) o[d][qb] *= alpha;
@@ -290,15 +290,16 @@ constexpr int QB = 2;                   // 16-query blocks per wavefront
 constexpr int NW = 8;                   // wavefronts per workgroup (two per SIMD)
 constexpr int BQ = NW * 16 * QB;        // queries per workgroup
 constexpr int NOPE_CH = 16, PE_CH = 8, V_CH = 16;   // 16-byte chunks per key row
+constexpr int NBUF = 3;                 // tile ring: t (values), t + 1 (scores), t + 2 (in flight)
 __device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch + (c ^ (row & 7)); }
 __device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 7) << 1)); }
 }  // namespace big
 
 __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnArgs a) {
   using namespace big;
-  __shared__ __attribute__((aligned(16))) bf16x8 knope[2][KT * NOPE_CH];
-  __shared__ __attribute__((aligned(16))) bf16x8 kpe[2][KT * PE_CH];
-  __shared__ __attribute__((aligned(16))) bf16x8 vt[2][KT * V_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 knope[NBUF][KT * NOPE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 kpe[NBUF][KT * PE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 vt[NBUF][KT * V_CH];
   __shared__ int iv[4];  // union lo, union hi, intersection lo, intersection hi
 
   // heaviest (latest, for causal masks) query tiles first
@@ -436,31 +437,14 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   const int ra = lr >> 2, rb = lr & 3;
   const bool active = qt * BQ + wave * 16 * QB < ql;
 
-  MLA_WAIT_VMCNT(0);  // query fragments landed: in the loop only tile copies are outstanding
-  if (kbeg < kend) issue(kbeg, 0);
-  int buf = 0;
-  for (int k0 = kbeg; k0 < kend; k0 += KT, buf ^= 1) {
-    if (k0 + KT < kend) {
-      issue(k0 + KT, buf ^ 1);
-      MLA_WAIT_VMCNT(5);  // 2 + 2 + 1 copies per wave of the next tile may stay in flight
-    } else {
-      MLA_WAIT_VMCNT(0);
-    }
-    lds_barrier();
-    const bf16x8* KN = knope[buf];
-    const bf16x8* KP = kpe[buf];
-    const bf16x8* VT = vt[buf];
-    if (!active) {  // no query of this wavefront exists: it only helps stream tiles
-      lds_barrier();
-      continue;
-    }
-
-    // ---- S^T = K Q^T: s[kb][qb][i] = key k0 + 16 kb + 4 g + i, query lr of block qb
-    floatx4 s[4][QB];
+  // ---- S^T = K Q^T of the tile in buffer `bf`: sc[kb][qb][i] = key 16 kb + 4 g + i, query lr of block qb
+  auto scores = [&](int bf, floatx4 (&sc)[4][QB]) {
+    const bf16x8* KN = knope[bf];
+    const bf16x8* KP = kpe[bf];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 6; ++ks) {
 #pragma unroll
@@ -469,14 +453,28 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
         const int row = kb * 16 + lr;
         kf.v = ks < 4 ? KN[kslot(row, ks * 4 + g, NOPE_CH)] : KP[kslot(row, (ks - 4) * 4 + g, PE_CH)];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma16(kf, qf[qb][ks], s[kb][qb]);
+        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma16(kf, qf[qb][ks], sc[kb][qb]);
       }
     }
-
-    // ---- online softmax (log2 domain) with lazy rescaling
-    const bool needmask = !(k0 >= in_lo && k0 + KT <= in_hi);
-    Frag<bf16> pf[QB][2];
-    float alpha[QB];
+  };
+  // ---- online softmax (log2 domain) with lazy rescaling of the tile at key
+  // k0; the probabilities replace the scores in place (fp32)
+  float alpha[QB];
+  // keys outside a row's visible interval (only on tiles that cross an
+  // interval end) score -inf: exp2(-inf) = 0, also for rows that have seen no
+  // visible key yet (their reference max stays -inf and is replaced by 0)
+  auto mask = [&](floatx4 (&sc)[4][QB], int k0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + kb * 16 + g * 4 + i;
+          if (key < lo[qb] || key >= hi[qb]) sc[kb][qb][i] = -INFINITY;
+        }
+  };
+  auto softmax = [&](floatx4 (&sc)[4][QB]) -> bool {
     bool rescale = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -484,52 +482,45 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[kb][qb][i] * sl2;
-          if (needmask) {
-            const int key = k0 + kb * 16 + g * 4 + i;
-            if (key < lo[qb] || key >= hi[qb]) x = -INFINITY;
-          }
-          s[kb][qb][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
+      mx = red4_max(mx);
+      mx *= sl2;  // the scale is positive: the max of the scaled scores
       const float mnew = (mx > m[qb] + 8.f) ? mx : m[qb];
-      // rows with nothing visible so far keep m = -inf and p = 0
       alpha[qb] = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
       rescale |= mnew != m[qb];
+      const float nm = (mnew == -INFINITY) ? 0.f : -mnew;
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (mnew == -INFINITY) ? 0.f : fast_exp2(s[kb][qb][i] - mnew);
-          s[kb][qb][i] = p;
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][qb][i], sl2, nm));
+          sc[kb][qb][i] = p;
           sum += p;
         }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = red4_sum(sum);
       l[qb] = l[qb] * alpha[qb] + sum;
       m[qb] = mnew;
+    }
+    return rescale;
+  };
+  // ---- O^T += V^T P^T; transposed V operand from the row-major tile: lane
+  // k = 4 a + b' of a 16-lane group points at key row 32 k2 + 4 g + a [+16],
+  // dims 16 d + 4 b' .. + 3, and receives keys 32 k2 + 4 g + {0..3} [+16] of dim 16 d + lr
+  auto pv = [&](int bf, const floatx4 (&sc)[4][QB]) {
+    const bf16x8* VT = vt[bf];
+    // probabilities as the B operand: element e of lane (g, lr) is key
+    // 32 k2 + 4 g + (e < 4 ? e : 16 + e - 4)
+    Frag<bf16> pf[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pf[qb][k2].v[e] = (bf16)s[2 * k2][qb][e];
-          pf[qb][k2].v[4 + e] = (bf16)s[2 * k2 + 1][qb][e];
+          pf[qb][k2].v[e] = (bf16)sc[2 * k2][qb][e];
+          pf[qb][k2].v[4 + e] = (bf16)sc[2 * k2 + 1][qb][e];
         }
-    }
-    if (__any(rescale)) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[d][qb] *= alpha[qb];
-    }
-
-    // ---- O^T += V^T P^T; transposed V operand from the row-major tile: lane
-    // k = 4 a + b' of a 16-lane group points at key row 32 k2 + 4 g + a [+16],
-    // dims 16 d + 4 b' .. + 3, and receives keys 32 k2 + 4 g + {0..3} [+16] of dim 16 d + lr
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const int el = d * 16 + rb * 4;
@@ -544,8 +535,51 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
         for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma16(vf, pf[qb][k2], o[d][qb]);
       }
     }
-    lds_barrier();
+  };
+
+  // ---- software pipeline over the key tiles: step t computes the scores of
+  // tile t + 1 (MFMA) in the same basic block as the softmax of tile t (VALU),
+  // so that the two units overlap, then P V of tile t; tile t + 2 streams in
+  // meanwhile. Two score arrays alternate (the loop is unrolled by two).
+  const int ntl = kbeg < kend ? (kend - kbeg + KT - 1) / KT : 0;
+  MLA_WAIT_VMCNT(0);  // query fragments landed: in the loop only tile copies are outstanding
+  if (ntl > 0) issue(kbeg, 0);
+  if (ntl > 1) issue(kbeg + KT, 1);
+  if (ntl > 1) MLA_WAIT_VMCNT(5);  // the copies of tile 1 may stay in flight
+  else MLA_WAIT_VMCNT(0);
+  lds_barrier();
+  floatx4 s0[4][QB], s1[4][QB];
+  if (active && ntl > 0) scores(0, s0);
+  auto step = [&](int t, floatx4 (&cur)[4][QB], floatx4 (&nxt)[4][QB]) {
+    const int k0 = kbeg + t * KT;
+    MLA_WAIT_VMCNT(0);  // tile t + 1 landed (the only copies in flight)
+    lds_barrier();      // ... for every wavefront; P V of tile t - 1 is done everywhere
+    if (t + 2 < ntl) issue(k0 + 2 * KT, (t + 2) % NBUF);
+    if (!active) return;  // no query of this wavefront exists: it only helps stream tiles
+    if (!(k0 >= in_lo && k0 + KT <= in_hi)) mask(cur, k0);
+    scores((t + 1) % NBUF, nxt);  // after the last tile: a stale buffer, unused
+    const bool rescale = softmax(cur);
+    // interleave the two: per group one LDS read, two MFMAs, six VALU
+#pragma unroll
+    for (int gi = 0; gi < 24; ++gi) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+    if (__any(rescale)) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[d][qb] *= alpha[qb];
+    }
+    pv(t % NBUF, cur);
+  };
+  int t = 0;
+  for (; t + 1 < ntl; t += 2) {
+    step(t, s0, s1);
+    step(t + 1, s1, s0);
   }
+  if (t < ntl) step(t, s0, s1);
 
   // ---- epilogue: lane holds O[query lr][d .. d+3], d = 16 db + 4 g
 #pragma unroll

@@ -64,6 +64,27 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Reductions over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the rows of one
+// MFMA output column) with the gfx950 VALU lane swaps: permlane16_swap(x, x)
+// returns {x[l], x[l ^ 16]} in every lane, permlane32_swap(x, x) returns
+// {x[l], x[l ^ 32]} (in some order), so no LDS round trip is needed.
+__device__ __forceinline__ float red4_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+__device__ __forceinline__ float red4_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's bytes land at LDS address lds_base + 16 l. Issued through inline
 // asm so that the compiler does not treat later LDS reads as aliasing the
