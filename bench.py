@@ -129,13 +129,88 @@ def kernel_source_sha(files):
     return h.hexdigest()[:16]
 
 
+_GEMM_SRC = ["gemm.hip", "gemm_big.hip", "gemm.h", "kernels.h", "common.h"]
 STAGE_SOURCES = {
-    "kv_b_expand": ["gemm.hip", "common.h"], "qkv_a_gemm": ["gemm.hip", "common.h"],
-    "q_b_gemm": ["gemm.hip", "common.h"], "o_proj_gemm": ["gemm.hip", "common.h"],
-    "wuk_absorb": ["gemm.hip", "common.h"], "wuv_gemm": ["gemm.hip", "common.h"],
-    "prefill_attn": ["attn_prefill.hip", "common.h"], "decode_attn": ["attn_decode.hip", "common.h"],
-    "decode_merge": ["attn_decode.hip", "common.h"], "rope_cache": ["rope_cache.hip", "common.h"],
+    "kv_b_expand": _GEMM_SRC, "qkv_a_gemm": _GEMM_SRC, "q_b_gemm": _GEMM_SRC, "o_proj_gemm": _GEMM_SRC,
+    "wuk_absorb": _GEMM_SRC, "wuv_gemm": _GEMM_SRC,
+    "prefill_attn": ["attn_prefill.hip", "kernels.h", "common.h"],
+    "decode_attn": ["attn_decode_sk.hip", "attn_decode.hip", "kernels.h", "common.h"],
+    "decode_merge": ["attn_decode_sk.hip", "attn_decode.hip", "kernels.h", "common.h"],
+    "rope_cache": ["rope_cache.hip", "kernels.h", "common.h"],
 }
+# kernel that carries a stage (the one whose counters are summarised); a
+# stage whose kernel name also runs other stages of the workload (a GEMM
+# shared with other projections) is only summarised when all its dispatches
+# have one grid size
+STAGE_KERNEL = {
+    "decode_attn": "decode_sk_kernel", "decode_merge": "decode_sk_merge_kernel",
+    "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
+    "rope_cache": "rope_cache_kernel",
+}
+COPY_KERNEL = "elementwise"  # torch's elementwise kernel of the copy calibration
+
+
+def _pmc_rows(d):
+    rows = []
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                import csv
+                rows += list(csv.DictReader(open(os.path.join(root, f))))
+    return rows
+
+
+def _per_dispatch(rows, counter, pat):
+    """{dispatch id: (grid size, counter value summed over its rows)} of kernels matching pat"""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter or pat not in r["Kernel_Name"]:
+            continue
+        k = r["Dispatch_Id"]
+        g, v = out.get(k, (int(r["Grid_Size"]), 0.0))
+        out[k] = (g, v + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands):
+    """profiles/traffic_<stage>_<workload>.json from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE: KiB per dispatch), each counter scaled by what
+    it reads for the copy calibration (copy_mib MiB read and written)."""
+    known_kib = copy_mib * 1024.0
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d)
+        cp = _per_dispatch(rows, counter, COPY_KERNEL)
+        if not cp:
+            raise SystemExit(f"no copy-calibration dispatches in {d}")
+        gmax = max(g for g, _ in cp.values())
+        vals = [v for g, v in cp.values() if g == gmax]
+        factor = known_kib / (sum(vals) / len(vals))
+        res[counter] = (rows, factor)
+    written = []
+    for stage, pat in STAGE_KERNEL.items():
+        per = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            rows, factor = res[counter]
+            disp = _per_dispatch(rows, counter, pat)
+            if not disp or len({g for g, _ in disp.values()}) != 1:
+                per = None
+                break
+            per[counter] = (sum(v for _, v in disp.values()) / len(disp), factor, len(disp))
+        if not per:
+            continue
+        fk, ff, n = per["FETCH_SIZE"]
+        wk, wf, _ = per["WRITE_SIZE"]
+        rec = {"stage": stage, "workload": workload, "kernel": pat, "dispatches": n,
+               "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+               "copy_calibration_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+               "bytes_per_launch": int((fk * ff + wk * wf) * 1024),
+               "source_sha": kernel_source_sha(STAGE_SOURCES[stage]), "commands": commands}
+        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        written.append(path)
+    return written
 
 
 def measured_traffic(stage, workload):
@@ -191,7 +266,20 @@ def main():
     ap.add_argument("--workload", default="draft_block_bf16", choices=sorted(DESCR))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="no per-stage events in the timed region")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise copy of MIB MiB three times (HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.json from two rocprofv3 --pmc runs of this workload "
+                         "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibrate; no GPU work")
     args = ap.parse_args()
+    if args.traffic_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
+               f"python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
+               f"--cpu-seconds 0 --copy-calibrate {args.copy_calibrate}")
+        for p in traffic_summary(*args.traffic_summary, args.workload, args.copy_calibrate,
+                                 [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")]):
+            print("wrote", p)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(each GPU would run its own sequences with no exchange).", file=sys.stderr)
@@ -201,6 +289,16 @@ def main():
     import mla_synth as ms
     from mla_synth.device import upload
     from draft_models_amd import binding as B
+
+    if args.copy_calibrate > 0:
+        # a plain elementwise kernel of known traffic: reads and writes copy_calibrate MiB
+        n = args.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = ms.make_workload(args.workload)
     t = upload(w)
