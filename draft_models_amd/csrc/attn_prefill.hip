@@ -302,8 +302,17 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   __shared__ __attribute__((aligned(16))) bf16x8 vt[NBUF][KT * V_CH];
   __shared__ int iv[4];  // union lo, union hi, intersection lo, intersection hi
 
-  // heaviest (latest, for causal masks) query tiles first
-  const int qt = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // workgroup id -> (query tile, head, sequence). Workgroups go to the 8 XCDs
+  // round-robin by id: XCD x takes the (sequence, head) pairs p = x mod 8, so
+  // every query tile of a pair reads its keys through one L2, and within the
+  // XCD the heaviest (latest, for causal masks) query tiles come first
+  const int np = a.H * a.batch, npx = (np + 7) / 8;
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int nqt = (a.max_q_len + BQ - 1) / BQ;
+  const int pr = (slot % npx) * 8 + xcd;
+  const int qt = nqt - 1 - slot / npx;
+  if (pr >= np || qt < 0) return;
+  const int h = pr % a.H, b = pr / a.H;
   int ql = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
   ql = min(max(ql, 0), a.max_q_len);
   if (qt * BQ >= ql) return;
@@ -637,8 +646,9 @@ const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16) {
 hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s) {
   if (a.batch <= 0 || a.max_q_len <= 0) return hipSuccess;
   if (is_bf16 && a.n == 128 && a.r == 64 && a.dv == 128 && a.c % 8 == 0 && a.page % big::KT == 0) {
-    dim3 grid((a.max_q_len + big::BQ - 1) / big::BQ, a.H, a.batch);
-    hipLaunchKernelGGL(prefill_attn_bf16_kernel, grid, dim3(64 * big::NW), 0, s, a);
+    const int64_t nqt = (a.max_q_len + big::BQ - 1) / big::BQ, npx = ((int64_t)a.H * a.batch + 7) / 8;
+    if (8 * npx * nqt > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_attn_bf16_kernel, dim3((unsigned)(8 * npx * nqt)), dim3(64 * big::NW), 0, s, a);
     return hipGetLastError();
   }
   return is_bf16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
