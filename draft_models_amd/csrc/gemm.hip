@@ -14,23 +14,27 @@ namespace mla {
 
 namespace {
 
-template <typename T>
+// RB bytes of k per tile row: 128, or 256 for few activation rows (the
+// weight-streaming shapes), where a deeper k tile doubles the bytes each
+// register prefetch has in flight
+template <typename T, int RB>
 struct Tile {
-  static constexpr int BK = 128 / sizeof(T);         // k elements per LDS row
+  static constexpr int BK = RB / sizeof(T);          // k elements per LDS row
   static constexpr int VEC = 16 / sizeof(T);         // elements per 16-byte vector
+  static constexpr int VPR = RB / 16;                // 16-byte vectors per row
   static constexpr int ROW = BK + VEC;                // padded LDS row (elements)
   static constexpr int KSTEPS = BK / 32;             // 32-element MFMA steps per k tile
 };
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int RB>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, float* ws, int splits) {
-  using TT = Tile<T>;
+  using TT = Tile<T, RB>;
   using V = typename Vec16<T>::type;
-  constexpr int BK = TT::BK, VEC = TT::VEC, ROW = TT::ROW;
+  constexpr int BK = TT::BK, VEC = TT::VEC, ROW = TT::ROW, VPR = TT::VPR;
   constexpr int TM = BM / WM, TN = BN / WN, MB = TM / 16, NB = TN / 16;
   static_assert(WM * WN == 4, "4 wavefronts");
   static_assert(MB >= 1 && NB >= 1, "wave tile");
-  constexpr int NV = (BM + BN) * 8;         // 16-byte vectors per k tile
+  constexpr int NV = (BM + BN) * VPR;       // 16-byte vectors per k tile
   constexpr int VPT = (NV + 255) / 256;
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * ROW];
   __shared__ int64_t rowoff[BM];
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, float* ws, int sp
       const int v = tid + i * 256;
       V val = {};
       if (v < NV) {
-        const int row = v >> 3, k = kbase + (v & 7) * VEC;
+        const int row = v / VPR, k = kbase + (v % VPR) * VEC;
         if (k < g.K) {
           if (row < BN) {
             const int n = n0 + row;
@@ -111,8 +115,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, float* ws, int sp
     for (int i = 0; i < VPT; ++i) {
       const int v = tid + i * 256;
       if (v < NV) {
-        const int row = v >> 3;
-        *reinterpret_cast<V*>(&lds[buf][row * ROW + (v & 7) * VEC]) = regs[i];
+        const int row = v / VPR;
+        *reinterpret_cast<V*>(&lds[buf][row * ROW + (v % VPR) * VEC]) = regs[i];
         if (g.epi == EPI_ROWNORM && row >= BN) {
 #pragma unroll
           for (int e = 0; e < VEC; ++e) {
@@ -158,16 +162,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, float* ws, int sp
   }
 
   if (g.epi == EPI_ROWNORM) {
-    // rows of A loaded by this thread: sum over the 8 lanes sharing a row
+    // rows of A loaded by this thread: sum over the VPR lanes sharing a row
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       float s = sq[i];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
+#pragma unroll
+      for (int o = 1; o < VPR; o <<= 1) s += __shfl_xor(s, o);
       const int v = tid + i * 256;
-      if (v < NV && (v & 7) == 0 && (v >> 3) >= BN)
-        rowscale[(v >> 3) - BN] = rsqrtf(s / (float)g.K + g.eps);
+      if (v < NV && (v % VPR) == 0 && (v / VPR) >= BN)
+        rowscale[(v / VPR) - BN] = rsqrtf(s / (float)g.K + g.eps);
     }
     __syncthreads();
   }
@@ -241,10 +244,10 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, int RB>
 hipError_t launch_cfg(const GemmArgs& g, float* ws, int splits, hipStream_t s) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, g.batch * splits);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN>), grid, dim3(256), 0, s, g, ws, splits);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, RB>), grid, dim3(256), 0, s, g, ws, splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = (int64_t)g.M * g.N;
@@ -256,7 +259,9 @@ hipError_t launch_cfg(const GemmArgs& g, float* ws, int splits, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_t(const GemmArgs& g, float* ws, int64_t ws_elems, hipStream_t s) {
-  constexpr int BK = Tile<T>::BK;
+  // k elements per tile: 256 bytes per row for few activation rows, else 128
+  const bool deep = g.M <= 64 && sizeof(T) == 2 && g.K >= 1024;
+  const int BK = (deep ? 256 : 128) / (int)sizeof(T);
   // tile shape by M; split-K when the grid is too small to fill 256 CUs
   int bm, bn;
   if (g.M <= 16) { bm = 16; bn = 64; }
@@ -267,7 +272,9 @@ hipError_t launch_t(const GemmArgs& g, float* ws, int64_t ws_elems, hipStream_t 
   int splits = 1;
   const int ktiles = (g.K + BK - 1) / BK;
   if (tiles < 512 && g.batch == 1 && g.epi == EPI_STORE && !g.gather && ws != nullptr) {
-    splits = (int)((512 + tiles - 1) / tiles);
+    // deep tiles (70 KB of LDS) fit two workgroups per CU: fill those 512
+    // slots in one round rather than spill a few workgroups into a second
+    splits = deep ? (int)std::max<int64_t>(1, 512 / tiles) : (int)((512 + tiles - 1) / tiles);
     splits = std::min(splits, std::max(1, ktiles / 4));
     splits = std::min(splits, 16);
     while (splits > 1 && (int64_t)splits * g.M * g.N > ws_elems) --splits;
@@ -277,9 +284,9 @@ hipError_t launch_t(const GemmArgs& g, float* ws, int64_t ws_elems, hipStream_t 
       splits = (ktiles + per - 1) / per;
     }
   }
-  if (bm == 16) return launch_cfg<T, 16, 64, 1, 4>(g, ws, splits, s);
-  if (bm == 64) return launch_cfg<T, 64, 64, 1, 4>(g, ws, splits, s);
-  return launch_cfg<T, 128, 128, 2, 2>(g, ws, splits, s);
+  if (bm == 16) return deep ? launch_cfg<T, 16, 64, 1, 4, 256>(g, ws, splits, s) : launch_cfg<T, 16, 64, 1, 4, 128>(g, ws, splits, s);
+  if (bm == 64) return deep ? launch_cfg<T, 64, 64, 1, 4, 256>(g, ws, splits, s) : launch_cfg<T, 64, 64, 1, 4, 128>(g, ws, splits, s);
+  return launch_cfg<T, 128, 128, 2, 2, 128>(g, ws, splits, s);
 }
 
 }  // namespace
