@@ -90,6 +90,16 @@ def test_decode_window_zero_bf16():
     assert np.all(out == 0)
 
 
+def test_decode_projection_k_tails():
+    """Few activation rows (M = 5) with projection k axes that are not a
+    multiple of the 128-element weight-streaming k tile (hidden and q_lora
+    1056), plus an output gate: the zero-filled k tail of every projection."""
+    w = ms.make_workload("decode_bf16", seq_lens=[40, 300, 64, 1, 129], seed=21,
+                         dims_override={"hidden_size": 1056, "num_heads": 16, "q_lora_rank": 1056,
+                                        "use_output_gate": True})
+    _run_and_check(w)
+
+
 def test_prefill_small():
     w = ms.make_workload("prefill_bf16", q_lens=[300, 129], prefix_lens=[0, 0])
     _run_and_check(w)
