@@ -77,9 +77,10 @@ __device__ __forceinline__ void dma16_v(const void* gptr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds) : "memory", "m0");
 }
 
-// Visible keys [lo, hi) of the query of sequence b (its own position L - 1)
+// Visible keys [lo, hi) of the query of sequence b (its own position L - 1;
+// a query block sees every entry of its physical sequence)
 __device__ __forceinline__ void visible(const DecodeAttnArgs& a, int b, int& lo, int& hi) {
-  const int L = min(max(a.seq_lens[b], 0), a.max_seq_len);
+  const int L = min(max(a.seq_lens[b / a.seq_div], 0), a.max_seq_len);
   lo = a.mask.kind == 2 ? max(0, L - a.mask.window) : 0;
   hi = L;
 }
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     visible(a, lb, lo, hi);
     const int k0 = (lo / KT + gi - tstart[lb]) * KT;
     const int pg = k0 / a.page;
-    const int blk = pg < a.max_blocks ? a.block_table[(int64_t)lb * a.max_blocks + pg] : -1;
+    const int blk = pg < a.max_blocks ? a.block_table[(int64_t)(lb / a.seq_div) * a.max_blocks + pg] : -1;
     t_ent[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.page + (k0 - pg * a.page) : -1;
     t_k0[i] = k0;
     t_seq[i] = lb;
@@ -255,7 +256,14 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     Frag<bf16> q[KS];
     {
       const bf16* ql = reinterpret_cast<const bf16*>(a.ql) + (int64_t)b * a.ldql + (int64_t)(hok ? h : 0) * a.c;
-      const bf16* qp = reinterpret_cast<const bf16*>(a.q) + (int64_t)b * a.ldq + (int64_t)(hok ? h : 0) * a.qk_head + a.n;
+      // roped query: token and head of the (query, head) pair in query blocks
+      int64_t qt = b, qh = hok ? h : 0;
+      if (a.Hr > 0) {
+        const int64_t pair = (int64_t)b * a.H + qh;
+        qt = pair / a.Hr;
+        qh = pair % a.Hr;
+      }
+      const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qt * a.ldq + qh * a.qk_head + a.n;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int e = s * 32 + g * 8;
@@ -465,6 +473,7 @@ const char* decode_sk_check(const DecodeAttnArgs& a) {
   if (a.batch > kDecodeMaxBatch) return "stream-K decode: batch above 1024";
   if ((int64_t)a.num_blocks * a.page >= ((int64_t)1 << 31)) return "stream-K decode: cache above 2^31 entries";
   if (a.ldql % 8 || a.ldq % 8 || a.qk_head % 8 || a.n % 8) return "stream-K decode: query strides must be 16-byte multiples";
+  if (a.seq_div < 1 || a.Hr < 0) return "stream-K decode: bad query-block mapping";
   if (a.ranges <= 0 || a.ranges % 8 || !a.tstart || !a.part_o || !a.part_lse || !a.zeros)
     return "stream-K decode: ranges (a multiple of 8) and workspaces are required";
   return nullptr;

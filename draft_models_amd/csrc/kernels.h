@@ -71,6 +71,13 @@ struct DecodeAttnArgs {
   // pieces in part_o [2 ranges, H, c] / part_lse [2 ranges, H]
   int ranges = 0;
   int32_t* tstart = nullptr;                        // [batch + 1] first tile of every sequence
+  // query blocks (stream-K only): sequence index b of this struct is a virtual
+  // sequence of H (query, head) pairs of physical sequence b / seq_div, which
+  // owns the block-table row and the length. With Hr > 0 the pair j of b is
+  // token (b H + j) / Hr, head (b H + j) % Hr of a model with Hr heads (the
+  // latent queries and outputs are then [tokens, Hr, c] in the same order).
+  int seq_div = 1;
+  int Hr = 0;
 };
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);

@@ -37,8 +37,10 @@ struct mla_ctx {
   void* qbuf = nullptr;    // [max_tokens, H (n + r)]  (low-rank Q path)
   void* kvexp = nullptr;   // [max_prefill_kv, H (n + dv)]
   void* attn = nullptr;    // [max_tokens, H dv]
-  void* qlat = nullptr;    // [max_batch, H, c]
-  void* olat = nullptr;    // [max_batch, H, c]
+  void* qlat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
+  void* olat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
+  int32_t* blk_cu = nullptr;    // query blocks: [max_batch + 1] token offsets b q_len
+  int32_t* blk_lens = nullptr;  // query blocks: [max_batch] cache lengths prefix + q_len
   float* part_o = nullptr;
   float* part_lse = nullptr;
   int max_splits = 32;
@@ -89,6 +91,13 @@ __global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst,
 }
 
 // Wuk_t[h][cc][nn] = kv_b_proj[h (n + dv) + nn][cc]
+// query blocks: cu[b] = b q_len (b <= batch), lens[b] = prefix_lens[b] + q_len
+__global__ void block_meta_kernel(const int32_t* prefix_lens, int batch, int q_len, int32_t* cu, int32_t* lens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b <= batch) cu[b] = b * q_len;
+  if (b < batch) lens[b] = prefix_lens[b] + q_len;
+}
+
 __global__ void wuk_transpose_kernel(const void* wkvb, void* out, int H, int n, int dv, int c, int bf) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)H * c * n;
@@ -131,8 +140,10 @@ int validate_config(const mla_config* c, const mla_weights* w) {
   if (!(c->rms_norm_eps >= 0.0) || !std::isfinite(c->rms_norm_eps)) return fail(MLA_ERR_INVALID_ARG, "rms_norm_eps must be >= 0");
   if (!std::isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (c->use_output_gate != 0 && c->use_output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "use_output_gate must be 0 or 1");
-  if (c->page_size <= 0 || c->max_batch <= 0 || c->max_tokens <= 0 || c->max_seq_len <= 0 || c->max_prefill_kv < 0)
-    return fail(MLA_ERR_INVALID_ARG, "page_size, max_batch, max_tokens, max_seq_len must be positive, max_prefill_kv >= 0");
+  if (c->page_size <= 0 || c->max_batch <= 0 || c->max_tokens <= 0 || c->max_seq_len <= 0 || c->max_prefill_kv < 0 ||
+      c->max_block_tokens < 0)
+    return fail(MLA_ERR_INVALID_ARG,
+                "page_size, max_batch, max_tokens, max_seq_len must be positive, max_prefill_kv and max_block_tokens >= 0");
   const int vec = c->dtype == MLA_DTYPE_BF16 ? 8 : 4;
   const int n = c->qk_nope_head_dim, r = c->qk_rope_head_dim, kc = c->kv_lora_rank, dv = c->v_head_dim;
   if (n % vec || r % vec || kc % vec || dv % vec || c->hidden_size % vec || (c->q_lora_rank % vec))
@@ -334,9 +345,14 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   if (ctx->ql > 0 && (e = dev_alloc(ctx, &ctx->qbuf, (size_t)T * H * ctx->qkh * esz))) return bail(e);
   if ((e = dev_alloc(ctx, &ctx->kvexp, (size_t)cfg->max_prefill_kv * kvb_rows * esz))) return bail(e);
   if ((e = dev_alloc(ctx, &ctx->attn, (size_t)T * H * ctx->dv * esz))) return bail(e);
-  if ((e = dev_alloc(ctx, &ctx->qlat, (size_t)B * H * ctx->c * esz))) return bail(e);
-  if ((e = dev_alloc(ctx, &ctx->olat, (size_t)B * H * ctx->c * esz))) return bail(e);
+  const int64_t QR = std::max<int64_t>(B, cfg->max_block_tokens);  // latent query / output rows
+  if ((e = dev_alloc(ctx, &ctx->qlat, (size_t)QR * H * ctx->c * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->olat, (size_t)QR * H * ctx->c * esz))) return bail(e);
   void* p;
+  if ((e = dev_alloc(ctx, &p, (size_t)(B + 1) * sizeof(int32_t)))) return bail(e);
+  ctx->blk_cu = static_cast<int32_t*>(p);
+  if ((e = dev_alloc(ctx, &p, (size_t)B * sizeof(int32_t)))) return bail(e);
+  ctx->blk_lens = static_cast<int32_t*>(p);
   if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess ||
       ctx->cus <= 0)
     return bail(fail(MLA_ERR_HIP, "querying the compute-unit count failed"));
@@ -345,16 +361,22 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   // per-split partials [B, splits, H, c] otherwise
   int64_t part_rows = 0;
   if (ctx->sk_shape) {
-    const int skb = (int)std::min<int64_t>(B, kDecodeMaxBatch);
+    // decode sequences, and the virtual sequences of query blocks (128
+    // (query, head) pairs each)
+    const int64_t vb = (int64_t)cfg->max_block_tokens * H / 128;
+    const int skb = (int)std::min<int64_t>(std::max<int64_t>(B, vb), kDecodeMaxBatch);
     ctx->sk_max_ranges = decode_sk_ranges(skb, cfg->max_seq_len, ctx->cus);
     part_rows = 2 * (int64_t)ctx->sk_max_ranges;
     if ((e = dev_alloc(ctx, &p, (size_t)(skb + 1) * sizeof(int32_t)))) return bail(e);
     ctx->sk_tstart = static_cast<int32_t*>(p);
   }
   if (!ctx->sk_shape || B > kDecodeMaxBatch) part_rows = std::max<int64_t>(part_rows, B * ctx->max_splits);
-  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * H * ctx->c * sizeof(float)))) return bail(e);
+  // partial rows hold every head of a (virtual) sequence: query blocks run
+  // with 128 (query, head) pairs per virtual sequence
+  const int64_t part_heads = cfg->max_block_tokens > 0 ? std::max(H, 128) : H;
+  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * part_heads * ctx->c * sizeof(float)))) return bail(e);
   ctx->part_o = static_cast<float*>(p);
-  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * H * sizeof(float)))) return bail(e);
+  if ((e = dev_alloc(ctx, &p, (size_t)part_rows * part_heads * sizeof(float)))) return bail(e);
   ctx->part_lse = static_cast<float*>(p);
   ctx->gemm_ws_elems = (int64_t)16 << 20;
   if ((e = dev_alloc(ctx, &p, (size_t)ctx->gemm_ws_elems * sizeof(float)))) return bail(e);
@@ -577,6 +599,120 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = batch; go.N = ctx->hid; go.K = H * ctx->dv;
+  StageTimer st(ctx, s, ST_O_PROJ);
+  return run_gemm(ctx, go, s);
+}
+
+int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_t q_len, void* kv_cache,
+                              int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* prefix_lens, int32_t max_kv_len, void* out, void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (!x || !kv_cache || !block_table || !prefix_lens || !out)
+    return fail(MLA_ERR_INVALID_ARG, "x, kv_cache, block_table, prefix_lens and out must not be NULL");
+  if (batch <= 0 || q_len <= 0 || num_blocks <= 0 || max_blocks <= 0 || max_kv_len <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch, q_len, num_blocks, max_blocks and max_kv_len must be positive");
+  if (max_kv_len < q_len) return fail(MLA_ERR_INVALID_ARG, "max_kv_len must cover the block (>= q_len)");
+  const mla_config& c = ctx->cfg;
+  const int H = ctx->H;
+  const int64_t T = (int64_t)batch * q_len;
+  if (batch > c.max_batch || T > c.max_block_tokens || T > c.max_tokens || max_kv_len > c.max_seq_len)
+    return fail(MLA_ERR_CAPACITY, "batch, batch * q_len or max_kv_len above the init limits");
+  if ((int64_t)max_blocks * c.page_size < max_kv_len)
+    return fail(MLA_ERR_INVALID_ARG, "max_blocks * page_size must cover max_kv_len");
+  if (!ctx->sk_shape) return fail(MLA_ERR_UNSUPPORTED, "query blocks need the bf16 512 + 64 latent and <= 128 heads");
+  if (((int64_t)q_len * H) % 128) return fail(MLA_ERR_UNSUPPORTED, "q_len * num_heads must be a multiple of 128");
+  const int64_t V = T * H / 128;  // virtual sequences of 128 (query, head) pairs
+  if (V > kDecodeMaxBatch) return fail(MLA_ERR_CAPACITY, "batch * q_len * num_heads above 128 K pairs");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  hipLaunchKernelGGL(block_meta_kernel, dim3((batch + 256) / 256), dim3(256), 0, s, prefix_lens, batch, q_len,
+                     ctx->blk_cu, ctx->blk_lens);
+  HIP_TRY(hipGetLastError());
+
+  void* q;
+  int64_t ldq;
+  if (int e = project(ctx, x, (int)T, s, &q, &ldq)) return e;
+
+  RopeCacheArgs rc;
+  rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
+  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.gamma_kv = ctx->gamma_kv;
+  rc.cache = kv_cache; rc.block_table = block_table;
+  rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
+  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
+  rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
+  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  rc.eps = (float)c.rms_norm_eps;
+  rc.decode = 0; rc.cu_seqlens = ctx->blk_cu; rc.prefix_lens = prefix_lens;
+  rc.max_q_len = q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
+  rc.total_tokens = (int)T;
+  {
+    StageTimer st(ctx, s, ST_ROPE_CACHE);
+    HIP_TRY(rope_cache_launch(rc, ctx->bf16, q_len, batch, s));
+  }
+
+  // W_UK absorption of every token: ql_nope[t, h] = q_nope[t, h] . W_UK^T[h]
+  GemmArgs ga;
+  ga.A = q; ga.lda = ldq; ga.sA = ctx->qkh;
+  ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
+  ga.C = ctx->qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
+  ga.M = (int)T; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
+  {
+    StageTimer st(ctx, s, ST_WUK);
+    if (int e = run_gemm(ctx, ga, s)) return e;
+  }
+
+  // latent attention: virtual sequence v holds the (token, head) pairs
+  // v * 128 .. v * 128 + 127 of [T, H] (q_len * H / 128 per sequence), all of
+  // whose tokens see the same cache entries
+  DecodeAttnArgs da;
+  da.ql = ctx->qlat; da.ldql = (int64_t)128 * ctx->c;
+  da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
+  da.cache = kv_cache; da.block_table = block_table;
+  da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
+  da.seq_lens = ctx->blk_lens; da.max_seq_len = max_kv_len; da.batch = (int)V;
+  da.H = 128; da.Hr = H; da.seq_div = (int)(V / batch);
+  da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
+  da.scale = ctx->scale;
+  da.mask.kind = MLA_MASK_FULL; da.mask.window = 0;
+  da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
+  da.o_lat = ctx->olat;
+  da.zeros = static_cast<const bf16_t*>(ctx->zeros);
+  da.ranges = decode_sk_ranges((int)V, max_kv_len, ctx->cus);
+  da.tstart = ctx->sk_tstart;
+  if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
+  if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
+  {
+    StageTimer st(ctx, s, ST_DECODE_ATTN);
+    HIP_TRY(decode_sk_launch(da, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_DECODE_MERGE);
+    HIP_TRY(decode_sk_merge_launch(da, s));
+  }
+
+  // W_UV of every token, gated
+  GemmArgs gv;
+  gv.A = ctx->olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
+  gv.W = static_cast<char*>(ctx->Wkvb) + (size_t)ctx->n * ctx->c * ctx->esz;
+  gv.ldw = ctx->c; gv.sW = (int64_t)(ctx->n + ctx->dv) * ctx->c;
+  gv.C = ctx->attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
+  gv.M = (int)T; gv.N = ctx->dv; gv.K = ctx->c; gv.batch = H;
+  if (ctx->off_g >= 0) {
+    gv.epi = EPI_GATE;
+    gv.G = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    gv.ldg = ctx->N1; gv.sG = ctx->dv;
+  }
+  {
+    StageTimer st(ctx, s, ST_WUV);
+    if (int e = run_gemm(ctx, gv, s)) return e;
+  }
+
+  GemmArgs go;
+  go.A = ctx->attn; go.lda = (int64_t)H * ctx->dv;
+  go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
+  go.C = out; go.ldc = ctx->hid;
+  go.M = (int)T; go.N = ctx->hid; go.K = H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
   return run_gemm(ctx, go, s);
 }

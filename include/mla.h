@@ -94,6 +94,7 @@ typedef struct mla_config {
   int32_t max_tokens;       /* new tokens per call (decode: = batch) */
   int32_t max_seq_len;      /* cache entries per sequence (positions < max_seq_len) */
   int32_t max_prefill_kv;   /* prefill: batch * max_kv_len rows of expanded K/V; 0 = no prefill */
+  int32_t max_block_tokens; /* mla_decode_absorbed_block: batch * q_len new tokens per call; 0 = not used */
 } mla_config;
 
 /* Layer weights, device pointers in nn.Linear [out, in] row-major layout with
@@ -174,6 +175,31 @@ MLA_API int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch,
                         void* kv_cache, int32_t num_blocks, const int32_t* block_table,
                         int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
                         int32_t mask_kind, int32_t window, void* out, void* stream);
+
+/*
+ * mla_decode_absorbed_block — a block of q_len new tokens per sequence (a
+ * draft block being verified) in absorbed form: every token of the block
+ * sees every cache entry of its sequence, the prefix and the whole block
+ * (block-visible, the FULL mask). The MLA blog's forward listing sends the
+ * tokens that the metadata counts as decode through this MQA branch, and the
+ * SpecForge PR "Add config-selectable MLA draft attention" (Test plan) runs
+ * its draft blocks through spec_generate decode; this is the same arithmetic
+ * as mla_prefill_expanded with the FULL mask, without expanding any latent.
+ *   x            device [batch * q_len, hidden]: token i of sequence b is row
+ *                b * q_len + i, at logical position prefix_lens[b] + i, and is
+ *                written to the cache before attention
+ *   prefix_lens  device int32 [batch]: cache entries before the block
+ *   max_kv_len   host: >= prefix_lens[b] + q_len for every b
+ *   out          device [batch * q_len, hidden]
+ * Requires the bf16 512 + 64 latent and q_len * num_heads a multiple of 128
+ * (MLA_ERR_UNSUPPORTED otherwise). Limits: batch <= max_batch,
+ * batch * q_len <= max_block_tokens and <= max_tokens, max_kv_len <= max_seq_len.
+ * Profiled under the decode stage names (wuk_absorb, decode_attn, ...).
+ */
+MLA_API int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_t q_len,
+                        void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* prefix_lens, int32_t max_kv_len,
+                        void* out, void* stream);
 
 /*
  * Stage timing, for measurement. When enabled, every launch sequence of the

@@ -21,24 +21,29 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool = False):
-    """One call of the workload's entry point. Returns (out [T, hidden], cache
-    [num_blocks, page, E]) as float32 numpy."""
+def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool = False, block: bool = False):
+    """One call of the workload's entry point (block: a prefill workload of
+    equal block lengths under the FULL mask through mla_decode_absorbed_block).
+    Returns (out [T, hidden], cache [num_blocks, page, E]) as float32 numpy."""
     say(f"[gpu] {w.name} mode={w.mode} B={w.batch} T={w.total_tokens} "
         f"max_kv={int(w.kv_lens.max())} mask={w.mask_kind} window={w.window} seed={w.seed}")
     t = upload(w)
     d = w.dims
     max_kv = int(w.kv_lens.max())
     prefill = w.mode == "prefill"
+    if block:
+        assert prefill and w.mask_kind == ms.MASK_FULL and len(set(int(q) for q in w.q_lens)) == 1
     cfg = B.make_config(d, max_batch=w.batch + (3 if extra_capacity else 0),
                         max_tokens=w.total_tokens + (5 if extra_capacity else 0),
                         max_seq_len=max_kv + (7 if extra_capacity else 0),
-                        max_prefill_kv=w.batch * max_kv if prefill else 0,
-                        softmax_scale=softmax_scale)
+                        max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
+                        softmax_scale=softmax_scale, max_block_tokens=w.total_tokens if block else 0)
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.full((w.total_tokens, d.hidden_size), float("nan"), dtype=dt, device="cuda")
-    if prefill:
+    if block:
+        m.decode_block(t["x"], int(w.q_lens[0]), t["cache"], t["block_table"], t["prefix_lens"], max_kv, out)
+    elif prefill:
         m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], int(w.q_lens.max()), max_kv, t["cache"],
                   t["block_table"], w.mask_kind, w.window, out, row_lo=t.get("row_lo"), row_hi=t.get("row_hi"))
     else:

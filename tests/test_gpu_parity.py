@@ -69,6 +69,22 @@ def test_draft_block_small():
     _run_and_check(w)
 
 
+def test_draft_block_absorbed_small():
+    """The draft-block shape through the absorbed block entry point: each
+    16-token block sees its whole prefix and itself; same oracle (expanded,
+    FULL mask) as the expanded entry point."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 16, 16], prefix_lens=[100, 37, 300])
+    _run_and_check(w, block=True)
+
+
+def test_draft_block_absorbed_gate_neox():
+    """Absorbed blocks with an output gate, NeoX RoPE, 8-token blocks of a
+    16-head model (two blocks per 128 (query, head) pairs) and a prefix of 0."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[8, 8, 8, 8], prefix_lens=[0, 63, 64, 1000], seed=23,
+                         dims_override={"num_heads": 16, "use_output_gate": True, "rope_style": ms.ROPE_NEOX})
+    _run_and_check(w, block=True)
+
+
 def test_decode_small():
     w = ms.make_workload("decode_bf16", seq_lens=[1, 65, 700, 333, 64])
     _run_and_check(w)
