@@ -48,7 +48,12 @@ DESCR = {
     "long_decode_bf16": "long-context decode bf16: 16 sequences, cache length uniform in [16384, 32768], "
                         "1024-token sliding window, sigmoid output gate, 128 heads, kv_lora 512, nope 128, "
                         "rope 64, v 128, hidden 7168, no q_lora",
+    "draft_block_absorbed_bf16": "the draft-block workload (8 x 16-token fully visible block over a 2048-entry "
+                                 "latent prefix, hidden 4096, 32 heads, q_lora 1536) through the absorbed "
+                                 "query-block entry point (no latent expansion)",
 }
+# workloads that run another workload's data through mla_decode_absorbed_block
+BLOCK_OF = {"draft_block_absorbed_bf16": "draft_block_bf16"}
 
 
 # ----------------------------------------------------------------------------
@@ -76,9 +81,10 @@ def visible_counts(w):
     return np.asarray(counts, dtype=np.int64)
 
 
-def stage_work(w, seqs=None):
+def stage_work(w, seqs=None, absorbed=False):
     """Algorithmic flops and bytes of each stage of one step (optionally for a
-    subset of the sequences)."""
+    subset of the sequences); absorbed: a prefill workload run through the
+    absorbed query-block path (no expansion; latent attention)."""
     d = w.dims
     esz = 2 if d.dtype == "bf16" else 4
     H, n, r, c, dv, hid, ql = (d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank,
@@ -96,13 +102,16 @@ def stage_work(w, seqs=None):
     if ql:
         work["q_b_gemm"] = dict(flops=2 * T * ql * H * (n + r), bytes=(H * (n + r) * ql + T * (ql + H * (n + r))) * esz)
     work["o_proj_gemm"] = dict(flops=2 * T * H * dv * hid, bytes=(hid * H * dv + T * (H * dv + hid)) * esz)
-    if w.mode == "prefill":
+    if w.mode == "prefill" and not absorbed:
         work["kv_b_expand"] = dict(flops=2 * kv * c * H * (n + dv),
                                    bytes=(H * (n + dv) * c + kv * (c + H * (n + dv))) * esz)
         work["prefill_attn"] = dict(flops=2 * pairs * H * (n + r + dv), bytes=None)
     else:
         work["wuk_absorb"] = dict(flops=2 * T * H * n * c, bytes=(H * n * c + T * H * (n + c)) * esz)
-        work["decode_attn"] = dict(flops=2 * pairs * H * (E + c), bytes=pairs * E * esz)
+        # bytes: the cache entries each sequence's queries read (once per
+        # sequence: every query of a block sees the same entries)
+        attn_bytes = pairs * E * esz if not absorbed else int(w.kv_lens[sel].sum()) * E * esz
+        work["decode_attn"] = dict(flops=2 * pairs * H * (E + c), bytes=attn_bytes)
         work["wuv_gemm"] = dict(flops=2 * T * H * c * dv, bytes=(H * dv * c + T * H * (c + dv)) * esz)
     work["_step"] = dict(flops=sum(v["flops"] for v in work.values()),
                          cache_bytes=pairs * E * esz,
@@ -229,7 +238,7 @@ def measured_traffic(stage, workload):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, absorbed: bool = False):
     from threadpoolctl import threadpool_info
     from oracle import mla as om
     order = list(np.argsort(w.kv_lens))  # shortest first keeps the sample bounded
@@ -248,7 +257,7 @@ def cpu_baseline(w, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    work = stage_work(w, seqs=done)
+    work = stage_work(w, seqs=done, absorbed=absorbed)  # counted like the GPU line
     per, unit = step_value(w, work)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": per / el, "unit": unit, "cores": int(threads), "kind": "oracle",
@@ -300,20 +309,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    w = ms.make_workload(args.workload)
+    block = args.workload in BLOCK_OF
+    w = ms.make_workload(BLOCK_OF.get(args.workload, args.workload))
     t = upload(w)
     d = w.dims
     max_kv = int(w.kv_lens.max())
     prefill = w.mode == "prefill"
     cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_kv,
-                        max_prefill_kv=w.batch * max_kv if prefill else 0)
+                        max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
+                        max_block_tokens=w.total_tokens if block else 0)
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.empty((w.total_tokens, d.hidden_size), dtype=dt, device="cuda")
     max_q = int(w.q_lens.max())
 
     def step():
-        if prefill:
+        if block:
+            m.decode_block(t["x"], max_q, t["cache"], t["block_table"], t["prefix_lens"], max_kv, out)
+        elif prefill:
             m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], max_q, max_kv, t["cache"], t["block_table"],
                       w.mask_kind, w.window, out)
         else:
@@ -336,7 +349,7 @@ def main():
     m.profile(False)
     ms_step = total_ms / args.steps
 
-    work = stage_work(w)
+    work = stage_work(w, absorbed=block)
     per_step, unit = step_value(w, work)
     value = per_step / (ms_step / 1e3)
 
@@ -347,7 +360,11 @@ def main():
         dom = max(timed, key=lambda k: timed[k][0])
         dom_ms = timed[dom][0] / timed[dom][1]
         wk = work.get(dom, {})
-        if dom in ("decode_attn", "rope_cache", "decode_merge") or (w.mode == "decode" and wk.get("bytes")):
+        # latent attention of query blocks reads each entry once for 16 queries
+        # (about 970 flop per byte): matrix-core bound
+        hbm = dom in ("rope_cache", "decode_merge") or (dom == "decode_attn" and not block) or \
+            (w.mode == "decode" and wk.get("bytes"))
+        if hbm:
             bound, peak, unit_r = "hbm", HBM_PEAK_GBS, "GB/s"
             achieved = (wk.get("bytes") or 0) / (dom_ms / 1e3) / 1e9
         else:
@@ -363,7 +380,8 @@ def main():
         "vs_baseline": None, "dtype": d.dtype, "data": "synthetic (seeded, random-init weights)",
         "config": {"workload": args.workload, "description": DESCR[args.workload], "batch": w.batch,
                    "new_tokens": w.total_tokens, "max_kv_len": max_kv, "entry_point":
-                       "mla_prefill_expanded" if prefill else "mla_decode_absorbed",
+                       "mla_decode_absorbed_block" if block else
+                       ("mla_prefill_expanded" if prefill else "mla_decode_absorbed"),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "stages_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in timed.items()},
@@ -374,7 +392,7 @@ def main():
         res["whole_call_gbps"] = round(work["_step"]["bytes"] / (ms_step / 1e3) / 1e9, 2)
     m.close()
     if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
