@@ -13,22 +13,27 @@
 // by a second kernel with log-sum-exp weights.
 //
 // Inside a workgroup: 8 wavefronts and all (at most 128) heads, so each
-// workgroup reads every tile once from HBM. The score product is split by
-// head: wavefront w computes the scores and the online softmax of heads
-// 16 w .. 16 w + 15 over all 576 dims, its latent queries held in registers.
-// The value product is split by latent dim: wavefront w accumulates
-// O^T = C^T P^T for latent dims 64 w .. 64 w + 63 and all heads, reading the
-// probabilities of every head block (bf16, 1 KB per block) and the rare
-// rescale factors that the other wavefronts shared through LDS. So the
-// transposing reads of the values touch each tile byte once per workgroup,
-// and the queries (72 VGPRs) plus outputs (128 VGPRs) of a wavefront fit two
-// wavefronts per SIMD. Tiles stream from HBM straight into LDS
-// (global_load_lds_dwordx4) through a ring of NBUF buffers; the scores read
-// 16-byte key-row fragments and the value product reads the same rows through
-// the transposing LDS read (ds_read_b64_tr_b16), so the tile is stored once,
-// row-major, with a swizzle that keeps both access patterns free of bank
-// conflicts.
+// workgroup reads every tile once from HBM. Tiles stream from HBM straight
+// into LDS (global_load_lds_dwordx4) through a ring of NBUF buffers, stored
+// once, row-major, with a swizzle that keeps both access patterns below free
+// of bank conflicts. The wavefronts have two roles:
+//  * score wavefront s (0..3) computes S^T (32 keys x 32 heads, heads
+//    32 s .. 32 s + 31) with the 32x32x16 MFMA: its latent queries (144
+//    VGPRs) are the B operand, and each 16-byte key fragment read from LDS
+//    serves 32 heads, half the LDS traffic of 16-head wavefronts. It runs the
+//    online softmax (one lane swap per row reduction) and publishes the bf16
+//    probabilities and the rare rescale factors in LDS;
+//  * every wavefront accumulates O^T = C^T P^T for its share of the 512
+//    latent dims over all heads, the value operand read through the
+//    transposing LDS read (ds_read_b64_tr_b16): a value wavefront holds 52
+//    16x16 blocks, a score wavefront 12 next to its queries.
+// Step t: the score wavefronts score tile t while all wavefronts multiply
+// tile t - 1 by its probabilities (double-buffered by tile parity), so the
+// MFMA pipe of each SIMD (score wavefront s and value wavefront s + 4) is fed
+// by both, and a step ends on one barrier. The two roles are compiled as two
+// copies of the piece loop, so each has its own register allocation.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -42,12 +47,11 @@ constexpr int ECH = 72;             // 16-byte chunks per 576-wide bf16 entry
 constexpr int SLOTS = KT * ECH;     // 16-byte chunks per tile
 constexpr int NW = 8;               // wavefronts per workgroup
 constexpr int NT = NW * 64;         // threads per workgroup
-constexpr int DMA_N = (SLOTS + NT - 1) / NT;  // DMA instructions per lane per tile (the last one partial)
-constexpr int KS = 18;              // 32-dim steps of the score product
-constexpr int DB = 32;              // 16-dim blocks of the 512 value dims
-constexpr int DBW = DB / NW;        // value blocks of one wavefront (64 latent dims)
-constexpr int HBW = NW;             // 16-head blocks of a workgroup (128 heads)
-static_assert(HBW == 8, "the rescale flags of the head blocks are read as one 8-byte word");
+constexpr int DMA_N = (SLOTS + NT - 1) / NT;  // copy instructions per lane per tile (the last one partial)
+static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane copy instructions");
+constexpr int KS2 = 36;             // 16-dim steps of the score product (32x32x16 MFMA)
+constexpr int HB = 8;               // 16-head blocks of a workgroup (128 heads)
+static_assert(HB == 8, "the rescale flags of the head blocks are read as one 8-byte word");
 constexpr int ROWB = ECH * 16;      // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane DMA instructions");
@@ -89,6 +93,30 @@ __device__ __forceinline__ int tile_count(int lo, int hi) { return hi > lo ? (hi
 // first tile of range r of R over T tiles
 __device__ __forceinline__ int range_start(int r, int R, int T) { return (int)(((int64_t)r * T) / R); }
 
+// O^T blocks (16 latent dims x 16 heads) held by one wavefront, as slots j
+// of 16 dims D(j) over a range of head blocks; reg(j, hb) is the index of the
+// block in the wavefront's register array (-1: not held). Score wavefront s
+// holds dims 16 (28 + s) .. for all heads and 16 (24 + s) .. for heads 0-63
+// (12 blocks after its 36 query registers); value wavefront v holds dims
+// 96 v .. 96 v + 95 for all heads and 16 (24 + v) .. for heads 64-127 (52
+// blocks). Value wavefronts multiply in two passes (4 + 3 slots) so that at
+// most 4 value operands are live.
+template <bool S> struct Blocks;
+template <> struct Blocks<true> {
+  static constexpr int NREG = 48, NSLOT = 2, NPASS = 1;
+  static constexpr int first(int) { return 0; }
+  static constexpr int last(int) { return 2; }
+  __device__ static int D(int j, int w) { return j == 0 ? 28 + w : 24 + w; }
+  static constexpr int reg(int j, int hb) { return j == 0 ? 36 + hb : (hb < 4 ? 44 + hb : -1); }
+};
+template <> struct Blocks<false> {
+  static constexpr int NREG = 52, NSLOT = 7, NPASS = 2;
+  static constexpr int first(int p) { return p == 0 ? 0 : 4; }
+  static constexpr int last(int p) { return p == 0 ? 4 : 7; }
+  __device__ static int D(int j, int v) { return j < 6 ? 6 * v + j : 24 + v; }
+  static constexpr int reg(int j, int hb) { return j < 6 ? 8 * j + hb : (hb >= 4 ? 44 + hb : -1); }
+};
+
 template <int NBUF>
 __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 tile[NBUF][SLOTS];
@@ -98,14 +126,16 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   __shared__ int t_lo[kDecodeMaxTiles], t_hi[kDecodeMaxTiles];
   __shared__ int t_end[kDecodeMaxTiles];  // end (local index) of the tile's piece
   __shared__ int wsum[NW];
-  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[HBW][64];  // probabilities of every head block
-  __shared__ float abuf[HBW][16];                                // rescale factors of every head
-  __shared__ __attribute__((aligned(8))) unsigned char aflag[HBW];  // head block needs a rescale
-  __shared__ float mbuf[HBW][16], lbuf[HBW][16];                 // softmax state at a piece's end
+  // probabilities of tile t in buffer t & 1, as the B operands of the value
+  // product: head block hb, lane (g, lr) -> 8 bf16 of head 16 hb + lr, keys
+  // 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3
+  __shared__ __attribute__((aligned(16))) bf16x8 pbuf[2][HB][64];
+  __shared__ float abuf[2][HB * 16];                                // rescale factor of every head
+  __shared__ __attribute__((aligned(8))) unsigned char aflag[2][HB];  // head block needs a rescale
+  __shared__ float lbuf[HB * 16];                                   // softmax normaliser at a piece's end
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, g = lane >> 4;
   const int R = a.ranges;
   // ranges r .. r + R/8 - 1 run on one XCD (workgroup id mod 8): neighbouring
   // ranges share sequences, so their latent queries are read from that L2
@@ -220,29 +250,100 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     }
   };
 
-  // ---- per-lane LDS read bases (bytes). Scores: rows lr and 16 + lr, chunk
-  // 4 s + g. Values (transposing reads) of this wavefront's 64 latent dims:
-  // lane k = 4 qa + qb of its 16-lane group points at rows 4 g + qa (and
-  // 16 + 4 g + qa), dims 64 wave + 16 d + 4 qb .. + 3.
-  int kbase[2], vrow, vx;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) kbase[x] = (lr * ECH + ((4 * x + g) ^ swz(lr))) * 16;
+  // ---- roles: wavefronts 0-3 score (heads 32 wave .. + 31), wavefronts
+  // 4-7 only multiply; wavefronts w and w + 4 share a SIMD. The O^T blocks of
+  // each role are listed in Blocks<>; a score wavefront keeps its queries in
+  // RG[0..35] of its register array.
+  const bool sw = wave < 4;
+  const int hs = wave * 32 + (lane & 31);  // score waves: head of this lane's scores
+  const bool hok = sw && hs < a.H;
+  const bool sact = sw && wave * 32 < a.H;  // the score wave owns at least one head
+  const int nhb = (a.H + 15) >> 4;           // head blocks with at least one head
+  const float sl2 = a.scale * kLog2e;
+  const int lr = lane & 15, g = (lane >> 4) & 3;
+
+  // score operand A (32 keys x 16 dims, step t): lane l reads key l % 32,
+  // dims 16 t + 8 (l / 32) .. + 7, i.e. chunk 2 t + l / 32 of the row, stored at
+  // 8 (t / 4) + ((2 (t % 4) + l / 32) ^ swz(row)); kb[u] is the byte offset for
+  // t % 4 == u without the 128 (t / 4)
+  int kb[4];
   {
-    // chunk 8 wave + (2 d + (qb >> 1)) of the row, the low 3 bits XOR-ed with swz(row)
+    const int row = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kb[u] = row * ROWB + (((2 * u) | hl) ^ swz(row)) * 16;
+  }
+  // value operand A (16 dims x 32 keys, transposing reads): lane k = 4 qa + qb
+  // of 16-lane group g points at rows 4 g + qa (and 16 + 4 g + qa), dims
+  // 16 D + 4 qb .. + 3 = chunk 2 D + qb / 2, byte (qb & 1) * 8 of the chunk
+  int vrow, vx;
+  {
     const int qa = lr >> 2, qb = lr & 3;
     const int row = 4 * g + qa;
-    vrow = (row * ECH + 8 * wave) * 16 + (qb & 1) * 8;
+    vrow = row * ROWB + (qb & 1) * 8;
     vx = (qb >> 1) ^ swz(row);
   }
 
-  const int h = wave * 16 + lr;  // head of this lane's scores and softmax
-  const bool hok = h < a.H;
-  const float sl2 = a.scale * kLog2e;
-
-  // ---- ring: tiles i + 1 .. i + NBUF - 1 are in flight while tile i is used
+  // O^T (this wavefront's blocks) += C^T P^T for tile t; operand element e of
+  // lane (g, lr) is key 16 (e / 4) + 4 g + e % 4
+  auto value = [&](floatx4* RG, auto rolec, int t) __attribute__((always_inline)) {
+    using BK = Blocks<decltype(rolec)::value>;
+    const int wl = wave & 3;
+    const char* Tb = reinterpret_cast<const char*>(&tile[t % NBUF][0]);
+    const int pb = t & 1;
+    // one 8-byte read of all the rescale flags (rare: lazy rescaling)
+    const uint64_t flags = *reinterpret_cast<const uint64_t*>(&aflag[pb][0]);
+    if (__builtin_amdgcn_readfirstlane((uint32_t)flags) | __builtin_amdgcn_readfirstlane((uint32_t)(flags >> 32))) {
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
+      for (int hb = 0; hb < HB; ++hb) {
+        if ((flags >> (8 * hb)) & 0xff) {
+          const float al = abuf[pb][hb * 16 + lr];
+#pragma unroll
+          for (int j = 0; j < BK::NSLOT; ++j)
+            if (BK::reg(j, hb) >= 0) RG[BK::reg(j, hb)] *= al;
+        }
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < BK::NPASS; ++ps) {
+      Frag<bf16> vf[4];
+#pragma unroll
+      for (int j = BK::first(ps); j < BK::last(ps); ++j) {
+        const int D = BK::D(j, wl);
+        const char* p = Tb + vrow + (D >> 2) * 128 + ((2 * (D & 3)) ^ vx) * 16;
+        vf[j - BK::first(ps)].v = tr_pair(p, p + 16 * ROWB);
+      }
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        if (hb < nhb) {
+          Frag<bf16> ph;
+          ph.v = pbuf[pb][hb][lane];
+#pragma unroll
+          for (int j = BK::first(ps); j < BK::last(ps); ++j)
+            if (BK::reg(j, hb) >= 0)
+              RG[BK::reg(j, hb)] = mfma16(vf[j - BK::first(ps)], ph, RG[BK::reg(j, hb)]);
+        }
+      }
+    }
+  };
+
+  // ---- ring of NBUF tiles: tile t is read in steps t (scores) and t + 1
+  // (values), so step t refills the buffer of tile t - 2 with tile t + NBUF - 2
+  static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 tiles");
+  auto wait_tiles = [&](int later) {  // all but the copies of the `later` tiles issued last have landed
+    if (later <= 0) MLA_WAIT_VMCNT(0);
+    else if (last_dma) MLA_WAIT_VMCNT(DMA_N);
+    else MLA_WAIT_VMCNT(DMA_N - 1);
+  };
+#pragma unroll
+  for (int i = 0; i < NBUF - 2; ++i)
     if (i < n) issue(i, i);
+
+  // the piece loop, compiled once per role: each copy has its own register
+  // allocation, and both run the same sequence of barriers
+  auto run = [&](auto rolec) __attribute__((always_inline)) {
+  constexpr bool sw = decltype(rolec)::value;
+  floatx4 RG[Blocks<sw>::NREG];
+  float m = -INFINITY, l = 0.f;
   int i = 0;
   while (i < n) {
     // ---- one piece: the consecutive tiles [i, iend) of sequence b
@@ -250,14 +351,16 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     const int iend = __builtin_amdgcn_readfirstlane(t_end[i]);
     const int lo = __builtin_amdgcn_readfirstlane(t_lo[i]);
     const int hi = __builtin_amdgcn_readfirstlane(t_hi[i]);
-    const bool piece_start = __builtin_amdgcn_readfirstlane(t_k0[i]) == (lo / KT) * KT;
+    const bool seq_start = __builtin_amdgcn_readfirstlane(t_k0[i]) == (lo / KT) * KT;
+    const bool whole = seq_start && __builtin_amdgcn_readfirstlane(t_k0[iend - 1]) + KT >= hi;
+    const int64_t slot = 2 * (int64_t)r + (seq_start ? 1 : 0);
 
-    // latent query of head h: B operand of S^T, dims 32 s + 8 g .. + 7
-    Frag<bf16> q[KS];
-    {
-      const bf16* ql = reinterpret_cast<const bf16*>(a.ql) + (int64_t)b * a.ldql + (int64_t)(hok ? h : 0) * a.c;
+    if constexpr (sw) {
+      // latent query of head hs: B operand of S^T, step t = dims 16 t + 8 (l / 32) .. + 7
+      const int hq = hok ? hs : 0;
+      const bf16* ql = reinterpret_cast<const bf16*>(a.ql) + (int64_t)b * a.ldql + (int64_t)hq * a.c;
       // roped query: token and head of the (query, head) pair in query blocks
-      int64_t qt = b, qh = hok ? h : 0;
+      int64_t qt = b, qh = hq;
       if (a.Hr > 0) {
         const int64_t pair = (int64_t)b * a.H + qh;
         qt = pair / a.Hr;
@@ -265,157 +368,154 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       }
       const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qt * a.ldq + qh * a.qk_head + a.n;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int e = s * 32 + g * 8;
-        const bf16* src = !hok ? a.zeros : (s < 16 ? ql + e : qp + (e - 512));
-        q[s].v = *reinterpret_cast<const bf16x8*>(src);
+      for (int t = 0; t < KS2; ++t) {
+        const int e = t * 16 + (lane >> 5) * 8;
+        const bf16* src = !hok ? a.zeros : (t < 32 ? ql + e : qp + (e - 512));
+        RG[t] = __builtin_bit_cast(floatx4, *reinterpret_cast<const bf16x8*>(src));
       }
+#pragma unroll
+      for (int k = KS2; k < Blocks<sw>::NREG; ++k) RG[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int k = 0; k < Blocks<sw>::NREG; ++k) RG[k] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    // the queries, and the outputs stored by the previous piece (stores may
-    // complete out of order with loads): wait for everything
+    // the queries, the tiles in flight and the outputs stored by the previous
+    // piece (stores may complete out of order with loads): wait for everything
     MLA_WAIT_VMCNT(0);
-    // O^T blocks: latent dims 64 wave + 16 d + 4 g + {0..3}, head 16 hb + lr
-    floatx4 o[DBW][HBW];
-#pragma unroll
-    for (int d = 0; d < DBW; ++d)
-#pragma unroll
-      for (int hb = 0; hb < HBW; ++hb) o[d][hb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
+    // ... for every wavefront; the previous piece's normalisers are no longer read
+    lds_barrier();
+    m = -INFINITY;
+    l = 0.f;
 
-    for (; i < iend; ++i) {
-      const int buf = i % NBUF;
-      const int later = min(NBUF - 2, n - 1 - i);  // tiles after i already issued
-      if (later <= 0) MLA_WAIT_VMCNT(0);
-      else if (later == 1) { if (last_dma) MLA_WAIT_VMCNT(DMA_N); else MLA_WAIT_VMCNT(DMA_N - 1); }
-      else { if (last_dma) MLA_WAIT_VMCNT(2 * DMA_N); else MLA_WAIT_VMCNT(2 * DMA_N - 2); }
-      lds_barrier();  // tile i is in LDS for every wavefront; tile i - 1 and the shared probabilities are no longer read
-      if (i + NBUF - 1 < n) issue(i + NBUF - 1, (i + NBUF - 1) % NBUF);
-      const int k0 = __builtin_amdgcn_readfirstlane(t_k0[i]);
-      const char* Tb = reinterpret_cast<const char*>(&tile[buf][0]);
-
-      // ---- S^T (32 keys x the 16 heads of this wavefront) = C q^T over the 576 dims
-      floatx4 sc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    // step it: the score wavefronts score tile it and publish its
+    // probabilities (buffer it & 1); every wavefront multiplies tile it - 1 by
+    // its probabilities (buffer (it - 1) & 1)
+    for (int it = i; it <= iend; ++it) {
+      // the copies of tile it + NBUF - 2 go into the buffer of tile it - 2
+      // (read last in step it - 1)
+      if (it < iend && it + NBUF - 2 < n) issue(it + NBUF - 2, (it + NBUF - 2) % NBUF);
+      if constexpr (sw) {
+        const bool scoring = it < iend && sact;
+        bf16x4 pq[4];
+        float alpha = 1.f;
+        if (scoring) {
+          // ---- S^T (32 keys x 32 heads) = C q^T over the 576 dims
+          const int k0 = __builtin_amdgcn_readfirstlane(t_k0[it]);
+          const char* Tb = reinterpret_cast<const char*>(&tile[it % NBUF][0]);
+          // key fragments are read KLA steps ahead of their MFMA (one wavefront
+          // per SIMD scores, so its own reads must cover the LDS latency)
+          constexpr int KLA = 4;
+          floatx16 sc = {};
+          bf16x8 kf[KLA];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        Frag<bf16> k0f, k1f;
-        const char* p = Tb + kbase[s & 1] + (s >> 1) * 128;
-        k0f.v = *reinterpret_cast<const bf16x8*>(p);
-        k1f.v = *reinterpret_cast<const bf16x8*>(p + 16 * ROWB);
-        sc[0] = mfma16(k0f, q[s], sc[0]);
-        sc[1] = mfma16(k1f, q[s], sc[1]);
-      }
-
-      // ---- online softmax of head h (log2 domain); lane holds keys 16 kb + 4 g + e
-      const bool edge = k0 < lo || k0 + KT > hi;
-      float mx = -INFINITY;
+          for (int t = 0; t < KLA; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(Tb + kb[t & 3] + (t >> 2) * 128);
+          // hard scheduling fences keep each read KLA steps ahead (the
+          // scheduler would otherwise sink it to its MFMA)
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float x = sc[kb][e] * sl2;
-          if (edge) {
-            const int key = k0 + kb * 16 + g * 4 + e;
-            if (key < lo || key >= hi) x = -INFINITY;
+          for (int t = 0; t < KS2; ++t) {
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KLA], __builtin_bit_cast(bf16x8, RG[t]), sc, 0, 0, 0);
+            if (t + KLA < KS2) kf[t % KLA] = *reinterpret_cast<const bf16x8*>(Tb + kb[(t + KLA) & 3] + ((t + KLA) >> 2) * 128);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          sc[kb][e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = red4_max(mx);
-      // lazy rescaling: the reference max moves only when exceeded by more
-      // than 2^8 (probabilities stay <= 256; exact after the division by l)
-      const float mnew = (mx > m + 8.f) ? mx : m;
-      const float alpha = m == -INFINITY ? 1.f : fast_exp2(m - mnew);
-      Frag<bf16> pf;
-      float sum = 0.f;
+          // ---- online softmax of head hs (log2 domain); element e of lane l
+          // is key 8 (e / 4) + 4 (l / 32) + e % 4; lanes l and l ^ 32 hold the
+          // same head
+          const bool edge = k0 < lo || k0 + KT > hi;
+          float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int e = 0; e < 16; ++e) {
+            float x = sc[e] * sl2;
+            if (edge) {
+              const int key = k0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              if (key < lo || key >= hi) x = -INFINITY;
+            }
+            sc[e] = x;
+            mx = fmaxf(mx, x);
+          }
+          mx = red2_max(mx);
+          // lazy rescaling: the reference max moves only when exceeded by
+          // more than 2^8 (probabilities stay <= 256; exact after the
+          // division by l)
+          const float mnew = (mx > m + 8.f) ? mx : m;
+          alpha = m == -INFINITY ? 1.f : fast_exp2(m - mnew);
+          float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = fast_exp2(sc[kb][e] - mnew);
-          sum += pv;
-          pf.v[kb * 4 + e] = (bf16)pv;
+          for (int e = 0; e < 16; ++e) {
+            const float pv = fast_exp2(sc[e] - mnew);
+            sum += pv;
+            pq[e >> 2][e & 3] = (bf16)pv;
+          }
+          l = l * alpha + red2_sum(sum);
+          m = mnew;
         }
-      l = l * alpha + sum;
-      m = mnew;
-      // share the probabilities (the B operand of head block `wave`) and the
-      // rescale factors with the wavefronts that own the other latent dims
-      pbuf[wave][lane] = pf.v;
-      const bool resc = __any(alpha != 1.f);
-      if (resc && g == 0) abuf[wave][lr] = alpha;
-      if (lane == 0) aflag[wave] = resc ? 1 : 0;
+        if (scoring) {
+          // probabilities: key group kg = 2 q + l / 32 (keys 4 kg .. 4 kg + 3)
+          // goes to lane 16 (kg % 4) + lr of head block hb, half kg / 4
+          const int hb = 2 * wave + ((lane >> 4) & 1);
+          char* pbase = reinterpret_cast<char*>(&pbuf[it & 1][hb][0]);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int kg = 2 * q4 + (lane >> 5);
+            *reinterpret_cast<bf16x4*>(pbase + (16 * (kg & 3) + lr) * 16 + (kg >> 2) * 8) = pq[q4];
+          }
+          const uint64_t rm = __ballot(alpha != 1.f);
+          if (lane < 32) abuf[it & 1][hs] = alpha;
+          if (lane == 0) {
+            aflag[it & 1][2 * wave] = (rm & 0xffffull) ? 1 : 0;
+            aflag[it & 1][2 * wave + 1] = (rm & 0xffff0000ull) ? 1 : 0;
+          }
+          if (it == iend - 1) {
+            // the piece ends here: share the normaliser; a cut piece also
+            // writes its log-sum-exp (slot 1: the piece starts the sequence
+            // and the range ends inside it; slot 0: the range starts inside
+            // the sequence)
+            if (lane < 32) lbuf[hs] = l;
+            if (!whole && lane < 32 && hok) a.part_lse[slot * a.H + hs] = m + __log2f(l);
+          }
+        } else if (it < iend && lane == 0) {
+          // no head of this wave: no rescale flags for its head blocks
+          aflag[it & 1][2 * wave] = 0;
+          aflag[it & 1][2 * wave + 1] = 0;
+        }
+        if (it > i) value(RG, rolec, it - 1);
+      } else if (it > i) {
+        value(RG, rolec, it - 1);
+      }
+      if (it < iend) wait_tiles(min(NBUF - 3, n - 2 - it));  // tile it + 1 landed
+      // tile it + 1 is in LDS for every wavefront; the probabilities of tile
+      // it are shared; tile it - 1 and the probabilities of tile it - 1 are no
+      // longer read
       lds_barrier();
-
-      // ---- O^T (this wavefront's 64 latent dims x 128 heads) += C^T P^T;
-      // operand element e of lane (g, lr) is key 16 (e / 4) + 4 g + e % 4,
-      // the order the scores came in
-      // one 8-byte read of all the rescale flags (rare: lazy rescaling)
-      const uint64_t flags = *reinterpret_cast<const uint64_t*>(aflag);
-      if (__builtin_amdgcn_readfirstlane((uint32_t)flags) | __builtin_amdgcn_readfirstlane((uint32_t)(flags >> 32))) {
-#pragma unroll
-        for (int hb = 0; hb < HBW; ++hb) {
-          if ((flags >> (8 * hb)) & 0xff) {
-            const float al = abuf[hb][lr];
-#pragma unroll
-            for (int d = 0; d < DBW; ++d) o[d][hb] *= al;
-          }
-        }
-      }
-      Frag<bf16> vf[DBW];
-#pragma unroll
-      for (int d = 0; d < DBW; ++d) {
-        const char* p = Tb + vrow + ((2 * d) ^ vx) * 16;
-        vf[d].v = tr_pair(p, p + 16 * ROWB);
-      }
-#pragma unroll
-      for (int hb = 0; hb < HBW; ++hb) {
-        Frag<bf16> ph;
-        ph.v = pbuf[hb][lane];
-#pragma unroll
-        for (int d = 0; d < DBW; ++d) o[d][hb] = mfma16(vf[d], ph, o[d][hb]);
-      }
     }
 
-    // ---- finish this piece of sequence b: whole sequence -> normalised latent
-    // output; a cut piece -> partial output + log-sum-exp in slot 1 (piece
-    // starts the sequence, range ends inside it) or slot 0 (the range starts
-    // inside the sequence). Each head's softmax state comes from the
-    // wavefront that owns its scores.
+    // ---- finish the piece: a whole sequence -> normalised latent output; a
+    // cut piece -> partial output (normalised by its own sum, stored as bf16:
+    // the merged latent output is rounded to bf16 in any case)
     {
-      const float lsum = red4_sum(l);
-      if (g == 0) {
-        mbuf[wave][lr] = m;
-        lbuf[wave][lr] = lsum;
-      }
-      lds_barrier();
-      const int klast = __builtin_amdgcn_readfirstlane(t_k0[iend - 1]);
-      const bool whole = piece_start && klast + KT >= hi;
-      const int64_t slot = 2 * (int64_t)r + (piece_start ? 1 : 0);
+      using BK = Blocks<sw>;
+      const int wl = wave & 3;
 #pragma unroll
-      for (int hb = 0; hb < HBW; ++hb) {
-        const int hh = hb * 16 + lr;
+      for (int hb = 0; hb < HB; ++hb) {
+        const int hh = 16 * hb + lr;
         if (hh >= a.H) continue;
-        const float inv = 1.f / lbuf[hb][lr];
-        if (whole) {
-          bf16* dst = reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + hh) * a.c + wave * 64 + g * 4;
+        const float inv = 1.f / lbuf[hh];
+        bf16* dst = whole ? reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + hh) * a.c
+                          : reinterpret_cast<bf16*>(a.part_o) + (slot * a.H + hh) * a.c;
+        dst += 4 * g;
 #pragma unroll
-          for (int d = 0; d < DBW; ++d) {
-            const floatx4 v = o[d][hb] * inv;
-            *reinterpret_cast<bf16x4*>(dst + d * 16) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-          }
-        } else {
-          // partial output, normalised by its own sum, stored as bf16 (the
-          // merged latent output is rounded to bf16 in any case)
-          bf16* dst = reinterpret_cast<bf16*>(a.part_o) + (slot * a.H + hh) * a.c + wave * 64 + g * 4;
-#pragma unroll
-          for (int d = 0; d < DBW; ++d) {
-            const floatx4 v = o[d][hb] * inv;
-            *reinterpret_cast<bf16x4*>(dst + d * 16) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-          }
+        for (int j = 0; j < BK::NSLOT; ++j) {
+          if (BK::reg(j, hb) < 0) continue;
+          const floatx4 v = RG[BK::reg(j, hb)] * inv;
+          *reinterpret_cast<bf16x4*>(dst + 16 * BK::D(j, wl)) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
         }
       }
-      if (!whole && g == 0 && hok) a.part_lse[slot * a.H + h] = m + __log2f(lsum);
     }
+    i = iend;
   }
+  };
+  if (sw) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // o_lat of the sequences that were cut between ranges: log-sum-exp weighted

@@ -85,6 +85,19 @@ __device__ __forceinline__ float red4_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
+// Reductions over the lane pair l, l ^ 32 (the two halves of a 32x32 MFMA
+// output column) with one permlane32_swap.
+__device__ __forceinline__ float red2_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+__device__ __forceinline__ float red2_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's bytes land at LDS address lds_base + 16 l. Issued through inline
 // asm so that the compiler does not treat later LDS reads as aliasing the
