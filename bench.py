@@ -222,6 +222,60 @@ def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands):
     return written
 
 
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+SIMD_NUM = 256 * 4  # MI355X: 256 compute units of 4 SIMDs
+XCD_NUM = 8         # the per-dispatch GRBM_GUI_ACTIVE value is the sum over the 8 XCDs
+
+
+def _kernel_short(name):
+    """mla::gemm_big_kernel from a demangled name (mangled names stay as they are)"""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].strip()
+
+
+def mfma_summary(pmc_dir, workload, command):
+    """profiles/mfma_<workload>.json from one rocprofv3 --pmc run of MFMA_COUNTERS:
+    per (kernel, grid size): MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES /
+    (GRBM_GUI_ACTIVE / XCD_NUM * SIMD_NUM) (rocprofv3's MfmaUtil, which takes
+    the largest per-XCD GUI-active count), and the bf16 MFMA flops the
+    counters saw (SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512) per dispatch."""
+    rows = _pmc_rows(pmc_dir)
+    disp = {}
+    for r in rows:
+        if r["Counter_Name"] not in MFMA_COUNTERS:
+            continue
+        k = r["Dispatch_Id"]
+        rec = disp.setdefault(k, {"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size"]), "ns": None})
+        rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("End_Timestamp") and r.get("Start_Timestamp"):
+            rec["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    groups = {}
+    for rec in disp.values():
+        if not all(c in rec for c in MFMA_COUNTERS) or rec["GRBM_GUI_ACTIVE"] <= 0:
+            continue
+        name = _kernel_short(rec["kernel"])
+        groups.setdefault((name, rec["grid"]), []).append(rec)
+    out = []
+    for (name, grid), recs in sorted(groups.items(), key=lambda kv: -sum(x["GRBM_GUI_ACTIVE"] for x in kv[1])):
+        busy = sum(x["SQ_VALU_MFMA_BUSY_CYCLES"] / (x["GRBM_GUI_ACTIVE"] / XCD_NUM * SIMD_NUM) for x in recs) / len(recs)
+        flops = sum(x["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for x in recs) / len(recs)
+        if flops <= 0:
+            continue
+        ent = {"kernel": name, "grid": grid, "dispatches": len(recs), "mfma_busy_pct": round(100 * busy, 2),
+               "bf16_mfma_gflop_per_dispatch": round(flops / 1e9, 3)}
+        ns = [x["ns"] for x in recs if x["ns"]]
+        if ns:
+            ent["avg_dispatch_us_under_counters"] = round(sum(ns) / len(ns) / 1e3, 2)
+            ent["mfma_tflops_under_counters"] = round(flops / (sum(ns) / len(ns)) / 1e3, 1)
+        out.append(ent)
+    srcs = sorted({f for v in STAGE_SOURCES.values() for f in v})
+    rec = {"workload": workload, "counters": MFMA_COUNTERS, "simd_num": SIMD_NUM, "xcd_num": XCD_NUM, "kernels": out,
+           "source_sha": kernel_source_sha(srcs), "command": command}
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    return path
+
+
 def measured_traffic(stage, workload):
     """HBM bytes per launch from profiles/traffic_<stage>_<workload>.json, or
     None when absent or taken on a different kernel source."""
@@ -280,7 +334,16 @@ def main():
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic_*.json from two rocprofv3 --pmc runs of this workload "
                          "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibrate; no GPU work")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write profiles/mfma_<workload>.json from one rocprofv3 --pmc run of this workload "
+                         "with the MFMA counters; no GPU work")
     args = ap.parse_args()
+    if args.mfma_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
+               f" --output-format csv -d <out> -o run -- python3 <repo>/bench.py --workload {args.workload} "
+               f"--steps {args.steps} --warmup {args.warmup} --cpu-seconds 0")
+        print("wrote", mfma_summary(args.mfma_summary, args.workload, cmd))
+        return
     if args.traffic_summary:
         cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
                f"python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
