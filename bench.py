@@ -181,7 +181,7 @@ def _per_dispatch(rows, counter, pat):
     return out
 
 
-def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands):
+def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands, out_dir=None):
     """profiles/traffic_<stage>_<workload>.json from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE: KiB per dispatch), each counter scaled by what
     it reads for the copy calibration (copy_mib MiB read and written)."""
@@ -215,7 +215,7 @@ def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands):
                "copy_calibration_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
                "bytes_per_launch": int((fk * ff + wk * wf) * 1024),
                "source_sha": kernel_source_sha(STAGE_SOURCES[stage]), "commands": commands}
-        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+        path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{stage}_{workload}.json")
         with open(path, "w") as fh:
             json.dump(rec, fh, indent=1)
         written.append(path)
@@ -232,7 +232,7 @@ def _kernel_short(name):
     return name.replace("(anonymous namespace)::", "").split("(")[0].strip()
 
 
-def mfma_summary(pmc_dir, workload, command):
+def mfma_summary(pmc_dir, workload, command, out_dir=None):
     """profiles/mfma_<workload>.json from one rocprofv3 --pmc run of MFMA_COUNTERS:
     per (kernel, grid size): MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES /
     (GRBM_GUI_ACTIVE / XCD_NUM * SIMD_NUM) (rocprofv3's MfmaUtil, which takes
@@ -270,7 +270,7 @@ def mfma_summary(pmc_dir, workload, command):
     srcs = sorted({f for v in STAGE_SOURCES.values() for f in v})
     rec = {"workload": workload, "counters": MFMA_COUNTERS, "simd_num": SIMD_NUM, "xcd_num": XCD_NUM, "kernels": out,
            "source_sha": kernel_source_sha(srcs), "command": command}
-    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"mfma_{workload}.json")
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     return path
