@@ -82,13 +82,13 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
     } else {
       const GatherA& ga = g.ga;
       const int b = m / ga.max_kv_len, jj = m % ga.max_kv_len;
+      // the block-table read does not wait for the lengths: its index is in
+      // bounds for every row (max_blocks * page covers max_kv_len, host check)
+      const int blk = ga.block_table[(int64_t)b * ga.max_blocks + jj / ga.page];
       int ql = ga.cu_seqlens[b + 1] - ga.cu_seqlens[b];
       ql = min(max(ql, 0), ga.max_q_len);
       const int pl = min(max(ga.prefix_lens[b], 0), ga.max_kv_len - ql);
-      if (jj < pl + ql) {
-        const int blk = ga.block_table[(int64_t)b * ga.max_blocks + jj / ga.page];
-        if (blk >= 0 && blk < ga.num_blocks) off = ((int64_t)blk * ga.page + jj % ga.page) * ga.entry;
-      }
+      if (jj < pl + ql && blk >= 0 && blk < ga.num_blocks) off = ((int64_t)blk * ga.page + jj % ga.page) * ga.entry;
     }
     aoff[j] = (uint32_t)(off * 2) + colb;
   }
