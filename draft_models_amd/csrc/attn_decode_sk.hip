@@ -540,22 +540,37 @@ __global__ __launch_bounds__(256) void decode_sk_merge_kernel(DecodeAttnArgs a) 
   const int gs = range_of(ts), ge = range_of(te - 1);
   if (gs == ge) return;  // finished inside one range
   const bf16* po = reinterpret_cast<const bf16*>(a.part_o);
-  float mx = -INFINITY;
-  for (int gg = gs; gg <= ge; ++gg) {
-    if (gg > gs && range_start_d(gg + 1, R, T) == range_start_d(gg, R, T)) continue;  // empty range
-    const int64_t slot = 2 * (int64_t)gg + (gg == gs ? 1 : 0);
-    mx = fmaxf(mx, a.part_lse[slot * a.H + h]);
-  }
+  // the pieces in groups of 8, each group's loads issued together, combined
+  // with a running maximum of the log-sum-exps
+  float mx = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int gg = gs; gg <= ge; ++gg) {
-    if (gg > gs && range_start_d(gg + 1, R, T) == range_start_d(gg, R, T)) continue;
-    const int64_t slot = 2 * (int64_t)gg + (gg == gs ? 1 : 0);
-    const float w = fast_exp2(a.part_lse[slot * a.H + h] - mx);
-    den += w;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(po + (slot * a.H + h) * a.c + t * 8);
+  for (int g0 = gs; g0 <= ge; g0 += 8) {
+    float lse[8];
+    bf16x8 x[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += w * (float)x[e];
+    for (int e = 0; e < 8; ++e) {
+      const int gg = g0 + e;
+      // (an empty range past the first holds no piece)
+      const bool ok = gg <= ge && (gg == gs || range_start_d(gg + 1, R, T) != range_start_d(gg, R, T));
+      const int64_t slot = 2 * (int64_t)gg + (gg == gs ? 1 : 0);
+      lse[e] = ok ? a.part_lse[slot * a.H + h] : -INFINITY;
+      x[e] = ok ? *reinterpret_cast<const bf16x8*>(po + (slot * a.H + h) * a.c + t * 8) : bf16x8{};
+    }
+    float cm = mx;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cm = fmaxf(cm, lse[e]);
+    const float sc = mx == -INFINITY ? 0.f : fast_exp2(mx - cm);
+    den *= sc;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float w = lse[e] == -INFINITY ? 0.f : fast_exp2(lse[e] - cm);
+      den += w;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[d] += w * (float)x[e][d];
+    }
+    mx = cm;
   }
   const float inv = 1.f / den;
   bf16x8 v;

@@ -43,14 +43,52 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
 
   // rotate q[t, h, n:] for every head, in place
   T* q = reinterpret_cast<T*>(a.q) + (int64_t)t * a.ldq;
-  for (int p = threadIdx.x; p < a.H * half; p += 256) {
-    const int h = p / half, j = p % half;
-    int ia, ib;
-    pair(j, ia, ib);
-    T* qh = q + (int64_t)h * a.qk_head + a.n;
-    const float xa = to_f32(qh[ia]), xb = to_f32(qh[ib]);
-    qh[ia] = from_f32<T>(xa * cs[j] - xb * sn[j]);
-    qh[ib] = from_f32<T>(xa * sn[j] + xb * cs[j]);
+  bool done = false;
+  if constexpr (sizeof(T) == 2) {
+    if (a.r == 64 && a.ldq % 8 == 0 && a.qk_head % 8 == 0 && a.n % 8 == 0) {
+      // thread (h, v) holds dims 8 v .. 8 v + 7 and 32 + 8 v .. of head h's
+      // 64 rope dims as two 16-byte vectors: NeoX pairs (j, j + 32) are the
+      // same element of both, interleaved pairs (2 j, 2 j + 1) neighbours in one
+      for (int p = threadIdx.x; p < a.H * 4; p += 256) {
+        const int h = p >> 2, v = p & 3;
+        bf16x8* qh = reinterpret_cast<bf16x8*>(q + (int64_t)h * a.qk_head + a.n);
+        bf16x8 x0 = qh[v], x1 = qh[v + 4];
+        if (a.interleaved) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j0 = 4 * v + e, j1 = 16 + 4 * v + e;
+            const float a0 = (float)x0[2 * e], b0 = (float)x0[2 * e + 1];
+            const float a1 = (float)x1[2 * e], b1 = (float)x1[2 * e + 1];
+            x0[2 * e] = (bf16)(a0 * cs[j0] - b0 * sn[j0]);
+            x0[2 * e + 1] = (bf16)(a0 * sn[j0] + b0 * cs[j0]);
+            x1[2 * e] = (bf16)(a1 * cs[j1] - b1 * sn[j1]);
+            x1[2 * e + 1] = (bf16)(a1 * sn[j1] + b1 * cs[j1]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = 8 * v + e;
+            const float xa = (float)x0[e], xb = (float)x1[e];
+            x0[e] = (bf16)(xa * cs[j] - xb * sn[j]);
+            x1[e] = (bf16)(xa * sn[j] + xb * cs[j]);
+          }
+        }
+        qh[v] = x0;
+        qh[v + 4] = x1;
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    for (int p = threadIdx.x; p < a.H * half; p += 256) {
+      const int h = p / half, j = p % half;
+      int ia, ib;
+      pair(j, ia, ib);
+      T* qh = q + (int64_t)h * a.qk_head + a.n;
+      const float xa = to_f32(qh[ia]), xb = to_f32(qh[ib]);
+      qh[ia] = from_f32<T>(xa * cs[j] - xb * sn[j]);
+      qh[ib] = from_f32<T>(xa * sn[j] + xb * cs[j]);
+    }
   }
 
   // RMSNorm of the latent
