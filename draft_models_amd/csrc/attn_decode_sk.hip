@@ -56,12 +56,11 @@ constexpr int ROWB = ECH * 16;      // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane DMA instructions");
 
-// Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ (row & 7))
-// of the row (rows are 72 chunks = 1152 bytes). Measured on gfx950 with the
-// LDS bank-conflict counter, this XOR keeps both access patterns of the tile
-// conflict free: 16-byte score reads (16 rows, one chunk) and transposing
-// value reads (4 rows x 2 adjacent chunks per 16 lanes).
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ swz(row))
+// of the row (rows are 72 chunks = 1152 bytes, so rows r and r + 2 start on
+// the same banks). The low bit of the XOR also takes bit 3 of the row: the
+// 32-row score reads then put rows r and r + 8 on different banks.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));

@@ -247,7 +247,8 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g, float* 
   constexpr int DPW = SLOTS / 256;        // copy instructions per wavefront per stage
   constexpr int WSL = BN * SCH;           // weight slots
   static_assert(NST >= 2 && NST <= 4, "ring of 2-4 stages");
-  // stage s, row r (weight rows 0..BN-1, activation rows BN..): chunk c at slot r * 16 + (c ^ (r & 7))
+  // stage s, row r (weight rows 0..BN-1, activation rows BN..): chunk c at slot r * SCH + (c ^ (r % SCH)),
+  // so the 16 rows of one fragment read land on distinct chunks of the row
   __shared__ __attribute__((aligned(16))) bf16x8 lds[NST][SLOTS];
   __shared__ float rowscale[BM];
 
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g, float* 
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int sl = (4 * j + wave) * 64 + lane;
-    const int row = sl / SCH, c = (sl % SCH) ^ (row & 7);
+    const int row = sl / SCH, c = (sl % SCH) ^ (row & (SCH - 1));
     if (row < BN) off[j] = (uint32_t)((int64_t)min(n0 + row, g.N - 1) * g.ldw * 2) + (uint32_t)(c * 16);
     else off[j] = (uint32_t)((int64_t)min(m0 + row - BN, g.M - 1) * g.lda * 2) + (uint32_t)(c * 16);
   }
@@ -305,12 +306,12 @@ __global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g, float* 
 #pragma unroll
       for (int a = 0; a < NB; ++a) {
         const int row = wn * TN + a * 16 + lr;
-        wf[a].v = T[row * SCH + ((ks * 4 + g4) ^ (row & 7))];
+        wf[a].v = T[row * SCH + ((ks * 4 + g4) ^ (row & (SCH - 1)))];
       }
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
         const int row = BN + wm * TM + b * 16 + lr;
-        af[b].v = T[row * SCH + ((ks * 4 + g4) ^ (row & 7))];
+        af[b].v = T[row * SCH + ((ks * 4 + g4) ^ (row & (SCH - 1)))];
       }
       if (rowstat) {
 #pragma unroll
