@@ -264,13 +264,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel for the DeepSeek head shape (n = 128, r = 64, dv = 128). One
-// workgroup = 4 wavefronts x 32 queries (two 16-query MFMA blocks each, so
+// workgroup = 8 wavefronts x 32 queries (two 16-query MFMA blocks each, so
 // every LDS fragment feeds two MFMAs) of one head. 64-key tiles stream from
 // HBM straight into LDS (global_load_lds_dwordx4), double-buffered: k_nope
 // and v rows of the expanded buffer through the scalar-base form, the shared
 // rope key from the paged cache. Rows are unpadded with XOR-swizzled 16-byte
-// chunks: by (row & 7) for the key tiles (conflict-free 16-byte score operand
-// reads) and by 2 (row & 7) for the value tile (chunk pairs stay adjacent;
+// chunks: by the row's low bits for the key tiles (row & 15 for the 16-chunk
+// k_nope rows, row & 7 for the 8-chunk rope rows: the 16 rows of a 16-byte
+// score operand read hit distinct banks) and by 2 (row & 7) for the value tile (chunk pairs stay adjacent;
 // the 8 rows read together by 32 lanes of transposing reads hit distinct banks). Tiles inside every query's visible interval skip the masking.
 // ---------------------------------------------------------------------------
 
@@ -291,7 +292,7 @@ constexpr int NW = 8;                   // wavefronts per workgroup (two per SIM
 constexpr int BQ = NW * 16 * QB;        // queries per workgroup
 constexpr int NOPE_CH = 16, PE_CH = 8, V_CH = 16;   // 16-byte chunks per key row
 constexpr int NBUF = 3;                 // tile ring: t (values), t + 1 (scores), t + 2 (in flight)
-__device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch + (c ^ (row & 7)); }
+__device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch + (c ^ (row & (ch - 1))); }
 __device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 7) << 1)); }
 }  // namespace big
 
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   for (int j = 0; j < 2; ++j) {
     const int sl = (j * NW + wave) * 64 + lane;
     const int row = sl / NOPE_CH, cs = sl % NOPE_CH;
-    noff[j] = (uint32_t)(row * row_bytes) + (uint32_t)((cs ^ (row & 7)) * 16);
+    noff[j] = (uint32_t)(row * row_bytes) + (uint32_t)((cs ^ (row & (NOPE_CH - 1))) * 16);
     const int cv = cs ^ ((row & 7) << 1);
     voff[j] = (uint32_t)(row * row_bytes) + 256u + (uint32_t)(cv * 16);
   }
