@@ -273,6 +273,20 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
                     row_lo=row_lo, row_hi=row_hi)
 
 
+def draw_topk(w: Workload, topk: int, seed: int) -> np.ndarray:
+    """Top-k key lists [B, topk] int32 for a decode workload: for sequence b,
+    min(topk, L_b) distinct positions drawn uniformly from [0, L_b) (its
+    query's own position L_b - 1 included with the rest), sorted, padded with
+    -1. Drawn from a generator of its own, after the workload."""
+    rng = np.random.default_rng(seed)
+    L = w.kv_lens
+    out = np.full((w.batch, topk), -1, dtype=np.int32)
+    for b in range(w.batch):
+        k = min(topk, int(L[b]))
+        out[b, :k] = np.sort(rng.choice(int(L[b]), size=k, replace=False))
+    return out
+
+
 def paged_cache(w: Workload) -> np.ndarray:
     """The paged latent cache [num_blocks, page, entry_dim] holding the prefix
     rows at their logical positions (other slots zero). float32 values."""

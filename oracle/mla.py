@@ -208,10 +208,21 @@ def _absorbed_attention(dims, W, q, entries, lo, hi, scale):
     return np.einsum("shc,hvc->shv", o_lat, W_UV)
 
 
+def listed_keys(key_list, L: int) -> np.ndarray:
+    """The keys a query of a sparse (top-k) attention sees: its listed logical
+    positions, in list order, without the entries outside [0, L) (padding
+    -1 and positions past the sequence). Each list slot is one key: a
+    position listed twice is attended twice. The pages leave the indexer
+    that produces the lists unspecified (MLA blog, the indexer branch of
+    MultiHeadLatentAttentionWrapper.forward), so the lists are inputs."""
+    idx = np.asarray(key_list, dtype=np.int64).reshape(-1)
+    return idx[(idx >= 0) & (idx < L)]
+
+
 def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
                      rows: Optional[Sequence[int]] = None, row_lo=None, row_hi=None,
                      form: str = "expanded", softmax_scale: Optional[float] = None,
-                     first_position: int = 0):
+                     first_position: int = 0, key_lists=None):
     """One sequence: S new tokens at logical positions P..P+S-1 after P cached
     prefix entries. The new entries are appended to the cache before attention,
     so each query sees its own entry (MLAAttention.forward listing: cache update
@@ -223,6 +234,11 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     first_position: the given prefix rows are the cache entries at positions
     first_position .. first_position + P - 1 (a window of a longer cache); every
     selected query must then see no key before first_position.
+    key_lists: sparse (top-k) attention, one list of logical key positions
+    per selected query (listed_keys), replacing the mask: a sparse backend
+    runs every token in the MQA form over its selected entries (MLA blog,
+    MLAAttention.forward listing, the sparse branch); the result is the same
+    attention restricted to those keys, evaluated here in the given form.
     Returns (out [len(rows), hidden], new entries [S, E], attn [len(rows), H*dv])."""
     x = _f64(x)
     prefix_rows = _f64(prefix_rows).reshape(-1, dims.kv_lora_rank + dims.qk_rope_head_dim)
@@ -246,7 +262,21 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
         if np.any((lo < f0) & (hi > lo)):
             raise ValueError("a query sees keys before first_position")
         lo, hi = np.maximum(lo - f0, 0), np.maximum(hi - f0, 0)
-    if form == "expanded":
+    if key_lists is not None:
+        if f0 or len(key_lists) != len(sel):
+            raise ValueError("key_lists: one list per selected query, whole cache given")
+        o = np.zeros((len(sel), H, dv))
+        if form == "expanded":
+            k, v = expand_kv(dims, W, entries)
+        for r, i in enumerate(sel):
+            idx = listed_keys(key_lists[r], L)
+            if form == "expanded":
+                o[r] = attention_core(q[i:i + 1], k[idx], v[idx], [0], [len(idx)], scale)[0][0]
+            elif form == "absorbed":
+                o[r] = _absorbed_attention(dims, W, q[i:i + 1], entries[idx], [0], [len(idx)], scale)[0]
+            else:
+                raise ValueError(form)
+    elif form == "expanded":
         k, v = expand_kv(dims, W, entries)
         o, _ = attention_core(q[sel], k, v, lo, hi, scale)
     elif form == "absorbed":
@@ -263,12 +293,15 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
 def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: int,
                 window: int = 0, row_lo=None, row_hi=None, form: str = "expanded",
                 seqs: Optional[Sequence[int]] = None, rows_per_seq: Optional[dict] = None,
-                softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None):
+                softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None,
+                key_lists: Optional[dict] = None):
     """A batch of sequences packed along the token axis (x is [sum q_lens, hidden]).
 
     seqs: the sequences to evaluate (default all); rows_per_seq: optional
     {seq: [row indices]} subset of queries; first_positions: optional
-    {seq: position of its first given prefix row}. Returns dict seq -> (out, entries, attn)."""
+    {seq: position of its first given prefix row}; key_lists: optional
+    {seq: one key list per evaluated query} (sparse attention, see
+    forward_sequence). Returns dict seq -> (out, entries, attn)."""
     q_lens = np.asarray(q_lens, dtype=np.int64)
     cu = np.concatenate([[0], np.cumsum(q_lens)])
     res = {}
@@ -281,7 +314,8 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
         res[b] = forward_sequence(dims, W, np.asarray(x)[s0:s1], prefix_rows[b], mask_kind, window,
                                   rows=rows, row_lo=lo, row_hi=hi, form=form,
                                   softmax_scale=softmax_scale,
-                                  first_position=0 if first_positions is None else first_positions.get(b, 0))
+                                  first_position=0 if first_positions is None else first_positions.get(b, 0),
+                                  key_lists=None if key_lists is None else key_lists.get(b))
     return res
 
 

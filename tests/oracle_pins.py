@@ -246,3 +246,66 @@ def pin_window_trim(w, window: int):
     trim = om.forward_sequence(w.dims, w.weights, x, pre[f0:], om.MASK_SLIDING, window, first_position=f0)
     assert np.max(np.abs(full[0] - trim[0])) == 0.0
     assert np.max(np.abs(full[1] - trim[1])) == 0.0
+
+
+def pin_sparse(w):
+    """Sparse (top-k) attention over listed keys, on one sequence of w:
+    special cases that reduce to the masks, invariances of a softmax over a
+    list, and the log-sum-exp merge of two lists (which fixes how a position
+    listed twice counts)."""
+    x, pre = w.x, w.prefix_rows[0]
+    S, P = x.shape[0], pre.shape[0]
+    L = P + S
+    pos = P + np.arange(S)
+    dims, W = w.dims, w.weights
+    full = om.forward_sequence(dims, W, x, pre, om.MASK_FULL)
+    tol = 1e-12 * max(1.0, np.abs(full[0]).max())  # per-query vs batched products: rounding order only
+    # every position listed, in order: the full mask
+    lists = [np.arange(L) for _ in range(S)]
+    sp = om.forward_sequence(dims, W, x, pre, om.MASK_CAUSAL, key_lists=lists)
+    assert np.max(np.abs(sp[0] - full[0])) <= tol
+    assert np.max(np.abs(sp[1] - full[1])) == 0.0  # the cache entries do not depend on the lists
+    # the last 3 positions up to the query's own: the sliding window of 3
+    win = om.forward_sequence(dims, W, x, pre, om.MASK_SLIDING, window=3)
+    lists = [np.arange(max(0, p - 2), p + 1) for p in pos]
+    sp = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=lists)
+    assert np.max(np.abs(sp[0] - win[0])) <= tol
+    # order of a list is irrelevant; padding and positions outside [0, L) are ignored
+    rng = np.random.default_rng(11)
+    lists = [rng.choice(L, size=5, replace=False) for _ in range(S)]
+    base = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=lists)
+    perm = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=[rng.permutation(a) for a in lists])
+    assert np.max(np.abs(perm[0] - base[0])) <= 1e-12 * max(1.0, np.abs(base[0]).max())
+    padded = [np.concatenate([[-1], a, [L, L + 7, -5, -1]]) for a in lists]
+    pad = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=padded)
+    assert np.max(np.abs(pad[0] - base[0])) == 0.0
+    # one listed key: the attention output is that key's value (P = 1)
+    j = np.array([int(rng.integers(0, L)) for _ in range(S)])
+    _, ent, attn = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=[[t] for t in j])
+    _, v = om.expand_kv(dims, W, np.concatenate([pre, ent]))
+    gate = om.project_tokens(dims, W, x, pos)[2]
+    own = v[j].reshape(S, -1) * (gate if gate is not None else 1.0)
+    assert np.max(np.abs(attn - own)) < 1e-12
+    # nothing listed (or only padding): the output row is exactly 0
+    out0, _, _ = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=[[-1, L] for _ in range(S)])
+    assert np.all(out0 == 0.0)
+    # a list split in two: the attention over the whole list is the
+    # log-sum-exp-weighted merge of the two halves' attentions (the merge of
+    # the MLA blog's prefix/suffix outputs); B repeats a position of A
+    q = om.project_tokens(dims, W, x, pos)[0]
+    k, v = om.expand_kv(dims, W, np.concatenate([pre, ent]))
+    scale = 1.0 / np.sqrt(dims.qk_nope_head_dim + dims.qk_rope_head_dim)
+    i = S - 1
+    A = np.array([0, 2, L - 1])
+    B = np.array([2, 1])
+    oa, la = om.attention_core(q[i:i + 1], k[A], v[A], [0], [len(A)], scale)
+    ob, lb = om.attention_core(q[i:i + 1], k[B], v[B], [0], [len(B)], scale)
+    m = np.maximum(la, lb)
+    wa, wb = np.exp(la - m), np.exp(lb - m)
+    merged = (wa[..., None] * oa + wb[..., None] * ob) / (wa + wb)[..., None]
+    _, _, at = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, rows=[i], key_lists=[np.concatenate([A, B])])
+    g = gate[i] if gate is not None else 1.0
+    assert np.max(np.abs(at[0] - merged.reshape(-1) * g)) < 1e-12
+    # the absorbed form over the same lists
+    ab = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=lists, form="absorbed")
+    assert np.max(np.abs(ab[0] - base[0])) <= 1e-12 * max(1.0, np.abs(base[0]).max())

@@ -195,3 +195,23 @@ def test_mutation_gate_dropped(monkeypatch):
         return q, e, None
     monkeypatch.setattr(om, "project_tokens", bad)
     _expect_fail(P.pin_brute_force, _tiny(use_output_gate=True))
+
+
+@pytest.mark.parametrize("variant", [dict(), dict(q_lora_rank=12, use_output_gate=True,
+                                                  rope_style=om.ROPE_INTERLEAVED)])
+def test_sparse_lists(variant):
+    P.pin_sparse(_tiny(**variant))
+
+
+def test_mutation_sparse_duplicates_once(monkeypatch):
+    # set semantics (a position listed twice counted once) breaks the merge pin
+    orig = om.listed_keys
+    monkeypatch.setattr(om, "listed_keys", lambda key_list, L: np.unique(orig(key_list, L)))
+    _expect_fail(P.pin_sparse, _tiny())
+
+
+def test_mutation_sparse_range_filter(monkeypatch):
+    # keeping position L (one past the sequence) wraps to another key
+    monkeypatch.setattr(om, "listed_keys",
+                        lambda key_list, L: (lambda i: i[(i >= 0) & (i <= L)] % L)(np.asarray(key_list).reshape(-1)))
+    _expect_fail(P.pin_sparse, _tiny())
