@@ -22,7 +22,7 @@ ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 
 EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_decode_absorbed_block",
-           "mla_free", "mla_last_error",
+           "mla_decode_absorbed_sparse", "mla_free", "mla_last_error",
            "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
 NUM_STAGES = 10
 
@@ -40,7 +40,7 @@ class mla_config(C.Structure):
                 ("rope_theta", C.c_double), ("rms_norm_eps", C.c_double), ("softmax_scale", C.c_double),
                 ("use_output_gate", C.c_int32), ("dtype", C.c_int32), ("page_size", C.c_int32),
                 ("max_batch", C.c_int32), ("max_tokens", C.c_int32), ("max_seq_len", C.c_int32),
-                ("max_prefill_kv", C.c_int32), ("max_block_tokens", C.c_int32)]
+                ("max_prefill_kv", C.c_int32), ("max_block_tokens", C.c_int32), ("max_topk", C.c_int32)]
 
 
 WEIGHT_NAMES = ("q_a_proj", "q_a_layernorm", "q_b_proj", "q_proj", "kv_a_proj_with_mqa",
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.mla_decode_absorbed.restype = C.c_int
     lib.mla_decode_absorbed_block.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode_absorbed_block.restype = C.c_int
+    lib.mla_decode_absorbed_sparse.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp, vp]
+    lib.mla_decode_absorbed_sparse.restype = C.c_int
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_last_error.argtypes = []
@@ -107,7 +109,7 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_prefill_kv: int,
-                softmax_scale: float = 0.0, max_block_tokens: int = 0) -> mla_config:
+                softmax_scale: float = 0.0, max_block_tokens: int = 0, max_topk: int = 0) -> mla_config:
     """mla_config from an object with the model-dimension attributes."""
     return mla_config(
         hidden_size=dims.hidden_size, num_heads=dims.num_heads, q_lora_rank=dims.q_lora_rank,
@@ -117,7 +119,7 @@ def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_
         softmax_scale=softmax_scale, use_output_gate=int(dims.use_output_gate),
         dtype=DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, page_size=dims.page_size,
         max_batch=max_batch, max_tokens=max_tokens, max_seq_len=max_seq_len,
-        max_prefill_kv=max_prefill_kv, max_block_tokens=max_block_tokens)
+        max_prefill_kv=max_prefill_kv, max_block_tokens=max_block_tokens, max_topk=max_topk)
 
 
 class MLA:
@@ -148,6 +150,13 @@ class MLA:
         _check(self._lib.mla_decode_absorbed_block(
             self.ctx, _ptr(x), prefix_lens.numel(), q_len, _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(prefix_lens), max_kv_len, _ptr(out), _stream(stream)))
+
+    def decode_sparse(self, x, kv_cache, block_table, seq_lens, max_seq_len: int, topk_indices, out, stream=None):
+        """One token per sequence attending to its listed positions (topk_indices [batch, topk] int32)."""
+        _check(self._lib.mla_decode_absorbed_sparse(
+            self.ctx, _ptr(x), x.shape[0], _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), max_seq_len, _ptr(topk_indices), topk_indices.shape[1],
+            _ptr(out), _stream(stream)))
 
     def profile(self, enable: bool):
         _check(self._lib.mla_profile_enable(self.ctx, int(enable)))

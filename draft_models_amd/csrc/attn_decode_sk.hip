@@ -81,8 +81,15 @@ __device__ __forceinline__ void dma16_v(const void* gptr, uint32_t lds) {
 }
 
 // Visible keys [lo, hi) of the query of sequence b (its own position L - 1;
-// a query block sees every entry of its physical sequence)
+// a query block sees every entry of its physical sequence; a sparse list is
+// its gather_k listed keys)
+template <bool GATHER>
 __device__ __forceinline__ void visible(const DecodeAttnArgs& a, int b, int& lo, int& hi) {
+  if constexpr (GATHER) {
+    lo = 0;
+    hi = a.gather_k;
+    return;
+  }
   const int L = min(max(a.seq_lens[b / a.seq_div], 0), a.max_seq_len);
   lo = a.mask.kind == 2 ? max(0, L - a.mask.window) : 0;
   hi = L;
@@ -116,7 +123,9 @@ template <> struct Blocks<false> {
   static constexpr int reg(int j, int hb) { return j < 6 ? 8 * j + hb : (hb >= 4 ? 44 + hb : -1); }
 };
 
-template <int NBUF>
+// GATHER: sparse lists (a.gather_ent), compiled separately so that the
+// contiguous-range kernel carries none of its registers
+template <int NBUF, bool GATHER>
 __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 tile[NBUF][SLOTS];
   __shared__ int t_ent[kDecodeMaxTiles];  // first cache entry of the tile, -1: unmapped page
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       cnt[i] = 0;
       if (b < B) {
         int lo, hi;
-        visible(a, b, lo, hi);
+        visible<GATHER>(a, b, lo, hi);
         cnt[i] = tile_count(lo, hi);
       }
       loc += cnt[i];
@@ -192,11 +201,15 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       else ub = mid;
     }
     int lo, hi;
-    visible(a, lb, lo, hi);
+    visible<GATHER>(a, lb, lo, hi);
     const int k0 = (lo / KT + gi - tstart[lb]) * KT;
-    const int pg = k0 / a.page;
-    const int blk = pg < a.max_blocks ? a.block_table[(int64_t)(lb / a.seq_div) * a.max_blocks + pg] : -1;
-    t_ent[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.page + (k0 - pg * a.page) : -1;
+    if constexpr (GATHER) {
+      t_ent[i] = lb * a.gather_k + k0;  // the tile's row 0 in the sparse lists
+    } else {
+      const int pg = k0 / a.page;
+      const int blk = pg < a.max_blocks ? a.block_table[(int64_t)(lb / a.seq_div) * a.max_blocks + pg] : -1;
+      t_ent[i] = (blk >= 0 && blk < a.num_blocks) ? blk * a.page + (k0 - pg * a.page) : -1;
+    }
     t_k0[i] = k0;
     t_seq[i] = lb;
     t_lo[i] = lo;
@@ -221,7 +234,23 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     return row * ROWB + c * 16u;
   };
 
-  auto issue = [&](int i, int buf) {
+  // ---- sparse lists: lane l holds the cache entry of row l % 32 of a tile
+  // (-1: no key), loaded one step before the tile's copies are issued, so
+  // that the issue never waits for it; its ballot is the tile's row mask
+  constexpr bool gather = GATHER;
+  const int gather_rows = a.num_blocks * a.page;
+  auto gather_load = [&](int t) {
+    int e = -1;
+    if (gather && t < n) {
+      const int row = lane & 31;
+      if (t_k0[t] + row < t_hi[t]) e = a.gather_ent[t_ent[t] + row];
+      if (e >= gather_rows) e = -1;
+    }
+    return e;
+  };
+
+  // ev: the gathered entries of tile i (sparse lists only)
+  auto issue = [&](int i, int buf, int ev) {
     const int ent = __builtin_amdgcn_readfirstlane(t_ent[i]);
     const int k0 = __builtin_amdgcn_readfirstlane(t_k0[i]);
     const int lo = __builtin_amdgcn_readfirstlane(t_lo[i]);
@@ -229,7 +258,19 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     const uint32_t dst = tile_lds + (uint32_t)buf * (SLOTS * 16) + (uint32_t)wave * 1024u;
     uint32_t z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-    if (ent >= 0 && k0 >= lo && k0 + KT <= hi) {
+    if (gather) {
+      // every row its own entry; rows without a key read the zero page
+#pragma unroll
+      for (int j = 0; j < DMA_N; ++j) {
+        if (j == DMA_N - 1 && !last_dma) continue;
+        const uint32_t off = slot_offset(j, z);
+        const int row = (int)(off / ROWB);
+        const int e = __shfl(ev, row);
+        const void* src = e >= 0 ? (const void*)(cache + (int64_t)e * ROWB + (off - (uint32_t)row * ROWB))
+                                 : (const void*)a.zeros;
+        dma16_v(src, dst + (uint32_t)j * (NW * 1024u));
+      }
+    } else if (ent >= 0 && k0 >= lo && k0 + KT <= hi) {
       const char* base = cache + (int64_t)ent * ROWB;
 #pragma unroll
       for (int j = 0; j < DMA_N; ++j)
@@ -333,9 +374,11 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     else if (last_dma) MLA_WAIT_VMCNT(DMA_N);
     else MLA_WAIT_VMCNT(DMA_N - 1);
   };
-#pragma unroll
-  for (int i = 0; i < NBUF - 2; ++i)
-    if (i < n) issue(i, i);
+  static_assert(NBUF == 3, "the sparse-list entries run one tile ahead of the copies");
+  int ev = gather_load(0);                              // entries of the next tile to copy
+  uint32_t gm = gather ? (uint32_t)__ballot(ev >= 0) : 0u;  // row mask of the next tile to score
+  issue(0, 0, ev);
+  ev = gather_load(1);
 
   // the piece loop, compiled once per role: each copy has its own register
   // allocation, and both run the same sequence of barriers
@@ -390,9 +433,16 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     // probabilities (buffer it & 1); every wavefront multiplies tile it - 1 by
     // its probabilities (buffer (it - 1) & 1)
     for (int it = i; it <= iend; ++it) {
-      // the copies of tile it + NBUF - 2 go into the buffer of tile it - 2
-      // (read last in step it - 1)
-      if (it < iend && it + NBUF - 2 < n) issue(it + NBUF - 2, (it + NBUF - 2) % NBUF);
+      // the copies of tile it + 1 go into the buffer of tile it - 2 (read
+      // last in step it - 1)
+      const uint32_t gm_cur = gm;  // row mask of tile it (sparse lists)
+      if (it < iend && it + 1 < n) {
+        issue(it + 1, (it + 1) % NBUF, ev);
+        if (gather) {
+          gm = (uint32_t)__ballot(ev >= 0);
+          ev = gather_load(it + 2);
+        }
+      }
       if constexpr (sw) {
         const bool scoring = it < iend && sact;
         bf16x4 pq[4];
@@ -420,14 +470,15 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
           // ---- online softmax of head hs (log2 domain); element e of lane l
           // is key 8 (e / 4) + 4 (l / 32) + e % 4; lanes l and l ^ 32 hold the
           // same head
-          const bool edge = k0 < lo || k0 + KT > hi;
+          const bool edge = gather || k0 < lo || k0 + KT > hi;
           float mx = -INFINITY;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             float x = sc[e] * sl2;
             if (edge) {
-              const int key = k0 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-              if (key < lo || key >= hi) x = -INFINITY;
+              const int kk = 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+              const int key = k0 + kk;
+              if (key < lo || key >= hi || (gather && !((gm_cur >> kk) & 1u))) x = -INFINITY;
             }
             sc[e] = x;
             mx = fmaxf(mx, x);
@@ -438,10 +489,12 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
           // division by l)
           const float mnew = (mx > m + 8.f) ? mx : m;
           alpha = m == -INFINITY ? 1.f : fast_exp2(m - mnew);
+          // (a sparse list can leave a whole tile without keys: weights 0)
+          const float mref = mnew == -INFINITY ? 0.f : mnew;
           float sum = 0.f;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float pv = fast_exp2(sc[e] - mnew);
+            const float pv = fast_exp2(sc[e] - mref);
             sum += pv;
             pq[e >> 2][e & 3] = (bf16)pv;
           }
@@ -498,7 +551,8 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       for (int hb = 0; hb < HB; ++hb) {
         const int hh = 16 * hb + lr;
         if (hh >= a.H) continue;
-        const float inv = 1.f / lbuf[hh];
+        const float lv = lbuf[hh];
+        const float inv = lv > 0.f ? 1.f / lv : 0.f;  // no key at all: a zero row
         bf16* dst = whole ? reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + hh) * a.c
                           : reinterpret_cast<bf16*>(a.part_o) + (slot * a.H + hh) * a.c;
         dst += 4 * g;
@@ -571,7 +625,7 @@ __global__ __launch_bounds__(256) void decode_sk_merge_kernel(DecodeAttnArgs a) 
     }
     mx = cm;
   }
-  const float inv = 1.f / den;
+  const float inv = den > 0.f ? 1.f / den : 0.f;  // no key in any piece: a zero row
   bf16x8 v;
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = (bf16)(acc[e] * inv);
@@ -588,6 +642,8 @@ const char* decode_sk_check(const DecodeAttnArgs& a) {
   if ((int64_t)a.num_blocks * a.page >= ((int64_t)1 << 31)) return "stream-K decode: cache above 2^31 entries";
   if (a.ldql % 8 || a.ldq % 8 || a.qk_head % 8 || a.n % 8) return "stream-K decode: query strides must be 16-byte multiples";
   if (a.seq_div < 1 || a.Hr < 0) return "stream-K decode: bad query-block mapping";
+  if (a.gather_ent && (a.gather_k <= 0 || (int64_t)a.batch * a.gather_k >= ((int64_t)1 << 31)))
+    return "stream-K decode: sparse lists need 0 < batch * gather_k < 2^31";
   if (a.ranges <= 0 || a.ranges % 8 || !a.tstart || !a.part_o || !a.part_lse || !a.zeros)
     return "stream-K decode: ranges (a multiple of 8) and workspaces are required";
   return nullptr;
@@ -603,7 +659,8 @@ int decode_sk_ranges(int batch, int max_visible, int cus) {
 
 hipError_t decode_sk_launch(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_sk_kernel<3>, dim3(a.ranges), dim3(NT), 0, s, a);
+  if (a.gather_ent) hipLaunchKernelGGL((decode_sk_kernel<3, true>), dim3(a.ranges), dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((decode_sk_kernel<3, false>), dim3(a.ranges), dim3(NT), 0, s, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   return hipSuccess;
 }

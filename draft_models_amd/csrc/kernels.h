@@ -78,6 +78,11 @@ struct DecodeAttnArgs {
   // latent queries and outputs are then [tokens, Hr, c] in the same order).
   int seq_div = 1;
   int Hr = 0;
+  // sparse lists (stream-K only): sequence b sees the gather_k keys
+  // gather_ent[b * gather_k + j], cache entry indices (-1 = no key), instead
+  // of the visible range of its block table
+  const int32_t* gather_ent = nullptr;
+  int gather_k = 0;
 };
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);

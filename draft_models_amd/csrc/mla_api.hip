@@ -39,6 +39,7 @@ struct mla_ctx {
   void* attn = nullptr;    // [max_tokens, H dv]
   void* qlat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
   void* olat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
+  int32_t* sp_ent = nullptr;  // [max_batch, max_topk] cache entries of the sparse lists
   int32_t* blk_cu = nullptr;    // query blocks: [max_batch + 1] token offsets b q_len
   int32_t* blk_lens = nullptr;  // query blocks: [max_batch] cache lengths prefix + q_len
   float* part_o = nullptr;
@@ -98,6 +99,24 @@ __global__ void block_meta_kernel(const int32_t* prefix_lens, int batch, int q_l
   if (b < batch) lens[b] = prefix_lens[b] + q_len;
 }
 
+// sparse lists: ent[b][j] = the cache entry of listed position idx[b][j] of
+// sequence b, -1 when the position is outside [0, L_b) or its page unmapped
+__global__ void sparse_entries_kernel(const int32_t* idx, int topk, const int32_t* seq_lens, int max_seq_len,
+                                      const int32_t* block_table, int max_blocks, int num_blocks, int page,
+                                      int32_t* ent) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x, b = blockIdx.y;
+  if (j >= topk) return;
+  const int64_t o = (int64_t)b * topk + j;
+  const int p = idx[o];
+  const int L = min(max(seq_lens[b], 0), max_seq_len);
+  int e = -1;
+  if (p >= 0 && p < L && p / page < max_blocks) {
+    const int blk = block_table[(int64_t)b * max_blocks + p / page];
+    if (blk >= 0 && blk < num_blocks) e = blk * page + p % page;
+  }
+  ent[o] = e;
+}
+
 __global__ void wuk_transpose_kernel(const void* wkvb, void* out, int H, int n, int dv, int c, int bf) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)H * c * n;
@@ -141,9 +160,9 @@ int validate_config(const mla_config* c, const mla_weights* w) {
   if (!std::isfinite(c->softmax_scale)) return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite");
   if (c->use_output_gate != 0 && c->use_output_gate != 1) return fail(MLA_ERR_INVALID_ARG, "use_output_gate must be 0 or 1");
   if (c->page_size <= 0 || c->max_batch <= 0 || c->max_tokens <= 0 || c->max_seq_len <= 0 || c->max_prefill_kv < 0 ||
-      c->max_block_tokens < 0)
-    return fail(MLA_ERR_INVALID_ARG,
-                "page_size, max_batch, max_tokens, max_seq_len must be positive, max_prefill_kv and max_block_tokens >= 0");
+      c->max_block_tokens < 0 || c->max_topk < 0)
+    return fail(MLA_ERR_INVALID_ARG, "page_size, max_batch, max_tokens, max_seq_len must be positive, "
+                                     "max_prefill_kv, max_block_tokens and max_topk >= 0");
   const int vec = c->dtype == MLA_DTYPE_BF16 ? 8 : 4;
   const int n = c->qk_nope_head_dim, r = c->qk_rope_head_dim, kc = c->kv_lora_rank, dv = c->v_head_dim;
   if (n % vec || r % vec || kc % vec || dv % vec || c->hidden_size % vec || (c->q_lora_rank % vec))
@@ -353,6 +372,10 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   ctx->blk_cu = static_cast<int32_t*>(p);
   if ((e = dev_alloc(ctx, &p, (size_t)B * sizeof(int32_t)))) return bail(e);
   ctx->blk_lens = static_cast<int32_t*>(p);
+  if (cfg->max_topk > 0) {
+    if ((e = dev_alloc(ctx, &p, (size_t)B * cfg->max_topk * sizeof(int32_t)))) return bail(e);
+    ctx->sp_ent = static_cast<int32_t*>(p);
+  }
   if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess ||
       ctx->cus <= 0)
     return bail(fail(MLA_ERR_HIP, "querying the compute-unit count failed"));
@@ -365,7 +388,7 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     // (query, head) pairs each)
     const int64_t vb = (int64_t)cfg->max_block_tokens * H / 128;
     const int skb = (int)std::min<int64_t>(std::max<int64_t>(B, vb), kDecodeMaxBatch);
-    ctx->sk_max_ranges = decode_sk_ranges(skb, cfg->max_seq_len, ctx->cus);
+    ctx->sk_max_ranges = decode_sk_ranges(skb, std::max(cfg->max_seq_len, cfg->max_topk), ctx->cus);
     part_rows = 2 * (int64_t)ctx->sk_max_ranges;
     if ((e = dev_alloc(ctx, &p, (size_t)(skb + 1) * sizeof(int32_t)))) return bail(e);
     ctx->sk_tstart = static_cast<int32_t*>(p);
@@ -480,9 +503,16 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   return run_gemm(ctx, go, s);
 }
 
-int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
-                        const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
-                        int32_t max_seq_len, int32_t mask_kind, int32_t window, void* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// one new token per sequence in absorbed form; with topk_idx, each query sees
+// only its listed positions (sparse lists, stream-K only)
+int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                int32_t mask_kind, int32_t window, const int32_t* topk_idx, int32_t topk, void* out,
+                void* stream) {
   if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
   if (!kv_cache) return fail(MLA_ERR_INVALID_ARG, "kv_cache must not be NULL (decode reads the latent cache)");
   if (!x || !block_table || !seq_lens || !out)
@@ -541,7 +571,12 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
   da.o_lat = ctx->olat;
   da.zeros = static_cast<const bf16_t*>(ctx->zeros);
-  const int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+  int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+  if (topk_idx) {
+    da.gather_ent = ctx->sp_ent;
+    da.gather_k = topk;
+    max_vis = topk;
+  }
   if (ctx->sk_shape && batch <= kDecodeMaxBatch) {
     // stream-K: equal tile ranges over all sequences, pieces merged afterwards
     da.ranges = decode_sk_ranges(batch, max_vis, ctx->cus);
@@ -550,12 +585,19 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
     if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
     {
       StageTimer st(ctx, s, ST_DECODE_ATTN);
+      if (topk_idx) {
+        hipLaunchKernelGGL(sparse_entries_kernel, dim3((topk + 255) / 256, batch), dim3(256), 0, s, topk_idx, topk,
+                           seq_lens, max_seq_len, block_table, max_blocks, num_blocks, c.page_size, ctx->sp_ent);
+        HIP_TRY(hipGetLastError());
+      }
       HIP_TRY(decode_sk_launch(da, s));
     }
     {
       StageTimer st(ctx, s, ST_DECODE_MERGE);
       HIP_TRY(decode_sk_merge_launch(da, s));
     }
+  } else if (topk_idx) {
+    return fail(MLA_ERR_UNSUPPORTED, "sparse lists need the bf16 512 + 64 latent with at most 128 heads");
   } else {
     // split-KV sizing from the longest visible range (keys per split a multiple of 32)
     const int groups = (H + 63) / 64;
@@ -601,6 +643,29 @@ int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cac
   go.M = batch; go.N = ctx->hid; go.K = H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
   return run_gemm(ctx, go, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+                        const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t mask_kind, int32_t window, void* out, void* stream) {
+  return decode_impl(ctx, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len, mask_kind,
+                     window, nullptr, 0, out, stream);
+}
+
+int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                               int32_t max_seq_len, const int32_t* topk_indices, int32_t topk, void* out,
+                               void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (!topk_indices) return fail(MLA_ERR_INVALID_ARG, "topk_indices must not be NULL");
+  if (topk <= 0) return fail(MLA_ERR_INVALID_ARG, "topk must be positive");
+  if (topk > ctx->cfg.max_topk) return fail(MLA_ERR_CAPACITY, "topk above the init max_topk");
+  return decode_impl(ctx, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
+                     MLA_MASK_FULL, 0, topk_indices, topk, out, stream);
 }
 
 int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_t q_len, void* kv_cache,

@@ -95,6 +95,7 @@ typedef struct mla_config {
   int32_t max_seq_len;      /* cache entries per sequence (positions < max_seq_len) */
   int32_t max_prefill_kv;   /* prefill: batch * max_kv_len rows of expanded K/V; 0 = no prefill */
   int32_t max_block_tokens; /* mla_decode_absorbed_block: batch * q_len new tokens per call; 0 = not used */
+  int32_t max_topk;         /* mla_decode_absorbed_sparse: listed keys per query; 0 = not used */
 } mla_config;
 
 /* Layer weights, device pointers in nn.Linear [out, in] row-major layout with
@@ -200,6 +201,31 @@ MLA_API int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch
                         void* kv_cache, int32_t num_blocks, const int32_t* block_table,
                         int32_t max_blocks, const int32_t* prefix_lens, int32_t max_kv_len,
                         void* out, void* stream);
+
+/*
+ * mla_decode_absorbed_sparse — mla_decode_absorbed where each sequence's query
+ * sees only the cache positions listed for it (sparse, top-k MLA). The MLA
+ * blog's wrapper forward computes top-k indices with an indexer when the layer
+ * is sparse, and its MLAAttention.forward sends every token of a sparse
+ * backend through the MQA (absorbed) branch; the indexer is not specified on
+ * the pages, so the lists are an input here.
+ *   topk_indices device int32 [batch, topk]: logical positions of sequence b's
+ *                keys, in any order; entries < 0 or >= seq_lens[b] (and
+ *                positions on unmapped pages) are ignored; a position listed
+ *                twice is attended twice. A query with no listed key gets an
+ *                attention output of exactly zero. The new token is written
+ *                to the cache (position seq_len - 1) before attention and is
+ *                attended only if listed.
+ *   topk         host: list length, 0 < topk <= max_topk
+ * Other arguments as mla_decode_absorbed (no mask: the lists replace it).
+ * Requires the bf16 512 + 64 latent with at most 128 heads (MLA_ERR_UNSUPPORTED
+ * otherwise). Profiled under the decode stage names; the entry lookup of the
+ * lists runs inside decode_attn.
+ */
+MLA_API int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batch,
+                        void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                        const int32_t* topk_indices, int32_t topk, void* out, void* stream);
 
 /*
  * Stage timing, for measurement. When enabled, every launch sequence of the

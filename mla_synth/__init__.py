@@ -273,6 +273,10 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
                     row_lo=row_lo, row_hi=row_hi)
 
 
+# seed of the sparse decode workload's lists (decode_bf16 shapes, 2048 per sequence)
+SPARSE_TOPK_SEED = 7
+
+
 def draw_topk(w: Workload, topk: int, seed: int) -> np.ndarray:
     """Top-k key lists [B, topk] int32 for a decode workload: for sequence b,
     min(topk, L_b) distinct positions drawn uniformly from [0, L_b) (its

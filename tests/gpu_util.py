@@ -21,10 +21,13 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool = False, block: bool = False):
+def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool = False, block: bool = False,
+            topk=None):
     """One call of the workload's entry point (block: a prefill workload of
-    equal block lengths under the FULL mask through mla_decode_absorbed_block).
-    Returns (out [T, hidden], cache [num_blocks, page, E]) as float32 numpy."""
+    equal block lengths under the FULL mask through mla_decode_absorbed_block;
+    topk: [batch, k] int32 key lists of a decode workload through
+    mla_decode_absorbed_sparse). Returns (out [T, hidden], cache
+    [num_blocks, page, E]) as float32 numpy."""
     say(f"[gpu] {w.name} mode={w.mode} B={w.batch} T={w.total_tokens} "
         f"max_kv={int(w.kv_lens.max())} mask={w.mask_kind} window={w.window} seed={w.seed}")
     t = upload(w)
@@ -37,11 +40,17 @@ def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool 
                         max_tokens=w.total_tokens + (5 if extra_capacity else 0),
                         max_seq_len=max_kv + (7 if extra_capacity else 0),
                         max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
-                        softmax_scale=softmax_scale, max_block_tokens=w.total_tokens if block else 0)
+                        softmax_scale=softmax_scale, max_block_tokens=w.total_tokens if block else 0,
+                        max_topk=0 if topk is None else topk.shape[1] + (9 if extra_capacity else 0))
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.full((w.total_tokens, d.hidden_size), float("nan"), dtype=dt, device="cuda")
-    if block:
+    if topk is not None:
+        assert not prefill
+        say(f"  sparse lists: {topk.shape[1]} per sequence")
+        lists = torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
+        m.decode_sparse(t["x"], t["cache"], t["block_table"], t["seq_lens"], max_kv, lists, out)
+    elif block:
         m.decode_block(t["x"], int(w.q_lens[0]), t["cache"], t["block_table"], t["prefix_lens"], max_kv, out)
     elif prefill:
         m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], int(w.q_lens.max()), max_kv, t["cache"],
@@ -54,10 +63,14 @@ def run_gpu(w: ms.Workload, *, softmax_scale: float = 0.0, extra_capacity: bool 
 
 
 def oracle(w: ms.Workload, seqs=None, rows_per_seq=None, form="expanded", first_positions=None,
-           softmax_scale=None):
+           softmax_scale=None, topk=None):
+    """topk: [batch, k] key lists of a decode workload (one query per sequence)."""
+    key_lists = None
+    if topk is not None:
+        key_lists = {b: [topk[b]] for b in (range(w.batch) if seqs is None else seqs)}
     return om.mla_forward(w.dims, w.weights, w.x, w.q_lens, w.prefix_rows, w.mask_kind, w.window,
                           w.row_lo, w.row_hi, form=form, seqs=seqs, rows_per_seq=rows_per_seq,
-                          softmax_scale=softmax_scale, first_positions=first_positions)
+                          softmax_scale=softmax_scale, first_positions=first_positions, key_lists=key_lists)
 
 
 def errors(got, ref):

@@ -116,6 +116,42 @@ def test_decode_projection_k_tails():
     _run_and_check(w)
 
 
+def test_sparse_decode_small():
+    """Sparse (top-k) lists through mla_decode_absorbed_sparse: 96 entries =
+    three 32-key tiles, lists longer than some sequences (padded with -1),
+    and on one sequence an unsorted list with a negative entry, entries at
+    and past its length (ignored) and a repeated position (attended twice)."""
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 40, 300, 64, 129, 700], seed=31)
+    topk = ms.draw_topk(w, 96, seed=32)
+    L2 = int(w.kv_lens[2])
+    row = topk[2].copy()
+    row[5], row[6], row[7], row[8] = -7, L2, L2 + 100, row[9]
+    topk[2] = np.random.default_rng(33).permutation(row)
+    out, cache = U.run_gpu(w, topk=topk)
+    U.check(w, out, cache, U.oracle(w, topk=topk))
+
+
+def test_sparse_decode_empty_and_tails():
+    """A list with no usable entry gives exactly zero; 33-entry lists (one
+    key in the second tile); a query whose own position is not listed."""
+    w = ms.make_workload("decode_bf16", seq_lens=[5, 64, 300, 33], seed=34)
+    topk = ms.draw_topk(w, 33, seed=35)
+    topk[0] = -1
+    topk[1][topk[1] == 63] = -1
+    out, cache = U.run_gpu(w, topk=topk, extra_capacity=True)
+    assert np.all(out[0] == 0)
+    U.check(w, out, cache, U.oracle(w, topk=topk))
+
+
+def test_sparse_decode_gate_heads16():
+    """Sparse lists with 16 heads (one score wavefront), an output gate and NeoX RoPE."""
+    w = ms.make_workload("decode_bf16", seq_lens=[70, 1000, 3, 257], seed=36,
+                         dims_override={"num_heads": 16, "use_output_gate": True, "rope_style": ms.ROPE_NEOX})
+    topk = ms.draw_topk(w, 200, seed=37)
+    out, cache = U.run_gpu(w, topk=topk)
+    U.check(w, out, cache, U.oracle(w, topk=topk))
+
+
 def test_prefill_small():
     w = ms.make_workload("prefill_bf16", q_lens=[300, 129], prefix_lens=[0, 0])
     _run_and_check(w)
@@ -185,6 +221,18 @@ def test_full_decode():
     L = w.kv_lens
     seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 17, 40})
     U.check(w, out, cache, U.oracle(w, seqs=seqs, form="absorbed"))
+
+
+def test_full_sparse_decode():
+    """The sparse decode workload: 64 sequences of 1024-8192 entries, 2048
+    listed positions each (shorter sequences padded); sampled sequences
+    against the oracle's absorbed form."""
+    w = ms.make_workload("decode_bf16")
+    topk = ms.draw_topk(w, 2048, seed=ms.SPARSE_TOPK_SEED)
+    out, cache = U.run_gpu(w, topk=topk)
+    L = w.kv_lens
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 17, 40})
+    U.check(w, out, cache, U.oracle(w, seqs=seqs, form="absorbed", topk=topk))
 
 
 def test_full_prefill():
