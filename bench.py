@@ -52,8 +52,20 @@ DESCR = {
                                  "latent prefix, hidden 4096, 32 heads, q_lora 1536) through the absorbed "
                                  "query-block entry point (no latent expansion)",
 }
+DESCR["sparse_decode_bf16"] = ("the decode workload (64 sequences, cache length uniform in [1024, 8192], 128 heads, "
+                               "q_lora 1536) through mla_decode_absorbed_sparse: each query attends 2048 listed "
+                               "positions (distinct, uniform over its sequence; all of a shorter sequence)")
 # workloads that run another workload's data through mla_decode_absorbed_block
 BLOCK_OF = {"draft_block_absorbed_bf16": "draft_block_bf16"}
+# workloads that run a decode workload through mla_decode_absorbed_sparse: (base, list length)
+SPARSE_OF = {"sparse_decode_bf16": ("decode_bf16", 2048)}
+
+
+def listed_keys(w, topk):
+    """Keys each sequence's query attends under its list (entries in [0, L))."""
+    L = np.asarray(w.kv_lens, dtype=np.int64)[:, None]
+    t = np.asarray(topk, dtype=np.int64)
+    return ((t >= 0) & (t < L)).sum(axis=1)
 
 
 # ----------------------------------------------------------------------------
@@ -81,10 +93,11 @@ def visible_counts(w):
     return np.asarray(counts, dtype=np.int64)
 
 
-def stage_work(w, seqs=None, absorbed=False):
+def stage_work(w, seqs=None, absorbed=False, topk=None):
     """Algorithmic flops and bytes of each stage of one step (optionally for a
     subset of the sequences); absorbed: a prefill workload run through the
-    absorbed query-block path (no expansion; latent attention)."""
+    absorbed query-block path (no expansion; latent attention); topk: the
+    key lists of a sparse decode (the attention reads the listed entries)."""
     d = w.dims
     esz = 2 if d.dtype == "bf16" else 4
     H, n, r, c, dv, hid, ql = (d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank,
@@ -96,6 +109,8 @@ def stage_work(w, seqs=None, absorbed=False):
     vis_all = visible_counts(w)
     cu = w.cu_seqlens
     pairs = int(sum(vis_all[cu[b]:cu[b + 1]].sum() for b in sel))
+    if topk is not None:
+        pairs = int(listed_keys(w, topk)[sel].sum())
     n1 = (ql if ql else H * (n + r)) + E + (H * dv if d.use_output_gate else 0)
     work = {}
     work["qkv_a_gemm"] = dict(flops=2 * T * hid * n1, bytes=(n1 * hid + T * (hid + n1)) * esz)
@@ -292,7 +307,7 @@ def measured_traffic(stage, workload):
 # CPU baseline: the fp64 oracle on a bounded sample
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w, budget_s: float, absorbed: bool = False):
+def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
     from threadpoolctl import threadpool_info
     from oracle import mla as om
     order = list(np.argsort(w.kv_lens))  # shortest first keeps the sample bounded
@@ -305,17 +320,24 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False):
             first[b] = max(0, int(w.kv_lens[b]) - w.window)
         pre = w.prefix_rows[b][first.get(b, 0):]
         cu = w.cu_seqlens
-        om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
-                            first_position=first.get(b, 0))
+        if topk is not None:
+            # the oracle's absorbed form over the listed entries (pinned equal
+            # to its expanded form, which expands every entry of the sequence)
+            om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
+                                form="absorbed", key_lists=[topk[b]])
+        else:
+            om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
+                                first_position=first.get(b, 0))
         done.append(b)
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    work = stage_work(w, seqs=done, absorbed=absorbed)  # counted like the GPU line
+    work = stage_work(w, seqs=done, absorbed=absorbed, topk=topk)  # counted like the GPU line
     per, unit = step_value(w, work)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": per / el, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} sequences (ids {sorted(done)}), expanded fp64 oracle, "
+            "sample": f"{len(done)} of {w.batch} sequences (ids {sorted(done)}), "
+                      f"{'absorbed' if topk is not None else 'expanded'} fp64 oracle, "
                       f"{el:.1f} s wall", "wall_s": round(el, 3)}
 
 
@@ -373,14 +395,20 @@ def main():
         del src, dst
 
     block = args.workload in BLOCK_OF
-    w = ms.make_workload(BLOCK_OF.get(args.workload, args.workload))
+    sparse = args.workload in SPARSE_OF
+    w = ms.make_workload(BLOCK_OF.get(args.workload, SPARSE_OF.get(args.workload, (args.workload,))[0]))
     t = upload(w)
+    topk = lists = None
+    if sparse:
+        topk = ms.draw_topk(w, SPARSE_OF[args.workload][1], ms.SPARSE_TOPK_SEED)
+        lists = torch.from_numpy(topk).cuda()
     d = w.dims
     max_kv = int(w.kv_lens.max())
     prefill = w.mode == "prefill"
     cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_kv,
                         max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
-                        max_block_tokens=w.total_tokens if block else 0)
+                        max_block_tokens=w.total_tokens if block else 0,
+                        max_topk=0 if topk is None else topk.shape[1])
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.empty((w.total_tokens, d.hidden_size), dtype=dt, device="cuda")
@@ -392,6 +420,8 @@ def main():
         elif prefill:
             m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], max_q, max_kv, t["cache"], t["block_table"],
                       w.mask_kind, w.window, out)
+        elif sparse:
+            m.decode_sparse(t["x"], t["cache"], t["block_table"], t["seq_lens"], max_kv, lists, out)
         else:
             m.decode(t["x"], t["cache"], t["block_table"], t["seq_lens"], max_kv, w.mask_kind, w.window, out)
 
@@ -420,7 +450,7 @@ def main():
         stages = m.profile_read()
         m.profile(False)
 
-    work = stage_work(w, absorbed=block)
+    work = stage_work(w, absorbed=block, topk=topk)
     per_step, unit = step_value(w, work)
     value = per_step / (ms_step / 1e3)
 
@@ -451,8 +481,8 @@ def main():
         "vs_baseline": None, "dtype": d.dtype, "data": "synthetic (seeded, random-init weights)",
         "config": {"workload": args.workload, "description": DESCR[args.workload], "batch": w.batch,
                    "new_tokens": w.total_tokens, "max_kv_len": max_kv, "entry_point":
-                       "mla_decode_absorbed_block" if block else
-                       ("mla_prefill_expanded" if prefill else "mla_decode_absorbed"),
+                       "mla_decode_absorbed_block" if block else ("mla_decode_absorbed_sparse" if sparse else
+                       ("mla_prefill_expanded" if prefill else "mla_decode_absorbed")),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "stages_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in timed.items()},
@@ -463,7 +493,7 @@ def main():
         res["whole_call_gbps"] = round(work["_step"]["bytes"] / (ms_step / 1e3) / 1e9, 2)
     m.close()
     if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block, topk=topk)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

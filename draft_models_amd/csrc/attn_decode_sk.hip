@@ -453,7 +453,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
           const char* Tb = reinterpret_cast<const char*>(&tile[it % NBUF][0]);
           // key fragments are read KLA steps ahead of their MFMA (one wavefront
           // per SIMD scores, so its own reads must cover the LDS latency)
-          constexpr int KLA = 4;
+          constexpr int KLA = GATHER ? 3 : 4;  // (the sparse lists hold more registers)
           floatx16 sc = {};
           bf16x8 kf[KLA];
 #pragma unroll

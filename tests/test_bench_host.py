@@ -109,3 +109,17 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_sparse_decode_counts_listed_entries():
+    # a list counts its entries inside [0, L): padding and positions past L read nothing
+    w = _shape_only("decode_bf16", [1, 1], [9, 4999], ms.MASK_CAUSAL, mode="decode")
+    topk = np.full((2, 16), -1, dtype=np.int32)
+    topk[0, :10] = np.arange(10)
+    topk[0, 10] = 10  # = L, ignored
+    topk[1, :16] = np.arange(0, 4800, 300)
+    work = bench.stage_work(w, topk=topk)
+    keys = 10 + 16
+    assert work["decode_attn"]["bytes"] == keys * 576 * 2
+    assert work["_step"]["cache_bytes"] == keys * 576 * 2
+    assert work["decode_attn"]["flops"] == 2 * keys * 128 * (576 + 512)
