@@ -121,6 +121,10 @@ def stage_work(w, seqs=None, absorbed=False, topk=None):
         work["kv_b_expand"] = dict(flops=2 * kv * c * H * (n + dv),
                                    bytes=(H * (n + dv) * c + kv * (c + H * (n + dv))) * esz)
         work["prefill_attn"] = dict(flops=2 * pairs * H * (n + r + dv), bytes=None)
+        # few new tokens per sequence: the library runs both in one kernel
+        # (expand_attn, the same algorithmic work) and merges its chunks
+        work["expand_attn"] = dict(flops=work["kv_b_expand"]["flops"] + work["prefill_attn"]["flops"],
+                                   bytes=None, fused_of=("kv_b_expand", "prefill_attn"))
     else:
         work["wuk_absorb"] = dict(flops=2 * T * H * n * c, bytes=(H * n * c + T * H * (n + c)) * esz)
         # bytes: the cache entries each sequence's queries read (once per
@@ -128,9 +132,10 @@ def stage_work(w, seqs=None, absorbed=False, topk=None):
         attn_bytes = pairs * E * esz if not absorbed else int(w.kv_lens[sel].sum()) * E * esz
         work["decode_attn"] = dict(flops=2 * pairs * H * (E + c), bytes=attn_bytes)
         work["wuv_gemm"] = dict(flops=2 * T * H * c * dv, bytes=(H * dv * c + T * H * (c + dv)) * esz)
-    work["_step"] = dict(flops=sum(v["flops"] for v in work.values()),
+    parts = [v for k, v in work.items() if k != "expand_attn"]
+    work["_step"] = dict(flops=sum(v["flops"] for v in parts),
                          cache_bytes=pairs * E * esz,
-                         bytes=sum((v["bytes"] or 0) for v in work.values()))
+                         bytes=sum((v["bytes"] or 0) for v in parts))
     return work
 
 
@@ -161,6 +166,8 @@ STAGE_SOURCES = {
     "decode_attn": ["attn_decode_sk.hip", "attn_decode.hip", "kernels.h", "common.h"],
     "decode_merge": ["attn_decode_sk.hip", "attn_decode.hip", "kernels.h", "common.h"],
     "rope_cache": ["rope_cache.hip", "kernels.h", "common.h"],
+    "expand_attn": ["attn_mha_fused.hip", "kernels.h", "common.h"],
+    "expand_merge": ["attn_mha_fused.hip", "kernels.h", "common.h"],
 }
 # kernel that carries a stage (the one whose counters are summarised); a
 # stage whose kernel name also runs other stages of the workload (a GEMM
@@ -169,7 +176,7 @@ STAGE_SOURCES = {
 STAGE_KERNEL = {
     "decode_attn": "decode_sk_kernel", "decode_merge": "decode_sk_merge_kernel",
     "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
-    "rope_cache": "rope_cache_kernel",
+    "rope_cache": "rope_cache_kernel", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
 }
 COPY_KERNEL = "elementwise"  # torch's elementwise kernel of the copy calibration
 

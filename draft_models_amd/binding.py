@@ -24,7 +24,7 @@ MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_decode_absorbed_block",
            "mla_decode_absorbed_sparse", "mla_free", "mla_last_error",
            "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
-NUM_STAGES = 10
+NUM_STAGES = 12
 
 
 class MLAError(RuntimeError):

@@ -51,6 +51,33 @@ struct PrefillAttnArgs {
 hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s);
 const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16);
 
+// Expanded-form attention with the kv_b expansion fused in, for few new
+// tokens per sequence (attn_mha_fused.hip): bf16, c 512, n 128, r 64, dv 128.
+constexpr int kMhaFusedMaxQ = 64;  // new tokens per sequence
+struct MhaFusedArgs {
+  const void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // roped q [T, H, n + r]
+  const void* cache = nullptr;                                  // latent cache [blocks, page, 576]
+  const int32_t* block_table = nullptr;
+  int num_blocks = 0, max_blocks = 0, page = 0;
+  const void* wkvb = nullptr;                                   // kv_b_proj [H (n + dv), c]
+  const int32_t* cu_seqlens = nullptr; const int32_t* prefix_lens = nullptr;
+  int batch = 0, max_q_len = 0, max_kv_len = 0, total_tokens = 0;
+  int H = 0;
+  float scale = 0.f;
+  MaskArgs mask;
+  int nchunks = 0;                                  // ceil(max_kv_len / 256)
+  int qblocks = 0;                                  // ceil(max_q_len / 16)
+  bf16_t* part_o = nullptr;                         // [batch, nchunks, qblocks, H, 16, dv]
+  float* part_lse = nullptr;                        // [batch, nchunks, qblocks, H, 16]
+  void* out = nullptr; int64_t ldo = 0;             // [T, H * dv]
+  const void* gate = nullptr; int64_t ldg = 0;      // raw gate pre-activation [T, H * dv] or null
+};
+const char* mha_fused_check(const MhaFusedArgs& a);
+// bytes of part_o (rounded up to 256) followed by part_lse
+size_t mha_fused_partial_bytes(int batch, int nchunks, int qblocks, int H);
+hipError_t mha_fused_launch(const MhaFusedArgs& a, hipStream_t s);
+hipError_t mha_fused_merge_launch(const MhaFusedArgs& a, hipStream_t s);
+
 struct DecodeAttnArgs {
   const void* ql = nullptr; int64_t ldql = 0;       // latent query q_nope W_UK [B, H, c], row stride ldql
   const void* q = nullptr; int64_t ldq = 0; int qk_head = 0;  // roped q (rope part at offset n)

@@ -188,9 +188,10 @@ int check_mask(int kind, int window) {
 }
 
 enum Stage { ST_QKV_A = 0, ST_Q_B, ST_ROPE_CACHE, ST_KV_B, ST_PREFILL_ATTN, ST_WUK, ST_DECODE_ATTN,
-             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_COUNT };
+             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_EXPAND_ATTN, ST_EXPAND_MERGE, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"qkv_a_gemm", "q_b_gemm", "rope_cache", "kv_b_expand", "prefill_attn",
-                                     "wuk_absorb", "decode_attn", "decode_merge", "wuv_gemm", "o_proj_gemm"};
+                                     "wuk_absorb", "decode_attn", "decode_merge", "wuv_gemm", "o_proj_gemm",
+                                     "expand_attn", "expand_merge"};
 
 hipEvent_t pool_event(mla_ctx* ctx) {
   if (!ctx->event_pool.empty()) {
@@ -455,6 +456,53 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   {
     StageTimer st(ctx, s, ST_ROPE_CACHE);
     HIP_TRY(rope_cache_launch(rc, ctx->bf16, max_q_len, batch, s));
+  }
+
+  // few new tokens per sequence: the expansion is fused into the attention
+  // (the expanded keys and values stay in registers; partial outputs per
+  // 256-entry chunk live in the expansion buffer, which this form does not use)
+  MhaFusedArgs fa;
+  fa.q = q; fa.ldq = ldq; fa.qk_head = ctx->qkh;
+  fa.cache = kv_cache; fa.block_table = block_table;
+  fa.num_blocks = num_blocks; fa.max_blocks = max_blocks; fa.page = c.page_size;
+  fa.wkvb = ctx->Wkvb;
+  fa.cu_seqlens = cu_seqlens_q; fa.prefix_lens = prefix_lens;
+  fa.batch = batch; fa.max_q_len = max_q_len; fa.max_kv_len = max_kv_len; fa.total_tokens = total_tokens;
+  fa.H = ctx->H; fa.scale = ctx->scale;
+  fa.mask.kind = mask_kind; fa.mask.window = window; fa.mask.row_lo = row_lo; fa.mask.row_hi = row_hi;
+  fa.nchunks = (max_kv_len + 255) / 256;
+  fa.qblocks = (max_q_len + 15) / 16;
+  fa.out = ctx->attn; fa.ldo = (int64_t)ctx->H * ctx->dv;
+  if (ctx->off_g >= 0) {
+    fa.gate = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    fa.ldg = ctx->N1;
+  }
+  const size_t part_bytes = mha_fused_partial_bytes(batch, fa.nchunks, fa.qblocks, ctx->H);
+  const size_t exp_bytes = (size_t)c.max_prefill_kv * ctx->H * (ctx->n + ctx->dv) * ctx->esz;
+  const bool fused_shape = ctx->bf16 && ctx->c == 512 && ctx->n == 128 && ctx->r == 64 && ctx->dv == 128 &&
+                           max_q_len <= kMhaFusedMaxQ && part_bytes <= exp_bytes;
+  if (fused_shape) {
+    fa.part_o = static_cast<bf16_t*>(ctx->kvexp);
+    fa.part_lse = reinterpret_cast<float*>(static_cast<char*>(ctx->kvexp) +
+                                           (((size_t)batch * fa.nchunks * fa.qblocks * ctx->H * 16 * 128 * 2 + 255) &
+                                            ~(size_t)255));
+  }
+  if (fused_shape && mha_fused_check(fa) == nullptr) {
+    {
+      StageTimer st(ctx, s, ST_EXPAND_ATTN);
+      HIP_TRY(mha_fused_launch(fa, s));
+    }
+    {
+      StageTimer st(ctx, s, ST_EXPAND_MERGE);
+      HIP_TRY(mha_fused_merge_launch(fa, s));
+    }
+    GemmArgs go;
+    go.A = ctx->attn; go.lda = (int64_t)ctx->H * ctx->dv;
+    go.W = ctx->Wo; go.ldw = (int64_t)ctx->H * ctx->dv;
+    go.C = out; go.ldc = ctx->hid;
+    go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
+    StageTimer st(ctx, s, ST_O_PROJ);
+    return run_gemm(ctx, go, s);
   }
 
   // expand every visible latent (prefix and new) through kv_b_proj

@@ -149,6 +149,11 @@ MLA_API int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* 
  *   out          device [total_tokens, hidden]
  * Limits: batch <= max_batch, total_tokens <= max_tokens, max_kv_len <=
  * max_seq_len, batch * max_kv_len <= max_prefill_kv (else MLA_ERR_CAPACITY).
+ * With at most 64 new tokens per sequence (bf16, 512 + 64 latent, 128 + 64 /
+ * 128 heads, heads a multiple of 8) the expanded keys and values are never
+ * stored: each 256-entry chunk is expanded and attended in one kernel and the
+ * chunks are merged by their log-sum-exp (same arithmetic, one fewer round
+ * trip through HBM).
  */
 MLA_API int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t total_tokens,
                          const int32_t* cu_seqlens_q, const int32_t* prefix_lens,
@@ -242,9 +247,14 @@ MLA_API int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batc
  *   7 decode_merge decode: log-sum-exp merge of the splits
  *   8 wuv_gemm     decode: latent output -> v_head_dim through W_UV (+ gate)
  *   9 o_proj_gemm  output projection
+ *  10 expand_attn  prefill with at most 64 new tokens per sequence (bf16,
+ *                  512 + 64 latent, 128 + 64 / 128 heads): the kv_b expansion
+ *                  and the attention over each 256-entry chunk of the cache in
+ *                  one kernel (stages 3 and 4 do not run then)
+ *  11 expand_merge log-sum-exp merge of those chunks (+ output gate)
  * A stage may be more than one kernel (a split-K GEMM adds its reduction).
  */
-#define MLA_NUM_STAGES 10
+#define MLA_NUM_STAGES 12
 MLA_API int mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* ms[i]: total elapsed milliseconds of stage i; count[i]: times it ran. Both
  * host arrays of MLA_NUM_STAGES entries (count may be NULL). Synchronises. */

@@ -35,6 +35,8 @@ def test_draft_block_work_matches_the_closed_form():
     proj = 2 * T * 4096 * (1536 + 576) + 2 * T * 1536 * H * 192 + 2 * T * H * 128 * 4096
     assert work["_step"]["flops"] == proj + 2 * kv * 512 * H * 256 + 2 * (T * 2064) * H * 320
     assert abs(work["_step"]["flops"] / 1e9 - 152.8) < 0.1
+    # the fused kernel carries the expansion and the attention, counted once in the step
+    assert work["expand_attn"]["flops"] == work["kv_b_expand"]["flops"] + work["prefill_attn"]["flops"]
 
 
 def test_causal_prefill_work_counts_the_triangle():

@@ -85,6 +85,24 @@ def test_draft_block_absorbed_gate_neox():
     _run_and_check(w, block=True)
 
 
+def test_expand_fused_query_blocks():
+    """The fused expansion + attention (at most 64 new tokens per sequence):
+    causal chunks of 1-64 tokens (up to four 16-query blocks) after prefixes
+    that end inside, at and across 256-entry chunk edges."""
+    w = ms.make_workload("prefill_bf16", q_lens=[40, 64, 17, 1], prefix_lens=[300, 0, 1000, 255],
+                         mask_kind=ms.MASK_CAUSAL, seed=41)
+    _run_and_check(w)
+
+
+def test_expand_fused_sliding_gate():
+    """Fused path with a sliding window (chunks wholly outside some windows),
+    the output gate and 16 heads (two heads per XCD band)."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 33, 5], prefix_lens=[500, 7, 256],
+                         mask_kind=ms.MASK_SLIDING, window=100, seed=42,
+                         dims_override={"num_heads": 16, "use_output_gate": True})
+    _run_and_check(w)
+
+
 def test_decode_small():
     w = ms.make_workload("decode_bf16", seq_lens=[1, 65, 700, 333, 64])
     _run_and_check(w)
