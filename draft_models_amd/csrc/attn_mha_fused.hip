@@ -12,21 +12,29 @@
 // mha_fused_merge_kernel combines the chunks of a sequence (the merge of
 // partial attention states the listing uses for prefix and suffix).
 //
-// Work item = (sequence, 256-entry chunk, head); 4 wavefronts, wavefront w
-// owns entries 64 w .. 64 w + 63 of the chunk and all 256 expansion columns
-// of the head (128 k_nope, 128 v). The k axis (512 latent dims) moves in
-// 64-wide steps: the head's kv_b_proj rows and the chunk's latent rows (read
-// from the paged cache through the block table) are copied HBM -> LDS with
-// global_load_lds_dwordx4, double-buffered, 16-byte chunks of a row XOR-ed
-// with (row & 7). The k_nope part is computed as K^T (kv_b rows as the MFMA A
-// operand) and the v part as V (latent rows as A), which leaves every lane
-// holding, for one entry, 4 consecutive k_nope dims per block, and for one v
-// dim, 4 consecutive entries per block. Pairs of blocks are then exactly the
-// operands of the score product S = K q^T (contraction over dims, in a fixed
-// permuted order that the q operand follows) and of the value product
-// O^T = V^T P^T (contraction over entries, in the order the score output
-// already has), so no LDS transposes are needed. The 4 wavefronts' partial
-// softmax states are merged through LDS.
+// Work item = (sequence, 256-entry chunk, head); 8 wavefronts, two per SIMD.
+// Wavefront w owns entries 64 (w & 3) .. + 63 of the chunk; w < 4 computes
+// their 128 k_nope columns, w >= 4 their 128 v columns. The k axis (512
+// latent dims) moves in 32-wide steps through a 4-buffer LDS ring: the head's
+// kv_b_proj rows and the chunk's latent rows (read from the paged cache
+// through the block table) are copied HBM -> LDS with global_load_lds_dwordx4
+// three steps ahead, each wavefront's copies spread between its MFMAs so that
+// the other wavefront of the SIMD keeps the matrix core busy while one waits
+// for the copy path. The 16-byte chunks of a 64-byte tile row are XOR-ed with
+// (row >> 2) & 3, so the 16 rows of a fragment read hit distinct banks.
+//
+// The k_nope part is computed as K^T (kv_b rows as the MFMA A operand) and
+// the v part as V (latent rows as A): every lane then holds, for one entry,
+// 4 consecutive k_nope dims per block, and for one v dim, 4 consecutive
+// entries per block. Pairs of blocks are exactly the operands of the score
+// product S = K q^T (contraction over dims, in a fixed permuted order that
+// the q operand follows) and of the value product O^T = V^T P^T (contraction
+// over entries, in the order the score output already has): the k_nope
+// wavefront of an entry block hands its probabilities to the v wavefront of
+// the same block through LDS in register order, and no transpose is needed.
+// The 4 entry blocks' softmax states are merged through LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -35,15 +43,20 @@ namespace mla {
 namespace {
 
 constexpr int kC = 512, kE = 576, kNope = 128, kDv = 128, kQk = 192;
-constexpr int KC = 256;                 // cache entries per chunk
-constexpr int BK = 64;                  // k step
-constexpr int ROWCH = BK / 8;           // 16-byte chunks per 128-byte tile row
-constexpr int SLOTS = 256 * ROWCH;      // 16-byte slots per operand tile
-constexpr int DMA_PER_WAVE = SLOTS / 256;
-constexpr int OPAD = kDv + 4;           // LDS row of one query's partial output (floats)
+constexpr int KC = 256;                  // cache entries per chunk
+constexpr int BK = 32;                   // k step
+constexpr int ROWCH = BK / 8;            // 16-byte chunks per 64-byte tile row
+constexpr int SLOTS = 256 * ROWCH;       // 16-byte slots per operand tile (16 KB)
+constexpr int NBUF = 4, LEAD = 3;        // ring buffers; steps copied ahead
+constexpr int NWAVE = 8;
+constexpr int DPW = SLOTS / (NWAVE * 64);  // copies per wavefront per operand per step
+constexpr int NK = kC / BK;               // expansion steps
+constexpr int NKR = NK + 2;               // + the rope keys (latent columns 512..575, no kv_b rows)
+constexpr int OPAD = kDv + 4;            // LDS row of one query's partial output (floats)
 constexpr float kLog2e = 1.4426950408889634f;
+static_assert(DPW == 2 && NK > LEAD + 1 && (kE - kC) == 2 * BK, "copy schedule assumes these sizes");
 
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 2) & 3)); }
 
 __device__ __forceinline__ void visible_rows(const MaskArgs& m, int t, int p, int L, int& lo, int& hi) {
   if (m.row_lo != nullptr && m.row_hi != nullptr) {
@@ -74,15 +87,15 @@ __device__ __forceinline__ SeqGeom seq_geom(const MhaFusedArgs& a, int b) {
   return g;
 }
 
-__global__ __launch_bounds__(256, 1) void mha_fused_kernel(MhaFusedArgs a) {
-  // operand rings (kv_b rows, then latent rows); after the k loop the same
-  // memory holds the wavefronts' partial outputs
-  __shared__ __attribute__((aligned(16))) bf16x8 lds[4 * SLOTS];
-  bf16x8 (*tw)[SLOTS] = reinterpret_cast<bf16x8(*)[SLOTS]>(&lds[0]);
-  bf16x8 (*ta)[SLOTS] = reinterpret_cast<bf16x8(*)[SLOTS]>(&lds[2 * SLOTS]);
-  float* om = reinterpret_cast<float*>(&lds[0]);  // [4 waves][16 queries][OPAD]
-  float* mm = om + 4 * 16 * OPAD;                  // [4][16] running max (log2 units)
-  float* ll = mm + 64;                             // [4][16] probability sums
+__global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a) {
+  // operand ring: buffer i = kv_b rows, then latent rows (16 KB each); after
+  // the k loop buffers 0 and 1 hold the rope keys, buffers 2 and 3 the
+  // epilogue's exchange areas
+  __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS];
+  bf16x8* pex = &lds[4 * SLOTS];                               // [4 blocks][64 lanes][2] probabilities
+  float* om = reinterpret_cast<float*>(&lds[4 * SLOTS + 4 * 64 * 2]);  // [4 blocks][16 queries][OPAD]
+  float* mm = om + 4 * 16 * OPAD;                              // [4][16] max (log2 units)
+  float* ll = mm + 64;                                         // [4][16] probability sums
 
   // work item: the heads of a sequence-chunk pair are spread over the XCD's
   // band of H / 8 heads; consecutive items of an XCD share the chunk's latent
@@ -98,6 +111,8 @@ __global__ __launch_bounds__(256, 1) void mha_fused_kernel(MhaFusedArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int eb = wave & 3;          // entry block: entries 64 eb .. 64 eb + 63
+  const bool vpart = wave >= 4;     // v columns (else k_nope columns)
   const int lr = lane & 15, g4 = lane >> 4;
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(a.wkvb);
   const bf16* __restrict__ cache = reinterpret_cast<const bf16*>(a.cache);
@@ -112,182 +127,202 @@ __global__ __launch_bounds__(256, 1) void mha_fused_kernel(MhaFusedArgs a) {
     return (blk >= 0 && blk < a.num_blocks) ? ((int64_t)blk * a.page + key % a.page) * kE : 0;
   };
 
-  uint32_t woff[DMA_PER_WAVE], aoff[DMA_PER_WAVE];
+  // copy geometry: slot (j * 8 + wave) * 64 + lane of an operand tile holds
+  // row s / 4, chunk s % 4 (swizzled) of the step's 32-wide k slice
+  uint32_t woff[DPW], aoff[DPW];
 #pragma unroll
-  for (int j = 0; j < DMA_PER_WAVE; ++j) {
-    const int s = (j * 4 + wave) * 64 + lane;
+  for (int j = 0; j < DPW; ++j) {
+    const int s = (j * NWAVE + wave) * 64 + lane;
     const int row = s / ROWCH, cs = s % ROWCH;
-    const uint32_t colb = (uint32_t)(cs ^ (row & 7)) * 16u;
+    const uint32_t colb = (uint32_t)(cs ^ ((row >> 2) & 3)) * 16u;
     woff[j] = (uint32_t)(((int64_t)h * 256 + row) * kC * 2) + colb;
     aoff[j] = (uint32_t)(entry_off(k0 + row) * 2) + colb;
   }
-  // the shared rope key of every entry this lane scores: entry 16 bb + lr of
-  // the wavefront's 64, rope dims 32 jr + 8 g4 .. + 7 (score A operand)
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  // copy g (0, 1: kv_b rows; 2, 3: latent rows) of step kt into its buffer;
+  // steps NK and NK + 1 copy only the latent rows' rope keys
+  auto copy = [&](int kt, int g) {
+    const uint32_t dst = lds0 + (uint32_t)((kt % NBUF) * 2 * SLOTS + (g >> 1) * SLOTS) * 16u +
+                         (uint32_t)(((g & 1) * NWAVE + wave) * 1024);
+    if (g < 2) dma16_sbase(woff[g & 1], W + kt * BK, dst);
+    else dma16_sbase(aoff[g & 1], cache + kt * BK, dst);
+  };
+
+  // k_nope wavefront: acc[x][y][i] = K^T[dim 16 x + 4 g4 + i][entry 16 y + lr]
+  // v wavefront:      acc[x][y][i] = V[entry 16 y + 4 g4 + i][v dim 16 x + lr]
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // one k step: fragments from buffer kt % NBUF, the copies of step kt + LEAD
+  // spread over the 32 MFMAs (one per 8)
+  auto step = [&](int kt, auto vtag) {
+    constexpr bool V = decltype(vtag)::value;
+    const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
+    const bf16x8* TA = TW + SLOTS;
+    Frag<bf16> af[4], wf[8];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) af[y].v = TA[swz(eb * 64 + y * 16 + lr, g4)];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) wf[x].v = TW[swz((V ? 128 : 0) + x * 16 + lr, g4)];
+    const int nx = kt + LEAD;
+    const int ncopy = nx < NK ? 4 : (nx < NKR ? 2 : 0);  // rope steps: the 2 latent copies
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (g < ncopy) copy(nx, ncopy == 4 ? g : g + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int x = 2 * g; x < 2 * g + 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = V ? mfma16(af[y], wf[x], acc[x][y]) : mfma16(wf[x], af[y], acc[x][y]);
+    }
+  };
+
+  for (int kt = 0; kt < LEAD; ++kt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) copy(kt, g);
+  auto kloop = [&](auto vtag) {
+    for (int kt = 0; kt < NK; ++kt) {
+      // this wavefront's copies of step kt are done once at most the newer
+      // steps' are in flight: steps kt + 1 and kt + 2, 4 copies each below
+      // NK, 2 for the rope steps (kt + 2 = NK is issued in step kt - 1)
+      if (kt + 2 < NK) MLA_WAIT_VMCNT(8);
+      else if (kt + 2 == NK) MLA_WAIT_VMCNT(6);
+      else MLA_WAIT_VMCNT(4);
+      lds_barrier();  // every wavefront's copies of step kt landed; step kt - 1 read by all
+      step(kt, vtag);
+    }
+  };
+  if (vpart) kloop(std::true_type{});
+  else kloop(std::false_type{});
+  MLA_WAIT_VMCNT(0);
+  lds_barrier();  // rope keys landed; the last buffers read by all before reuse
+
+  // the shared rope key of every entry a k_nope lane scores: entry 16 y + lr
+  // of the block, rope dims 32 jr + 8 g4 .. + 7 (score A operand), from the
+  // rope steps' latent tiles
   bf16x8 kpe[4][2];
+  if (!vpart) {
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-    const bf16* er = cache + entry_off(k0 + wave * 64 + bb * 16 + lr) + kC + 8 * g4;
+    for (int jr = 0; jr < 2; ++jr) {
+      const bf16x8* TA = &lds[((NK + jr) % NBUF) * 2 * SLOTS + SLOTS];
 #pragma unroll
-    for (int jr = 0; jr < 2; ++jr) kpe[bb][jr] = *reinterpret_cast<const bf16x8*>(er + 32 * jr);
+      for (int y = 0; y < 4; ++y) kpe[y][jr] = TA[swz(eb * 64 + y * 16 + lr, g4)];
+    }
   }
-
-  const uint32_t tw_lds = lds_addr(&tw[0][0]), ta_lds = lds_addr(&ta[0][0]);
-  auto issue = [&](int kt, int buf) {
-    const bf16* wb = W + kt * BK;
-    const bf16* ab = cache + kt * BK;
-    const uint32_t bo = (uint32_t)buf * SLOTS * 16u;
-#pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) dma16_sbase(woff[j], wb, tw_lds + bo + (uint32_t)(j * 4 + wave) * 1024u);
-#pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) dma16_sbase(aoff[j], ab, ta_lds + bo + (uint32_t)(j * 4 + wave) * 1024u);
-  };
-
-  // accK[a][bb][i] = K^T[dim 16 a + 4 g4 + i][entry 16 bb + lr]
-  // accV[a][bb][i] = V[entry 16 bb + 4 g4 + i][v dim 16 a + lr]
-  floatx4 accK[8][4], accV[8][4];
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      accK[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
-      accV[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  auto compute = [&](const bf16x8* TW, const bf16x8* TA) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      Frag<bf16> wf[16], af[4];
-#pragma unroll
-      for (int x = 0; x < 16; ++x) wf[x].v = TW[swz(x * 16 + lr, ks * 4 + g4)];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wave * 64 + y * 16 + lr, ks * 4 + g4)];
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) accK[x][y] = mfma16(wf[x], af[y], accK[x][y]);
-#pragma unroll
-      for (int x = 0; x < 8; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) accV[x][y] = mfma16(af[y], wf[8 + x], accV[x][y]);
-    }
-  };
-
-  constexpr int nk = kC / BK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      issue(kt + 1, buf ^ 1);
-      MLA_WAIT_VMCNT(2 * DMA_PER_WAVE);
-    } else {
-      MLA_WAIT_VMCNT(0);
-    }
-    lds_barrier();
-    compute(tw[buf], ta[buf]);
-    lds_barrier();
-  }
-
-  // expanded keys and values in bf16 (the rounding a stored expansion has):
-  // kop[bb][j] = K[entry 16 bb + lr][dims 32 j + 4 g4 + (0..3), 32 j + 16 + 4 g4 + (0..3)]
-  // vop[x][j]  = V^T[v dim 16 x + lr][entries 32 j + 4 g4 + (0..3), 32 j + 16 + 4 g4 + (0..3)]
-  bf16x8 kop[4][4], vop[8][2];
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kop[bb][j] = pack8(accK[2 * j][bb], accK[2 * j + 1][bb]);
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) vop[x][j] = pack8(accV[x][2 * j], accV[x][2 * j + 1]);
 
   const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q);
   const float sl2 = a.scale * kLog2e;
-  const int key_w = k0 + wave * 64;  // first entry of this wavefront
+  const int key_b = k0 + eb * 64;  // first entry of this block
   const int qblocks = (sg.ql + 15) >> 4;
+  // expanded keys (k_nope wavefronts) or values (v wavefronts) in bf16, the
+  // rounding a stored expansion has:
+  //   op[y][j] = K[entry 16 y + lr][dims 32 j + 4 g4 + (0..3), 32 j + 16 + 4 g4 + (0..3)]   (y, j < 4)
+  //   op[x][j] = V^T[v dim 16 x + lr][entries 32 j + 4 g4 + (0..3), 32 j + 16 + 4 g4 + (0..3)]  (x < 8, j < 2)
+  bf16x8 op[8][2];
+  bf16x8 kop[4][4];
+  if (vpart) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) op[x][j] = pack8(acc[x][2 * j], acc[x][2 * j + 1]);
+  } else {
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kop[y][j] = pack8(acc[2 * j][y], acc[2 * j + 1][y]);
+  }
+
   for (int qb = 0; qb < qblocks; ++qb) {
-    // query lr of the block: q operands in the dims order of kop
-    const int qi = qb * 16 + lr;
-    const int t = sg.q0 + qi;
-    const bool qok = qi < sg.ql && t < a.total_tokens;
-    int lo = 0, hi = 0;
-    if (qok) visible_rows(a.mask, t, sg.pl + qi, sg.L, lo, hi);
-    bf16x8 qn[4], qp[2];
-    if (qok) {
-      const bf16* qr = Q + (int64_t)t * a.ldq + (int64_t)h * kQk;
+    if (!vpart) {
+      // query lr of the block: q operands in the dims order of kop
+      const int qi = qb * 16 + lr;
+      const int t = sg.q0 + qi;
+      const bool qok = qi < sg.ql && t < a.total_tokens;
+      int lo = 0, hi = 0;
+      if (qok) visible_rows(a.mask, t, sg.pl + qi, sg.L, lo, hi);
+      bf16x8 qn[4], qp[2];
+      if (qok) {
+        const bf16* qr = Q + (int64_t)t * a.ldq + (int64_t)h * kQk;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 4 * g4);
-        const bf16x4 y = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 16 + 4 * g4);
-        qn[j] = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        for (int j = 0; j < 4; ++j) {
+          const bf16x4 x = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 4 * g4);
+          const bf16x4 y = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 16 + 4 * g4);
+          qn[j] = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        }
+#pragma unroll
+        for (int jr = 0; jr < 2; ++jr) qp[jr] = *reinterpret_cast<const bf16x8*>(qr + kNope + 32 * jr + 8 * g4);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qn[j] = bf16x8{};
+        qp[0] = qp[1] = bf16x8{};
       }
+      // scores s[y][i] = S[entry 16 y + 4 g4 + i][query lr]
+      floatx4 s[4];
 #pragma unroll
-      for (int jr = 0; jr < 2; ++jr) qp[jr] = *reinterpret_cast<const bf16x8*>(qr + kNope + 32 * jr + 8 * g4);
-    } else {
+      for (int y = 0; y < 4; ++y) {
+        floatx4 z = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qn[j] = bf16x8{};
-      qp[0] = qp[1] = bf16x8{};
-    }
-
-    // scores s[bb][i] = S[entry 16 bb + 4 g4 + i][query lr]
-    floatx4 s[4];
+        for (int j = 0; j < 4; ++j) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[y][j], qn[j], z, 0, 0, 0);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      floatx4 z = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[bb][j], qn[j], z, 0, 0, 0);
-#pragma unroll
-      for (int jr = 0; jr < 2; ++jr) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kpe[bb][jr], qp[jr], z, 0, 0, 0);
-      s[bb] = z;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key_w + bb * 16 + 4 * g4 + i;
-        const float x = (key >= lo && key < hi) ? s[bb][i] * sl2 : -INFINITY;
-        s[bb][i] = x;
-        mx = fmaxf(mx, x);
+        for (int jr = 0; jr < 2; ++jr) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kpe[y][jr], qp[jr], z, 0, 0, 0);
+        s[y] = z;
       }
-    mx = red4_max(mx);
-    const float mref = mx == -INFINITY ? 0.f : mx;
-    float lsum = 0.f;
+      float mx = -INFINITY;
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb)
+      for (int y = 0; y < 4; ++y)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[bb][i] - mref);  // masked -> 0
-        s[bb][i] = p;
-        lsum += p;
+        for (int i = 0; i < 4; ++i) {
+          const int key = key_b + y * 16 + 4 * g4 + i;
+          const float x = (key >= lo && key < hi) ? s[y][i] * sl2 : -INFINITY;
+          s[y][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = red4_max(mx);
+      const float mref = mx == -INFINITY ? 0.f : mx;
+      float lsum = 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(s[y][i] - mref);  // masked -> 0
+          s[y][i] = p;
+          lsum += p;
+        }
+      lsum = red4_sum(lsum);
+      // the v wavefront's B operands, in register order
+      pex[(eb * 64 + lane) * 2] = pack8(s[0], s[1]);
+      pex[(eb * 64 + lane) * 2 + 1] = pack8(s[2], s[3]);
+      if (g4 == 0) {
+        mm[eb * 16 + lr] = mx;
+        ll[eb * 16 + lr] = lsum;
       }
-    lsum = red4_sum(lsum);
-    const bf16x8 pop0 = pack8(s[0], s[1]), pop1 = pack8(s[2], s[3]);
-    // o[x][i] = O^T[v dim 16 x + 4 g4 + i][query lr] over this wavefront's entries
-    floatx4 o[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      floatx4 z = floatx4{0.f, 0.f, 0.f, 0.f};
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[x][0], pop0, z, 0, 0, 0);
-      z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[x][1], pop1, z, 0, 0, 0);
-      o[x] = z;
     }
-
-    // merge the 4 wavefronts' states: max, sum and unnormalised output per query
-    float* orow = om + (wave * 16 + lr) * OPAD;
+    __syncthreads();
+    if (vpart) {
+      // o[x][i] = O^T[v dim 16 x + 4 g4 + i][query lr] over the block's entries
+      const bf16x8 p0 = pex[(eb * 64 + lane) * 2], p1 = pex[(eb * 64 + lane) * 2 + 1];
+      float* orow = om + (eb * 16 + lr) * OPAD;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) *reinterpret_cast<floatx4*>(orow + 16 * x + 4 * g4) = o[x];
-    if (g4 == 0) {
-      mm[wave * 16 + lr] = mx;
-      ll[wave * 16 + lr] = lsum;
+      for (int x = 0; x < 8; ++x) {
+        floatx4 z = floatx4{0.f, 0.f, 0.f, 0.f};
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[x][0], p0, z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[x][1], p1, z, 0, 0, 0);
+        *reinterpret_cast<floatx4*>(orow + 16 * x + 4 * g4) = z;
+      }
     }
     __syncthreads();
     {
-      const int q = tid >> 4, d8 = (tid & 15) * 8;
+      // merge the 4 entry blocks: query tid / 32, v dims 4 (tid % 32) .. + 3
+      const int q = tid >> 5, d4 = (tid & 31) * 4;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < 4; ++w) M = fmaxf(M, mm[w * 16 + q]);
       float den = 0.f;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      floatx4 o4 = floatx4{0.f, 0.f, 0.f, 0.f};
       if (M != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -295,23 +330,16 @@ __global__ __launch_bounds__(256, 1) void mha_fused_kernel(MhaFusedArgs a) {
           if (mw == -INFINITY) continue;
           const float e = fast_exp2(mw - M);
           den += e * ll[w * 16 + q];
-          const float* src = om + (w * 16 + q) * OPAD + d8;
-          const floatx4 v0 = *reinterpret_cast<const floatx4*>(src);
-          const floatx4 v1 = *reinterpret_cast<const floatx4*>(src + 4);
+          const floatx4 v = *reinterpret_cast<const floatx4*>(om + (w * 16 + q) * OPAD + d4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] += e * v0[i];
-            acc[4 + i] += e * v1[i];
-          }
+          for (int i = 0; i < 4; ++i) o4[i] += e * v[i];
         }
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
       const int64_t pi = (((int64_t)b * a.nchunks + ch) * a.qblocks + qb) * a.H + h;
-      bf16x8 ov;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ov[i] = (bf16)(acc[i] * inv);
-      *reinterpret_cast<bf16x8*>(a.part_o + (pi * 16 + q) * kDv + d8) = ov;
-      if (d8 == 0) a.part_lse[pi * 16 + q] = den > 0.f ? M + __log2f(den) : -INFINITY;
+      *reinterpret_cast<bf16x4*>(a.part_o + (pi * 16 + q) * kDv + d4) =
+          bf16x4{(bf16)(o4[0] * inv), (bf16)(o4[1] * inv), (bf16)(o4[2] * inv), (bf16)(o4[3] * inv)};
+      if (d4 == 0) a.part_lse[pi * 16 + q] = den > 0.f ? M + __log2f(den) : -INFINITY;
     }
     __syncthreads();
   }
@@ -386,7 +414,7 @@ size_t mha_fused_partial_bytes(int batch, int nchunks, int qblocks, int H) {
 }
 
 hipError_t mha_fused_launch(const MhaFusedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(mha_fused_kernel, dim3((unsigned)(a.batch * a.nchunks * a.H)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mha_fused_kernel, dim3((unsigned)(a.batch * a.nchunks * a.H)), dim3(NWAVE * 64), 0, s, a);
   return hipGetLastError();
 }
 
