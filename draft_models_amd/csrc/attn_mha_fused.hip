@@ -21,7 +21,8 @@
 // three steps ahead, each wavefront's copies spread between its MFMAs so that
 // the other wavefront of the SIMD keeps the matrix core busy while one waits
 // for the copy path. The 16-byte chunks of a 64-byte tile row are XOR-ed with
-// (row >> 2) & 3, so the 16 rows of a fragment read hit distinct banks.
+// (row >> 1) & 3, so every 8 consecutive rows of a fragment read (the lanes
+// the LDS serves together, 128 bytes) hit distinct banks.
 //
 // The k_nope part is computed as K^T (kv_b rows as the MFMA A operand) and
 // the v part as V (latent rows as A): every lane then holds, for one entry,
@@ -56,7 +57,7 @@ constexpr int OPAD = kDv + 4;            // LDS row of one query's partial outpu
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(DPW == 2 && NK > LEAD + 1 && (kE - kC) == 2 * BK, "copy schedule assumes these sizes");
 
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 2) & 3)); }
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 3)); }
 
 __device__ __forceinline__ void visible_rows(const MaskArgs& m, int t, int p, int L, int& lo, int& hi) {
   if (m.row_lo != nullptr && m.row_hi != nullptr) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
   // the k loop buffers 0 and 1 hold the rope keys, buffers 2 and 3 the
   // epilogue's exchange areas
   __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS];
-  bf16x8* pex = &lds[4 * SLOTS];                               // [4 blocks][64 lanes][2] probabilities
+  bf16x8* pex = &lds[4 * SLOTS];                               // [4 blocks][2][64 lanes] probabilities
   float* om = reinterpret_cast<float*>(&lds[4 * SLOTS + 4 * 64 * 2]);  // [4 blocks][16 queries][OPAD]
   float* mm = om + 4 * 16 * OPAD;                              // [4][16] max (log2 units)
   float* ll = mm + 64;                                         // [4][16] probability sums
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
   for (int j = 0; j < DPW; ++j) {
     const int s = (j * NWAVE + wave) * 64 + lane;
     const int row = s / ROWCH, cs = s % ROWCH;
-    const uint32_t colb = (uint32_t)(cs ^ ((row >> 2) & 3)) * 16u;
+    const uint32_t colb = (uint32_t)(cs ^ ((row >> 1) & 3)) * 16u;
     woff[j] = (uint32_t)(((int64_t)h * 256 + row) * kC * 2) + colb;
     aoff[j] = (uint32_t)(entry_off(k0 + row) * 2) + colb;
   }
@@ -294,8 +295,8 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
         }
       lsum = red4_sum(lsum);
       // the v wavefront's B operands, in register order
-      pex[(eb * 64 + lane) * 2] = pack8(s[0], s[1]);
-      pex[(eb * 64 + lane) * 2 + 1] = pack8(s[2], s[3]);
+      pex[eb * 128 + lane] = pack8(s[0], s[1]);
+      pex[eb * 128 + 64 + lane] = pack8(s[2], s[3]);
       if (g4 == 0) {
         mm[eb * 16 + lr] = mx;
         ll[eb * 16 + lr] = lsum;
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
     __syncthreads();
     if (vpart) {
       // o[x][i] = O^T[v dim 16 x + 4 g4 + i][query lr] over the block's entries
-      const bf16x8 p0 = pex[(eb * 64 + lane) * 2], p1 = pex[(eb * 64 + lane) * 2 + 1];
+      const bf16x8 p0 = pex[eb * 128 + lane], p1 = pex[eb * 128 + 64 + lane];
       float* orow = om + (eb * 16 + lr) * OPAD;
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
