@@ -359,21 +359,37 @@ __global__ __launch_bounds__(256) void mha_fused_merge_kernel(MhaFusedArgs a) {
   const int nc = (sg.L + KC - 1) / KC;
   const int64_t base = (((int64_t)b * a.nchunks) * a.qblocks + qb) * a.H + h;  // chunk 0
   const int64_t cstride = (int64_t)a.qblocks * a.H;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_lse[(base + c * cstride) * 16 + q]);
+  // groups of 8 chunks: their loads issued together, a running max across groups
+  constexpr int G = 8;
+  float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (M != -INFINITY) {
-    for (int c = 0; c < nc; ++c) {
-      const int64_t pi = base + c * cstride;
-      const float l = a.part_lse[pi * 16 + q];
-      if (l == -INFINITY) continue;
-      const float e = fast_exp2(l - M);
-      den += e;
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(a.part_o + (pi * 16 + q) * kDv + d8);
+  for (int c0 = 0; c0 < nc; c0 += G) {
+    float l[G];
+    bf16x8 v[G];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += e * (float)v[i];
+    for (int k = 0; k < G; ++k) {
+      const int c = c0 + k;
+      const int64_t pi = base + (int64_t)min(c, nc - 1) * cstride;  // every chunk below nc was written
+      l[k] = c < nc ? a.part_lse[pi * 16 + q] : -INFINITY;
+      v[k] = *reinterpret_cast<const bf16x8*>(a.part_o + (pi * 16 + q) * kDv + d8);
     }
+    float mg = M;
+#pragma unroll
+    for (int k = 0; k < G; ++k) mg = fmaxf(mg, l[k]);
+    if (mg == -INFINITY) continue;
+    const float r = fast_exp2(M - mg);  // 0 while M is still -inf
+    den *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      if (l[k] == -INFINITY) continue;
+      const float e = fast_exp2(l[k] - mg);
+      den += e;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += e * (float)v[k][i];
+    }
+    M = mg;
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   bf16x8 ov;
