@@ -54,6 +54,8 @@ constexpr int DPW = SLOTS / (NWAVE * 64);  // copies per wavefront per operand p
 constexpr int NK = kC / BK;               // expansion steps
 constexpr int NKR = NK + 2;               // + the rope keys (latent columns 512..575, no kv_b rows)
 constexpr int OPAD = kDv + 4;            // LDS row of one query's partial output (floats)
+constexpr int QCH = kQk / 8;             // 16-byte chunks of one query row (24)
+constexpr int QSLOTS = (kMhaFusedMaxQ / 16) * 16 * QCH;  // LDS copy of the item's queries
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(DPW == 2 && NK > LEAD + 1 && (kE - kC) == 2 * BK, "copy schedule assumes these sizes");
 
@@ -92,7 +94,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
   // operand ring: buffer i = kv_b rows, then latent rows (16 KB each); after
   // the k loop buffers 0 and 1 hold the rope keys, buffers 2 and 3 the
   // epilogue's exchange areas
-  __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS];
+  __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS + QSLOTS];
+  // the sequence's roped queries of this head, row r = query r, chunk c at
+  // position c ^ (r & 7) (copied before the k loop, read by the epilogue)
+  const bf16x8* qlds = &lds[NBUF * 2 * SLOTS];
   bf16x8* pex = &lds[4 * SLOTS];                               // [4 blocks][2][64 lanes] probabilities
   float* om = reinterpret_cast<float*>(&lds[4 * SLOTS + 4 * 64 * 2]);  // [4 blocks][16 queries][OPAD]
   float* mm = om + 4 * 16 * OPAD;                              // [4][16] max (log2 units)
@@ -182,6 +187,19 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
     }
   };
 
+  // the queries (1 KB per copy, 6 per 16-query block) go first: the first
+  // wait of the k loop covers them
+  {
+    const int nq = ((sg.ql + 15) >> 4) * 16 * QCH / 64;
+    const bf16* Qh = reinterpret_cast<const bf16*>(a.q) + (int64_t)sg.q0 * a.ldq + (int64_t)h * kQk;
+    for (int i = wave; i < nq; i += NWAVE) {
+      const int c = i * 64 + lane;
+      const int r = c / QCH, p = c % QCH;
+      const int rr = min(r, sg.ql - 1);  // rows past the sequence re-read its last query (masked)
+      const uint32_t off = (uint32_t)(((int64_t)rr * a.ldq + (p ^ (r & 7)) * 8) * 2);
+      dma16_sbase(off, Qh, lds0 + (uint32_t)(NBUF * 2 * SLOTS + i * 64) * 16u);
+    }
+  }
   for (int kt = 0; kt < LEAD; ++kt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) copy(kt, g);
@@ -215,7 +233,6 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
     }
   }
 
-  const bf16* __restrict__ Q = reinterpret_cast<const bf16*>(a.q);
   const float sl2 = a.scale * kLog2e;
   const int key_b = k0 + eb * 64;  // first entry of this block
   const int qblocks = (sg.ql + 15) >> 4;
@@ -246,20 +263,17 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
       int lo = 0, hi = 0;
       if (qok) visible_rows(a.mask, t, sg.pl + qi, sg.L, lo, hi);
       bf16x8 qn[4], qp[2];
-      if (qok) {
-        const bf16* qr = Q + (int64_t)t * a.ldq + (int64_t)h * kQk;
+      {
+        const int r = qb * 16 + lr;
+        auto qc = [&](int c) { return reinterpret_cast<const char*>(qlds + r * QCH + (c ^ (r & 7))); };
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bf16x4 x = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 4 * g4);
-          const bf16x4 y = *reinterpret_cast<const bf16x4*>(qr + 32 * j + 16 + 4 * g4);
+          const bf16x4 x = *reinterpret_cast<const bf16x4*>(qc(4 * j + (g4 >> 1)) + (g4 & 1) * 8);
+          const bf16x4 y = *reinterpret_cast<const bf16x4*>(qc(4 * j + 2 + (g4 >> 1)) + (g4 & 1) * 8);
           qn[j] = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
         }
 #pragma unroll
-        for (int jr = 0; jr < 2; ++jr) qp[jr] = *reinterpret_cast<const bf16x8*>(qr + kNope + 32 * jr + 8 * g4);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qn[j] = bf16x8{};
-        qp[0] = qp[1] = bf16x8{};
+        for (int jr = 0; jr < 2; ++jr) qp[jr] = *reinterpret_cast<const bf16x8*>(qc(16 + 4 * jr + g4));
       }
       // scores s[y][i] = S[entry 16 y + 4 g4 + i][query lr]
       floatx4 s[4];
