@@ -103,6 +103,40 @@ def test_expand_fused_sliding_gate():
     _run_and_check(w)
 
 
+def test_expand_fused_many_sequences():
+    """Fused expansion + attention over 8 sequences x 32 heads: 1-16 new
+    tokens, prefixes ending inside, at and across 256-entry chunk and
+    64-entry page edges."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 5, 1, 16, 9, 16, 16, 3],
+                         prefix_lens=[100, 37, 300, 0, 255, 240, 511, 700], seed=43)
+    _run_and_check(w)
+
+
+def test_expand_fused_causal_gate():
+    """Fused path with a causal mask, the output gate, NeoX RoPE and 16 heads
+    over 16 sequences."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16] * 8 + [7] * 8,
+                         prefix_lens=[40 * i + 3 for i in range(16)], mask_kind=ms.MASK_CAUSAL, seed=44,
+                         dims_override={"num_heads": 16, "use_output_gate": True, "rope_style": ms.ROPE_NEOX})
+    _run_and_check(w)
+
+
+def test_expand_fused_dropped_rows():
+    """Explicit visible intervals through the fused path: dropped rows are
+    exactly zero; an interval inside the prefix only."""
+    q_lens, prefix = [16] * 8, [300, 20, 64, 1000, 5, 256, 128, 77]
+    T = sum(q_lens)
+    lo = np.zeros(T, np.int32)
+    hi = np.array([p + q for p, q in zip(prefix, q_lens) for _ in range(q)], np.int32)
+    hi[3:9] = 0
+    lo[20:24] = 30
+    hi[20:24] = 30
+    lo[50:52], hi[50:52] = 600, 900
+    w = ms.make_workload("draft_block_bf16", q_lens=q_lens, prefix_lens=prefix, row_interval=(lo, hi), seed=45)
+    out = _run_and_check(w)
+    assert np.all(out[3:9] == 0) and np.all(out[20:24] == 0)
+
+
 def test_decode_small():
     w = ms.make_workload("decode_bf16", seq_lens=[1, 65, 700, 333, 64])
     _run_and_check(w)
