@@ -15,12 +15,13 @@
 // Work item = (sequence, 256-entry chunk, head); 8 wavefronts, two per SIMD.
 // Wavefront w owns entries 64 (w & 3) .. + 63 of the chunk; w < 4 computes
 // their 128 k_nope columns, w >= 4 their 128 v columns. The k axis (512
-// latent dims) moves in 32-wide steps through a 4-buffer LDS ring: the head's
-// kv_b_proj rows and the chunk's latent rows (read from the paged cache
-// through the block table) are copied HBM -> LDS with global_load_lds_dwordx4
-// three steps ahead, each wavefront's copies spread between its MFMAs so that
-// the other wavefront of the SIMD keeps the matrix core busy while one waits
-// for the copy path. The 16-byte chunks of a 64-byte tile row are XOR-ed with
+// latent dims) moves in 32-wide steps through a 4-buffer LDS ring, two steps
+// per barrier: while steps kt and kt + 1 are multiplied, the head's kv_b_proj
+// rows and the chunk's latent rows (read from the paged cache through the
+// block table) for steps kt + 2 and kt + 3 are copied HBM -> LDS with
+// global_load_lds_dwordx4, each wavefront's copies spread between the MFMAs
+// of the first step so that the other wavefront of the SIMD keeps the matrix
+// core busy while one waits for the copy path. The 16-byte chunks of a 64-byte tile row are XOR-ed with
 // (row >> 1) & 3, so every 8 consecutive rows of a fragment read (the lanes
 // the LDS serves together, 128 bytes) hit distinct banks.
 //
@@ -48,7 +49,7 @@ constexpr int KC = 256;                  // cache entries per chunk
 constexpr int BK = 32;                   // k step
 constexpr int ROWCH = BK / 8;            // 16-byte chunks per 64-byte tile row
 constexpr int SLOTS = 256 * ROWCH;       // 16-byte slots per operand tile (16 KB)
-constexpr int NBUF = 4, LEAD = 3;        // ring buffers; steps copied ahead
+constexpr int NBUF = 4;                  // ring buffers (two steps multiplied, two copied)
 constexpr int NWAVE = 8;
 constexpr int DPW = SLOTS / (NWAVE * 64);  // copies per wavefront per operand per step
 constexpr int NK = kC / BK;               // expansion steps
@@ -57,7 +58,7 @@ constexpr int OPAD = kDv + 4;            // LDS row of one query's partial outpu
 constexpr int QCH = kQk / 8;             // 16-byte chunks of one query row (24)
 constexpr int QSLOTS = (kMhaFusedMaxQ / 16) * 16 * QCH;  // LDS copy of the item's queries
 constexpr float kLog2e = 1.4426950408889634f;
-static_assert(DPW == 2 && NK > LEAD + 1 && (kE - kC) == 2 * BK, "copy schedule assumes these sizes");
+static_assert(DPW == 2 && NK % 2 == 0 && (kE - kC) == 2 * BK, "copy schedule assumes these sizes");
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 3)); }
 
@@ -162,9 +163,9 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one k step: fragments from buffer kt % NBUF, the copies of step kt + LEAD
-  // spread over the 32 MFMAs (one per 8)
-  auto step = [&](int kt, auto vtag) {
+  // one k step: fragments from buffer kt % NBUF; with `copies`, the copies of
+  // steps kt + 2 and kt + 3 spread over its 32 MFMAs (one per 4)
+  auto step = [&](int kt, auto vtag, bool copies) {
     constexpr bool V = decltype(vtag)::value;
     const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
     const bf16x8* TA = TW + SLOTS;
@@ -173,17 +174,20 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
     for (int y = 0; y < 4; ++y) af[y].v = TA[swz(eb * 64 + y * 16 + lr, g4)];
 #pragma unroll
     for (int x = 0; x < 8; ++x) wf[x].v = TW[swz((V ? 128 : 0) + x * 16 + lr, g4)];
-    const int nx = kt + LEAD;
-    const int ncopy = nx < NK ? 4 : (nx < NKR ? 2 : 0);  // rope steps: the 2 latent copies
+    // rope steps: the 2 latent copies only
+    const int n0 = copies ? (kt + 2 < NK ? 4 : (kt + 2 < NKR ? 2 : 0)) : 0;
+    const int n1 = copies ? (kt + 3 < NK ? 4 : (kt + 3 < NKR ? 2 : 0)) : 0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int x = 0; x < 8; ++x) {
       __builtin_amdgcn_sched_barrier(0);
-      if (g < ncopy) copy(nx, ncopy == 4 ? g : g + 2);
+      if (x < 4) {
+        if (x < n0) copy(kt + 2, n0 == 4 ? x : x + 2);
+      } else {
+        if (x - 4 < n1) copy(kt + 3, n1 == 4 ? x - 4 : x - 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int x = 2 * g; x < 2 * g + 2; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = V ? mfma16(af[y], wf[x], acc[x][y]) : mfma16(wf[x], af[y], acc[x][y]);
+      for (int y = 0; y < 4; ++y) acc[x][y] = V ? mfma16(af[y], wf[x], acc[x][y]) : mfma16(wf[x], af[y], acc[x][y]);
     }
   };
 
@@ -200,19 +204,17 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
       dma16_sbase(off, Qh, lds0 + (uint32_t)(NBUF * 2 * SLOTS + i * 64) * 16u);
     }
   }
-  for (int kt = 0; kt < LEAD; ++kt)
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) copy(kt, g);
   auto kloop = [&](auto vtag) {
-    for (int kt = 0; kt < NK; ++kt) {
-      // this wavefront's copies of step kt are done once at most the newer
-      // steps' are in flight: steps kt + 1 and kt + 2, 4 copies each below
-      // NK, 2 for the rope steps (kt + 2 = NK is issued in step kt - 1)
-      if (kt + 2 < NK) MLA_WAIT_VMCNT(8);
-      else if (kt + 2 == NK) MLA_WAIT_VMCNT(6);
-      else MLA_WAIT_VMCNT(4);
-      lds_barrier();  // every wavefront's copies of step kt landed; step kt - 1 read by all
-      step(kt, vtag);
+    for (int kt = 0; kt < NK; kt += 2) {
+      // this wavefront's copies of steps kt, kt + 1 (issued during step
+      // kt - 2) are done; no newer ones exist yet
+      MLA_WAIT_VMCNT(0);
+      lds_barrier();  // every wavefront's copies of kt, kt + 1 landed; kt - 2, kt - 1 read by all
+      step(kt, vtag, true);
+      step(kt + 1, vtag, false);
     }
   };
   if (vpart) kloop(std::true_type{});
