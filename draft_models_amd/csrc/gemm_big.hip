@@ -1,15 +1,19 @@
 // Large-tile bf16 MFMA GEMM for gfx950: C[M, N] = A[M, K] . W[N, K]^T.
 //
-// A 256 x 256 output tile per workgroup of 4 wavefronts (2 x 2, 128 x 128
-// each, 64 accumulator blocks of 16 x 16 held in AGPRs). The k axis moves in
-// 64-wide steps; both operand tiles (256 rows x 128 bytes) stream from HBM
-// straight into LDS with global_load_lds_dwordx4 (no register staging),
-// double-buffered so that step t+1 is in flight while step t feeds the
-// MFMAs. LDS rows are unpadded; the 16-byte chunk index of a row is XOR-ed
-// with (row & 7), so the fragment reads (8 consecutive rows, one chunk) hit
-// distinct banks. Rows that do not exist (past M or N, or absent gathered
-// rows) read a zero page. Tiles are placed on XCDs in 2-D blocks (see
-// TileMap) so that each XCD's L2 keeps its band of weight rows.
+// A 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD:
+// wavefront w computes rows 64 (w & 3) .. + 63 and columns 128 (w >> 2) ..
+// + 127 (32 accumulator blocks of 16 x 16). The k axis moves in 32-wide steps
+// through a 4-buffer LDS ring, two steps per barrier: while steps kt and
+// kt + 1 are multiplied, both operand tiles of steps kt + 2 and kt + 3 (256
+// rows x 64 bytes each) stream from HBM straight into LDS with
+// global_load_lds_dwordx4, each wavefront's copies spread between the MFMAs
+// of the first step, so that one wavefront's copy-issue stall is covered by
+// the other wavefront of its SIMD. The 16-byte chunks of a 64-byte row are
+// XOR-ed with (row >> 1) & 3: the LDS serves a 16-byte read 8 lanes (8 rows)
+// at a time, and those rows then hit distinct banks. Rows that do not exist
+// (past M or N, or absent gathered rows) re-read an existing row and are not
+// stored. Tiles are placed on XCDs in 2-D blocks (see TileMap) so that each
+// XCD's L2 keeps its band of weight rows.
 #include <algorithm>
 
 #include "common.h"
@@ -19,13 +23,15 @@ namespace mla {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int ROWCH = BK / 8;                    // 16-byte chunks per tile row
-constexpr int TILE_SLOTS = 256 * ROWCH;          // per operand
-constexpr int DMA_PER_WAVE = TILE_SLOTS / 256;   // per operand per wave per k step
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int ROWCH = BK / 8;                    // 16-byte chunks per 64-byte tile row
+constexpr int SLOTS = 256 * ROWCH;               // 16-byte slots per operand tile (16 KB)
+constexpr int NBUF = 4;                          // ring buffers (two steps multiplied, two copied)
+constexpr int NWAVE = 8;
+constexpr int DPW = SLOTS / (NWAVE * 64);        // copies per wavefront per operand per step
+static_assert(DPW == 2, "copy schedule assumes 2 copies per operand and wavefront");
 
-
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ (row & 7)); }
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 3)); }
 
 // Tile placement: the 8 XCDs (workgroup id mod 8) form an xm x xn grid; XCD
 // (xi, xj) owns the block of M-tile band xi and N-tile band xj and walks it
@@ -36,12 +42,10 @@ struct TileMap {
   int mtiles, ntiles, xm, xn;
 };
 
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm) {
-  // operand rings (weight rows, then activation rows); after the k loop the
-  // same 128 KB stage the output tile for coalesced stores
-  __shared__ __attribute__((aligned(16))) bf16x8 lds[4 * TILE_SLOTS];
-  bf16x8 (*tw)[TILE_SLOTS] = reinterpret_cast<bf16x8(*)[TILE_SLOTS]>(&lds[0]);
-  bf16x8 (*ta)[TILE_SLOTS] = reinterpret_cast<bf16x8(*)[TILE_SLOTS]>(&lds[2 * TILE_SLOTS]);
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, TileMap tm) {
+  // operand ring (buffer i: weight rows, then activation rows); after the k
+  // loop the same 128 KB stage the output tile for coalesced stores
+  __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS];
   __shared__ float rowscale[BM];
   __shared__ int rowok[BM];  // output row exists (inside M, gathered row present)
 
@@ -57,22 +61,21 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   const int lr = lane & 15, g4 = lane >> 4;
   const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
 
-  // per-lane DMA geometry (k-independent): slot s of a tile holds chunk
-  // (row, c); its source is byte offset row_base + 16 c of the operand, the
-  // base (advanced by k) sitting in scalar registers. Rows that do not exist
-  // are clamped to an existing row: their products are never stored. Offsets
-  // fit 32 bits (host check).
-  uint32_t woff[DMA_PER_WAVE], aoff[DMA_PER_WAVE];
+  // per-lane copy geometry (k-independent): slot s = (j * 8 + wave) * 64 +
+  // lane of a tile holds chunk (row s / 4, c), its source at byte offset
+  // row_base + 16 (c ^ ((row >> 1) & 3)), the base (advanced by k) in scalar
+  // registers. Offsets fit 32 bits (host check).
+  uint32_t woff[DPW], aoff[DPW];
 #pragma unroll
-  for (int j = 0; j < DMA_PER_WAVE; ++j) {
-    const int s = (j * 4 + wave) * 64 + lane;
+  for (int j = 0; j < DPW; ++j) {
+    const int s = (j * NWAVE + wave) * 64 + lane;
     const int row = s / ROWCH, cs = s % ROWCH;
-    const uint32_t colb = (uint32_t)(cs ^ (row & 7)) * 16u;
+    const uint32_t colb = (uint32_t)(cs ^ ((row >> 1) & 3)) * 16u;
     const int n = min(n0 + row, g.N - 1);
     woff[j] = (uint32_t)((int64_t)n * g.ldw * 2) + colb;
     const int m = min(m0 + row, g.M - 1);
@@ -93,8 +96,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
     aoff[j] = (uint32_t)(off * 2) + colb;
   }
 
-  {
-    const int m = m0 + tid;  // 256 threads, one output row each
+  if (tid < BM) {
+    const int m = m0 + tid;  // one output row per thread
     bool ok = m < g.M;
     if (ok && g.gather) {
       const GatherA& ga = g.ga;
@@ -106,96 +109,97 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
     }
     rowok[tid] = ok;
   }
-  const uint32_t tw_lds = lds_addr(&tw[0][0]), ta_lds = lds_addr(&ta[0][0]);
-  auto issue = [&](int kt, int buf) {
-    const bf16* wb = W + kt * BK;
-    const bf16* ab = A + kt * BK;
-    const uint32_t bo = (uint32_t)buf * TILE_SLOTS * 16u;
-#pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) dma16_sbase(woff[j], wb, tw_lds + bo + (uint32_t)(j * 4 + wave) * 1024u);
-#pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) dma16_sbase(aoff[j], ab, ta_lds + bo + (uint32_t)(j * 4 + wave) * 1024u);
+  const uint32_t lds0 = lds_addr(&lds[0]);
+  // copy q (0, 1: weight rows; 2, 3: activation rows) of step kt into its buffer
+  auto copy = [&](int kt, int q) {
+    const uint32_t dst = lds0 + (uint32_t)((kt % NBUF) * 2 * SLOTS + (q >> 1) * SLOTS) * 16u +
+                         (uint32_t)(((q & 1) * NWAVE + wave) * 1024);
+    if (q < 2) dma16_sbase(woff[q & 1], W + kt * BK, dst);
+    else dma16_sbase(aoff[q & 1], A + kt * BK, dst);
   };
 
-  floatx4 acc[8][8];  // [n block][m block]
+  floatx4 acc[8][4];  // [n block][m block]: C[m 64 wm + 16 y + lr][n 128 wn + 16 x + 4 g4 + i]
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int x = 0; x < 8; ++x)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float sq[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) sq[b] = 0.f;
+    for (int y = 0; y < 4; ++y) acc[x][y] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float sq[4] = {0.f, 0.f, 0.f, 0.f};
   // the RMSNorm row statistic: only the wavefronts that publish it (wn == 0)
   const bool rownorm = g.epi == EPI_ROWNORM;
   const bool rowstat = rownorm && wn == 0;
+  const int NK = g.K / BK;
 
-  auto compute = [&](const bf16x8* TW, const bf16x8* TA) {
+  // one k step: fragments from buffer kt % NBUF; with `copies`, the copies of
+  // steps kt + 2 and kt + 3 spread over its 32 MFMAs (one per 4)
+  auto step = [&](int kt, bool copies) {
+    const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
+    const bf16x8* TA = TW + SLOTS;
+    Frag<bf16> af[4], wf[8];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      Frag<bf16> wf[8], af[8];
+    for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wm * 64 + y * 16 + lr, g4)];
 #pragma unroll
-      for (int a = 0; a < 8; ++a) wf[a].v = TW[swz(wn * 128 + a * 16 + lr, ks * 4 + g4)];
+    for (int x = 0; x < 8; ++x) wf[x].v = TW[swz(wn * 128 + x * 16 + lr, g4)];
+    const bool c0 = copies && kt + 2 < NK, c1 = copies && kt + 3 < NK;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) af[b].v = TA[swz(wm * 128 + b * 16 + lr, ks * 4 + g4)];
-      if (rowstat) {
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (x < 4 ? c0 : c1) copy(x < 4 ? kt + 2 : kt + 3, x & 3);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
+      for (int y = 0; y < 4; ++y) acc[x][y] = mfma16(wf[x], af[y], acc[x][y]);
+    }
+    if (rowstat) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float f = (float)af[b].v[e];
-            sq[b] += f * f;
-          }
-      }
+      for (int y = 0; y < 4; ++y)
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = mfma16(wf[a], af[b], acc[a][b]);
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)af[y].v[e];
+          sq[y] += f * f;
+        }
     }
   };
 
-  // double buffer: step t+1 streams in while step t is multiplied
-  const int nk = g.K / BK;
-  issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      issue(kt + 1, buf ^ 1);
-      MLA_WAIT_VMCNT(2 * DMA_PER_WAVE);
-    } else {
-      MLA_WAIT_VMCNT(0);
-    }
-    lds_barrier();
-    compute(tw[buf], ta[buf]);
-    lds_barrier();
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) copy(kt, q);
+  for (int kt = 0; kt < NK; kt += 2) {
+    // this wavefront's copies of steps kt, kt + 1 (issued during step kt - 2)
+    // are done; no newer ones exist yet
+    MLA_WAIT_VMCNT(0);
+    lds_barrier();  // every wavefront's copies of kt, kt + 1 landed; kt - 2, kt - 1 read by all
+    step(kt, true);
+    step(kt + 1, false);
   }
+  lds_barrier();  // the ring is read by all before it stages the output
 
   if (rownorm) {
     // lanes lr, lr+16, lr+32, lr+48 hold disjoint k chunks of the same rows;
-    // waves wn = 0 and 1 both saw every row of their wm half: wave wn = 0 writes
+    // wavefronts wn = 0 and 1 both saw every row of their wm band: wn = 0 writes
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      float s = sq[b];
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      if (wn == 0 && g4 == 0) rowscale[wm * 128 + b * 16 + lr] = rsqrtf(s / (float)g.K + g.eps);
+    for (int y = 0; y < 4; ++y) {
+      float t = sq[y];
+      t += __shfl_xor(t, 16);
+      t += __shfl_xor(t, 32);
+      if (wn == 0 && g4 == 0) rowscale[wm * 64 + y * 16 + lr] = rsqrtf(t / (float)g.K + g.eps);
     }
     __syncthreads();
   }
 
   // epilogue, staged through LDS: lane holds C[m][n .. n + 3] for
-  // m = 128 wm + 16 b + lr, n = 128 wn + 16 a + 4 g4 (tile-local). The bf16
+  // m = 64 wm + 16 y + lr, n = 128 wn + 16 x + 4 g4 (tile-local). The bf16
   // tile is written as 256 rows of 32 16-byte chunks, chunk c of row r at
   // position c ^ (r & 31) (the 16 rows of one write land on distinct chunks),
   // then stored to C with 16 contiguous bytes per lane, 512 bytes per row.
   char* cst = reinterpret_cast<char*>(&lds[0]);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int ml = wm * 128 + b * 16 + lr;
+  for (int y = 0; y < 4; ++y) {
+    const int ml = wm * 64 + y * 16 + lr;
     const float rs = rownorm ? rowscale[ml] : 1.f;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const floatx4 v = acc[a][b] * rs;
-      const int c = wn * 16 + a * 2 + (g4 >> 1);
+    for (int x = 0; x < 8; ++x) {
+      const floatx4 v = acc[x][y] * rs;
+      const int c = wn * 16 + x * 2 + (g4 >> 1);
       *reinterpret_cast<bf16x4*>(cst + (ml * 32 + (c ^ (ml & 31))) * 16 + (g4 & 1) * 8) =
           bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
     }
@@ -206,8 +210,8 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
   const int c = tid & 31;
   const int n = n0 + c * 8;
 #pragma unroll 4
-  for (int it = 0; it < BM / 8; ++it) {
-    const int ml = it * 8 + (tid >> 5);
+  for (int it = 0; it < BM / 16; ++it) {
+    const int ml = it * 16 + (tid >> 5);
     const int m = m0 + ml;
     if (!rowok[ml] || n >= g.N) continue;
     bf16x8 v = *reinterpret_cast<const bf16x8*>(cst + (ml * 32 + (c ^ (ml & 31))) * 16);
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(GemmArgs g, TileMap tm
 }  // namespace
 
 bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) {
-  if (!is_bf16 || g.batch != 1 || g.K % BK != 0 || g.M < 512 || g.N < 256) return false;
+  if (!is_bf16 || g.batch != 1 || g.K % (2 * BK) != 0 || g.M < 512 || g.N < 256) return false;  // two steps per barrier
   // 16-byte output stores (and gate loads)
   if (g.ldc % 8 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
   if (g.epi == EPI_GATE && (g.ldg % 8 || (reinterpret_cast<uintptr_t>(g.G) & 15))) return false;
@@ -267,7 +271,7 @@ hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s) 
     const int nb = (xj + 1) * tm.ntiles / tm.xn - xj * tm.ntiles / tm.xn;
     per = std::max(per, mb * nb);
   }
-  hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8), dim3(256), 0, s, g, tm);
+  hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8), dim3(NWAVE * 64), 0, s, g, tm);
   return hipGetLastError();
 }
 

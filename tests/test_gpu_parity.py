@@ -214,6 +214,15 @@ def test_long_decode_small():
     _run_and_check(w)
 
 
+def test_prefill_big_tiles():
+    """Prefill with enough rows for the 256 x 256 GEMM tiles (900 tokens):
+    partial last N tile of the first projection (2112 columns), the q_a
+    RMSNorm row scale of the q_b GEMM, gathered expansion rows with a ragged
+    last M tile, causal attention."""
+    w = ms.make_workload("prefill_bf16", q_lens=[600, 300], prefix_lens=[0, 37], seed=46)
+    _run_and_check(w)
+
+
 def test_prefill_chunked_sliding():
     """Causal prefill of a chunk after a cached prefix under a sliding window."""
     w = ms.make_workload("prefill_bf16", q_lens=[77, 200], prefix_lens=[300, 5], mask_kind=ms.MASK_SLIDING,
