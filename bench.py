@@ -341,8 +341,17 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
     el = time.perf_counter() - t0
     work = stage_work(w, seqs=done, absorbed=absorbed, topk=topk)  # counted like the GPU line
     per, unit = step_value(w, work)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"})
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": per / el, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "blas": ", ".join(blas),
             "sample": f"{len(done)} of {w.batch} sequences (ids {sorted(done)}), "
                       f"{'absorbed' if topk is not None else 'expanded'} fp64 oracle, "
                       f"{el:.1f} s wall", "wall_s": round(el, 3)}
@@ -358,6 +367,9 @@ def main():
     ap.add_argument("--workload", default="draft_block_bf16", choices=sorted(DESCR))
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass (no roofline)")
+    ap.add_argument("--flushed-steps", type=int, default=10,
+                    help="decode workloads: calls timed one by one after writing 512 MiB (evicts the 256 MB "
+                         "Infinity Cache); reported as mall_flushed, 0 = skip")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="first run a plain elementwise copy of MIB MiB three times (HBM counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -446,6 +458,22 @@ def main():
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
     ms_step = total_ms / args.steps
+    # decode: calls timed one by one, each after a 512 MiB write that evicts
+    # the Infinity Cache (the back-to-back figure above is the headline)
+    flushed = None
+    if w.mode == "decode" and args.flushed_steps > 0:
+        scratch = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(args.flushed_steps):
+            scratch.fill_(1.0)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        flushed = {"ms_per_step_median": round(float(np.median(times)), 5), "steps": len(times), "flush_mib": 512}
     # then a separate pass of the same steps with the library's stage events
     # (HIP events on its own stream) for the per-kernel times of the roofline
     stages = {}
@@ -498,6 +526,10 @@ def main():
     }
     if not prefill:
         res["whole_call_gbps"] = round(work["_step"]["bytes"] / (ms_step / 1e3) / 1e9, 2)
+    if flushed is not None:
+        flushed["value"] = round(per_step / (flushed["ms_per_step_median"] / 1e3), 3)
+        flushed["unit"] = unit
+        res["mall_flushed"] = flushed
     m.close()
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block, topk=topk)
