@@ -30,6 +30,48 @@ def _f64(a) -> np.ndarray:
 # building blocks
 # ---------------------------------------------------------------------------
 
+# 8-bit cache entries. The MLA blog's MLAAttention.forward listing computes
+# dynamic q/k/v scales for an FP8 KV cache, and its cache-shape listings name
+# a packed 656-byte fp8 format without specifying its packing; the plain
+# reading taken here: each of the 576 values of an entry is one OCP E4M3
+# ("fn": no infinities, one NaN per sign) code of value / scale, with one
+# scale per cache tensor.
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 code: sign bit 7, exponent bits 6..3 (bias 7),
+    mantissa bits 2..0; exponent 0 encodes m/8 * 2^-6, others
+    (1 + m/8) * 2^(e-7); codes 0x7F / 0xFF are NaN."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, s * mag)
+
+
+_FP8_POS = fp8_e4m3_decode(np.arange(0x7F))  # the 127 finite non-negative values, increasing
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of v (a tie goes to the code with an even mantissa),
+    saturating to +-448; the sign of zero is kept."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), FP8_E4M3_MAX)
+    hi = np.clip(np.searchsorted(_FP8_POS, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _FP8_POS[lo], _FP8_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize(x, scale: float) -> np.ndarray:
+    """The value an 8-bit cache holds for x: decode(encode(x / scale)) * scale."""
+    return fp8_e4m3_decode(fp8_e4m3_encode(_f64(x) / scale)) * scale
+
+
 def rms_norm(x, gamma, eps: float) -> np.ndarray:
     """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * gamma.
 
@@ -222,7 +264,7 @@ def listed_keys(key_list, L: int) -> np.ndarray:
 def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
                      rows: Optional[Sequence[int]] = None, row_lo=None, row_hi=None,
                      form: str = "expanded", softmax_scale: Optional[float] = None,
-                     first_position: int = 0, key_lists=None):
+                     first_position: int = 0, key_lists=None, kv_scale: Optional[float] = None):
     """One sequence: S new tokens at logical positions P..P+S-1 after P cached
     prefix entries. The new entries are appended to the cache before attention,
     so each query sees its own entry (MLAAttention.forward listing: cache update
@@ -239,6 +281,9 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     runs every token in the MQA form over its selected entries (MLA blog,
     MLAAttention.forward listing, the sparse branch); the result is the same
     attention restricted to those keys, evaluated here in the given form.
+    kv_scale: an 8-bit cache with this scale (fp8_quantize): the given prefix
+    rows are the values it holds, the new entries are stored (and returned)
+    quantized, and attention reads the stored values.
     Returns (out [len(rows), hidden], new entries [S, E], attn [len(rows), H*dv])."""
     x = _f64(x)
     prefix_rows = _f64(prefix_rows).reshape(-1, dims.kv_lora_rank + dims.qk_rope_head_dim)
@@ -249,6 +294,8 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(dims.qk_nope_head_dim + dims.qk_rope_head_dim)
     positions = f0 + P + np.arange(S)
     q, new_entries, gate = project_tokens(dims, W, x, positions)
+    if kv_scale is not None:
+        new_entries = fp8_quantize(new_entries, kv_scale)
     entries = np.concatenate([prefix_rows, new_entries], axis=0)
     sel = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     if row_lo is not None:
@@ -294,7 +341,7 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                 window: int = 0, row_lo=None, row_hi=None, form: str = "expanded",
                 seqs: Optional[Sequence[int]] = None, rows_per_seq: Optional[dict] = None,
                 softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None,
-                key_lists: Optional[dict] = None):
+                key_lists: Optional[dict] = None, kv_scale: Optional[float] = None):
     """A batch of sequences packed along the token axis (x is [sum q_lens, hidden]).
 
     seqs: the sequences to evaluate (default all); rows_per_seq: optional
@@ -315,7 +362,7 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                                   rows=rows, row_lo=lo, row_hi=hi, form=form,
                                   softmax_scale=softmax_scale,
                                   first_position=0 if first_positions is None else first_positions.get(b, 0),
-                                  key_lists=None if key_lists is None else key_lists.get(b))
+                                  key_lists=None if key_lists is None else key_lists.get(b), kv_scale=kv_scale)
     return res
 
 

@@ -309,3 +309,69 @@ def pin_sparse(w):
     # the absorbed form over the same lists
     ab = om.forward_sequence(dims, W, x, pre, om.MASK_FULL, key_lists=lists, form="absorbed")
     assert np.max(np.abs(ab[0] - base[0])) <= 1e-12 * max(1.0, np.abs(base[0]).max())
+
+
+def pin_fp8_e4m3():
+    """The 8-bit cache format against its definition (OCP E4M3 "fn") and an
+    independent implementation of it (torch's float8_e4m3fn cast): closed
+    forms of named codes, every finite code decodes and re-encodes to itself,
+    ties between neighbouring codes go to the even mantissa, values beyond
+    the largest finite value saturate."""
+    dec, enc = om.fp8_e4m3_decode, om.fp8_e4m3_encode
+    named = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x3F: 1.875, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for code, value in named.items():
+        assert dec(code) == value, (hex(code), dec(code), value)
+    assert np.isnan(dec(0x7F)) and np.isnan(dec(0xFF))
+    codes = np.arange(256)
+    vals = dec(codes)
+    fin = ~np.isnan(vals)
+    assert np.all(enc(vals[fin]) == codes[fin])
+    pos = np.sort(vals[fin & (vals > 0)])
+    assert pos[0] == 2.0 ** -9 and pos[-1] == 448.0 and np.all(np.diff(pos) > 0) and len(pos) == 126
+    # the same codes as torch's cast: random values and every midpoint (a tie)
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.standard_normal(2000) * 0.01,
+                        (pos[1:] + pos[:-1]) / 2, -(pos[1:] + pos[:-1]) / 2]).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(enc(x.astype(np.float64)), ref)
+    mids = (pos[1:] + pos[:-1]) / 2
+    got = enc(mids)
+    assert np.all(dec(got) % 1 == dec(got) % 1)  # finite
+    assert np.all((got & 1) == 0), "a tie goes to the even mantissa"
+    assert enc(1e4) == 0x7E and enc(-1e4) == 0xFE and enc(448.0 + 15.9) == 0x7E
+    # quantize: idempotent, scale-covariant for power-of-two scales
+    y = rng.standard_normal(1000) * 3
+    q = om.fp8_quantize(y, 0.0625)
+    assert np.array_equal(om.fp8_quantize(q, 0.0625), q)
+    assert np.array_equal(om.fp8_quantize(y * 2, 0.125), q * 2)
+    assert np.max(np.abs(q - y) / np.maximum(np.abs(y), 2.0 ** -6 * 0.0625)) <= 2.0 ** -4 + 1e-12
+
+
+def pin_fp8_cache(w, kv_scale: float):
+    """Forward with an 8-bit cache: the new entries are stored as the codes an
+    independent E4M3 implementation (torch's float8_e4m3fn cast) gives for
+    entry / scale, and attention reads the stored values: the last query's
+    output equals a one-token run whose prefix holds all stored entries
+    before it."""
+    d, W = w.dims, w.weights
+    x = w.x
+    pre = torch.from_numpy((np.asarray(w.prefix_rows[0], np.float32) / kv_scale).clip(-448, 448)).to(
+        torch.float8_e4m3fn).to(torch.float64).numpy() * kv_scale
+    out, ent, attn = om.forward_sequence(d, W, x, pre, w.mask_kind, w.window, kv_scale=kv_scale)
+    _, ent_plain, _ = om.forward_sequence(d, W, x, pre, w.mask_kind, w.window)
+    # torch's cast rounds the fp32 value: compare where the fp64 value is not
+    # within fp32 rounding of a tie between two codes
+    v = ent_plain / kv_scale
+    expect = torch.from_numpy(v.clip(-448, 448)).to(torch.float8_e4m3fn).to(torch.float64).numpy() * kv_scale
+    pos = np.sort(om.fp8_e4m3_decode(np.arange(1, 0x7F)))
+    mids = np.concatenate([[2.0 ** -10], (pos[1:] + pos[:-1]) / 2])
+    near_tie = np.min(np.abs(np.abs(v)[..., None] - mids), axis=-1) <= 1e-6 * np.maximum(np.abs(v), 1.0)
+    assert np.array_equal(ent[~near_tie], expect[~near_tie]), "new entries are not stored as 8-bit values"
+    S = x.shape[0]
+    if w.mask_kind != om.MASK_SLIDING and S > 1:
+        pre2 = np.concatenate([pre, ent[:-1]], axis=0)
+        out2, ent2, _ = om.forward_sequence(d, W, x[-1:], pre2, w.mask_kind, w.window, kv_scale=kv_scale)
+        assert np.array_equal(ent2[0], ent[-1])
+        assert np.max(np.abs(out2[0] - out[-1])) <= 1e-12 * max(1.0, np.abs(out[-1]).max())

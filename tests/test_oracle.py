@@ -215,3 +215,38 @@ def test_mutation_sparse_range_filter(monkeypatch):
     monkeypatch.setattr(om, "listed_keys",
                         lambda key_list, L: (lambda i: i[(i >= 0) & (i <= L)] % L)(np.asarray(key_list).reshape(-1)))
     _expect_fail(P.pin_sparse, _tiny())
+
+
+def test_fp8_e4m3():
+    P.pin_fp8_e4m3()
+
+
+@pytest.mark.parametrize("variant", [dict(), dict(q_lora_rank=12, use_output_gate=True)])
+def test_fp8_cache(variant):
+    P.pin_fp8_cache(_tiny(**variant), 0.0625)
+
+
+def test_mutation_fp8_round_half_up(monkeypatch):
+    # rounding ties away from zero instead of to the even code
+    def enc(v):
+        v = np.asarray(v, dtype=np.float64)
+        a = np.minimum(np.abs(v), om.FP8_E4M3_MAX)
+        hi = np.clip(np.searchsorted(om._FP8_POS, a, side="left"), 0, 0x7E)
+        lo = np.maximum(hi - 1, 0)
+        code = np.where(om._FP8_POS[hi] - a <= a - om._FP8_POS[lo], hi, lo)
+        return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+    monkeypatch.setattr(om, "fp8_e4m3_encode", enc)
+    _expect_fail(P.pin_fp8_e4m3)
+
+
+def test_mutation_fp8_new_entries_unquantized(monkeypatch):
+    # attending to (and storing) the new entries at full precision
+    monkeypatch.setattr(om, "fp8_quantize", lambda x, s: np.asarray(x, np.float64))
+    _expect_fail(P.pin_fp8_cache, _tiny(), 0.0625)
+
+
+def test_mutation_fp8_scale_inverted(monkeypatch):
+    # multiplying by the scale where the definition divides
+    monkeypatch.setattr(om, "fp8_quantize",
+                        lambda x, s: om.fp8_e4m3_decode(om.fp8_e4m3_encode(np.asarray(x, np.float64) * s)) / s)
+    _expect_fail(P.pin_fp8_cache, _tiny(), 0.0625)
