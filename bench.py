@@ -55,10 +55,15 @@ DESCR = {
 DESCR["sparse_decode_bf16"] = ("the decode workload (64 sequences, cache length uniform in [1024, 8192], 128 heads, "
                                "q_lora 1536) through mla_decode_absorbed_sparse: each query attends 2048 listed "
                                "positions (distinct, uniform over its sequence; all of a shorter sequence)")
+DESCR["decode_fp8"] = ("the decode workload (64 sequences, cache length uniform in [1024, 8192], 128 heads, "
+                       "q_lora 1536) over an 8-bit latent cache: OCP E4M3 codes with one per-tensor scale "
+                       "(2^-5), 576 bytes per entry")
 # workloads that run another workload's data through mla_decode_absorbed_block
 BLOCK_OF = {"draft_block_absorbed_bf16": "draft_block_bf16"}
 # workloads that run a decode workload through mla_decode_absorbed_sparse: (base, list length)
 SPARSE_OF = {"sparse_decode_bf16": ("decode_bf16", 2048)}
+# workloads that store another workload's cache as 8-bit codes: (base, scale)
+FP8_OF = {"decode_fp8": ("decode_bf16", 2.0 ** -5)}
 
 
 def listed_keys(w, topk):
@@ -103,6 +108,7 @@ def stage_work(w, seqs=None, absorbed=False, topk=None):
     H, n, r, c, dv, hid, ql = (d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank,
                               d.v_head_dim, d.hidden_size, d.q_lora_rank)
     E = c + r
+    cesz = 1 if getattr(w, "kv_scale", 0.0) > 0 else esz  # bytes per cached value (8-bit cache: one)
     sel = np.arange(w.batch) if seqs is None else np.asarray(seqs)
     T = int(w.q_lens[sel].sum())
     kv = int(w.kv_lens[sel].sum())
@@ -129,12 +135,12 @@ def stage_work(w, seqs=None, absorbed=False, topk=None):
         work["wuk_absorb"] = dict(flops=2 * T * H * n * c, bytes=(H * n * c + T * H * (n + c)) * esz)
         # bytes: the cache entries each sequence's queries read (once per
         # sequence: every query of a block sees the same entries)
-        attn_bytes = pairs * E * esz if not absorbed else int(w.kv_lens[sel].sum()) * E * esz
+        attn_bytes = pairs * E * cesz if not absorbed else int(w.kv_lens[sel].sum()) * E * cesz
         work["decode_attn"] = dict(flops=2 * pairs * H * (E + c), bytes=attn_bytes)
         work["wuv_gemm"] = dict(flops=2 * T * H * c * dv, bytes=(H * dv * c + T * H * (c + dv)) * esz)
     parts = [v for k, v in work.items() if k != "expand_attn"]
     work["_step"] = dict(flops=sum(v["flops"] for v in parts),
-                         cache_bytes=pairs * E * esz,
+                         cache_bytes=pairs * E * cesz,
                          bytes=sum((v["bytes"] or 0) for v in parts))
     return work
 
@@ -168,6 +174,7 @@ STAGE_SOURCES = {
     "rope_cache": ["rope_cache.hip", "kernels.h", "common.h"],
     "expand_attn": ["attn_mha_fused.hip", "kernels.h", "common.h"],
     "expand_merge": ["attn_mha_fused.hip", "kernels.h", "common.h"],
+    "kv_dequant": ["mla_api.hip", "kernels.h", "common.h"],
 }
 # kernel that carries a stage (the one whose counters are summarised); a
 # stage whose kernel name also runs other stages of the workload (a GEMM
@@ -177,6 +184,7 @@ STAGE_KERNEL = {
     "decode_attn": "decode_sk_kernel", "decode_merge": "decode_sk_merge_kernel",
     "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
     "rope_cache": "rope_cache_kernel", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
+    "kv_dequant": "kv_shadow_kernel",
 }
 COPY_KERNEL = "elementwise"  # torch's elementwise kernel of the copy calibration
 
@@ -334,7 +342,7 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
                                 form="absorbed", key_lists=[topk[b]])
         else:
             om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
-                                first_position=first.get(b, 0))
+                                first_position=first.get(b, 0), kv_scale=w.kv_scale if w.kv_scale > 0 else None)
         done.append(b)
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -415,7 +423,8 @@ def main():
 
     block = args.workload in BLOCK_OF
     sparse = args.workload in SPARSE_OF
-    w = ms.make_workload(BLOCK_OF.get(args.workload, SPARSE_OF.get(args.workload, (args.workload,))[0]))
+    base = BLOCK_OF.get(args.workload, SPARSE_OF.get(args.workload, FP8_OF.get(args.workload, (args.workload,)))[0])
+    w = ms.make_workload(base, kv_scale=FP8_OF[args.workload][1] if args.workload in FP8_OF else 0.0)
     t = upload(w)
     topk = lists = None
     if sparse:
@@ -427,7 +436,7 @@ def main():
     cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_kv,
                         max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
                         max_block_tokens=w.total_tokens if block else 0,
-                        max_topk=0 if topk is None else topk.shape[1])
+                        max_topk=0 if topk is None else topk.shape[1], kv_scale=w.kv_scale)
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.empty((w.total_tokens, d.hidden_size), dtype=dt, device="cuda")

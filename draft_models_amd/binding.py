@@ -24,7 +24,7 @@ MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_decode_absorbed_block",
            "mla_decode_absorbed_sparse", "mla_free", "mla_last_error",
            "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
-NUM_STAGES = 12
+NUM_STAGES = 13
 
 
 class MLAError(RuntimeError):
@@ -40,7 +40,10 @@ class mla_config(C.Structure):
                 ("rope_theta", C.c_double), ("rms_norm_eps", C.c_double), ("softmax_scale", C.c_double),
                 ("use_output_gate", C.c_int32), ("dtype", C.c_int32), ("page_size", C.c_int32),
                 ("max_batch", C.c_int32), ("max_tokens", C.c_int32), ("max_seq_len", C.c_int32),
-                ("max_prefill_kv", C.c_int32), ("max_block_tokens", C.c_int32), ("max_topk", C.c_int32)]
+                ("max_prefill_kv", C.c_int32), ("max_block_tokens", C.c_int32), ("max_topk", C.c_int32),
+                ("kv_cache_dtype", C.c_int32), ("kv_cache_scale", C.c_float)]
+
+KV_CACHE_COMPUTE, KV_CACHE_FP8_E4M3 = 0, 1
 
 
 WEIGHT_NAMES = ("q_a_proj", "q_a_layernorm", "q_b_proj", "q_proj", "kv_a_proj_with_mqa",
@@ -109,8 +112,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_prefill_kv: int,
-                softmax_scale: float = 0.0, max_block_tokens: int = 0, max_topk: int = 0) -> mla_config:
-    """mla_config from an object with the model-dimension attributes."""
+                softmax_scale: float = 0.0, max_block_tokens: int = 0, max_topk: int = 0,
+                kv_scale: float = 0.0) -> mla_config:
+    """mla_config from an object with the model-dimension attributes; kv_scale
+    > 0 selects the 8-bit (E4M3) cache with that per-tensor scale."""
     return mla_config(
         hidden_size=dims.hidden_size, num_heads=dims.num_heads, q_lora_rank=dims.q_lora_rank,
         kv_lora_rank=dims.kv_lora_rank, qk_nope_head_dim=dims.qk_nope_head_dim,
@@ -119,7 +124,8 @@ def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_
         softmax_scale=softmax_scale, use_output_gate=int(dims.use_output_gate),
         dtype=DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, page_size=dims.page_size,
         max_batch=max_batch, max_tokens=max_tokens, max_seq_len=max_seq_len,
-        max_prefill_kv=max_prefill_kv, max_block_tokens=max_block_tokens, max_topk=max_topk)
+        max_prefill_kv=max_prefill_kv, max_block_tokens=max_block_tokens, max_topk=max_topk,
+        kv_cache_dtype=KV_CACHE_FP8_E4M3 if kv_scale > 0 else KV_CACHE_COMPUTE, kv_cache_scale=float(kv_scale))
 
 
 class MLA:

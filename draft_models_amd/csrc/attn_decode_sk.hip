@@ -55,6 +55,13 @@ static_assert(HB == 8, "the rescale flags of the head blocks are read as one 8-b
 constexpr int ROWB = ECH * 16;      // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane DMA instructions");
+// 8-bit cache: a tile is copied as 36 chunks of 16 codes per row into a
+// staging area, then widened to bf16 into the ring by the wavefront that
+// copied each chunk
+constexpr int ECH8 = 36;
+constexpr int SLOTS8 = KT * ECH8;
+constexpr int DMA_N8 = (SLOTS8 + NT - 1) / NT;
+static_assert(SLOTS8 % 64 == 0 && ECH8 * 16 == ROWB / 2, "8-bit tile: whole 64-lane copy instructions");
 
 // Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ swz(row))
 // of the row (rows are 72 chunks = 1152 bytes, so rows r and r + 2 start on
@@ -125,9 +132,10 @@ template <> struct Blocks<false> {
 
 // GATHER: sparse lists (a.gather_ent), compiled separately so that the
 // contiguous-range kernel carries none of its registers
-template <int NBUF, bool GATHER>
+template <int NBUF, bool GATHER, bool FP8>
 __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16x8 tile[NBUF][SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 stage8[FP8 ? SLOTS8 : 1];  // 8-bit tile being copied
   __shared__ int t_ent[kDecodeMaxTiles];  // first cache entry of the tile, -1: unmapped page
   __shared__ int t_k0[kDecodeMaxTiles];   // key of the tile's row 0
   __shared__ int t_seq[kDecodeMaxTiles];
@@ -249,12 +257,73 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     return e;
   };
 
+  // 8-bit cache: instruction j of this wavefront copies chunks
+  // [(NW j + wave) 64, +64) of the tile (row p / 36, codes 16 (p % 36) ..)
+  const bool last_dma8 = (DMA_N8 - 1) * NW * 64 + wave * 64 < SLOTS8;
+  const uint32_t stage_lds = lds_addr(&stage8[0]);
+  auto issue8 = [&](int ent, int k0, int lo, int hi, int ev) {
+    const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(a.cache);
+    uint32_t z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    const bool inner = !gather && ent >= 0 && k0 >= lo && k0 + KT <= hi;
+#pragma unroll
+    for (int j = 0; j < DMA_N8; ++j) {
+      if (j == DMA_N8 - 1 && !last_dma8) continue;
+      const int pidx = (j * NW + wave) * 64 + lane + (int)z;
+      const int row = pidx / ECH8;
+      const void* src;
+      if (gather) {
+        const int e = __shfl(ev, row);
+        src = e >= 0 ? (const void*)(cache8 + (int64_t)e * (ECH8 * 16) + (pidx - row * ECH8) * 16) : (const void*)a.zeros;
+      } else {
+        const int key = k0 + row;
+        const bool ok = inner || (ent >= 0 && key >= lo && key < hi);
+        src = ok ? (const void*)(cache8 + (int64_t)ent * (ECH8 * 16) + pidx * 16) : (const void*)a.zeros;
+      }
+      dma16_v(src, stage_lds + (uint32_t)(j * NW + wave) * 1024u);
+    }
+  };
+  // widen this wavefront's chunks of the staged 8-bit tile into ring buffer
+  // `buf` (after its copies landed): codes 16 m .. 16 m + 15 of a row are
+  // bf16 chunks 2 m and 2 m + 1 (exact: every E4M3 value is a bf16 value)
+  auto widen8 = [&](int buf) {
+    char* T = reinterpret_cast<char*>(&tile[buf][0]);
+#pragma unroll
+    for (int j = 0; j < DMA_N8; ++j) {
+      if (j == DMA_N8 - 1 && !last_dma8) continue;
+      const int pidx = (j * NW + wave) * 64 + lane;
+      const uint4 w = stage8[pidx];
+      const int row = pidx / ECH8, m = pidx - row * ECH8;
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      bf16x8 o[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q] >> (16 * h), 1.0f, false);
+          o[q >> 1][4 * (q & 1) + 2 * h] = d[0];
+          o[q >> 1][4 * (q & 1) + 2 * h + 1] = d[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = 2 * m + u;
+        const int pos = (c & ~7) | ((c & 7) ^ swz(row));
+        *reinterpret_cast<bf16x8*>(T + row * ROWB + pos * 16) = o[u];
+      }
+    }
+  };
+
   // ev: the gathered entries of tile i (sparse lists only)
   auto issue = [&](int i, int buf, int ev) {
     const int ent = __builtin_amdgcn_readfirstlane(t_ent[i]);
     const int k0 = __builtin_amdgcn_readfirstlane(t_k0[i]);
     const int lo = __builtin_amdgcn_readfirstlane(t_lo[i]);
     const int hi = __builtin_amdgcn_readfirstlane(t_hi[i]);
+    if constexpr (FP8) {
+      issue8(ent, k0, lo, hi, ev);
+      return;
+    }
     const uint32_t dst = tile_lds + (uint32_t)buf * (SLOTS * 16) + (uint32_t)wave * 1024u;
     uint32_t z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -299,7 +368,9 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   const bool hok = sw && hs < a.H;
   const bool sact = sw && wave * 32 < a.H;  // the score wave owns at least one head
   const int nhb = (a.H + 15) >> 4;           // head blocks with at least one head
-  const float sl2 = a.scale * kLog2e;
+  // (an 8-bit cache: the scale of the codes multiplies every score and output)
+  const float kvs = FP8 ? a.kv_scale : 1.f;
+  const float sl2 = a.scale * kLog2e * kvs;
   const int lr = lane & 15, g = (lane >> 4) & 3;
 
   // score operand A (32 keys x 16 dims, step t): lane l reads key l % 32,
@@ -424,6 +495,10 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     // the queries, the tiles in flight and the outputs stored by the previous
     // piece (stores may complete out of order with loads): wait for everything
     MLA_WAIT_VMCNT(0);
+    // (8-bit cache: tile 0 was copied before the loop; later pieces' first
+    // tiles were widened at the end of the previous piece)
+    if constexpr (FP8)
+      if (i == 0) widen8(0);
     // ... for every wavefront; the previous piece's normalisers are no longer read
     lds_barrier();
     m = -INFINITY;
@@ -535,6 +610,8 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         value(RG, rolec, it - 1);
       }
       if (it < iend) wait_tiles(min(NBUF - 3, n - 2 - it));  // tile it + 1 landed
+      if constexpr (FP8)
+        if (it < iend && it + 1 < n) widen8((it + 1) % NBUF);
       // tile it + 1 is in LDS for every wavefront; the probabilities of tile
       // it are shared; tile it - 1 and the probabilities of tile it - 1 are no
       // longer read
@@ -552,7 +629,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         const int hh = 16 * hb + lr;
         if (hh >= a.H) continue;
         const float lv = lbuf[hh];
-        const float inv = lv > 0.f ? 1.f / lv : 0.f;  // no key at all: a zero row
+        const float inv = lv > 0.f ? kvs / lv : 0.f;  // no key at all: a zero row
         bf16* dst = whole ? reinterpret_cast<bf16*>(a.o_lat) + ((int64_t)b * a.H + hh) * a.c
                           : reinterpret_cast<bf16*>(a.part_o) + (slot * a.H + hh) * a.c;
         dst += 4 * g;
@@ -644,6 +721,7 @@ const char* decode_sk_check(const DecodeAttnArgs& a) {
   if (a.seq_div < 1 || a.Hr < 0) return "stream-K decode: bad query-block mapping";
   if (a.gather_ent && (a.gather_k <= 0 || (int64_t)a.batch * a.gather_k >= ((int64_t)1 << 31)))
     return "stream-K decode: sparse lists need 0 < batch * gather_k < 2^31";
+  if (a.kv_fp8 && !(a.kv_scale > 0.f)) return "stream-K decode: the 8-bit cache needs a positive scale";
   if (a.ranges <= 0 || a.ranges % 8 || !a.tstart || !a.part_o || !a.part_lse || !a.zeros)
     return "stream-K decode: ranges (a multiple of 8) and workspaces are required";
   return nullptr;
@@ -659,8 +737,14 @@ int decode_sk_ranges(int batch, int max_visible, int cus) {
 
 hipError_t decode_sk_launch(const DecodeAttnArgs& a, hipStream_t s) {
   if (a.batch <= 0) return hipSuccess;
-  if (a.gather_ent) hipLaunchKernelGGL((decode_sk_kernel<3, true>), dim3(a.ranges), dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL((decode_sk_kernel<3, false>), dim3(a.ranges), dim3(NT), 0, s, a);
+  if (a.kv_fp8) {
+    if (a.gather_ent) hipLaunchKernelGGL((decode_sk_kernel<3, true, true>), dim3(a.ranges), dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((decode_sk_kernel<3, false, true>), dim3(a.ranges), dim3(NT), 0, s, a);
+  } else if (a.gather_ent) {
+    hipLaunchKernelGGL((decode_sk_kernel<3, true, false>), dim3(a.ranges), dim3(NT), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_sk_kernel<3, false, false>), dim3(a.ranges), dim3(NT), 0, s, a);
+  }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   return hipSuccess;
 }

@@ -25,6 +25,9 @@ struct RopeCacheArgs {
   const int32_t* cu_seqlens = nullptr;   // prefill
   const int32_t* prefix_lens = nullptr;  // prefill
   int max_q_len = 0, max_kv_len = 0, max_seq_len = 0, total_tokens = 0;
+  // 8-bit cache (OCP E4M3 codes of value / scale), else the compute dtype
+  int kv_fp8 = 0;
+  float kv_scale_inv = 1.f;
 };
 hipError_t rope_cache_launch(const RopeCacheArgs& a, bool is_bf16, int grid_x, int batch, hipStream_t s);
 
@@ -110,6 +113,9 @@ struct DecodeAttnArgs {
   // of the visible range of its block table
   const int32_t* gather_ent = nullptr;
   int gather_k = 0;
+  // 8-bit cache (stream-K only): entries are 576 OCP E4M3 codes, value = code * kv_scale
+  int kv_fp8 = 0;
+  float kv_scale = 1.f;
 };
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);

@@ -52,6 +52,12 @@ struct mla_ctx {
   float* gemm_ws = nullptr;
   int64_t gemm_ws_elems = 0;
   void* zeros = nullptr;   // 256 zero bytes: source of padding chunks in streamed tiles
+  // 8-bit cache (codes of value / kv_scale): the prefill reads a bf16 copy of
+  // the visible entries, sequence b's page p at block b mbs + p of kv_shadow
+  bool kv_fp8 = false;
+  float kv_scale = 1.f;
+  void* kv_shadow = nullptr;        // [max_prefill_kv + max_batch page, c + r] bf16
+  int32_t* kv_shadow_bt = nullptr;  // [max_batch, ceil(max_seq_len / page)] identity block table
   std::vector<void*> allocs;
   // stage timing (mla_profile_*)
   bool profiling = false;
@@ -117,6 +123,43 @@ __global__ void sparse_entries_kernel(const int32_t* idx, int topk, const int32_
   ent[o] = e;
 }
 
+// bf16 copy of the visible entries of an 8-bit cache (576 codes per entry):
+// grid (mbs pages, batch); page p of sequence b goes to block b mbs + p of the
+// copy, each code decoded (exact in bf16) and multiplied by the cache scale in
+// fp32; entries at or past the sequence's length prefix + q_len, and unmapped
+// pages, are zero. Also writes the copy's identity block table.
+__global__ __launch_bounds__(256) void kv_shadow_kernel(const uint8_t* cache, const int32_t* block_table,
+                                                        int max_blocks, int num_blocks, int page,
+                                                        const int32_t* cu_seqlens, const int32_t* prefix_lens,
+                                                        int mbs, float scale, bf16* shadow, int32_t* shadow_bt) {
+  constexpr int CH = 36;  // 16-code chunks per entry
+  const int p = blockIdx.x, b = blockIdx.y;
+  const int L = prefix_lens[b] + cu_seqlens[b + 1] - cu_seqlens[b];
+  const int blk = block_table[(int64_t)b * max_blocks + p];
+  const bool mapped = blk >= 0 && blk < num_blocks;
+  const int64_t dblk = (int64_t)b * mbs + p;
+  if (threadIdx.x == 0) shadow_bt[dblk] = (int32_t)dblk;
+  for (int i = threadIdx.x; i < page * CH; i += 256) {
+    const int e = i / CH, ch = i % CH;
+    uint4 w = {0u, 0u, 0u, 0u};
+    if (mapped && p * page + e < L) w = *reinterpret_cast<const uint4*>(cache + ((int64_t)blk * page + e) * (CH * 16) + ch * 16);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    bf16x8 o[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q] >> (16 * h), 1.0f, false);
+        o[q >> 1][4 * (q & 1) + 2 * h] = (bf16)((float)d[0] * scale);
+        o[q >> 1][4 * (q & 1) + 2 * h + 1] = (bf16)((float)d[1] * scale);
+      }
+    }
+    bf16x8* dst = reinterpret_cast<bf16x8*>(shadow + ((dblk * page + e) * CH + ch) * 16);
+    dst[0] = o[0];
+    dst[1] = o[1];
+  }
+}
+
 __global__ void wuk_transpose_kernel(const void* wkvb, void* out, int H, int n, int dv, int c, int bf) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)H * c * n;
@@ -171,6 +214,15 @@ int validate_config(const mla_config* c, const mla_weights* w) {
     return fail(MLA_ERR_UNSUPPORTED, "n + r, c + r and c must be multiples of 8");
   if (n + r > 192 || dv > 128 || kc > 512 || kc + r > 576)
     return fail(MLA_ERR_UNSUPPORTED, "head dims above n + r = 192, dv = 128, c = 512, c + r = 576 are not supported");
+  if (c->kv_cache_dtype != MLA_KV_CACHE_COMPUTE && c->kv_cache_dtype != MLA_KV_CACHE_FP8_E4M3)
+    return fail(MLA_ERR_INVALID_ARG, "unknown kv_cache_dtype");
+  if (c->kv_cache_dtype == MLA_KV_CACHE_FP8_E4M3) {
+    if (!(c->kv_cache_scale > 0.f) || !std::isfinite(c->kv_cache_scale))
+      return fail(MLA_ERR_INVALID_ARG, "kv_cache_scale must be > 0 and finite");
+    if (c->dtype != MLA_DTYPE_BF16 || kc != 512 || r != 64 || c->num_heads > 128 || c->page_size % 32)
+      return fail(MLA_ERR_UNSUPPORTED, "the 8-bit cache needs bf16, c = 512, r = 64, <= 128 heads and a page "
+                                       "size that is a multiple of 32");
+  }
   if (!w->kv_a_proj_with_mqa || !w->kv_a_layernorm || !w->kv_b_proj || !w->o_proj)
     return fail(MLA_ERR_INVALID_ARG, "kv_a_proj_with_mqa, kv_a_layernorm, kv_b_proj and o_proj are required");
   if (c->q_lora_rank > 0 && (!w->q_a_proj || !w->q_a_layernorm || !w->q_b_proj))
@@ -188,10 +240,10 @@ int check_mask(int kind, int window) {
 }
 
 enum Stage { ST_QKV_A = 0, ST_Q_B, ST_ROPE_CACHE, ST_KV_B, ST_PREFILL_ATTN, ST_WUK, ST_DECODE_ATTN,
-             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_EXPAND_ATTN, ST_EXPAND_MERGE, ST_COUNT };
+             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_EXPAND_ATTN, ST_EXPAND_MERGE, ST_KV_DEQUANT, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"qkv_a_gemm", "q_b_gemm", "rope_cache", "kv_b_expand", "prefill_attn",
                                      "wuk_absorb", "decode_attn", "decode_merge", "wuv_gemm", "o_proj_gemm",
-                                     "expand_attn", "expand_merge"};
+                                     "expand_attn", "expand_merge", "kv_dequant"};
 
 hipEvent_t pool_event(mla_ctx* ctx) {
   if (!ctx->event_pool.empty()) {
@@ -407,6 +459,16 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   ctx->gemm_ws = static_cast<float*>(p);
   if ((e = dev_alloc(ctx, &ctx->zeros, 256))) return bail(e);
   if (hipMemsetAsync(ctx->zeros, 0, 256, s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "zero page init failed"));
+  ctx->kv_fp8 = cfg->kv_cache_dtype == MLA_KV_CACHE_FP8_E4M3;
+  ctx->kv_scale = ctx->kv_fp8 ? cfg->kv_cache_scale : 1.f;
+  if (ctx->kv_fp8 && cfg->max_prefill_kv > 0) {
+    // per sequence, max_kv_len rounded up to whole pages
+    const int64_t rows = (int64_t)cfg->max_prefill_kv + B * cfg->page_size;
+    const int64_t mbs = (cfg->max_seq_len + cfg->page_size - 1) / cfg->page_size;
+    if ((e = dev_alloc(ctx, &ctx->kv_shadow, (size_t)rows * ctx->E * 2))) return bail(e);
+    if ((e = dev_alloc(ctx, &p, (size_t)B * mbs * sizeof(int32_t)))) return bail(e);
+    ctx->kv_shadow_bt = static_cast<int32_t*>(p);
+  }
 
   if (hipStreamSynchronize(s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "stream synchronize failed"));
   *out = ctx;
@@ -450,6 +512,7 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   rc.H = ctx->H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
   rc.decode = 0; rc.cu_seqlens = cu_seqlens_q; rc.prefix_lens = prefix_lens;
   rc.max_q_len = max_q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = total_tokens;
@@ -458,13 +521,28 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
     HIP_TRY(rope_cache_launch(rc, ctx->bf16, max_q_len, batch, s));
   }
 
+  // an 8-bit cache: the attention reads a bf16 copy of the visible entries
+  const void* acache = kv_cache;
+  const int32_t* abt = block_table;
+  int anb = num_blocks, amb = max_blocks;
+  if (ctx->kv_fp8) {
+    const int mbs = (max_kv_len + c.page_size - 1) / c.page_size;
+    StageTimer st(ctx, s, ST_KV_DEQUANT);
+    hipLaunchKernelGGL(kv_shadow_kernel, dim3(mbs, batch), dim3(256), 0, s, static_cast<const uint8_t*>(kv_cache),
+                       block_table, max_blocks, num_blocks, c.page_size, cu_seqlens_q, prefix_lens, mbs,
+                       ctx->kv_scale, static_cast<bf16*>(ctx->kv_shadow), ctx->kv_shadow_bt);
+    HIP_TRY(hipGetLastError());
+    acache = ctx->kv_shadow; abt = ctx->kv_shadow_bt;
+    anb = batch * mbs; amb = mbs;
+  }
+
   // few new tokens per sequence: the expansion is fused into the attention
   // (the expanded keys and values stay in registers; partial outputs per
   // 256-entry chunk live in the expansion buffer, which this form does not use)
   MhaFusedArgs fa;
   fa.q = q; fa.ldq = ldq; fa.qk_head = ctx->qkh;
-  fa.cache = kv_cache; fa.block_table = block_table;
-  fa.num_blocks = num_blocks; fa.max_blocks = max_blocks; fa.page = c.page_size;
+  fa.cache = acache; fa.block_table = abt;
+  fa.num_blocks = anb; fa.max_blocks = amb; fa.page = c.page_size;
   fa.wkvb = ctx->Wkvb;
   fa.cu_seqlens = cu_seqlens_q; fa.prefix_lens = prefix_lens;
   fa.batch = batch; fa.max_q_len = max_q_len; fa.max_kv_len = max_kv_len; fa.total_tokens = total_tokens;
@@ -508,11 +586,11 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   // expand every visible latent (prefix and new) through kv_b_proj
   GemmArgs gk;
   gk.gather = true;
-  gk.ga.cache = kv_cache; gk.ga.block_table = block_table; gk.ga.cu_seqlens = cu_seqlens_q;
+  gk.ga.cache = acache; gk.ga.block_table = abt; gk.ga.cu_seqlens = cu_seqlens_q;
   gk.ga.prefix_lens = prefix_lens; gk.ga.batch = batch; gk.ga.max_kv_len = max_kv_len;
-  gk.ga.page = c.page_size; gk.ga.max_blocks = max_blocks; gk.ga.num_blocks = num_blocks;
+  gk.ga.page = c.page_size; gk.ga.max_blocks = amb; gk.ga.num_blocks = anb;
   gk.ga.entry = ctx->E; gk.ga.max_q_len = max_q_len;
-  gk.A = kv_cache; gk.lda = ctx->E;
+  gk.A = acache; gk.lda = ctx->E;
   gk.W = ctx->Wkvb; gk.ldw = ctx->c;
   gk.C = ctx->kvexp; gk.ldc = (int64_t)ctx->H * (ctx->n + ctx->dv);
   gk.M = batch * max_kv_len; gk.N = ctx->H * (ctx->n + ctx->dv); gk.K = ctx->c;
@@ -524,8 +602,8 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   PrefillAttnArgs pa;
   pa.q = q; pa.ldq = ldq; pa.qk_head = ctx->qkh;
   pa.kv = ctx->kvexp; pa.ldkv = (int64_t)ctx->H * (ctx->n + ctx->dv);
-  pa.cache = kv_cache; pa.block_table = block_table;
-  pa.num_blocks = num_blocks; pa.max_blocks = max_blocks; pa.page = c.page_size;
+  pa.cache = acache; pa.block_table = abt;
+  pa.num_blocks = anb; pa.max_blocks = amb; pa.page = c.page_size;
   pa.cu_seqlens = cu_seqlens_q; pa.prefix_lens = prefix_lens;
   pa.batch = batch; pa.max_q_len = max_q_len; pa.max_kv_len = max_kv_len; pa.total_tokens = total_tokens;
   pa.H = ctx->H; pa.n = ctx->n; pa.r = ctx->r; pa.c = ctx->c; pa.dv = ctx->dv;
@@ -590,6 +668,7 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
   rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
   rc.decode = 1; rc.seq_lens = seq_lens; rc.max_seq_len = max_seq_len; rc.total_tokens = batch;
   {
     StageTimer st(ctx, s, ST_ROPE_CACHE);
@@ -615,6 +694,7 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
   da.seq_lens = seq_lens; da.max_seq_len = max_seq_len; da.batch = batch;
   da.H = H; da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
   da.scale = ctx->scale;
+  da.kv_fp8 = ctx->kv_fp8; da.kv_scale = ctx->kv_scale;
   da.mask.kind = mask_kind; da.mask.window = window;
   da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
   da.o_lat = ctx->olat;
@@ -646,6 +726,8 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
     }
   } else if (topk_idx) {
     return fail(MLA_ERR_UNSUPPORTED, "sparse lists need the bf16 512 + 64 latent with at most 128 heads");
+  } else if (ctx->kv_fp8) {
+    return fail(MLA_ERR_UNSUPPORTED, "the 8-bit cache decodes at most 1024 sequences per call");
   } else {
     // split-KV sizing from the longest visible range (keys per split a multiple of 32)
     const int groups = (H + 63) / 64;
@@ -756,6 +838,7 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
   rc.decode = 0; rc.cu_seqlens = ctx->blk_cu; rc.prefix_lens = prefix_lens;
   rc.max_q_len = q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = (int)T;
@@ -787,6 +870,7 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   da.H = 128; da.Hr = H; da.seq_div = (int)(V / batch);
   da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
   da.scale = ctx->scale;
+  da.kv_fp8 = ctx->kv_fp8; da.kv_scale = ctx->kv_scale;
   da.mask.kind = MLA_MASK_FULL; da.mask.window = 0;
   da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
   da.o_lat = ctx->olat;

@@ -109,10 +109,29 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
   if (pos / a.page >= a.max_blocks) return;
   const int blk = a.block_table[(int64_t)b * a.max_blocks + pos / a.page];
   if (blk < 0 || blk >= a.num_blocks) return;
-  T* dst = reinterpret_cast<T*>(a.cache) + ((int64_t)blk * a.page + pos % a.page) * (a.c + a.r);
+  const int64_t ent = ((int64_t)blk * a.page + pos % a.page) * (a.c + a.r);
   const T* gamma = reinterpret_cast<const T*>(a.gamma_kv);
-  for (int e = threadIdx.x; e < a.c; e += 256) dst[e] = from_f32<T>(to_f32(kv[e]) * scale * to_f32(gamma[e]));
   const T* kpe = kv + a.c;
+  if (a.kv_fp8) {
+    // 8-bit entry: the E4M3 code of value / scale, rounded to nearest (ties
+    // to the even code) by the hardware conversion, saturated to +-448
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache) + ent;
+    auto code = [&](float v) {
+      const float x = fminf(fmaxf(v * a.kv_scale_inv, -448.f), 448.f);
+      return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+    };
+    for (int e = threadIdx.x; e < a.c; e += 256) dst[e] = code(to_f32(kv[e]) * scale * to_f32(gamma[e]));
+    for (int j = threadIdx.x; j < half; j += 256) {
+      int ia, ib;
+      pair(j, ia, ib);
+      const float xa = to_f32(kpe[ia]), xb = to_f32(kpe[ib]);
+      dst[a.c + ia] = code(xa * cs[j] - xb * sn[j]);
+      dst[a.c + ib] = code(xa * sn[j] + xb * cs[j]);
+    }
+    return;
+  }
+  T* dst = reinterpret_cast<T*>(a.cache) + ent;
+  for (int e = threadIdx.x; e < a.c; e += 256) dst[e] = from_f32<T>(to_f32(kv[e]) * scale * to_f32(gamma[e]));
   for (int j = threadIdx.x; j < half; j += 256) {
     int ia, ib;
     pair(j, ia, ib);

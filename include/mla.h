@@ -74,6 +74,17 @@ typedef enum mla_rope_style { MLA_ROPE_NEOX = 0, MLA_ROPE_INTERLEAVED = 1 } mla_
  * an attention output of exactly zero. */
 typedef enum mla_mask_kind { MLA_MASK_FULL = 0, MLA_MASK_CAUSAL = 1, MLA_MASK_SLIDING = 2 } mla_mask_kind;
 
+/* Cache entry storage. COMPUTE: the entries in the compute dtype (c + r
+ * values of `dtype`). FP8_E4M3: c + r bytes per entry, each the OCP E4M3
+ * ("fn" variant: no infinities, 0x7F/0xFF NaN) code of value / kv_cache_scale,
+ * rounded to nearest with ties to the even code and saturated to +-448; one
+ * scale for the whole cache. The MLA blog's MLAAttention.forward listing
+ * computes dynamic q/k/v scales for an FP8 KV cache and its cache-shape
+ * listings name a packed 656-byte fp8 entry without its packing; this plain
+ * 576-byte entry with a per-tensor scale is the reading taken (the scale is
+ * an input, not computed). */
+typedef enum mla_kv_cache_dtype { MLA_KV_CACHE_COMPUTE = 0, MLA_KV_CACHE_FP8_E4M3 = 1 } mla_kv_cache_dtype;
+
 typedef struct mla_config {
   int32_t hidden_size;
   int32_t num_heads;
@@ -96,6 +107,9 @@ typedef struct mla_config {
   int32_t max_prefill_kv;   /* prefill: batch * max_kv_len rows of expanded K/V; 0 = no prefill */
   int32_t max_block_tokens; /* mla_decode_absorbed_block: batch * q_len new tokens per call; 0 = not used */
   int32_t max_topk;         /* mla_decode_absorbed_sparse: listed keys per query; 0 = not used */
+  int32_t kv_cache_dtype;   /* mla_kv_cache_dtype; FP8_E4M3 needs dtype BF16, c = 512, r = 64 */
+  float kv_cache_scale;     /* FP8_E4M3: value = code * scale (> 0, finite); a power of two keeps the
+                               prefill's bf16 copy of the entries exact */
 } mla_config;
 
 /* Layer weights, device pointers in nn.Linear [out, in] row-major layout with
@@ -252,9 +266,10 @@ MLA_API int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batc
  *                  and the attention over each 256-entry chunk of the cache in
  *                  one kernel (stages 3 and 4 do not run then)
  *  11 expand_merge log-sum-exp merge of those chunks (+ output gate)
+ *  12 kv_dequant   8-bit cache, prefill: bf16 copy of the visible entries
  * A stage may be more than one kernel (a split-K GEMM adds its reduction).
  */
-#define MLA_NUM_STAGES 12
+#define MLA_NUM_STAGES 13
 MLA_API int mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* ms[i]: total elapsed milliseconds of stage i; count[i]: times it ran. Both
  * host arrays of MLA_NUM_STAGES entries (count may be NULL). Synchronises. */

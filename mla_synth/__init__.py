@@ -86,6 +86,10 @@ class Workload:
     window: int = 0
     row_lo: Optional[np.ndarray] = None  # [T] int32 explicit visible interval (prefill)
     row_hi: Optional[np.ndarray] = None
+    # 8-bit cache: scale > 0; prefix_codes are the stored E4M3 codes (uint8)
+    # and prefix_rows the values they hold
+    kv_scale: float = 0.0
+    prefix_codes: Optional[List[np.ndarray]] = None
 
     @property
     def batch(self) -> int:
@@ -200,7 +204,7 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
                   mask_kind: Optional[int] = None, window: Optional[int] = None,
                   gamma_noise: bool = False, dims: Optional[ModelDims] = None,
                   dims_override: Optional[dict] = None, mode: Optional[str] = None,
-                  row_interval: Optional[tuple] = None) -> Workload:
+                  row_interval: Optional[tuple] = None, kv_scale: float = 0.0) -> Workload:
     """Draw one workload. Keyword arguments override the named full-size shape
     (smaller batches and ragged lengths for the parity tests)."""
     d = dims if dims is not None else DIMS[name]
@@ -249,6 +253,17 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
     # 4. latent-prefix rows
     E = d.entry_dim
     prefix_rows = [_draw_normal(rng, (int(p), E), 1.0, d.dtype) for p in pl]
+    prefix_codes = None
+    if kv_scale > 0:
+        # 8-bit cache: the rows stored as E4M3 codes of row / kv_scale by
+        # torch's float8_e4m3fn cast, and the values those codes hold
+        import torch
+        prefix_codes, vals = [], []
+        for rows in prefix_rows:
+            f8 = torch.from_numpy(np.ascontiguousarray(rows / np.float32(kv_scale))).to(torch.float8_e4m3fn)
+            prefix_codes.append(f8.view(torch.uint8).numpy().copy())
+            vals.append((f8.to(torch.float32) * kv_scale).numpy())
+        prefix_rows = vals
 
     # 5. paged cache: a random permutation of physical blocks
     page = d.page_size
@@ -270,7 +285,7 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
     return Workload(name=name, dims=d, mode=mode, seed=seed, weights=weights, x=x,
                     q_lens=ql, prefix_lens=pl, prefix_rows=prefix_rows, block_table=bt,
                     num_blocks=total, mask_kind=mask_kind, window=window,
-                    row_lo=row_lo, row_hi=row_hi)
+                    row_lo=row_lo, row_hi=row_hi, kv_scale=float(kv_scale), prefix_codes=prefix_codes)
 
 
 # seed of the sparse decode workload's lists (decode_bf16 shapes, 2048 per sequence)
@@ -293,10 +308,12 @@ def draw_topk(w: Workload, topk: int, seed: int) -> np.ndarray:
 
 def paged_cache(w: Workload) -> np.ndarray:
     """The paged latent cache [num_blocks, page, entry_dim] holding the prefix
-    rows at their logical positions (other slots zero). float32 values."""
+    rows at their logical positions (other slots zero). float32 values; uint8
+    codes for an 8-bit cache."""
     d = w.dims
-    cache = np.zeros((w.num_blocks, d.page_size, d.entry_dim), dtype=np.float32)
-    for b, rows in enumerate(w.prefix_rows):
+    fp8 = w.kv_scale > 0
+    cache = np.zeros((w.num_blocks, d.page_size, d.entry_dim), dtype=np.uint8 if fp8 else np.float32)
+    for b, rows in enumerate(w.prefix_codes if fp8 else w.prefix_rows):
         for j0 in range(0, rows.shape[0], d.page_size):
             blk = w.block_table[b, j0 // d.page_size]
             n = min(d.page_size, rows.shape[0] - j0)

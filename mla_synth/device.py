@@ -27,7 +27,8 @@ def upload(w: Workload, device="cuda") -> dict:
     t = {
         "weights": {k: to_torch(v, d.dtype, device) for k, v in w.weights.items()},
         "x": to_torch(w.x, d.dtype, device),
-        "cache": to_torch(paged_cache(w), d.dtype, device),
+        "cache": (torch.from_numpy(paged_cache(w)).to(device) if w.kv_scale > 0
+                  else to_torch(paged_cache(w), d.dtype, device)),
         "block_table": i32(w.block_table),
         "cu_seqlens": i32(w.cu_seqlens),
         "prefix_lens": i32(w.prefix_lens),

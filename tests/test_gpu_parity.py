@@ -266,6 +266,54 @@ def test_capacity_above_call():
 
 # ------------------------------------------------ full sizes, sampled checks
 
+# ---------------------------------------------------------------- 8-bit cache
+# E4M3 codes of value / kv_scale; a power-of-two scale keeps every value the
+# cache holds exact in bf16, the decode cases also take one that is not.
+
+def test_fp8_decode_small():
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 65, 700, 333, 64, 31], seed=41, kv_scale=0.0421875)
+    _run_and_check(w)
+
+
+def test_fp8_decode_sliding():
+    """Window edges that are not tile multiples, lengths around tile and page edges."""
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 31, 32, 33, 95, 130, 700], mask_kind=ms.MASK_SLIDING,
+                         window=33, seed=42, kv_scale=2.0 ** -5)
+    _run_and_check(w)
+
+
+def test_fp8_sparse_decode():
+    """Sparse lists over an 8-bit cache: 96 listed keys (three tiles), lists
+    longer than some sequences."""
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 40, 300, 64, 129, 700], seed=43, kv_scale=2.0 ** -5)
+    topk = ms.draw_topk(w, 96, seed=47)
+    out, cache = U.run_gpu(w, topk=topk)
+    U.check(w, out, cache, U.oracle(w, topk=topk))
+
+
+def test_fp8_query_blocks():
+    """Query blocks (mla_decode_absorbed_block) over an 8-bit cache."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 16, 16], prefix_lens=[100, 300, 0], seed=44,
+                         mask_kind=ms.MASK_FULL, kv_scale=2.0 ** -5)
+    out, cache = U.run_gpu(w, block=True)
+    U.check(w, out, cache, U.oracle(w))
+
+
+def test_fp8_prefill_fused():
+    """Draft blocks (fused expansion) reading the bf16 copy of an 8-bit cache,
+    ragged blocks and prefixes, one prefix that is not a page multiple."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 7, 16], prefix_lens=[100, 300, 0], seed=45,
+                         kv_scale=2.0 ** -5)
+    _run_and_check(w)
+
+
+def test_fp8_prefill_expanded():
+    """Long prefills (the kv_b expansion GEMM gathers from the bf16 copy),
+    causal, one with a cached prefix."""
+    w = ms.make_workload("prefill_bf16", q_lens=[300, 129], prefix_lens=[0, 70], seed=46, kv_scale=2.0 ** -4)
+    _run_and_check(w)
+
+
 def test_full_draft_block():
     """8 sequences x 16 fully visible tokens over a 2048-entry latent prefix."""
     w = ms.make_workload("draft_block_bf16")
@@ -294,6 +342,16 @@ def test_full_sparse_decode():
     L = w.kv_lens
     seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 17, 40})
     U.check(w, out, cache, U.oracle(w, seqs=seqs, form="absorbed", topk=topk))
+
+
+def test_full_fp8_decode():
+    """The decode workload (64 sequences of 1024-8192 entries) over an 8-bit
+    cache (scale 2^-5); sampled sequences against the oracle's absorbed form."""
+    w = ms.make_workload("decode_bf16", kv_scale=2.0 ** -5)
+    out, cache = U.run_gpu(w)
+    L = w.kv_lens
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 17, 40})
+    U.check(w, out, cache, U.oracle(w, seqs=seqs, form="absorbed"))
 
 
 def test_full_prefill():
