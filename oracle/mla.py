@@ -67,6 +67,16 @@ def fp8_e4m3_encode(v) -> np.ndarray:
     return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
+def round_bf16(x) -> np.ndarray:
+    """x rounded to fp32 and then to the nearest bfloat16 (ties to even), as
+    fp64 values: the storage of a result accumulated in fp32 and kept in a
+    bf16 buffer."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def fp8_quantize(x, scale: float) -> np.ndarray:
     """The value an 8-bit cache holds for x: decode(encode(x / scale)) * scale."""
     return fp8_e4m3_decode(fp8_e4m3_encode(_f64(x) / scale)) * scale
@@ -185,7 +195,7 @@ def attention_core(q, k, v, lo, hi, scale: float, return_probs: bool = False):
 # the MLA layer
 # ---------------------------------------------------------------------------
 
-def project_tokens(dims, W: Dict[str, np.ndarray], x, positions):
+def project_tokens(dims, W: Dict[str, np.ndarray], x, positions, kv_round_bf16: bool = False):
     """Projections of the new tokens (MLA blog, MultiHeadLatentAttentionWrapper.forward
     and DeepseekV2MLAAttention.__init__ listings).
 
@@ -196,7 +206,10 @@ def project_tokens(dims, W: Dict[str, np.ndarray], x, positions):
 
     Returns q [S, H, n+r], the cache entries [S, E] = [RMSNorm(kv_c) | rope(k_pe)]
     (the layout concat_and_cache_mla writes, do_kv_cache_update listing), and
-    the output-gate value sigma(x W_g^T) [S, H*dv] or None."""
+    the output-gate value sigma(x W_g^T) [S, H*dv] or None.
+    kv_round_bf16: the kv projection output is stored in bf16 before the
+    RMSNorm and RoPE (the precision in which a bf16 kernel decides the codes
+    of an 8-bit cache; see forward_sequence)."""
     x = _f64(x)
     S = x.shape[0]
     H, n, r, c = dims.num_heads, dims.qk_nope_head_dim, dims.qk_rope_head_dim, dims.kv_lora_rank
@@ -209,6 +222,8 @@ def project_tokens(dims, W: Dict[str, np.ndarray], x, positions):
         q = x @ _f64(W["q_proj"]).T
     q = q.reshape(S, H, n + r).copy()
     kv = x @ _f64(W["kv_a_proj_with_mqa"]).T
+    if kv_round_bf16:
+        kv = round_bf16(kv)
     kv_c, k_pe = kv[:, :c], kv[:, c:]
     kv_c_normed = rms_norm(kv_c, W["kv_a_layernorm"], eps)
     q[:, :, n:] = apply_rope(q[:, :, n:], positions, dims.rope_theta, dims.rope_style)
@@ -264,7 +279,8 @@ def listed_keys(key_list, L: int) -> np.ndarray:
 def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
                      rows: Optional[Sequence[int]] = None, row_lo=None, row_hi=None,
                      form: str = "expanded", softmax_scale: Optional[float] = None,
-                     first_position: int = 0, key_lists=None, kv_scale: Optional[float] = None):
+                     first_position: int = 0, key_lists=None, kv_scale: Optional[float] = None,
+                     kv_round_bf16: bool = False):
     """One sequence: S new tokens at logical positions P..P+S-1 after P cached
     prefix entries. The new entries are appended to the cache before attention,
     so each query sees its own entry (MLAAttention.forward listing: cache update
@@ -284,6 +300,10 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     kv_scale: an 8-bit cache with this scale (fp8_quantize): the given prefix
     rows are the values it holds, the new entries are stored (and returned)
     quantized, and attention reads the stored values.
+    kv_round_bf16: the entries are computed from the kv projection output
+    rounded to bf16. Quantizing decides an integer code, so a comparison with
+    a kernel that keeps that output in bf16 takes the decision from the same
+    bf16 value; every other step stays in fp64.
     Returns (out [len(rows), hidden], new entries [S, E], attn [len(rows), H*dv])."""
     x = _f64(x)
     prefix_rows = _f64(prefix_rows).reshape(-1, dims.kv_lora_rank + dims.qk_rope_head_dim)
@@ -293,7 +313,7 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     H, dv = dims.num_heads, dims.v_head_dim
     scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(dims.qk_nope_head_dim + dims.qk_rope_head_dim)
     positions = f0 + P + np.arange(S)
-    q, new_entries, gate = project_tokens(dims, W, x, positions)
+    q, new_entries, gate = project_tokens(dims, W, x, positions, kv_round_bf16=kv_round_bf16)
     if kv_scale is not None:
         new_entries = fp8_quantize(new_entries, kv_scale)
     entries = np.concatenate([prefix_rows, new_entries], axis=0)
@@ -341,7 +361,8 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                 window: int = 0, row_lo=None, row_hi=None, form: str = "expanded",
                 seqs: Optional[Sequence[int]] = None, rows_per_seq: Optional[dict] = None,
                 softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None,
-                key_lists: Optional[dict] = None, kv_scale: Optional[float] = None):
+                key_lists: Optional[dict] = None, kv_scale: Optional[float] = None,
+                kv_round_bf16: bool = False):
     """A batch of sequences packed along the token axis (x is [sum q_lens, hidden]).
 
     seqs: the sequences to evaluate (default all); rows_per_seq: optional
@@ -362,7 +383,8 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                                   rows=rows, row_lo=lo, row_hi=hi, form=form,
                                   softmax_scale=softmax_scale,
                                   first_position=0 if first_positions is None else first_positions.get(b, 0),
-                                  key_lists=None if key_lists is None else key_lists.get(b), kv_scale=kv_scale)
+                                  key_lists=None if key_lists is None else key_lists.get(b), kv_scale=kv_scale,
+                                  kv_round_bf16=kv_round_bf16)
     return res
 
 

@@ -349,6 +349,36 @@ def pin_fp8_e4m3():
     assert np.max(np.abs(q - y) / np.maximum(np.abs(y), 2.0 ** -6 * 0.0625)) <= 2.0 ** -4 + 1e-12
 
 
+def pin_round_bf16():
+    """round_bf16 against torch's float32 -> bfloat16 cast (round to nearest,
+    ties to even), on values over many binades and on exact ties."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(4096) * 10.0 ** rng.integers(-30, 30, 4096)
+    bits = (rng.integers(0, 0x7F000000, 2048, dtype=np.uint64) & ~np.uint64(0xFFFF)) | np.uint64(0x8000)
+    ties = bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    x = np.concatenate([x, ties, -ties, [0.0, 1.0, -2.5]])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(om.round_bf16(x), want)
+
+
+def pin_kv_round_one_hot(w, kv_scale: float):
+    """With one-hot token rows and bf16 weights the kv projection output is a
+    weight column, already bf16: rounding it changes nothing, so the flag
+    acts on that output and nowhere else; with the workload's own tokens the
+    entries move by at most one code step."""
+    d, W = w.dims, w.weights
+    S = w.x.shape[0]
+    x1 = np.zeros_like(w.x)
+    x1[np.arange(S), (7 * np.arange(S)) % d.hidden_size] = 1.0
+    pre = np.zeros((0, d.kv_lora_rank + d.qk_rope_head_dim))
+    a = om.forward_sequence(d, W, x1, pre, w.mask_kind, kv_scale=kv_scale)
+    b = om.forward_sequence(d, W, x1, pre, w.mask_kind, kv_scale=kv_scale, kv_round_bf16=True)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    _, e0, _ = om.forward_sequence(d, W, w.x, pre, w.mask_kind, kv_scale=kv_scale)
+    _, e1, _ = om.forward_sequence(d, W, w.x, pre, w.mask_kind, kv_scale=kv_scale, kv_round_bf16=True)
+    assert np.max(np.abs(e1 - e0) / np.maximum(np.abs(e0), kv_scale)) <= 0.25
+
+
 def pin_fp8_cache(w, kv_scale: float):
     """Forward with an 8-bit cache: the new entries are stored as the codes an
     independent E4M3 implementation (torch's float8_e4m3fn cast) gives for

@@ -221,6 +221,14 @@ def test_fp8_e4m3():
     P.pin_fp8_e4m3()
 
 
+def test_round_bf16():
+    P.pin_round_bf16()
+
+
+def test_kv_round_one_hot():
+    P.pin_kv_round_one_hot(_tiny(dtype="bf16"), 0.0625)
+
+
 @pytest.mark.parametrize("variant", [dict(), dict(q_lora_rank=12, use_output_gate=True)])
 def test_fp8_cache(variant):
     P.pin_fp8_cache(_tiny(**variant), 0.0625)
