@@ -186,7 +186,7 @@ STAGE_KERNEL = {
     "rope_cache": "rope_cache_kernel", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
     "kv_dequant": "kv_shadow_kernel",
 }
-COPY_KERNEL = "elementwise"  # torch's elementwise kernel of the copy calibration
+COPY_KERNEL = "neg_kernel"  # torch's elementwise negation kernel of the copy calibration (not the flush fill)
 
 
 def _pmc_rows(d):

@@ -71,12 +71,17 @@ def _write_pmc(d, rows):
 def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
     # the copy of 256 MiB reads 96 MiB of FETCH_SIZE and 256 MiB of WRITE_SIZE
     fetch, write = str(tmp_path / "f"), str(tmp_path / "w")
-    copy = "void at::native::elementwise_kernel<128, 4>(int)"
+    # (the 512 MiB fill that evicts the Infinity Cache before flushed decode
+    # calls is another elementwise kernel of the same grid: not a copy)
+    copy = "void at::native::vectorized_elementwise_kernel<4, at::native::neg_kernel_cuda(...)>(int)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<float> >(int)"
     k = "void mla::(anonymous namespace)::decode_sk_kernel<3>(mla::DecodeAttnArgs)"
     _write_pmc(fetch, [(1, 67108864, copy, "FETCH_SIZE", 96 * 1024, 0, 1),
+                       (4, 67108864, fill, "FETCH_SIZE", 16.0, 0, 1),
                        (2, 131072, k, "FETCH_SIZE", 1000.0, 0, 1),
                        (3, 131072, k, "FETCH_SIZE", 3000.0, 0, 1)])
     _write_pmc(write, [(1, 67108864, copy, "WRITE_SIZE", 256 * 1024, 0, 1),
+                       (4, 67108864, fill, "WRITE_SIZE", 512 * 1024, 0, 1),
                        (2, 131072, k, "WRITE_SIZE", 10.0, 0, 1),
                        (3, 131072, k, "WRITE_SIZE", 30.0, 0, 1)])
     paths = bench.traffic_summary(fetch, write, "unit", 256, ["a", "b"], out_dir=str(tmp_path))
