@@ -2,7 +2,12 @@
 
 Everything is float64 numpy; inputs are the same dtype-rounded values the GPU
 receives, upcast. Nothing here is blocked, fused or reordered beyond the
-definitions below; a matmul is the only library primitive used.
+definitions below; a matmul is the only library primitive used. One option
+leaves fp64: with an 8-bit cache, kv_round_bf16 rounds the kv projection
+output to bf16 before the codes are decided (a code is an integer decision,
+taken from the value a bf16 kernel stores). Every function is pinned by the
+CPU tests (tests/oracle_pins.py), including the E4M3 encode/decode against
+torch's float8_e4m3fn cast and round_bf16 against torch's bfloat16 cast.
 
 Notation (as on the pages): n = qk_nope_head_dim, r = qk_rope_head_dim,
 c = kv_lora_rank, dv = v_head_dim, H = heads, E = c + r (one cache entry).
