@@ -82,7 +82,13 @@ typedef enum mla_mask_kind { MLA_MASK_FULL = 0, MLA_MASK_CAUSAL = 1, MLA_MASK_SL
  * computes dynamic q/k/v scales for an FP8 KV cache and its cache-shape
  * listings name a packed 656-byte fp8 entry without its packing; this plain
  * 576-byte entry with a per-tensor scale is the reading taken (the scale is
- * an input, not computed). */
+ * an input, not computed). With FP8_E4M3, mla_init_weights returns
+ * MLA_ERR_UNSUPPORTED unless dtype is BF16, c = 512, r = 64, num_heads <= 128
+ * and page_size % 32 == 0, and MLA_ERR_INVALID_ARG for a scale that is not
+ * finite and > 0; the decode entry points take at most 1024 sequences per
+ * call (else MLA_ERR_UNSUPPORTED); the prefill reads a library-owned bf16
+ * copy of the visible entries (max_prefill_kv + max_batch * page_size rows,
+ * allocated at init). The caller's cache is c + r bytes per entry. */
 typedef enum mla_kv_cache_dtype { MLA_KV_CACHE_COMPUTE = 0, MLA_KV_CACHE_FP8_E4M3 = 1 } mla_kv_cache_dtype;
 
 typedef struct mla_config {
