@@ -27,7 +27,7 @@ struct RopeCacheArgs {
   int max_q_len = 0, max_kv_len = 0, max_seq_len = 0, total_tokens = 0;
   // 8-bit cache (OCP E4M3 codes of value / scale), else the compute dtype
   int kv_fp8 = 0;
-  float kv_scale_inv = 1.f;
+  float kv_scale = 1.f;
 };
 hipError_t rope_cache_launch(const RopeCacheArgs& a, bool is_bf16, int grid_x, int batch, hipStream_t s);
 

@@ -113,11 +113,14 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
   const T* gamma = reinterpret_cast<const T*>(a.gamma_kv);
   const T* kpe = kv + a.c;
   if (a.kv_fp8) {
-    // 8-bit entry: the E4M3 code of value / scale, rounded to nearest (ties
-    // to the even code) by the hardware conversion, saturated to +-448
+    // 8-bit entry. The wrapper forward hands the cache update bf16 tensors
+    // (kv_c_normed and the roped k_pe of a bf16 model), so each value is
+    // rounded to bf16 first; its code is the E4M3 code of value / scale
+    // (a correctly rounded fp32 division), rounded to nearest with ties to
+    // the even code by the hardware conversion, saturated to +-448.
     uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache) + ent;
     auto code = [&](float v) {
-      const float x = fminf(fmaxf(v * a.kv_scale_inv, -448.f), 448.f);
+      const float x = fminf(fmaxf((float)(bf16)v / a.kv_scale, -448.f), 448.f);
       return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
     };
     for (int e = threadIdx.x; e < a.c; e += 256) dst[e] = code(to_f32(kv[e]) * scale * to_f32(gamma[e]));

@@ -12,7 +12,8 @@ Sources (web pages, cited by title and section):
     Structure) and PR "extract GQA/MLA attention into reusable layers"
     (Modifications, Accuracy Test).
 
-Parity status: every function is pinned by tests/test_oracle_*.py except the
+Parity status: every function is pinned by the CPU tests (tests/oracle_pins.py,
+run by tests/test_oracle.py) except the
 choices the pages leave open (RMSNorm eps value, softmax scale, RoPE theta,
 output-gate form), which are "parity unpinned" conventions shared with the
 library.

@@ -3,11 +3,13 @@
 Everything is float64 numpy; inputs are the same dtype-rounded values the GPU
 receives, upcast. Nothing here is blocked, fused or reordered beyond the
 definitions below; a matmul is the only library primitive used. One option
-leaves fp64: with an 8-bit cache, kv_round_bf16 rounds the kv projection
-output to bf16 before the codes are decided (a code is an integer decision,
-taken from the value a bf16 kernel stores). Every function is pinned by the
-CPU tests (tests/oracle_pins.py), including the E4M3 encode/decode against
-torch's float8_e4m3fn cast and round_bf16 against torch's bfloat16 cast.
+leaves fp64: model_bf16 keeps the three tensors that the MLA blog's wrapper
+forward hands to the cache update as bf16 values (kv_lora, kv_c_normed and
+the roped k_pe of a bf16 model), the precision in which an 8-bit cache's
+codes are decided (a code is an integer decision). Every function is pinned
+by the CPU tests (tests/oracle_pins.py), including the E4M3 encode/decode
+against torch's float8_e4m3fn cast, round_bf16 against torch's bfloat16 cast
+and the model_bf16 entries against a torch construction of them.
 
 Notation (as on the pages): n = qk_nope_head_dim, r = qk_rope_head_dim,
 c = kv_lora_rank, dv = v_head_dim, H = heads, E = c + r (one cache entry).
@@ -200,7 +202,7 @@ def attention_core(q, k, v, lo, hi, scale: float, return_probs: bool = False):
 # the MLA layer
 # ---------------------------------------------------------------------------
 
-def project_tokens(dims, W: Dict[str, np.ndarray], x, positions, kv_round_bf16: bool = False):
+def project_tokens(dims, W: Dict[str, np.ndarray], x, positions, model_bf16: bool = False):
     """Projections of the new tokens (MLA blog, MultiHeadLatentAttentionWrapper.forward
     and DeepseekV2MLAAttention.__init__ listings).
 
@@ -212,9 +214,12 @@ def project_tokens(dims, W: Dict[str, np.ndarray], x, positions, kv_round_bf16: 
     Returns q [S, H, n+r], the cache entries [S, E] = [RMSNorm(kv_c) | rope(k_pe)]
     (the layout concat_and_cache_mla writes, do_kv_cache_update listing), and
     the output-gate value sigma(x W_g^T) [S, H*dv] or None.
-    kv_round_bf16: the kv projection output is stored in bf16 before the
-    RMSNorm and RoPE (the precision in which a bf16 kernel decides the codes
-    of an 8-bit cache; see forward_sequence)."""
+    model_bf16: the layer's activations are bf16 tensors. In the wrapper
+    forward listing the cache entry is built from three of them: kv_lora
+    (the kv projection's output), kv_c_normed (kv_a_layernorm's output) and
+    k_pe after the rotary embedding; each is rounded to bf16 where the
+    listing produces it (round_bf16), the arithmetic in between stays fp64.
+    The query path is not rounded."""
     x = _f64(x)
     S = x.shape[0]
     H, n, r, c = dims.num_heads, dims.qk_nope_head_dim, dims.qk_rope_head_dim, dims.kv_lora_rank
@@ -227,12 +232,14 @@ def project_tokens(dims, W: Dict[str, np.ndarray], x, positions, kv_round_bf16: 
         q = x @ _f64(W["q_proj"]).T
     q = q.reshape(S, H, n + r).copy()
     kv = x @ _f64(W["kv_a_proj_with_mqa"]).T
-    if kv_round_bf16:
+    if model_bf16:
         kv = round_bf16(kv)
     kv_c, k_pe = kv[:, :c], kv[:, c:]
     kv_c_normed = rms_norm(kv_c, W["kv_a_layernorm"], eps)
     q[:, :, n:] = apply_rope(q[:, :, n:], positions, dims.rope_theta, dims.rope_style)
     k_pe = apply_rope(k_pe, positions, dims.rope_theta, dims.rope_style)
+    if model_bf16:
+        kv_c_normed, k_pe = round_bf16(kv_c_normed), round_bf16(k_pe)
     entries = np.concatenate([kv_c_normed, k_pe], axis=1)
     gate = None
     if dims.use_output_gate:
@@ -285,7 +292,7 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
                      rows: Optional[Sequence[int]] = None, row_lo=None, row_hi=None,
                      form: str = "expanded", softmax_scale: Optional[float] = None,
                      first_position: int = 0, key_lists=None, kv_scale: Optional[float] = None,
-                     kv_round_bf16: bool = False):
+                     model_bf16: bool = False):
     """One sequence: S new tokens at logical positions P..P+S-1 after P cached
     prefix entries. The new entries are appended to the cache before attention,
     so each query sees its own entry (MLAAttention.forward listing: cache update
@@ -305,10 +312,9 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     kv_scale: an 8-bit cache with this scale (fp8_quantize): the given prefix
     rows are the values it holds, the new entries are stored (and returned)
     quantized, and attention reads the stored values.
-    kv_round_bf16: the entries are computed from the kv projection output
-    rounded to bf16. Quantizing decides an integer code, so a comparison with
-    a kernel that keeps that output in bf16 takes the decision from the same
-    bf16 value; every other step stays in fp64.
+    model_bf16: the new entries are built from the bf16 tensors of a bf16
+    model (project_tokens). Quantizing decides an integer code, and the cache
+    update listing encodes those bf16 values; every other step stays fp64.
     Returns (out [len(rows), hidden], new entries [S, E], attn [len(rows), H*dv])."""
     x = _f64(x)
     prefix_rows = _f64(prefix_rows).reshape(-1, dims.kv_lora_rank + dims.qk_rope_head_dim)
@@ -318,7 +324,7 @@ def forward_sequence(dims, W, x, prefix_rows, mask_kind: int, window: int = 0,
     H, dv = dims.num_heads, dims.v_head_dim
     scale = softmax_scale if softmax_scale else 1.0 / math.sqrt(dims.qk_nope_head_dim + dims.qk_rope_head_dim)
     positions = f0 + P + np.arange(S)
-    q, new_entries, gate = project_tokens(dims, W, x, positions, kv_round_bf16=kv_round_bf16)
+    q, new_entries, gate = project_tokens(dims, W, x, positions, model_bf16=model_bf16)
     if kv_scale is not None:
         new_entries = fp8_quantize(new_entries, kv_scale)
     entries = np.concatenate([prefix_rows, new_entries], axis=0)
@@ -367,7 +373,7 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                 seqs: Optional[Sequence[int]] = None, rows_per_seq: Optional[dict] = None,
                 softmax_scale: Optional[float] = None, first_positions: Optional[dict] = None,
                 key_lists: Optional[dict] = None, kv_scale: Optional[float] = None,
-                kv_round_bf16: bool = False):
+                model_bf16: bool = False):
     """A batch of sequences packed along the token axis (x is [sum q_lens, hidden]).
 
     seqs: the sequences to evaluate (default all); rows_per_seq: optional
@@ -389,7 +395,7 @@ def mla_forward(dims, W, x, q_lens, prefix_rows: List[np.ndarray], mask_kind: in
                                   softmax_scale=softmax_scale,
                                   first_position=0 if first_positions is None else first_positions.get(b, 0),
                                   key_lists=None if key_lists is None else key_lists.get(b), kv_scale=kv_scale,
-                                  kv_round_bf16=kv_round_bf16)
+                                  model_bf16=model_bf16)
     return res
 
 

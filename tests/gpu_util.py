@@ -75,7 +75,7 @@ def oracle(w: ms.Workload, seqs=None, rows_per_seq=None, form="expanded", first_
                           w.row_lo, w.row_hi, form=form, seqs=seqs, rows_per_seq=rows_per_seq,
                           softmax_scale=softmax_scale, first_positions=first_positions, key_lists=key_lists,
                           kv_scale=w.kv_scale if w.kv_scale > 0 else None,
-                          kv_round_bf16=w.kv_scale > 0 and w.dims.dtype == "bf16")
+                          model_bf16=w.kv_scale > 0 and w.dims.dtype == "bf16")
 
 
 def errors(got, ref):
@@ -108,32 +108,70 @@ def assert_close(got, ref, dtype: str, what: str, magnitude_scaled: bool = False
         assert rel <= tol["rel_l2"], f"{what}: relative L2 error {rel} > {tol['rel_l2']}"
 
 
-def check_codes(got, ref_vals, scale: float):
-    """8-bit cache entries against the oracle's quantized entries (ref_vals,
-    values code * scale). The GPU rounds the kv_a projection output to the
-    compute dtype (bf16) before the RMSNorm and RoPE, a relative change of up
-    to 2^-9 per input: a value then lands on the other side of a code boundary
-    (code steps are 2^-4 to 2^-3 relative) for about 2 % of the entries, and
-    the RoPE rotation, a difference of two products, can move a value near
-    zero by more than one step of its own size. The bar: at most 5 % of the
-    codes differ, and every stored value is within one E4M3 step of the
-    oracle's, |got - ref| <= 2^-3 max(scale, |ref|) (the magnitude-scaled bar
-    of the bf16 cache check with a one-code width)."""
-    got = np.asarray(got, np.uint8)
-    ref_vals = np.asarray(ref_vals, np.float64)
-    ref = np.asarray(om.fp8_e4m3_encode(ref_vals / scale), np.uint8)
+# 8-bit cache codes: differing codes allowed per 10 000 (at least three)
+CODE_DIFF_PER = 10000
+CODE_DIFF_MIN = 3
+# a differing code must be the neighbour across an E4M3 midpoint that lies
+# within this relative distance of the oracle's value (two bf16 steps)
+CODE_TIE_RADIUS = 2.0 ** -6
+
+
+def tie_radius(entries, dims):
+    """Per value of the oracle's bf16 entries [S, E], the size that a bf16
+    rounding of its inputs can move it by, up to CODE_TIE_RADIUS: |value|
+    for the latent, and for a rope value the norm of its rotated pair (a
+    rotation mixes the two inputs, so a change of either moves the result by
+    a step of the pair's size)."""
+    e = np.asarray(entries, np.float64)
+    c, r = dims.kv_lora_rank, dims.qk_rope_head_dim
+    rho = np.abs(e).copy()
+    a, b = om.rope_pairs(r, dims.rope_style)
+    nrm = np.sqrt(e[:, c + a] ** 2 + e[:, c + b] ** 2)
+    rho[:, c + a] = nrm
+    rho[:, c + b] = nrm
+    return rho
+
+
+def check_codes(got, ref_unq, rho, scale: float):
+    """8-bit cache entries against the oracle. ref_unq: the oracle's entries
+    before encoding (the bf16 values of a bf16 model, model_bf16); rho: their
+    tie_radius. The codes the oracle stores are encode(ref_unq / scale). The
+    library computes the same bf16 values in fp32 from a bf16 projection
+    that may sit one bf16 step off the oracle's rounding where the fp64
+    projection is near a bf16 tie, so a code can legitimately differ only
+    where the oracle's value lies near an E4M3 midpoint (a simulation of the
+    fp32 arithmetic on the decode shapes gives about 4 per 100 000). The bar:
+    at most one code per CODE_DIFF_PER differs (CODE_DIFF_MIN at least, for
+    small calls), and each differing
+    code is the neighbour of the oracle's across a midpoint m with
+    |ref_unq - m scale| <= CODE_TIE_RADIUS rho."""
+    got = np.asarray(got, np.uint8).reshape(-1)
+    ref_unq = np.asarray(ref_unq, np.float64).reshape(-1)
+    rho = np.asarray(rho, np.float64).reshape(-1)
+    ref = np.asarray(om.fp8_e4m3_encode(ref_unq / scale), np.uint8)
     diff = got != ref
     n = int(diff.sum())
-    gv = om.fp8_e4m3_decode(got.astype(np.int64)) * scale
-    err = np.abs(gv - ref_vals) / np.maximum(scale, np.abs(ref_vals))
-    worst = float(err.max()) if err.size else 0.0
-    say(f"  cache codes: {n} of {got.size} differ, worst scaled error {worst:.3e}")
-    if n:
-        idx = np.flatnonzero(diff)[:6]
-        say("  first differing codes (index, got, oracle, oracle value / scale): " + ", ".join(
-            f"({i}, {got.flat[i]:#04x}, {ref.flat[i]:#04x}, {ref_vals.flat[i] / scale:.5g})" for i in idx))
-    assert n <= max(2, got.size // 20), f"{n} of {got.size} codes differ"
-    assert worst <= 0.125, f"a stored value is more than one code step from the oracle's ({worst})"
+    say(f"  cache codes: {n} of {got.size} differ")
+    assert n <= max(CODE_DIFF_MIN, got.size // CODE_DIFF_PER), f"{n} of {got.size} codes differ"
+
+    def ordinal(cd):
+        cd = cd.astype(np.int64)
+        mag = cd & 0x7F
+        return np.where(cd & 0x80, -mag, mag)
+    idx = np.flatnonzero(diff)
+    for i in idx:
+        og, orf = int(ordinal(got[i:i + 1])[0]), int(ordinal(ref[i:i + 1])[0])
+        gv = float(om.fp8_e4m3_decode(int(got[i])))
+        rv = float(om.fp8_e4m3_decode(int(ref[i])))
+        say(f"    code {i}: got {got[i]:#04x} ({gv * scale:.6g}) oracle {ref[i]:#04x} ({rv * scale:.6g}), "
+            f"oracle value {ref_unq[i]:.8g}, radius {rho[i]:.4g}")
+        assert not np.isnan(gv), f"code {i} is NaN"
+        if gv == rv:  # +0 / -0
+            continue
+        assert abs(og - orf) == 1, f"code {i} is not the neighbour of the oracle's"
+        mid = (gv + rv) / 2 * scale
+        assert abs(ref_unq[i] - mid) <= CODE_TIE_RADIUS * rho[i], \
+            f"code {i} differs away from a tie: |{ref_unq[i]} - {mid}| > {CODE_TIE_RADIUS} * {rho[i]}"
 
 
 def check(w: ms.Workload, out, cache, res, rows_per_seq=None):
@@ -153,7 +191,16 @@ def check(w: ms.Workload, out, cache, res, rows_per_seq=None):
             want = w.prefix_codes[b] if w.kv_scale > 0 else w.prefix_rows[b]
             assert np.array_equal(kept, want), f"prefix entries of sequence {b} changed"
     if w.kv_scale > 0:
-        check_codes(np.concatenate(got_e), np.concatenate(ref_e), w.kv_scale)
+        # the oracle's entries before encoding: the bf16 tensors the cache
+        # update receives (new tokens depend only on x and the weights)
+        unq = []
+        for b in res:
+            P, S = int(w.prefix_lens[b]), int(w.q_lens[b])
+            unq.append(om.project_tokens(w.dims, w.weights, w.x[cu[b]:cu[b] + S], P + np.arange(S),
+                                         model_bf16=True)[1])
+        unq = np.concatenate(unq)
+        assert np.array_equal(om.fp8_quantize(unq, w.kv_scale), np.concatenate(ref_e))
+        check_codes(np.concatenate(got_e), unq, tie_radius(unq, w.dims), w.kv_scale)
     else:
         assert_close(np.concatenate(got_e), np.concatenate(ref_e), w.dims.dtype, "cache entries",
                      magnitude_scaled=True)

@@ -361,22 +361,38 @@ def pin_round_bf16():
     assert np.array_equal(om.round_bf16(x), want)
 
 
-def pin_kv_round_one_hot(w, kv_scale: float):
-    """With one-hot token rows and bf16 weights the kv projection output is a
-    weight column, already bf16: rounding it changes nothing, so the flag
-    acts on that output and nowhere else; with the workload's own tokens the
-    entries move by at most one code step."""
+def pin_model_bf16(w):
+    """The cache entries of a bf16 model (project_tokens with model_bf16)
+    against a construction from other primitives: a float64 torch matmul,
+    torch's float32 -> bfloat16 cast at each bf16 tensor of the wrapper
+    forward listing (kv_lora, kv_c_normed, the roped k_pe), torch's rms_norm
+    and RoPE as a complex rotation. With one-hot tokens kv_lora is a weight
+    column (already bf16), and the entries are then the fp64 entries rounded
+    once."""
     d, W = w.dims, w.weights
+    c = d.kv_lora_rank
     S = w.x.shape[0]
+    pos = int(w.prefix_lens[0]) + np.arange(S)
+
+    def bf(t):
+        return t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+    def build(x):
+        kv = bf(torch.from_numpy(np.asarray(x, np.float64)) @
+                torch.from_numpy(np.asarray(W["kv_a_proj_with_mqa"], np.float64)).T)
+        lat = bf(torch.nn.functional.rms_norm(kv[:, :c], (c,), torch.from_numpy(
+            np.asarray(W["kv_a_layernorm"], np.float64)), eps=d.rms_norm_eps))
+        pe = bf(torch.from_numpy(_rope_complex(kv[:, c:].numpy(), pos, d.rope_theta, d.rope_style)))
+        return torch.cat([lat, pe], 1).numpy()
+
+    _, got, _ = om.project_tokens(d, W, w.x, pos, model_bf16=True)
+    assert np.array_equal(got, build(w.x)), "bf16 entries differ from the torch construction"
     x1 = np.zeros_like(w.x)
     x1[np.arange(S), (7 * np.arange(S)) % d.hidden_size] = 1.0
-    pre = np.zeros((0, d.kv_lora_rank + d.qk_rope_head_dim))
-    a = om.forward_sequence(d, W, x1, pre, w.mask_kind, kv_scale=kv_scale)
-    b = om.forward_sequence(d, W, x1, pre, w.mask_kind, kv_scale=kv_scale, kv_round_bf16=True)
-    assert all(np.array_equal(u, v) for u, v in zip(a, b))
-    _, e0, _ = om.forward_sequence(d, W, w.x, pre, w.mask_kind, kv_scale=kv_scale)
-    _, e1, _ = om.forward_sequence(d, W, w.x, pre, w.mask_kind, kv_scale=kv_scale, kv_round_bf16=True)
-    assert np.max(np.abs(e1 - e0) / np.maximum(np.abs(e0), kv_scale)) <= 0.25
+    _, plain, _ = om.project_tokens(d, W, x1, pos)
+    _, rounded, _ = om.project_tokens(d, W, x1, pos, model_bf16=True)
+    want = torch.from_numpy(plain).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(rounded, want)
 
 
 def pin_fp8_cache(w, kv_scale: float):

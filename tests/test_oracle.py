@@ -225,8 +225,27 @@ def test_round_bf16():
     P.pin_round_bf16()
 
 
-def test_kv_round_one_hot():
-    P.pin_kv_round_one_hot(_tiny(dtype="bf16"), 0.0625)
+@pytest.mark.parametrize("variant", [dict(dtype="bf16"), dict(dtype="bf16", rope_style=om.ROPE_INTERLEAVED,
+                                                              q_lora_rank=12)])
+def test_model_bf16(variant):
+    w = ms.make_workload("tiny", dims=P.tiny_dims(**variant), seed=5, q_lens=[9], prefix_lens=[6],
+                         mask_kind=ms.MASK_CAUSAL, gamma_noise=True)
+    P.pin_model_bf16(w)
+
+
+@pytest.mark.parametrize("skip", [0, 1, 2])
+def test_mutation_model_bf16_rounding_point(monkeypatch, skip):
+    # leaving out any one of the three roundings (kv_lora, kv_c_normed, the
+    # roped k_pe) fails the pin
+    orig, calls = om.round_bf16, []
+
+    def rnd(x):
+        calls.append(1)
+        return np.asarray(x, np.float64) if (len(calls) - 1) % 3 == skip else orig(x)
+    monkeypatch.setattr(om, "round_bf16", rnd)
+    w = ms.make_workload("tiny", dims=P.tiny_dims(dtype="bf16"), seed=5, q_lens=[9], prefix_lens=[6],
+                         mask_kind=ms.MASK_CAUSAL)
+    _expect_fail(P.pin_model_bf16, w)
 
 
 @pytest.mark.parametrize("variant", [dict(), dict(q_lora_rank=12, use_output_gate=True)])
