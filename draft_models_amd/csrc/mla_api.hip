@@ -15,6 +15,22 @@
 
 using namespace mla;
 
+// Per-call device workspaces of the projections, the decode attention and
+// the split-K GEMMs.
+struct Workspace {
+  void* buf1 = nullptr;     // [tokens, N1] fused first projection output
+  void* qbuf = nullptr;     // [tokens, H (n + r)]  (low-rank Q path)
+  void* qlat = nullptr;     // [rows, H, c] latent queries
+  void* olat = nullptr;     // [rows, H, c] latent outputs
+  void* attn = nullptr;     // [tokens, H dv]
+  float* part_o = nullptr;  // decode partial outputs
+  float* part_lse = nullptr;
+  int32_t* sk_tstart = nullptr;  // [batch + 1] stream-K tile offsets
+  float* gemm_ws = nullptr;      // split-K partial sums
+  int64_t gemm_ws_elems = 0;
+  int32_t* sp_ent = nullptr;     // [batch, topk] cache entries of the sparse lists
+};
+
 struct mla_ctx {
   mla_config cfg;
   bool bf16 = true;
@@ -32,25 +48,15 @@ struct mla_ctx {
   void* gamma_kv = nullptr;
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
-  // workspaces
-  void* buf1 = nullptr;    // [max_tokens, N1]
-  void* qbuf = nullptr;    // [max_tokens, H (n + r)]  (low-rank Q path)
+  // workspaces of the calls (allocated at init from the capacity fields)
+  Workspace ws;
   void* kvexp = nullptr;   // [max_prefill_kv, H (n + dv)]
-  void* attn = nullptr;    // [max_tokens, H dv]
-  void* qlat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
-  void* olat = nullptr;    // [max(max_batch, max_block_tokens), H, c]
-  int32_t* sp_ent = nullptr;  // [max_batch, max_topk] cache entries of the sparse lists
   int32_t* blk_cu = nullptr;    // query blocks: [max_batch + 1] token offsets b q_len
   int32_t* blk_lens = nullptr;  // query blocks: [max_batch] cache lengths prefix + q_len
-  float* part_o = nullptr;
-  float* part_lse = nullptr;
   int max_splits = 32;
   int cus = 256;            // compute units of the device
   bool sk_shape = false;    // bf16 512 + 64 latent: stream-K decode
   int sk_max_ranges = 0;
-  int32_t* sk_tstart = nullptr;
-  float* gemm_ws = nullptr;
-  int64_t gemm_ws_elems = 0;
   void* zeros = nullptr;   // 256 zero bytes: source of padding chunks in streamed tiles
   // 8-bit cache (codes of value / kv_scale): the prefill reads a bf16 copy of
   // the visible entries, sequence b's page p at block b mbs + p of kv_shadow
@@ -59,6 +65,7 @@ struct mla_ctx {
   void* kv_shadow = nullptr;        // [max_prefill_kv + max_batch page, c + r] bf16
   int32_t* kv_shadow_bt = nullptr;  // [max_batch, ceil(max_seq_len / page)] identity block table
   std::vector<void*> allocs;
+  hipEvent_t done = nullptr;  // recorded on the call's stream when an entry point returns
   // stage timing (mla_profile_*)
   bool profiling = false;
   struct Mark { int stage; hipEvent_t start, stop; };
@@ -222,6 +229,8 @@ int validate_config(const mla_config* c, const mla_weights* w) {
     if (c->dtype != MLA_DTYPE_BF16 || kc != 512 || r != 64 || c->num_heads > 128 || c->page_size % 32)
       return fail(MLA_ERR_UNSUPPORTED, "the 8-bit cache needs bf16, c = 512, r = 64, <= 128 heads and a page "
                                        "size that is a multiple of 32");
+    if (c->max_batch > 1024)
+      return fail(MLA_ERR_UNSUPPORTED, "the 8-bit cache decodes at most 1024 sequences per call (max_batch)");
   }
   if (!w->kv_a_proj_with_mqa || !w->kv_a_layernorm || !w->kv_b_proj || !w->o_proj)
     return fail(MLA_ERR_INVALID_ARG, "kv_a_proj_with_mqa, kv_a_layernorm, kv_b_proj and o_proj are required");
@@ -275,41 +284,57 @@ struct StageTimer {
   }
 };
 
-int run_gemm(mla_ctx* ctx, const GemmArgs& g0, hipStream_t s) {
+// Records the context's completion event on the call's stream when the
+// entry point returns (mla_free waits for it).
+struct CallDone {
+  mla_ctx* ctx;
+  hipStream_t s;
+  CallDone(mla_ctx* c, hipStream_t st) : ctx(c), s(st) {}
+  ~CallDone() { (void)hipEventRecord(ctx->done, s); }
+};
+
+int run_gemm(mla_ctx* ctx, const Workspace& ws, const GemmArgs& g0, hipStream_t s) {
   GemmArgs g = g0;
   g.zeros = ctx->zeros;
   if (const char* m = gemm_check(g, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
-  HIP_TRY(gemm_launch(g, ctx->bf16, ctx->gemm_ws, ctx->gemm_ws_elems, s));
+  HIP_TRY(gemm_launch(g, ctx->bf16, ws.gemm_ws, ws.gemm_ws_elems, s));
   return MLA_OK;
+}
+
+// where project() leaves the roped-to-be query [T, H, n + r] and its row stride
+void query_buffer(mla_ctx* ctx, const Workspace& ws, void** q, int64_t* ldq) {
+  if (ctx->ql > 0) {
+    *q = ws.qbuf;
+    *ldq = (int64_t)ctx->H * ctx->qkh;
+  } else {
+    *q = static_cast<char*>(ws.buf1) + (size_t)ctx->off_q * ctx->esz;
+    *ldq = ctx->N1;
+  }
 }
 
 // fused first projection and (low-rank path) the q_b projection with the
 // q_a RMSNorm folded into its epilogue; fills q / ldq
-int project(mla_ctx* ctx, const void* x, int T, hipStream_t s, void** q, int64_t* ldq) {
+int project(mla_ctx* ctx, const Workspace& ws, const void* x, int T, hipStream_t s, void** q, int64_t* ldq) {
   GemmArgs g1;
   g1.A = x; g1.lda = ctx->hid;
   g1.W = ctx->W1; g1.ldw = ctx->hid;
-  g1.C = ctx->buf1; g1.ldc = ctx->N1;
+  g1.C = ws.buf1; g1.ldc = ctx->N1;
   g1.M = T; g1.N = ctx->N1; g1.K = ctx->hid;
   {
     StageTimer st(ctx, s, ST_QKV_A);
-    if (int e = run_gemm(ctx, g1, s)) return e;
+    if (int e = run_gemm(ctx, ws, g1, s)) return e;
   }
   if (ctx->ql > 0) {
     GemmArgs g2;
-    g2.A = ctx->buf1; g2.lda = ctx->N1;
+    g2.A = ws.buf1; g2.lda = ctx->N1;
     g2.W = ctx->Wqb; g2.ldw = ctx->ql;
-    g2.C = ctx->qbuf; g2.ldc = (int64_t)ctx->H * ctx->qkh;
+    g2.C = ws.qbuf; g2.ldc = (int64_t)ctx->H * ctx->qkh;
     g2.M = T; g2.N = ctx->H * ctx->qkh; g2.K = ctx->ql;
     g2.epi = EPI_ROWNORM; g2.eps = (float)ctx->cfg.rms_norm_eps;
     StageTimer st(ctx, s, ST_Q_B);
-    if (int e = run_gemm(ctx, g2, s)) return e;
-    *q = ctx->qbuf;
-    *ldq = (int64_t)ctx->H * ctx->qkh;
-  } else {
-    *q = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_q * ctx->esz;
-    *ldq = ctx->N1;
+    if (int e = run_gemm(ctx, ws, g2, s)) return e;
   }
+  query_buffer(ctx, ws, q, ldq);
   return MLA_OK;
 }
 
@@ -337,10 +362,15 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
 
   auto bail = [&](int e) {
     free_all(ctx);
+    if (ctx->done) (void)hipEventDestroy(ctx->done);
     delete ctx;
     return e;
   };
   if (hipGetDevice(&ctx->device) != hipSuccess) return bail(fail(MLA_ERR_HIP, "hipGetDevice failed"));
+  if (hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
+    ctx->done = nullptr;
+    return bail(fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed"));
+  }
 
   // fused first projection rows: [q_a_proj | q_proj] ; kv_a_proj_with_mqa ; g_proj
   const int nq = ctx->ql > 0 ? ctx->ql : H * ctx->qkh;
@@ -413,13 +443,13 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
 
   // workspaces
   const int64_t T = cfg->max_tokens, B = cfg->max_batch;
-  if ((e = dev_alloc(ctx, &ctx->buf1, (size_t)T * ctx->N1 * esz))) return bail(e);
-  if (ctx->ql > 0 && (e = dev_alloc(ctx, &ctx->qbuf, (size_t)T * H * ctx->qkh * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->ws.buf1, (size_t)T * ctx->N1 * esz))) return bail(e);
+  if (ctx->ql > 0 && (e = dev_alloc(ctx, &ctx->ws.qbuf, (size_t)T * H * ctx->qkh * esz))) return bail(e);
   if ((e = dev_alloc(ctx, &ctx->kvexp, (size_t)cfg->max_prefill_kv * kvb_rows * esz))) return bail(e);
-  if ((e = dev_alloc(ctx, &ctx->attn, (size_t)T * H * ctx->dv * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->ws.attn, (size_t)T * H * ctx->dv * esz))) return bail(e);
   const int64_t QR = std::max<int64_t>(B, cfg->max_block_tokens);  // latent query / output rows
-  if ((e = dev_alloc(ctx, &ctx->qlat, (size_t)QR * H * ctx->c * esz))) return bail(e);
-  if ((e = dev_alloc(ctx, &ctx->olat, (size_t)QR * H * ctx->c * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->ws.qlat, (size_t)QR * H * ctx->c * esz))) return bail(e);
+  if ((e = dev_alloc(ctx, &ctx->ws.olat, (size_t)QR * H * ctx->c * esz))) return bail(e);
   void* p;
   if ((e = dev_alloc(ctx, &p, (size_t)(B + 1) * sizeof(int32_t)))) return bail(e);
   ctx->blk_cu = static_cast<int32_t*>(p);
@@ -427,7 +457,7 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   ctx->blk_lens = static_cast<int32_t*>(p);
   if (cfg->max_topk > 0) {
     if ((e = dev_alloc(ctx, &p, (size_t)B * cfg->max_topk * sizeof(int32_t)))) return bail(e);
-    ctx->sp_ent = static_cast<int32_t*>(p);
+    ctx->ws.sp_ent = static_cast<int32_t*>(p);
   }
   if (hipDeviceGetAttribute(&ctx->cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess ||
       ctx->cus <= 0)
@@ -444,19 +474,19 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     ctx->sk_max_ranges = decode_sk_ranges(skb, std::max(cfg->max_seq_len, cfg->max_topk), ctx->cus);
     part_rows = 2 * (int64_t)ctx->sk_max_ranges;
     if ((e = dev_alloc(ctx, &p, (size_t)(skb + 1) * sizeof(int32_t)))) return bail(e);
-    ctx->sk_tstart = static_cast<int32_t*>(p);
+    ctx->ws.sk_tstart = static_cast<int32_t*>(p);
   }
   if (!ctx->sk_shape || B > kDecodeMaxBatch) part_rows = std::max<int64_t>(part_rows, B * ctx->max_splits);
   // partial rows hold every head of a (virtual) sequence: query blocks run
   // with 128 (query, head) pairs per virtual sequence
   const int64_t part_heads = cfg->max_block_tokens > 0 ? std::max(H, 128) : H;
   if ((e = dev_alloc(ctx, &p, (size_t)part_rows * part_heads * ctx->c * sizeof(float)))) return bail(e);
-  ctx->part_o = static_cast<float*>(p);
+  ctx->ws.part_o = static_cast<float*>(p);
   if ((e = dev_alloc(ctx, &p, (size_t)part_rows * part_heads * sizeof(float)))) return bail(e);
-  ctx->part_lse = static_cast<float*>(p);
-  ctx->gemm_ws_elems = (int64_t)16 << 20;
-  if ((e = dev_alloc(ctx, &p, (size_t)ctx->gemm_ws_elems * sizeof(float)))) return bail(e);
-  ctx->gemm_ws = static_cast<float*>(p);
+  ctx->ws.part_lse = static_cast<float*>(p);
+  ctx->ws.gemm_ws_elems = (int64_t)16 << 20;
+  if ((e = dev_alloc(ctx, &p, (size_t)ctx->ws.gemm_ws_elems * sizeof(float)))) return bail(e);
+  ctx->ws.gemm_ws = static_cast<float*>(p);
   if ((e = dev_alloc(ctx, &ctx->zeros, 256))) return bail(e);
   if (hipMemsetAsync(ctx->zeros, 0, 256, s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "zero page init failed"));
   ctx->kv_fp8 = cfg->kv_cache_dtype == MLA_KV_CACHE_FP8_E4M3;
@@ -497,14 +527,16 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   if ((int64_t)max_blocks * c.page_size < max_kv_len)
     return fail(MLA_ERR_INVALID_ARG, "max_blocks * page_size must cover max_kv_len");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  CallDone call_done(ctx, s);
+  const Workspace& ws = ctx->ws;
 
   void* q;
   int64_t ldq;
-  if (int e = project(ctx, x, total_tokens, s, &q, &ldq)) return e;
+  if (int e = project(ctx, ws, x, total_tokens, s, &q, &ldq)) return e;
 
   RopeCacheArgs rc;
   rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
-  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.kv = static_cast<char*>(ws.buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
   rc.gamma_kv = ctx->gamma_kv;
   rc.cache = kv_cache; rc.block_table = block_table;
   rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
@@ -512,7 +544,7 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   rc.H = ctx->H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
-  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale = ctx->kv_scale;
   rc.decode = 0; rc.cu_seqlens = cu_seqlens_q; rc.prefix_lens = prefix_lens;
   rc.max_q_len = max_q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = total_tokens;
@@ -550,9 +582,9 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   fa.mask.kind = mask_kind; fa.mask.window = window; fa.mask.row_lo = row_lo; fa.mask.row_hi = row_hi;
   fa.nchunks = (max_kv_len + 255) / 256;
   fa.qblocks = (max_q_len + 15) / 16;
-  fa.out = ctx->attn; fa.ldo = (int64_t)ctx->H * ctx->dv;
+  fa.out = ws.attn; fa.ldo = (int64_t)ctx->H * ctx->dv;
   if (ctx->off_g >= 0) {
-    fa.gate = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    fa.gate = static_cast<char*>(ws.buf1) + (size_t)ctx->off_g * ctx->esz;
     fa.ldg = ctx->N1;
   }
   const size_t part_bytes = mha_fused_partial_bytes(batch, fa.nchunks, fa.qblocks, ctx->H);
@@ -575,12 +607,12 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
       HIP_TRY(mha_fused_merge_launch(fa, s));
     }
     GemmArgs go;
-    go.A = ctx->attn; go.lda = (int64_t)ctx->H * ctx->dv;
+    go.A = ws.attn; go.lda = (int64_t)ctx->H * ctx->dv;
     go.W = ctx->Wo; go.ldw = (int64_t)ctx->H * ctx->dv;
     go.C = out; go.ldc = ctx->hid;
     go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
     StageTimer st(ctx, s, ST_O_PROJ);
-    return run_gemm(ctx, go, s);
+    return run_gemm(ctx, ws, go, s);
   }
 
   // expand every visible latent (prefix and new) through kv_b_proj
@@ -596,7 +628,7 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   gk.M = batch * max_kv_len; gk.N = ctx->H * (ctx->n + ctx->dv); gk.K = ctx->c;
   {
     StageTimer st(ctx, s, ST_KV_B);
-    if (int e = run_gemm(ctx, gk, s)) return e;
+    if (int e = run_gemm(ctx, ws, gk, s)) return e;
   }
 
   PrefillAttnArgs pa;
@@ -609,9 +641,9 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   pa.H = ctx->H; pa.n = ctx->n; pa.r = ctx->r; pa.c = ctx->c; pa.dv = ctx->dv;
   pa.scale = ctx->scale;
   pa.mask.kind = mask_kind; pa.mask.window = window; pa.mask.row_lo = row_lo; pa.mask.row_hi = row_hi;
-  pa.out = ctx->attn; pa.ldo = (int64_t)ctx->H * ctx->dv;
+  pa.out = ws.attn; pa.ldo = (int64_t)ctx->H * ctx->dv;
   if (ctx->off_g >= 0) {
-    pa.gate = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    pa.gate = static_cast<char*>(ws.buf1) + (size_t)ctx->off_g * ctx->esz;
     pa.ldg = ctx->N1;
   }
   if (const char* m = prefill_attn_check(pa, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
@@ -621,21 +653,26 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   }
 
   GemmArgs go;
-  go.A = ctx->attn; go.lda = (int64_t)ctx->H * ctx->dv;
+  go.A = ws.attn; go.lda = (int64_t)ctx->H * ctx->dv;
   go.W = ctx->Wo; go.ldw = (int64_t)ctx->H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
-  return run_gemm(ctx, go, s);
+  return run_gemm(ctx, ws, go, s);
 }
 
 }  // extern "C"
 
 namespace {
 
+// longest visible key range of a decode query (sizes the split-KV partition)
+int decode_max_visible(int mask_kind, int window, int max_seq_len) {
+  return mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+}
+
 // one new token per sequence in absorbed form; with topk_idx, each query sees
 // only its listed positions (sparse lists, stream-K only)
-int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+int decode_impl(mla_ctx* ctx, const Workspace& ws, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
                 const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
                 int32_t mask_kind, int32_t window, const int32_t* topk_idx, int32_t topk, void* out,
                 void* stream) {
@@ -652,42 +689,16 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
   if ((int64_t)max_blocks * c.page_size < max_seq_len)
     return fail(MLA_ERR_INVALID_ARG, "max_blocks * page_size must cover max_seq_len");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  CallDone call_done(ctx, s);
   const int H = ctx->H;
 
+  // the attention path and its arguments are settled before the first
+  // launch, so a call that cannot run leaves the caller's cache untouched
   void* q;
   int64_t ldq;
-  if (int e = project(ctx, x, batch, s, &q, &ldq)) return e;
-
-  RopeCacheArgs rc;
-  rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
-  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
-  rc.gamma_kv = ctx->gamma_kv;
-  rc.cache = kv_cache; rc.block_table = block_table;
-  rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
-  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
-  rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
-  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
-  rc.eps = (float)c.rms_norm_eps;
-  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
-  rc.decode = 1; rc.seq_lens = seq_lens; rc.max_seq_len = max_seq_len; rc.total_tokens = batch;
-  {
-    StageTimer st(ctx, s, ST_ROPE_CACHE);
-    HIP_TRY(rope_cache_launch(rc, ctx->bf16, 1, batch, s));
-  }
-
-  // W_UK absorption: ql_nope[b, h] = q_nope[b, h] . W_UK^T[h]   (per head: [B, n] x [n, c])
-  GemmArgs ga;
-  ga.A = q; ga.lda = ldq; ga.sA = ctx->qkh;
-  ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
-  ga.C = ctx->qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
-  ga.M = batch; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
-  {
-    StageTimer st(ctx, s, ST_WUK);
-    if (int e = run_gemm(ctx, ga, s)) return e;
-  }
-
+  query_buffer(ctx, ws, &q, &ldq);
   DecodeAttnArgs da;
-  da.ql = ctx->qlat; da.ldql = (int64_t)H * ctx->c;
+  da.ql = ws.qlat; da.ldql = (int64_t)H * ctx->c;
   da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
   da.cache = kv_cache; da.block_table = block_table;
   da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
@@ -696,34 +707,22 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
   da.scale = ctx->scale;
   da.kv_fp8 = ctx->kv_fp8; da.kv_scale = ctx->kv_scale;
   da.mask.kind = mask_kind; da.mask.window = window;
-  da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
-  da.o_lat = ctx->olat;
+  da.part_o = ws.part_o; da.part_lse = ws.part_lse;
+  da.o_lat = ws.olat;
   da.zeros = static_cast<const bf16_t*>(ctx->zeros);
-  int max_vis = mask_kind == MLA_MASK_SLIDING ? std::min(window, max_seq_len) : max_seq_len;
+  int max_vis = decode_max_visible(mask_kind, window, max_seq_len);
   if (topk_idx) {
-    da.gather_ent = ctx->sp_ent;
+    da.gather_ent = ws.sp_ent;
     da.gather_k = topk;
     max_vis = topk;
   }
-  if (ctx->sk_shape && batch <= kDecodeMaxBatch) {
+  const bool stream_k = ctx->sk_shape && batch <= kDecodeMaxBatch;
+  if (stream_k) {
     // stream-K: equal tile ranges over all sequences, pieces merged afterwards
     da.ranges = decode_sk_ranges(batch, max_vis, ctx->cus);
-    da.tstart = ctx->sk_tstart;
+    da.tstart = ws.sk_tstart;
     if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
     if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
-    {
-      StageTimer st(ctx, s, ST_DECODE_ATTN);
-      if (topk_idx) {
-        hipLaunchKernelGGL(sparse_entries_kernel, dim3((topk + 255) / 256, batch), dim3(256), 0, s, topk_idx, topk,
-                           seq_lens, max_seq_len, block_table, max_blocks, num_blocks, c.page_size, ctx->sp_ent);
-        HIP_TRY(hipGetLastError());
-      }
-      HIP_TRY(decode_sk_launch(da, s));
-    }
-    {
-      StageTimer st(ctx, s, ST_DECODE_MERGE);
-      HIP_TRY(decode_sk_merge_launch(da, s));
-    }
   } else if (topk_idx) {
     return fail(MLA_ERR_UNSUPPORTED, "sparse lists need the bf16 512 + 64 latent with at most 128 heads");
   } else if (ctx->kv_fp8) {
@@ -739,6 +738,53 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
     if ((int64_t)splits * chunk < max_vis) chunk = ((max_vis + splits - 1) / splits + 31) / 32 * 32;
     da.chunk = chunk; da.splits = splits;
     if (const char* m = decode_attn_check(da, ctx->bf16)) return fail(MLA_ERR_UNSUPPORTED, m);
+  }
+
+  if (int e = project(ctx, ws, x, batch, s, &q, &ldq)) return e;
+
+  RopeCacheArgs rc;
+  rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
+  rc.kv = static_cast<char*>(ws.buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.gamma_kv = ctx->gamma_kv;
+  rc.cache = kv_cache; rc.block_table = block_table;
+  rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
+  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
+  rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
+  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  rc.eps = (float)c.rms_norm_eps;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale = ctx->kv_scale;
+  rc.decode = 1; rc.seq_lens = seq_lens; rc.max_seq_len = max_seq_len; rc.total_tokens = batch;
+  {
+    StageTimer st(ctx, s, ST_ROPE_CACHE);
+    HIP_TRY(rope_cache_launch(rc, ctx->bf16, 1, batch, s));
+  }
+
+  // W_UK absorption: ql_nope[b, h] = q_nope[b, h] . W_UK^T[h]   (per head: [B, n] x [n, c])
+  GemmArgs ga;
+  ga.A = q; ga.lda = ldq; ga.sA = ctx->qkh;
+  ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
+  ga.C = ws.qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
+  ga.M = batch; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
+  {
+    StageTimer st(ctx, s, ST_WUK);
+    if (int e = run_gemm(ctx, ws, ga, s)) return e;
+  }
+
+  if (stream_k) {
+    {
+      StageTimer st(ctx, s, ST_DECODE_ATTN);
+      if (topk_idx) {
+        hipLaunchKernelGGL(sparse_entries_kernel, dim3((topk + 255) / 256, batch), dim3(256), 0, s, topk_idx, topk,
+                           seq_lens, max_seq_len, block_table, max_blocks, num_blocks, c.page_size, ws.sp_ent);
+        HIP_TRY(hipGetLastError());
+      }
+      HIP_TRY(decode_sk_launch(da, s));
+    }
+    {
+      StageTimer st(ctx, s, ST_DECODE_MERGE);
+      HIP_TRY(decode_sk_merge_launch(da, s));
+    }
+  } else {
     {
       StageTimer st(ctx, s, ST_DECODE_ATTN);
       HIP_TRY(decode_attn_launch(da, ctx->bf16, s));
@@ -751,28 +797,28 @@ int decode_impl(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int3
 
   // W_UV: out_v[b, h] = o_lat[b, h] . W_UV[h]^T (per head: [B, c] x [c, dv]), gated
   GemmArgs gv;
-  gv.A = ctx->olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
+  gv.A = ws.olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
   gv.W = static_cast<char*>(ctx->Wkvb) + (size_t)ctx->n * ctx->c * ctx->esz;
   gv.ldw = ctx->c; gv.sW = (int64_t)(ctx->n + ctx->dv) * ctx->c;
-  gv.C = ctx->attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
+  gv.C = ws.attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
   gv.M = batch; gv.N = ctx->dv; gv.K = ctx->c; gv.batch = H;
   if (ctx->off_g >= 0) {
     gv.epi = EPI_GATE;
-    gv.G = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    gv.G = static_cast<char*>(ws.buf1) + (size_t)ctx->off_g * ctx->esz;
     gv.ldg = ctx->N1; gv.sG = ctx->dv;
   }
   {
     StageTimer st(ctx, s, ST_WUV);
-    if (int e = run_gemm(ctx, gv, s)) return e;
+    if (int e = run_gemm(ctx, ws, gv, s)) return e;
   }
 
   GemmArgs go;
-  go.A = ctx->attn; go.lda = (int64_t)H * ctx->dv;
+  go.A = ws.attn; go.lda = (int64_t)H * ctx->dv;
   go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = batch; go.N = ctx->hid; go.K = H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
-  return run_gemm(ctx, go, s);
+  return run_gemm(ctx, ws, go, s);
 }
 
 }  // namespace
@@ -782,8 +828,9 @@ extern "C" {
 int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
                         const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
                         int32_t max_seq_len, int32_t mask_kind, int32_t window, void* out, void* stream) {
-  return decode_impl(ctx, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len, mask_kind,
-                     window, nullptr, 0, out, stream);
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  return decode_impl(ctx, ctx->ws, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
+                     mask_kind, window, nullptr, 0, out, stream);
 }
 
 int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
@@ -794,7 +841,7 @@ int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batch, void*
   if (!topk_indices) return fail(MLA_ERR_INVALID_ARG, "topk_indices must not be NULL");
   if (topk <= 0) return fail(MLA_ERR_INVALID_ARG, "topk must be positive");
   if (topk > ctx->cfg.max_topk) return fail(MLA_ERR_CAPACITY, "topk above the init max_topk");
-  return decode_impl(ctx, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
+  return decode_impl(ctx, ctx->ws, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
                      MLA_MASK_FULL, 0, topk_indices, topk, out, stream);
 }
 
@@ -819,18 +866,44 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   const int64_t V = T * H / 128;  // virtual sequences of 128 (query, head) pairs
   if (V > kDecodeMaxBatch) return fail(MLA_ERR_CAPACITY, "batch * q_len * num_heads above 128 K pairs");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  CallDone call_done(ctx, s);
+  const Workspace& ws = ctx->ws;
+
+  // latent attention (its arguments are settled and checked before the first
+  // launch): virtual sequence v holds the (token, head) pairs
+  // v * 128 .. v * 128 + 127 of [T, H] (q_len * H / 128 per sequence), all of
+  // whose tokens see the same cache entries
+  DecodeAttnArgs da;
+  da.ql = ws.qlat; da.ldql = (int64_t)128 * ctx->c;
+  void* q;
+  int64_t ldq;
+  query_buffer(ctx, ws, &q, &ldq);
+  da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
+  da.cache = kv_cache; da.block_table = block_table;
+  da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
+  da.seq_lens = ctx->blk_lens; da.max_seq_len = max_kv_len; da.batch = (int)V;
+  da.H = 128; da.Hr = H; da.seq_div = (int)(V / batch);
+  da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
+  da.scale = ctx->scale;
+  da.kv_fp8 = ctx->kv_fp8; da.kv_scale = ctx->kv_scale;
+  da.mask.kind = MLA_MASK_FULL; da.mask.window = 0;
+  da.part_o = ws.part_o; da.part_lse = ws.part_lse;
+  da.o_lat = ws.olat;
+  da.zeros = static_cast<const bf16_t*>(ctx->zeros);
+  da.ranges = decode_sk_ranges((int)V, max_kv_len, ctx->cus);
+  da.tstart = ws.sk_tstart;
+  if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
+  if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
 
   hipLaunchKernelGGL(block_meta_kernel, dim3((batch + 256) / 256), dim3(256), 0, s, prefix_lens, batch, q_len,
                      ctx->blk_cu, ctx->blk_lens);
   HIP_TRY(hipGetLastError());
 
-  void* q;
-  int64_t ldq;
-  if (int e = project(ctx, x, (int)T, s, &q, &ldq)) return e;
+  if (int e = project(ctx, ws, x, (int)T, s, &q, &ldq)) return e;
 
   RopeCacheArgs rc;
   rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
-  rc.kv = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
+  rc.kv = static_cast<char*>(ws.buf1) + (size_t)ctx->off_kv * ctx->esz; rc.ldkv = ctx->N1;
   rc.gamma_kv = ctx->gamma_kv;
   rc.cache = kv_cache; rc.block_table = block_table;
   rc.num_blocks = num_blocks; rc.max_blocks = max_blocks; rc.page = c.page_size;
@@ -838,7 +911,7 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
-  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale_inv = 1.f / ctx->kv_scale;
+  rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale = ctx->kv_scale;
   rc.decode = 0; rc.cu_seqlens = ctx->blk_cu; rc.prefix_lens = prefix_lens;
   rc.max_q_len = q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = (int)T;
@@ -851,34 +924,13 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   GemmArgs ga;
   ga.A = q; ga.lda = ldq; ga.sA = ctx->qkh;
   ga.W = ctx->Wuk_t; ga.ldw = ctx->n; ga.sW = (int64_t)ctx->c * ctx->n;
-  ga.C = ctx->qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
+  ga.C = ws.qlat; ga.ldc = (int64_t)H * ctx->c; ga.sC = ctx->c;
   ga.M = (int)T; ga.N = ctx->c; ga.K = ctx->n; ga.batch = H;
   {
     StageTimer st(ctx, s, ST_WUK);
-    if (int e = run_gemm(ctx, ga, s)) return e;
+    if (int e = run_gemm(ctx, ws, ga, s)) return e;
   }
 
-  // latent attention: virtual sequence v holds the (token, head) pairs
-  // v * 128 .. v * 128 + 127 of [T, H] (q_len * H / 128 per sequence), all of
-  // whose tokens see the same cache entries
-  DecodeAttnArgs da;
-  da.ql = ctx->qlat; da.ldql = (int64_t)128 * ctx->c;
-  da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
-  da.cache = kv_cache; da.block_table = block_table;
-  da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
-  da.seq_lens = ctx->blk_lens; da.max_seq_len = max_kv_len; da.batch = (int)V;
-  da.H = 128; da.Hr = H; da.seq_div = (int)(V / batch);
-  da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
-  da.scale = ctx->scale;
-  da.kv_fp8 = ctx->kv_fp8; da.kv_scale = ctx->kv_scale;
-  da.mask.kind = MLA_MASK_FULL; da.mask.window = 0;
-  da.part_o = ctx->part_o; da.part_lse = ctx->part_lse;
-  da.o_lat = ctx->olat;
-  da.zeros = static_cast<const bf16_t*>(ctx->zeros);
-  da.ranges = decode_sk_ranges((int)V, max_kv_len, ctx->cus);
-  da.tstart = ctx->sk_tstart;
-  if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
-  if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
   {
     StageTimer st(ctx, s, ST_DECODE_ATTN);
     HIP_TRY(decode_sk_launch(da, s));
@@ -890,28 +942,28 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
 
   // W_UV of every token, gated
   GemmArgs gv;
-  gv.A = ctx->olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
+  gv.A = ws.olat; gv.lda = (int64_t)H * ctx->c; gv.sA = ctx->c;
   gv.W = static_cast<char*>(ctx->Wkvb) + (size_t)ctx->n * ctx->c * ctx->esz;
   gv.ldw = ctx->c; gv.sW = (int64_t)(ctx->n + ctx->dv) * ctx->c;
-  gv.C = ctx->attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
+  gv.C = ws.attn; gv.ldc = (int64_t)H * ctx->dv; gv.sC = ctx->dv;
   gv.M = (int)T; gv.N = ctx->dv; gv.K = ctx->c; gv.batch = H;
   if (ctx->off_g >= 0) {
     gv.epi = EPI_GATE;
-    gv.G = static_cast<char*>(ctx->buf1) + (size_t)ctx->off_g * ctx->esz;
+    gv.G = static_cast<char*>(ws.buf1) + (size_t)ctx->off_g * ctx->esz;
     gv.ldg = ctx->N1; gv.sG = ctx->dv;
   }
   {
     StageTimer st(ctx, s, ST_WUV);
-    if (int e = run_gemm(ctx, gv, s)) return e;
+    if (int e = run_gemm(ctx, ws, gv, s)) return e;
   }
 
   GemmArgs go;
-  go.A = ctx->attn; go.lda = (int64_t)H * ctx->dv;
+  go.A = ws.attn; go.lda = (int64_t)H * ctx->dv;
   go.W = ctx->Wo; go.ldw = (int64_t)H * ctx->dv;
   go.C = out; go.ldc = ctx->hid;
   go.M = (int)T; go.N = ctx->hid; go.K = H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
-  return run_gemm(ctx, go, s);
+  return run_gemm(ctx, ws, go, s);
 }
 
 int mla_profile_enable(mla_ctx* ctx, int32_t enable) {
@@ -949,7 +1001,9 @@ void mla_free(mla_ctx* ctx) {
   int cur = 0;
   (void)hipGetDevice(&cur);
   (void)hipSetDevice(ctx->device);
-  (void)hipDeviceSynchronize();
+  // the last call's work (stream order covers the calls before it)
+  (void)hipEventSynchronize(ctx->done);
+  (void)hipEventDestroy(ctx->done);
   for (auto& mk : ctx->marks) {
     (void)hipEventDestroy(mk.start);
     (void)hipEventDestroy(mk.stop);

@@ -82,11 +82,13 @@ typedef enum mla_mask_kind { MLA_MASK_FULL = 0, MLA_MASK_CAUSAL = 1, MLA_MASK_SL
  * computes dynamic q/k/v scales for an FP8 KV cache and its cache-shape
  * listings name a packed 656-byte fp8 entry without its packing; this plain
  * 576-byte entry with a per-tensor scale is the reading taken (the scale is
- * an input, not computed). With FP8_E4M3, mla_init_weights returns
- * MLA_ERR_UNSUPPORTED unless dtype is BF16, c = 512, r = 64, num_heads <= 128
- * and page_size % 32 == 0, and MLA_ERR_INVALID_ARG for a scale that is not
- * finite and > 0; the decode entry points take at most 1024 sequences per
- * call (else MLA_ERR_UNSUPPORTED); the prefill reads a library-owned bf16
+ * an input, not computed). The encoded values are the bf16 tensors the MLA
+ * blog's wrapper forward hands to the cache update (kv_c_normed and the roped
+ * k_pe of a bf16 model): each entry value is rounded to bf16 before its code
+ * is taken. With FP8_E4M3, mla_init_weights returns
+ * MLA_ERR_UNSUPPORTED unless dtype is BF16, c = 512, r = 64, num_heads <= 128,
+ * page_size % 32 == 0 and max_batch <= 1024, and MLA_ERR_INVALID_ARG for a
+ * scale that is not finite and > 0; the prefill reads a library-owned bf16
  * copy of the visible entries (max_prefill_kv + max_batch * page_size rows,
  * allocated at init). The caller's cache is c + r bytes per entry. */
 typedef enum mla_kv_cache_dtype { MLA_KV_CACHE_COMPUTE = 0, MLA_KV_CACHE_FP8_E4M3 = 1 } mla_kv_cache_dtype;
@@ -208,7 +210,7 @@ MLA_API int mla_decode_absorbed(mla_ctx* ctx, const void* x, int32_t batch,
  * sees every cache entry of its sequence, the prefix and the whole block
  * (block-visible, the FULL mask). The MLA blog's forward listing sends the
  * tokens that the metadata counts as decode through this MQA branch, and the
- * SpecForge PR "Add config-selectable MLA draft attention" (Test plan) runs
+ * SpecForge PR "Add config-selectable MLA draft attention" (Validation) runs
  * its draft blocks through spec_generate decode; this is the same arithmetic
  * as mla_prefill_expanded with the FULL mask, without expanding any latent.
  *   x            device [batch * q_len, hidden]: token i of sequence b is row
@@ -282,8 +284,10 @@ MLA_API int mla_profile_enable(mla_ctx* ctx, int32_t enable);
 MLA_API int mla_profile_read(mla_ctx* ctx, double* ms, int32_t* count);
 MLA_API const char* mla_profile_stage_name(int32_t stage);
 
-/* mla_free — release everything the context owns (waits for its device work
- * to finish on the device). NULL is a no-op. */
+/* mla_free — release everything the context owns. It first waits for the
+ * context's last call to finish (an event recorded on that call's stream when
+ * it returned; stream order covers the calls before it), not for other work
+ * on the device. NULL is a no-op. */
 MLA_API void mla_free(mla_ctx* ctx);
 
 /* mla_last_error — message of the last failure on the calling thread

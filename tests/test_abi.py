@@ -89,6 +89,10 @@ def _init(cfg, w):
     (dict(qk_nope_head_dim=18), 3),        # not a 16-byte multiple of fp32
     (dict(use_output_gate=1), 1),          # g_proj missing
     (dict(q_lora_rank=64), 1),             # q_a_proj / q_b_proj missing
+    (dict(kv_cache_dtype=1, kv_cache_scale=0.0), 1),  # 8-bit cache needs a positive scale
+    (dict(kv_cache_dtype=1, kv_cache_scale=0.5), 3),  # 8-bit cache needs bf16, c 512, r 64
+    (dict(kv_cache_dtype=1, kv_cache_scale=0.5, dtype=B.DTYPE_BF16, kv_lora_rank=512, qk_rope_head_dim=64,
+          qk_nope_head_dim=128, v_head_dim=128, max_batch=1025), 3),  # 8-bit cache: at most 1024 sequences
 ])
 def test_init_validation(kw, code):
     got, ctx = _init(_good_cfg(**kw), _good_weights())

@@ -314,6 +314,53 @@ def test_fp8_prefill_expanded():
     _run_and_check(w)
 
 
+def test_fp8_prefill_fused_scale_not_pow2():
+    """Draft blocks (fused expansion) over an 8-bit cache whose scale is not a
+    power of two: the prefill's bf16 copy of the entries (code * scale) is
+    then rounded, not exact."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[16, 9, 16], prefix_lens=[200, 41, 0], seed=48,
+                         kv_scale=0.0421875)
+    _run_and_check(w)
+
+
+def test_fp8_prefill_expanded_scale_not_pow2():
+    """Long causal prefills (the expansion GEMM gathers from the bf16 copy)
+    over an 8-bit cache with a scale that is not a power of two."""
+    w = ms.make_workload("prefill_bf16", q_lens=[257, 100], prefix_lens=[30, 0], seed=49, kv_scale=0.0371)
+    _run_and_check(w)
+
+
+# ------------------------------------- generic split-KV decode (bf16 shapes)
+
+def test_decode_generic_160_heads_bf16():
+    """bf16 decode with 160 heads (above the stream-K kernel's 128): the
+    generic split-KV kernel and its merge, in bf16, with an output gate."""
+    w = ms.make_workload("decode_bf16", seq_lens=[1, 40, 700, 129, 2000], seed=50,
+                         dims_override={"num_heads": 160, "hidden_size": 1024, "q_lora_rank": 256,
+                                        "use_output_gate": True})
+    _run_and_check(w)
+
+
+def test_decode_generic_small_latent_bf16():
+    """bf16 decode with a 256 + 32 latent and a page of 16 tokens (not the
+    stream-K shape), sliding window."""
+    w = ms.make_workload("decode_bf16", seq_lens=[3, 64, 500, 17], seed=51, mask_kind=ms.MASK_SLIDING, window=70,
+                         dims_override={"kv_lora_rank": 256, "qk_rope_head_dim": 32, "num_heads": 16,
+                                        "hidden_size": 512, "q_lora_rank": 128, "page_size": 16})
+    _run_and_check(w)
+
+
+def test_decode_generic_batch_above_1024_bf16():
+    """1100 bf16 decode sequences (above the stream-K kernel's 1024 per
+    call): the generic split-KV kernel; sampled sequences checked."""
+    rng = np.random.default_rng(52)
+    w = ms.make_workload("decode_bf16", seq_lens=list(rng.integers(1, 90, 1100)), seed=52,
+                         dims_override={"num_heads": 16, "hidden_size": 512, "q_lora_rank": 128})
+    out, cache = U.run_gpu(w)
+    seqs = [0, 1, 517, 1023, 1024, 1099]
+    U.check(w, out, cache, U.oracle(w, seqs=seqs))
+
+
 def test_full_draft_block():
     """8 sequences x 16 fully visible tokens over a 2048-entry latent prefix."""
     w = ms.make_workload("draft_block_bf16")
