@@ -22,7 +22,7 @@ ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 
 EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_decode_absorbed_block",
-           "mla_decode_absorbed_sparse", "mla_free", "mla_last_error",
+           "mla_decode_absorbed_sparse", "mla_decode_absorbed_noalloc", "mla_free", "mla_last_error",
            "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
 NUM_STAGES = 13
 
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.mla_decode_absorbed_block.restype = C.c_int
     lib.mla_decode_absorbed_sparse.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp, vp]
     lib.mla_decode_absorbed_sparse.restype = C.c_int
+    lib.mla_decode_absorbed_noalloc.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, vp, vp]
+    lib.mla_decode_absorbed_noalloc.restype = C.c_int
     lib.mla_free.argtypes = [vp]
     lib.mla_free.restype = None
     lib.mla_last_error.argtypes = []
@@ -148,6 +150,13 @@ class MLA:
     def decode(self, x, kv_cache, block_table, seq_lens, max_seq_len: int, mask_kind: int, window: int, out,
                stream=None):
         _check(self._lib.mla_decode_absorbed(
+            self.ctx, _ptr(x), x.shape[0], _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), max_seq_len, mask_kind, window, _ptr(out), _stream(stream)))
+
+    def decode_noalloc(self, x, kv_cache, block_table, seq_lens, max_seq_len: int, mask_kind: int, window: int,
+                       out, stream=None):
+        """decode() with the per-call workspaces in the library's static scratch array."""
+        _check(self._lib.mla_decode_absorbed_noalloc(
             self.ctx, _ptr(x), x.shape[0], _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
             block_table.shape[1], _ptr(seq_lens), max_seq_len, mask_kind, window, _ptr(out), _stream(stream)))
 

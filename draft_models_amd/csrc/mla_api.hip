@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -16,7 +17,8 @@
 using namespace mla;
 
 // Per-call device workspaces of the projections, the decode attention and
-// the split-K GEMMs.
+// the split-K GEMMs (a context's own, or carved from the static scratch array
+// by mla_decode_absorbed_noalloc).
 struct Workspace {
   void* buf1 = nullptr;     // [tokens, N1] fused first projection output
   void* qbuf = nullptr;     // [tokens, H (n + r)]  (low-rank Q path)
@@ -88,6 +90,36 @@ int fail(int code, const std::string& msg) {
     if (_e != hipSuccess)                                                          \
       return fail(MLA_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(_e)); \
   } while (0)
+
+// Static device scratch of mla_decode_absorbed_noalloc. Each device the
+// library runs on holds its own copy until the process ends. Host code never
+// uses the array's name as an address: its device address is looked up once
+// per device (scratch_setup, at context creation with that device current)
+// and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+constexpr size_t kScratchGemmBytes = (size_t)8 << 20;  // split-K partial sums of its GEMMs
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_setup(int device) {
+  if (device < 0 || device >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return MLA_OK;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p)
+    return fail(MLA_ERR_HIP, std::string("hipGetSymbolAddress of the scratch array failed: ") + hipGetErrorString(e));
+  g_scratch_ptr[device] = p;
+  return MLA_OK;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
+}
 
 __global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst, int64_t rows, int cols, int bf) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -371,6 +403,7 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     ctx->done = nullptr;
     return bail(fail(MLA_ERR_HIP, "hipEventCreateWithFlags failed"));
   }
+  if (int e = scratch_setup(ctx->device)) return bail(e);
 
   // fused first projection rows: [q_a_proj | q_proj] ; kv_a_proj_with_mqa ; g_proj
   const int nq = ctx->ql > 0 ? ctx->ql : H * ctx->qkh;
@@ -843,6 +876,47 @@ int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batch, void*
   if (topk > ctx->cfg.max_topk) return fail(MLA_ERR_CAPACITY, "topk above the init max_topk");
   return decode_impl(ctx, ctx->ws, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
                      MLA_MASK_FULL, 0, topk_indices, topk, out, stream);
+}
+
+int mla_decode_absorbed_noalloc(mla_ctx* ctx, const void* x, int32_t batch, void* kv_cache, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                                int32_t max_seq_len, int32_t mask_kind, int32_t window, void* out, void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (batch <= 0 || max_seq_len <= 0) return fail(MLA_ERR_INVALID_ARG, "batch and max_seq_len must be positive");
+  if (int e = check_mask(mask_kind, window)) return e;
+  if (!ctx->sk_shape || batch > kDecodeMaxBatch)
+    return fail(MLA_ERR_UNSUPPORTED, "the allocation-free decode needs the bf16 512 + 64 latent, <= 128 heads, "
+                                     "a page size that is a multiple of 32 and <= 1024 sequences");
+  char* base = static_cast<char*>(scratch_ptr(ctx->device));
+  if (!base) return fail(MLA_ERR_HIP, "no scratch address for the context's device");
+  // carve the call's workspaces out of the scratch array (256-byte aligned)
+  const int H = ctx->H;
+  const int ranges = decode_sk_ranges(batch, decode_max_visible(mask_kind, window, max_seq_len), ctx->cus);
+  size_t off = 0;
+  auto carve = [&](size_t bytes) {
+    char* p = base + off;
+    off += (bytes + 255) & ~(size_t)255;
+    return static_cast<void*>(p);
+  };
+  Workspace ws;
+  ws.buf1 = carve((size_t)batch * ctx->N1 * ctx->esz);
+  if (ctx->ql > 0) ws.qbuf = carve((size_t)batch * H * ctx->qkh * ctx->esz);
+  ws.qlat = carve((size_t)batch * H * ctx->c * ctx->esz);
+  ws.olat = carve((size_t)batch * H * ctx->c * ctx->esz);
+  ws.attn = carve((size_t)batch * H * ctx->dv * ctx->esz);
+  ws.sk_tstart = static_cast<int32_t*>(carve((size_t)(batch + 1) * sizeof(int32_t)));
+  // stream-K pieces: two per range, bf16 partial outputs and fp32 LSEs
+  ws.part_o = static_cast<float*>(carve((size_t)2 * ranges * H * ctx->c * sizeof(bf16_t)));
+  ws.part_lse = static_cast<float*>(carve((size_t)2 * ranges * H * sizeof(float)));
+  ws.gemm_ws = static_cast<float*>(carve(kScratchGemmBytes));
+  ws.gemm_ws_elems = (int64_t)(kScratchGemmBytes / sizeof(float));
+  if (off > kScratchBytes)
+    return fail(MLA_ERR_CAPACITY, "the call's workspaces (" + std::to_string(off) + " bytes) exceed the " +
+                                      std::to_string(kScratchBytes) + "-byte scratch array");
+  // nothing in these workspaces needs to start at zero: every kernel writes
+  // what a later kernel reads
+  return decode_impl(ctx, ws, x, batch, kv_cache, num_blocks, block_table, max_blocks, seq_lens, max_seq_len,
+                     mask_kind, window, nullptr, 0, out, stream);
 }
 
 int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_t q_len, void* kv_cache,

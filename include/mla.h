@@ -255,6 +255,29 @@ MLA_API int mla_decode_absorbed_sparse(mla_ctx* ctx, const void* x, int32_t batc
                         const int32_t* topk_indices, int32_t topk, void* out, void* stream);
 
 /*
+ * mla_decode_absorbed_noalloc — mla_decode_absorbed for callers that cannot
+ * allocate device memory during the call (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, errors
+ * and result as mla_decode_absorbed (the same kernels; outputs are bitwise
+ * equal), but every per-call workspace (projection outputs, latent queries
+ * and outputs, stream-K partials, split-K GEMM sums) is carved from one
+ * static device array of 128 MiB that the library holds on each device it
+ * runs on until the process ends; the call allocates nothing. The context
+ * (weights, RoPE table) still comes from mla_init_weights.
+ * Requires the stream-K shape (bf16, 512 + 64 latent, <= 128 heads, page
+ * size a multiple of 32) and batch <= 1024, else MLA_ERR_UNSUPPORTED; a call
+ * whose workspaces exceed the array returns MLA_ERR_CAPACITY before any
+ * launch (the DeepSeek-V3 decode of 64 sequences x 128 heads needs about
+ * 95 MiB). Every call on a device shares that device's array, which keeps
+ * the last call's contents: calls that overlap on one device (on different
+ * streams, or different contexts) race and must be serialised by the caller.
+ */
+MLA_API int mla_decode_absorbed_noalloc(mla_ctx* ctx, const void* x, int32_t batch,
+                        void* kv_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t max_seq_len,
+                        int32_t mask_kind, int32_t window, void* out, void* stream);
+
+/*
  * Stage timing, for measurement. When enabled, every launch sequence of the
  * context records a pair of HIP events around each stage on the call's own
  * stream (the stream the stage's kernels run on); mla_profile_read waits for
