@@ -1,20 +1,22 @@
 #!/usr/bin/env python3
 """MLA forward benchmark on one MI355X.
 
-Default workload: the draft-block MLA layer -- 8 sequences, each a 16-token
-block that sees all of itself and a 2048-entry latent prefix (FULL mask),
-hidden 4096, 32 heads, q_lora_rank 1536, kv_lora_rank 512, qk_nope 128,
-qk_rope 64, v_head 128, interleaved RoPE, bf16, through mla_prefill_expanded.
-One step = one call of the entry point = the whole hot path (projections,
-latent RMSNorm + RoPE + cache write, expansion of every visible latent, flash
-attention, o_proj). Inputs are synthetic (seeded), resident in HBM before the
-timed region.
-
-Prints one JSON line: value = algorithmic work of the step / step time
-(TFLOP/s for prefill workloads, latent-cache GB/s for decode workloads),
-plus the roofline of the dominant kernel (timed live with HIP events on the
-library's stream) and the fp64 oracle timed on the host cores on a bounded
-sample of the same workload.
+Default (the headline line): the two configurations the metric is quoted on,
+each through the library's C ABI on synthetic seeded inputs already resident
+in HBM when the timed region starts:
+  * value: expanded prefill bf16 -- 4 x 4096 causal tokens, hidden 4096, 32
+    heads, q_lora_rank 1536, kv_lora_rank 512, qk_nope 128, qk_rope 64, v_head
+    128, NeoX RoPE (mla_prefill_expanded), in TFLOP/s of algorithmic work;
+  * "decode": DeepSeek-V3-shaped absorbed decode bf16 -- 64 sequences x 1
+    query, cache length uniform in [1024, 8192], hidden 7168, 128 heads
+    (mla_decode_absorbed), in latent-cache GB/s.
+One step = one call of the entry point = the whole hot path of that form.
+Each carries the roofline of its dominant kernel (HIP events on the library's
+stream, with the profiled launches queued behind a GPU spin so that no host
+gap enters a stage), the measured roofline denominators (copy / read / MFMA
+loop kernels of libmla_peaks.so) and the fp64 oracle timed on the host cores
+on a bounded sample of the same workload. --workload NAME measures one other
+workload on its own line (parity-test configurations, profiling runs).
 """
 from __future__ import annotations
 
@@ -214,7 +216,9 @@ def _per_dispatch(rows, counter, pat):
 def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands, out_dir=None):
     """profiles/traffic_<stage>_<workload>.json from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE: KiB per dispatch), each counter scaled by what
-    it reads for the copy calibration (copy_mib MiB read and written)."""
+    it reads for the copy calibration (copy_mib MiB read and written by each
+    of several negation dispatches, each after a 512 MiB eviction write): the
+    factor is the mean over those dispatches, its spread is recorded."""
     known_kib = copy_mib * 1024.0
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -223,26 +227,28 @@ def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands, out_dir=
         if not cp:
             raise SystemExit(f"no copy-calibration dispatches in {d}")
         gmax = max(g for g, _ in cp.values())
-        vals = [v for g, v in cp.values() if g == gmax]
-        factor = known_kib / (sum(vals) / len(vals))
-        res[counter] = (rows, factor)
+        fac = [known_kib / v for g, v in cp.values() if g == gmax and v > 0]
+        res[counter] = (rows, sum(fac) / len(fac), (min(fac), max(fac)), len(fac))
     written = []
     for stage, pat in STAGE_KERNEL.items():
         per = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            rows, factor = res[counter]
+            rows, factor, spread, ncal = res[counter]
             disp = _per_dispatch(rows, counter, pat)
             if not disp or len({g for g, _ in disp.values()}) != 1:
                 per = None
                 break
-            per[counter] = (sum(v for _, v in disp.values()) / len(disp), factor, len(disp))
+            per[counter] = (sum(v for _, v in disp.values()) / len(disp), factor, len(disp), spread, ncal)
         if not per:
             continue
-        fk, ff, n = per["FETCH_SIZE"]
-        wk, wf, _ = per["WRITE_SIZE"]
+        fk, ff, n, fs, fn = per["FETCH_SIZE"]
+        wk, wf, _, ws, wn = per["WRITE_SIZE"]
         rec = {"stage": stage, "workload": workload, "kernel": pat, "dispatches": n,
                "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
                "copy_calibration_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+               "fetch_factor_spread": [round(fs[0], 4), round(fs[1], 4)],
+               "write_factor_spread": [round(ws[0], 4), round(ws[1], 4)],
+               "calibration_dispatches": [fn, wn],
                "bytes_per_launch": int((fk * ff + wk * wf) * 1024),
                "source_sha": kernel_source_sha(STAGE_SOURCES[stage]), "commands": commands}
         path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{stage}_{workload}.json")
@@ -250,6 +256,39 @@ def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands, out_dir=
             json.dump(rec, fh, indent=1)
         written.append(path)
     return written
+
+
+def trace_summary(stats_csv, workload, command, bench_line, out_dir=None):
+    """profiles/<stage>_<workload>.md: the rocprofv3 --kernel-trace --stats
+    table of a bench.py run, with the bench line of the same run and the
+    hash of the kernel sources it was taken on."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    line = json.loads(bench_line)
+    rf = line.get("roofline") or {}
+    stage = rf.get("kernel", "step")
+    srcs = sorted({f for v in STAGE_SOURCES.values() for f in v})
+    out = [f"# {stage} on the {workload} workload", "",
+           f"Kernel sources (sha256 of {', '.join(srcs)}, first 16 hex): `{kernel_source_sha(srcs)}`;"
+           f" dominant-stage sources: `{kernel_source_sha(STAGE_SOURCES.get(stage, srcs))}`.", "",
+           "Command (`<repo>` is the repository root, `<out>` any output directory):", "",
+           f"    {command}", "", f"Workload: {DESCR.get(workload, workload)}.", "",
+           "## rocprofv3 kernel statistics (all calls, including warmup and context setup)", "",
+           "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows[:12]:
+        name = r["Name"][:90]
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    out += ["", "## bench.py line of the same run (stage times from HIP events on the library's stream)", "",
+            f"- value: {line['value']} {line['unit']}, ms_per_step {line['ms_per_step']}"]
+    if rf:
+        out.append(f"- dominant stage `{stage}`: {rf['kernel_ms']} ms per launch, {rf['achieved']} {rf['unit']} = "
+                   f"{100 * rf['frac']:.1f}% of {rf['peak']} ({rf['bound']} bound)")
+    out.append("- stage ms per launch: " + ", ".join(f"{k} {v}" for k, v in line.get("stages_ms", {}).items()))
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{stage}_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    return path
 
 
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU_MFMA_MOPS_BF16"]
@@ -367,68 +406,75 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
 
 # ----------------------------------------------------------------------------
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="draft_block_bf16", choices=sorted(DESCR))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
-    ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass (no roofline)")
-    ap.add_argument("--flushed-steps", type=int, default=10,
-                    help="decode workloads: calls timed one by one after writing 512 MiB (evicts the 256 MB "
-                         "Infinity Cache); reported as mall_flushed, 0 = skip")
-    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
-                    help="first run a plain elementwise copy of MIB MiB three times (HBM counter calibration)")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/traffic_*.json from two rocprofv3 --pmc runs of this workload "
-                         "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibrate; no GPU work")
-    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
-                    help="write profiles/mfma_<workload>.json from one rocprofv3 --pmc run of this workload "
-                         "with the MFMA counters; no GPU work")
-    args = ap.parse_args()
-    if args.mfma_summary:
-        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
-               f" --output-format csv -d <out> -o run -- python3 <repo>/bench.py --workload {args.workload} "
-               f"--steps {args.steps} --warmup {args.warmup} --cpu-seconds 0")
-        print("wrote", mfma_summary(args.mfma_summary, args.workload, cmd))
-        return
-    if args.traffic_summary:
-        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
-               f"python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
-               f"--cpu-seconds 0 --copy-calibrate {args.copy_calibrate}")
-        for p in traffic_summary(*args.traffic_summary, args.workload, args.copy_calibrate,
-                                 [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")]):
-            print("wrote", p)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(each GPU would run its own sequences with no exchange).", file=sys.stderr)
-        sys.exit(2)
+# ----------------------------------------------------------------------------
+# measured roofline denominators (libmla_peaks.so)
+# ----------------------------------------------------------------------------
 
-    import torch
+def measured_peaks(torch):
+    """HBM copy and read bandwidth over 2 GiB buffers (8x the Infinity Cache)
+    and the bf16 MFMA issue rate of a register-only MFMA loop, each the best
+    of three timed launches (HIP events on the current stream)."""
+    import ctypes as C
+    path = os.path.join(ROOT, "draft_models_amd", "libmla_peaks.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = C.CDLL(path)
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+    lib.peaks_copy.argtypes = [vp, vp, i64, i32, vp]
+    lib.peaks_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.peaks_mfma.argtypes = [i32, i32, i32, vp, vp]
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    blocks = 256 * 16
+    red = torch.empty(blocks, dtype=torch.int32, device="cuda")
+
+    def best(fn, n=3):
+        t = []
+        for _ in range(n + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if fn() != 0:
+                raise RuntimeError("peaks kernel launch failed")
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t[1:])  # the first launch loads the code object
+    copy_ms = best(lambda: lib.peaks_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, st))
+    read_ms = best(lambda: lib.peaks_read(src.data_ptr(), nbytes, blocks, red.data_ptr(), st))
+    del src, dst, red
+    res = {"hbm_copy_gbs": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1),
+           "hbm_read_gbs": round(nbytes / (read_ms / 1e3) / 1e9, 1), "buffer_gib": nbytes >> 30}
+    mblocks, iters = 256 * 8, 4000
+    out = torch.empty(mblocks * 256, dtype=torch.float32, device="cuda")
+    for shape, flops in ((32, 32768), (16, 16384)):
+        ms = best(lambda: lib.peaks_mfma(shape, iters, mblocks, out.data_ptr(), st))
+        res[f"mfma_bf16_{shape}x{shape}x{512 // shape}_tflops"] = round(
+            mblocks * 4 * 4 * iters * flops / (ms / 1e3) / 1e12, 1)
+    del out
+    res["mfma_bf16_tflops"] = max(v for k, v in res.items() if k.startswith("mfma_bf16_") and k.endswith("tflops"))
+    return res
+
+
+# ----------------------------------------------------------------------------
+# one workload
+# ----------------------------------------------------------------------------
+
+def measure(name, args, torch, peaks=None):
+    """Time one workload through its entry point; returns its JSON object."""
     import mla_synth as ms
     from mla_synth.device import upload
     from draft_models_amd import binding as B
 
-    if args.copy_calibrate > 0:
-        # a plain elementwise kernel of known traffic: reads and writes copy_calibrate MiB
-        n = args.copy_calibrate * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-
-    block = args.workload in BLOCK_OF
-    sparse = args.workload in SPARSE_OF
-    base = BLOCK_OF.get(args.workload, SPARSE_OF.get(args.workload, FP8_OF.get(args.workload, (args.workload,)))[0])
-    w = ms.make_workload(base, kv_scale=FP8_OF[args.workload][1] if args.workload in FP8_OF else 0.0)
+    block = name in BLOCK_OF
+    sparse = name in SPARSE_OF
+    base = BLOCK_OF.get(name, SPARSE_OF.get(name, FP8_OF.get(name, (name,)))[0])
+    w = ms.make_workload(base, kv_scale=FP8_OF[name][1] if name in FP8_OF else 0.0)
     t = upload(w)
     topk = lists = None
     if sparse:
-        topk = ms.draw_topk(w, SPARSE_OF[args.workload][1], ms.SPARSE_TOPK_SEED)
+        topk = ms.draw_topk(w, SPARSE_OF[name][1], ms.SPARSE_TOPK_SEED)
         lists = torch.from_numpy(topk).cuda()
     d = w.dims
     max_kv = int(w.kv_lens.max())
@@ -456,17 +502,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # the timed region: K steps with no per-stage events (recording them costs
-    # 15-20 % of a decode step)
+    # the timed region: K steps back to back, no per-stage events
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     ev0.record()
     for _ in range(args.steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
-    total_ms = ev0.elapsed_time(ev1)
-    ms_step = total_ms / args.steps
+    ms_step = ev0.elapsed_time(ev1) / args.steps
     # decode: calls timed one by one, each after a 512 MiB write that evicts
     # the Infinity Cache (the back-to-back figure above is the headline)
     flushed = None
@@ -483,12 +526,18 @@ def main():
             times.append(e0.elapsed_time(e1))
         del scratch
         flushed = {"ms_per_step_median": round(float(np.median(times)), 5), "steps": len(times), "flush_mib": 512}
-    # then a separate pass of the same steps with the library's stage events
-    # (HIP events on its own stream) for the per-kernel times of the roofline
+    # per-stage times: a separate pass of the same steps with the library's
+    # stage events (HIP events recorded on the call's stream around each
+    # stage's launches). The steps are queued behind a GPU spin of about
+    # 0.1 s so that every launch is in the queue before the GPU reaches it:
+    # a stage's events then bracket its kernels with no host gap.
     stages = {}
     if not args.no_profile:
         m.profile(True)
         m.profile_read()  # clear
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(200_000_000)
         for _ in range(max(3, min(args.steps, 10))):
             step()
         stages = m.profile_read()
@@ -512,18 +561,24 @@ def main():
         if hbm:
             bound, peak, unit_r = "hbm", HBM_PEAK_GBS, "GB/s"
             achieved = (wk.get("bytes") or 0) / (dom_ms / 1e3) / 1e9
+            mpeak = (peaks or {}).get("hbm_read_gbs")
         else:
             bound, peak, unit_r = "mfma", MFMA_PEAK_TFLOPS[d.dtype], "TFLOP/s"
             achieved = wk.get("flops", 0) / (dom_ms / 1e3) / 1e12
+            mpeak = (peaks or {}).get("mfma_bf16_tflops") if d.dtype == "bf16" else None
         roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                     "unit": unit_r, "frac": round(achieved / peak, 4),
-                    "traffic": measured_traffic(dom, args.workload), "kernel_ms": round(dom_ms, 5)}
+                    "traffic": measured_traffic(dom, name), "kernel_ms": round(dom_ms, 5),
+                    "algorithmic": (wk.get("bytes") if hbm else wk.get("flops"))}
+        if mpeak:
+            roofline["measured_peak"] = mpeak
+            roofline["frac_of_measured"] = round(achieved / mpeak, 4)
 
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": d.dtype, "data": "synthetic (seeded, random-init weights)",
-        "config": {"workload": args.workload, "description": DESCR[args.workload], "batch": w.batch,
+        "config": {"workload": name, "description": DESCR[name], "batch": w.batch,
                    "new_tokens": w.total_tokens, "max_kv_len": max_kv, "entry_point":
                        "mla_decode_absorbed_block" if block else ("mla_decode_absorbed_sparse" if sparse else
                        ("mla_prefill_expanded" if prefill else "mla_decode_absorbed")),
@@ -540,11 +595,104 @@ def main():
         flushed["unit"] = unit
         res["mall_flushed"] = flushed
     m.close()
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block, topk=topk)
-    else:
-        res["cpu_baseline"] = None
-    print(json.dumps(res), flush=True)
+    del t, out, lists
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    res["_w"] = (w, block, topk)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, choices=sorted(DESCR),
+                    help="measure this one workload (default: the prefill and decode headline pair)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget per workload (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true", help="skip the profiled pass (no roofline)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak kernels")
+    ap.add_argument("--flushed-steps", type=int, default=10,
+                    help="decode workloads: calls timed one by one after writing 512 MiB (evicts the 256 MB "
+                         "Infinity Cache); reported as mall_flushed, 0 = skip")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="first run a plain elementwise copy of MIB MiB five times, each after a 512 MiB "
+                         "eviction write (HBM counter calibration)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_*.json from two rocprofv3 --pmc runs of --workload "
+                         "(FETCH_SIZE, WRITE_SIZE) made with --copy-calibrate; no GPU work")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write profiles/mfma_<workload>.json from one rocprofv3 --pmc run of --workload "
+                         "with the MFMA counters; no GPU work")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="write profiles/<stage>_<workload>.md from the kernel_stats.csv of a rocprofv3 "
+                         "--kernel-trace --stats run of --workload and that run's bench line; no GPU work")
+    args = ap.parse_args()
+    if args.mfma_summary or args.traffic_summary or args.trace_summary:
+        if not args.workload:
+            raise SystemExit("the summary modes need --workload")
+    if args.mfma_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
+               f" --output-format csv -d <out> -o run -- python3 <repo>/bench.py --workload {args.workload} "
+               f"--steps {args.steps} --warmup {args.warmup} --cpu-seconds 0 --no-peaks")
+        print("wrote", mfma_summary(args.mfma_summary, args.workload, cmd))
+        return
+    if args.traffic_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
+               f"python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
+               f"--cpu-seconds 0 --no-peaks --copy-calibrate {args.copy_calibrate}")
+        for p in traffic_summary(*args.traffic_summary, args.workload, args.copy_calibrate,
+                                 [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")]):
+            print("wrote", p)
+        return
+    if args.trace_summary:
+        cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> "
+               f"-o run -- python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} "
+               f"--warmup {args.warmup} --cpu-seconds 0 --no-peaks")
+        line = next(ln for ln in open(args.trace_summary[1]) if ln.startswith("{"))
+        print("wrote", trace_summary(args.trace_summary[0], args.workload, cmd, line))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each GPU would run its own sequences with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibrate > 0:
+        # a plain elementwise kernel of known traffic (reads and writes
+        # copy_calibrate MiB), each launch after a 512 MiB write that evicts
+        # the Infinity Cache
+        n = args.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        evict = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+        for _ in range(5):
+            evict.fill_(2.0)
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst, evict
+
+    peaks = None if args.no_peaks else measured_peaks(torch)
+    names = [args.workload] if args.workload else ["prefill_bf16", "decode_bf16"]
+    results = [measure(nm, args, torch, peaks) for nm in names]
+    for r in results:
+        w, block, topk = r.pop("_w")
+        if args.cpu_seconds > 0:
+            r["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, absorbed=block, topk=topk)
+        else:
+            r["cpu_baseline"] = None
+    line = results[0]
+    if len(results) > 1:
+        dec = results[1]
+        for k in ("metric", "n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline", "data"):
+            dec.pop(k, None)
+        line["decode"] = dec
+        line["config"]["headline"] = ("value: prefill TFLOP/s (mla_prefill_expanded); decode: latent-cache GB/s "
+                                      "(mla_decode_absorbed)")
+    if peaks is not None:
+        line["measured_peaks"] = peaks
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

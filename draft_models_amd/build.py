@@ -47,6 +47,26 @@ def _compile(src: str) -> str:
     return obj
 
 
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_OUT = os.path.join(PKG, "libmla_peaks.so")
+
+
+def build_peaks(verbose: bool = True) -> str:
+    """libmla_peaks.so: the measured-roofline kernels (copy, read, MFMA loop)
+    used by bench.py; separate from the MLA library."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    obj = _compile(PEAKS_SRC)
+    tmp = PEAKS_OUT + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", obj, "-o", tmp], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, PEAKS_OUT)
+    if verbose:
+        print(f"built {PEAKS_OUT}")
+    return PEAKS_OUT
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
@@ -66,3 +86,4 @@ def build(verbose: bool = True) -> str:
 
 if __name__ == "__main__":
     build()
+    build_peaks()
