@@ -12,6 +12,8 @@ Sources (web pages, cited by title and section):
     Structure) and PR "extract GQA/MLA attention into reusable layers"
     (Modifications, Accuracy Test).
 
+The gradient of the expanded layer (training form) is in oracle.backward.
+
 Parity status: every function is pinned by the CPU tests (tests/oracle_pins.py,
 run by tests/test_oracle.py) except the
 choices the pages leave open (RMSNorm eps value, softmax scale, RoPE theta,

@@ -421,3 +421,109 @@ def pin_fp8_cache(w, kv_scale: float):
         out2, ent2, _ = om.forward_sequence(d, W, x[-1:], pre2, w.mask_kind, w.window, kv_scale=kv_scale)
         assert np.array_equal(ent2[0], ent[-1])
         assert np.max(np.abs(out2[0] - out[-1])) <= 1e-12 * max(1.0, np.abs(out[-1]).max())
+
+
+# --------------------------------------------------------------------------
+# gradient of the expanded layer (training form)
+# --------------------------------------------------------------------------
+
+def _loss(dims, W, x, mask, window, dout, lo, hi):
+    """<dout, out> of the oracle's forward on one training sequence (no prefix)."""
+    pre = np.zeros((0, dims.kv_lora_rank + dims.qk_rope_head_dim))
+    out, _, _ = om.forward_sequence(dims, W, x, pre, mask, window, row_lo=lo, row_hi=hi)
+    return float(np.sum(out * dout))
+
+
+def pin_backward_fd(w, rows=None, seed: int = 21):
+    """Every gradient of oracle.backward against central finite differences
+    of the oracle's forward (an independent code path: the forward is pinned
+    on its own), along a random direction per tensor and at a few single
+    elements. Five-point central stencil (truncation O(h^4)), h = 1e-4;
+    agreement 1e-6 relative, plus the rounding of the loss differences
+    (1e-14 sum|dout * out| / h)."""
+    from oracle import backward as ob
+    d, W = w.dims, {k: np.asarray(v, np.float64) for k, v in w.weights.items()}
+    x = np.asarray(w.x, np.float64)
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((x.shape[0], d.hidden_size))
+    lo, hi = (None, None) if rows is None else rows
+    dx, dW, out = ob.backward_sequence(d, W, x, w.mask_kind, dout, w.window, lo, hi)
+    pre = np.zeros((0, d.entry_dim))
+    ref_out, _, _ = om.forward_sequence(d, W, x, pre, w.mask_kind, w.window, row_lo=lo, row_hi=hi)
+    assert np.max(np.abs(out - ref_out)) <= 1e-12 * max(1.0, np.abs(ref_out).max())
+    eps = 1e-4
+    L0 = float(np.sum(np.abs(dout * ref_out)))
+    tensors = {"x": (x, dx)}
+    tensors.update({k: (W[k], dW[k]) for k in W})
+    assert set(dW) == set(W), (set(dW), set(W))
+    for name, (val, grad) in tensors.items():
+        dirs = [rng.standard_normal(val.shape)]
+        for _ in range(2):
+            e = np.zeros(val.size)
+            e[rng.integers(val.size)] = 1.0
+            dirs.append(e.reshape(val.shape))
+        for u in dirs:
+            def at(t):
+                if name == "x":
+                    return _loss(d, W, val + t * u, w.mask_kind, w.window, dout, lo, hi)
+                W2 = dict(W)
+                W2[name] = val + t * u
+                return _loss(d, W2, x, w.mask_kind, w.window, dout, lo, hi)
+            fd = (8 * (at(eps) - at(-eps)) - (at(2 * eps) - at(-2 * eps))) / (12 * eps)
+            an = float(np.sum(grad * u))
+            scale = max(1e-3, abs(fd), np.sqrt(np.sum(grad * grad)) * np.sqrt(np.sum(u * u)) * 1e-3)
+            assert abs(fd - an) <= 1e-6 * scale + 1e-14 * L0 / eps, (name, fd, an)
+
+
+def pin_backward_autograd(w, seed: int = 22):
+    """oracle.backward against torch.autograd of a float64 torch forward built
+    from torch's own primitives (linear layers as matmuls, rms_norm, RoPE as a
+    complex rotation, scaled_dot_product_attention with a boolean mask).
+    Masks with at least one visible key per row. Agreement 1e-10 relative."""
+    from oracle import backward as ob
+    d = w.dims
+    W = {k: torch.tensor(np.asarray(v, np.float64), requires_grad=True) for k, v in w.weights.items()}
+    x = torch.tensor(np.asarray(w.x, np.float64), requires_grad=True)
+    S, H, n, r, c, dv = x.shape[0], d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank, d.v_head_dim
+    pos = torch.arange(S, dtype=torch.float64)
+    inv = d.rope_theta ** (-2.0 * torch.arange(r // 2, dtype=torch.float64) / r)
+    rot = torch.polar(torch.ones(S, r // 2, dtype=torch.float64), pos[:, None] * inv[None, :])
+
+    def rope(t):  # t [S, ..., r]
+        if d.rope_style == om.ROPE_NEOX:
+            z = torch.complex(t[..., : r // 2], t[..., r // 2:])
+        else:
+            z = torch.complex(t[..., 0::2], t[..., 1::2])
+        z = z * rot.reshape((S,) + (1,) * (t.dim() - 2) + (r // 2,))
+        if d.rope_style == om.ROPE_NEOX:
+            return torch.cat([z.real, z.imag], dim=-1)
+        return torch.stack([z.real, z.imag], dim=-1).reshape(t.shape)
+
+    rms = lambda t, g: torch.nn.functional.rms_norm(t, (t.shape[-1],), g, eps=d.rms_norm_eps)
+    if d.q_lora_rank > 0:
+        q = rms(x @ W["q_a_proj"].T, W["q_a_layernorm"]) @ W["q_b_proj"].T
+    else:
+        q = x @ W["q_proj"].T
+    q = q.reshape(S, H, n + r)
+    kv = x @ W["kv_a_proj_with_mqa"].T
+    cn = rms(kv[:, :c], W["kv_a_layernorm"])
+    Q = torch.cat([q[..., :n], rope(q[..., n:])], dim=-1)
+    kvb = (cn @ W["kv_b_proj"].T).reshape(S, H, n + dv)
+    K = torch.cat([kvb[..., :n], rope(kv[:, c:])[:, None, :].expand(S, H, r)], dim=-1)
+    vis = np.zeros((S, S), dtype=bool)
+    for i in range(S):
+        a, b = om.visible_interval(i, S, w.mask_kind, w.window)
+        vis[i, a:b] = True
+    assert vis.any(axis=1).all()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        Q.transpose(0, 1), K.transpose(0, 1), kvb[..., n:].transpose(0, 1), attn_mask=torch.from_numpy(vis),
+        scale=1.0 / math.sqrt(n + r)).transpose(0, 1).reshape(S, H * dv)
+    if d.use_output_gate:
+        o = o * torch.sigmoid(x @ W["g_proj"].T)
+    out = o @ W["o_proj"].T
+    dout = np.random.default_rng(seed).standard_normal((S, d.hidden_size))
+    out.backward(torch.from_numpy(dout))
+    dx, dW, _ = ob.backward_sequence(d, w.weights, w.x, w.mask_kind, dout, w.window)
+    assert _rel(dx, x.grad.numpy()) <= 1e-10
+    for k in W:
+        assert _rel(dW[k], W[k].grad.numpy()) <= 1e-10, k

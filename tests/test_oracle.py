@@ -277,3 +277,85 @@ def test_mutation_fp8_scale_inverted(monkeypatch):
     monkeypatch.setattr(om, "fp8_quantize",
                         lambda x, s: om.fp8_e4m3_decode(om.fp8_e4m3_encode(np.asarray(x, np.float64) * s)) / s)
     _expect_fail(P.pin_fp8_cache, _tiny(), 0.0625)
+
+
+# ------------------------------------------------------------ backward pass
+
+def _train(mask=ms.MASK_CAUSAL, window=0, S=9, **dims_kw):
+    return ms.make_workload("tiny", dims=P.tiny_dims(**dims_kw), seed=6, q_lens=[S], prefix_lens=[0],
+                            mask_kind=mask, window=window, gamma_noise=True)
+
+
+_BW_VARIANTS = [
+    dict(),
+    dict(q_lora_rank=12, use_output_gate=True, rope_style=om.ROPE_INTERLEAVED),
+]
+
+
+@pytest.mark.parametrize("variant", _BW_VARIANTS)
+@pytest.mark.parametrize("mask,window", [(ms.MASK_CAUSAL, 0), (ms.MASK_FULL, 0), (ms.MASK_SLIDING, 3)])
+def test_backward_finite_differences(variant, mask, window):
+    P.pin_backward_fd(_train(mask, window, **variant))
+
+
+def test_backward_finite_differences_dropped_rows():
+    # explicit intervals: an empty row (its output is the constant 0) and a
+    # row that sees only earlier keys
+    lo = np.array([0, 0, 0, 5, 0, 0, 1, 0, 0])
+    hi = np.array([1, 2, 3, 5, 5, 6, 4, 8, 9])
+    P.pin_backward_fd(_train(q_lora_rank=12, use_output_gate=True), rows=(lo, hi))
+
+
+@pytest.mark.parametrize("variant", _BW_VARIANTS)
+@pytest.mark.parametrize("mask,window", [(ms.MASK_CAUSAL, 0), (ms.MASK_SLIDING, 4)])
+def test_backward_autograd(variant, mask, window):
+    P.pin_backward_autograd(_train(mask, window, **variant))
+
+
+def test_mutation_backward_softmax_no_row_term(monkeypatch):
+    # dS = P * dP (the row term sum_j P_j dP_j left out)
+    from oracle import backward as ob
+
+    def bad(q, k, v, lo, hi, scale, do):
+        _, _, Pr = om.attention_core(q, k, v, lo, hi, scale, return_probs=True)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for h in range(q.shape[1]):
+            Ph = Pr[:, h, :]
+            dv[:, h] = Ph.T @ do[:, h]
+            dS = Ph * (do[:, h] @ v[:, h].T)
+            dq[:, h], dk[:, h] = scale * dS @ k[:, h], scale * dS.T @ q[:, h]
+        return dq, dk, dv
+    monkeypatch.setattr(ob, "attention_backward", bad)
+    _expect_fail(P.pin_backward_fd, _train())
+
+
+def test_mutation_backward_rope_forward_turn(monkeypatch):
+    # the gradient turned by +angle instead of -angle
+    from oracle import backward as ob
+    monkeypatch.setattr(ob, "rope_backward", lambda dy, pos, theta, style: om.apply_rope(dy, pos, theta, style))
+    _expect_fail(P.pin_backward_fd, _train())
+
+
+def test_mutation_backward_rope_key_one_head(monkeypatch):
+    # the shared rope key's gradient taken from head 0 only
+    from oracle import backward as ob
+    orig = ob.attention_backward
+
+    def bad(q, k, v, lo, hi, scale, do):
+        dq, dk, dv = orig(q, k, v, lo, hi, scale, do)
+        dk = dk.copy()
+        dk[:, 1:, -k.shape[2] + q.shape[2] - 6:] = 0.0  # rope part (r = 6) of heads >= 1
+        return dq, dk, dv
+    monkeypatch.setattr(ob, "attention_backward", bad)
+    _expect_fail(P.pin_backward_fd, _train())
+
+
+def test_mutation_backward_rmsnorm_no_mean_term(monkeypatch):
+    # dx = rho * dy * gamma only (the statistic's own dependence left out)
+    from oracle import backward as ob
+
+    def bad(x, gamma, eps, dy):
+        rho = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+        return rho * dy * gamma, np.sum(dy * x * rho, axis=0)
+    monkeypatch.setattr(ob, "rms_norm_backward", bad)
+    _expect_fail(P.pin_backward_fd, _train())
