@@ -60,6 +60,11 @@ DESCR["sparse_decode_bf16"] = ("the decode workload (64 sequences, cache length 
 DESCR["decode_fp8"] = ("the decode workload (64 sequences, cache length uniform in [1024, 8192], 128 heads, "
                        "q_lora 1536) over an 8-bit latent cache: OCP E4M3 codes with one per-tensor scale "
                        "(2^-5), 576 bytes per entry")
+DESCR["train_bf16"] = ("backward pass bf16 (mla_backward_expanded): 4 x 2048 causal training tokens at the "
+                       "draft-block model dims (hidden 4096, 32 heads, q_lora 1536, kv_lora 512, nope 128, rope 64, "
+                       "v 128, interleaved RoPE); dx and every weight gradient, forward recomputed in the call")
+# training workloads (the backward entry point)
+TRAIN = {"train_bf16"}
 # workloads that run another workload's data through mla_decode_absorbed_block
 BLOCK_OF = {"draft_block_absorbed_bf16": "draft_block_bf16"}
 # workloads that run a decode workload through mla_decode_absorbed_sparse: (base, list length)
@@ -98,6 +103,35 @@ def visible_counts(w):
                 lo, hi = max(0, p - w.window + 1), min(p + 1, L)
             counts.append(max(0, hi - lo))
     return np.asarray(counts, dtype=np.int64)
+
+
+def train_work(w, seqs=None):
+    """Algorithmic flops of one backward call (forward recomputation up to
+    the attention output, then the gradient): GEMMs 2 M N K each; the
+    attention forward 2 H (n + r + dv) per visible (query, key) pair and its
+    gradient 2 H (2 (n + r) + 2 dv) (dV, dP, dQ, dK; the recomputed scores are
+    not counted)."""
+    d = w.dims
+    H, n, r, c, dv, hid, ql = (d.num_heads, d.qk_nope_head_dim, d.qk_rope_head_dim, d.kv_lora_rank,
+                              d.v_head_dim, d.hidden_size, d.q_lora_rank)
+    sel = np.arange(w.batch) if seqs is None else np.asarray(seqs)
+    T = int(w.q_lens[sel].sum())
+    vis = visible_counts(w)
+    cu = w.cu_seqlens
+    pairs = int(sum(vis[cu[b]:cu[b + 1]].sum() for b in sel))
+    E = c + r
+    n1 = (ql if ql else H * (n + r)) + E + (H * dv if d.use_output_gate else 0)
+    f_qkv, f_qb = 2 * T * hid * n1, (2 * T * ql * H * (n + r) if ql else 0)
+    f_kvb, f_o = 2 * T * c * H * (n + dv), 2 * T * H * dv * hid
+    work = {"qkv_a_gemm": dict(flops=f_qkv, bytes=None), "kv_b_expand": dict(flops=f_kvb, bytes=None),
+            "prefill_attn": dict(flops=2 * pairs * H * (n + r + dv), bytes=None),
+            "attn_bwd": dict(flops=2 * pairs * H * (2 * (n + r) + 2 * dv), bytes=None),
+            "bwd_gemm": dict(flops=f_o + f_kvb + f_qb + f_qkv, bytes=None),
+            "wgrad_gemm": dict(flops=f_o + f_kvb + f_qb + f_qkv, bytes=None)}
+    if ql:
+        work["q_b_gemm"] = dict(flops=f_qb, bytes=None)
+    work["_step"] = dict(flops=sum(v["flops"] for v in work.values()), cache_bytes=0, bytes=0)
+    return work
 
 
 def stage_work(w, seqs=None, absorbed=False, topk=None):
@@ -374,7 +408,12 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
             first[b] = max(0, int(w.kv_lens[b]) - w.window)
         pre = w.prefix_rows[b][first.get(b, 0):]
         cu = w.cu_seqlens
-        if topk is not None:
+        if getattr(w, "_train_dout", None) is not None:
+            # the oracle's analytic gradient of the sequence
+            from oracle import backward as ob
+            ob.backward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], w.mask_kind, w._train_dout[cu[b]:cu[b + 1]],
+                                 w.window)
+        elif topk is not None:
             # the oracle's absorbed form over the listed entries (pinned equal
             # to its expanded form, which expands every entry of the sequence)
             om.forward_sequence(w.dims, w.weights, w.x[cu[b]:cu[b + 1]], pre, w.mask_kind, w.window,
@@ -386,7 +425,8 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    work = stage_work(w, seqs=done, absorbed=absorbed, topk=topk)  # counted like the GPU line
+    train = getattr(w, "_train_dout", None) is not None
+    work = train_work(w, seqs=done) if train else stage_work(w, seqs=done, absorbed=absorbed, topk=topk)
     per, unit = step_value(w, work)
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
@@ -400,7 +440,7 @@ def cpu_baseline(w, budget_s: float, absorbed: bool = False, topk=None):
     return {"value": per / el, "unit": unit, "cores": int(threads), "kind": "oracle",
             "cpu_model": model, "blas": ", ".join(blas),
             "sample": f"{len(done)} of {w.batch} sequences (ids {sorted(done)}), "
-                      f"{'absorbed' if topk is not None else 'expanded'} fp64 oracle, "
+                      f"{'gradient' if train else ('absorbed' if topk is not None else 'expanded')} fp64 oracle, "
                       f"{el:.1f} s wall", "wall_s": round(el, 3)}
 
 
@@ -469,9 +509,11 @@ def measure(name, args, torch, peaks=None):
 
     block = name in BLOCK_OF
     sparse = name in SPARSE_OF
+    train = name in TRAIN
     base = BLOCK_OF.get(name, SPARSE_OF.get(name, FP8_OF.get(name, (name,)))[0])
     w = ms.make_workload(base, kv_scale=FP8_OF[name][1] if name in FP8_OF else 0.0)
     t = upload(w)
+    w._train_dout = ms.draw_dout(w, ms.TRAIN_DOUT_SEED) if train else None
     topk = lists = None
     if sparse:
         topk = ms.draw_topk(w, SPARSE_OF[name][1], ms.SPARSE_TOPK_SEED)
@@ -479,17 +521,25 @@ def measure(name, args, torch, peaks=None):
     d = w.dims
     max_kv = int(w.kv_lens.max())
     prefill = w.mode == "prefill"
+    max_q = int(w.q_lens.max())
+    lp = -(-max_q // d.page_size) * d.page_size
     cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_kv,
-                        max_prefill_kv=w.batch * max_kv if prefill and not block else 0,
+                        max_prefill_kv=(w.batch * (lp if train else max_kv)) if prefill and not block else 0,
                         max_block_tokens=w.total_tokens if block else 0,
-                        max_topk=0 if topk is None else topk.shape[1], kv_scale=w.kv_scale)
+                        max_topk=0 if topk is None else topk.shape[1], kv_scale=w.kv_scale,
+                        max_train_tokens=w.total_tokens if train else 0)
     m = B.MLA(cfg, t["weights"])
     dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
     out = torch.empty((w.total_tokens, d.hidden_size), dtype=dt, device="cuda")
-    max_q = int(w.q_lens.max())
+    if train:
+        from mla_synth.device import to_torch
+        dout_t = to_torch(w._train_dout, d.dtype, "cuda")
+        grads = {k: torch.empty_like(v) for k, v in t["weights"].items()}
 
     def step():
-        if block:
+        if train:
+            m.backward(t["x"], t["cu_seqlens"], max_q, w.mask_kind, w.window, dout_t, out, grads)
+        elif block:
             m.decode_block(t["x"], max_q, t["cache"], t["block_table"], t["prefix_lens"], max_kv, out)
         elif prefill:
             m.prefill(t["x"], t["cu_seqlens"], t["prefix_lens"], max_q, max_kv, t["cache"], t["block_table"],
@@ -543,7 +593,7 @@ def measure(name, args, torch, peaks=None):
         stages = m.profile_read()
         m.profile(False)
 
-    work = stage_work(w, absorbed=block, topk=topk)
+    work = train_work(w) if train else stage_work(w, absorbed=block, topk=topk)
     per_step, unit = step_value(w, work)
     value = per_step / (ms_step / 1e3)
 
@@ -580,8 +630,9 @@ def measure(name, args, torch, peaks=None):
         "vs_baseline": None, "dtype": d.dtype, "data": "synthetic (seeded, random-init weights)",
         "config": {"workload": name, "description": DESCR[name], "batch": w.batch,
                    "new_tokens": w.total_tokens, "max_kv_len": max_kv, "entry_point":
-                       "mla_decode_absorbed_block" if block else ("mla_decode_absorbed_sparse" if sparse else
-                       ("mla_prefill_expanded" if prefill else "mla_decode_absorbed")),
+                       "mla_backward_expanded" if train else
+                       ("mla_decode_absorbed_block" if block else ("mla_decode_absorbed_sparse" if sparse else
+                        ("mla_prefill_expanded" if prefill else "mla_decode_absorbed"))),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "stages_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in timed.items()},
@@ -595,6 +646,8 @@ def measure(name, args, torch, peaks=None):
         flushed["unit"] = unit
         res["mall_flushed"] = flushed
     m.close()
+    if train:
+        del grads, dout_t
     del t, out, lists
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -21,10 +21,11 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 MASK_FULL, MASK_CAUSAL, MASK_SLIDING = 0, 1, 2
 
-EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_decode_absorbed", "mla_decode_absorbed_block",
+EXPORTS = ("mla_init_weights", "mla_prefill_expanded", "mla_backward_expanded", "mla_decode_absorbed",
+           "mla_decode_absorbed_block",
            "mla_decode_absorbed_sparse", "mla_decode_absorbed_noalloc", "mla_free", "mla_last_error",
            "mla_profile_enable", "mla_profile_read", "mla_profile_stage_name")
-NUM_STAGES = 13
+NUM_STAGES = 17
 
 
 class MLAError(RuntimeError):
@@ -41,7 +42,7 @@ class mla_config(C.Structure):
                 ("use_output_gate", C.c_int32), ("dtype", C.c_int32), ("page_size", C.c_int32),
                 ("max_batch", C.c_int32), ("max_tokens", C.c_int32), ("max_seq_len", C.c_int32),
                 ("max_prefill_kv", C.c_int32), ("max_block_tokens", C.c_int32), ("max_topk", C.c_int32),
-                ("kv_cache_dtype", C.c_int32), ("kv_cache_scale", C.c_float)]
+                ("kv_cache_dtype", C.c_int32), ("kv_cache_scale", C.c_float), ("max_train_tokens", C.c_int32)]
 
 KV_CACHE_COMPUTE, KV_CACHE_FP8_E4M3 = 0, 1
 
@@ -51,6 +52,10 @@ WEIGHT_NAMES = ("q_a_proj", "q_a_layernorm", "q_b_proj", "q_proj", "kv_a_proj_wi
 
 
 class mla_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_NAMES]
+
+
+class mla_grads(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in WEIGHT_NAMES]
 
 
@@ -71,6 +76,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     lib.mla_prefill_expanded.argtypes = [vp, vp, i32, i32, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32,
                                          vp, vp, vp, vp]
     lib.mla_prefill_expanded.restype = C.c_int
+    lib.mla_backward_expanded.argtypes = [vp, vp, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp, C.POINTER(mla_grads),
+                                          vp]
+    lib.mla_backward_expanded.restype = C.c_int
     lib.mla_decode_absorbed.argtypes = [vp, vp, i32, vp, i32, vp, i32, vp, i32, i32, i32, vp, vp]
     lib.mla_decode_absorbed.restype = C.c_int
     lib.mla_decode_absorbed_block.argtypes = [vp, vp, i32, i32, vp, i32, vp, i32, vp, i32, vp, vp]
@@ -115,7 +123,7 @@ def _stream(stream) -> Optional[int]:
 
 def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_prefill_kv: int,
                 softmax_scale: float = 0.0, max_block_tokens: int = 0, max_topk: int = 0,
-                kv_scale: float = 0.0) -> mla_config:
+                kv_scale: float = 0.0, max_train_tokens: int = 0) -> mla_config:
     """mla_config from an object with the model-dimension attributes; kv_scale
     > 0 selects the 8-bit (E4M3) cache with that per-tensor scale."""
     return mla_config(
@@ -127,7 +135,8 @@ def make_config(dims, *, max_batch: int, max_tokens: int, max_seq_len: int, max_
         dtype=DTYPE_BF16 if dims.dtype == "bf16" else DTYPE_F32, page_size=dims.page_size,
         max_batch=max_batch, max_tokens=max_tokens, max_seq_len=max_seq_len,
         max_prefill_kv=max_prefill_kv, max_block_tokens=max_block_tokens, max_topk=max_topk,
-        kv_cache_dtype=KV_CACHE_FP8_E4M3 if kv_scale > 0 else KV_CACHE_COMPUTE, kv_cache_scale=float(kv_scale))
+        kv_cache_dtype=KV_CACHE_FP8_E4M3 if kv_scale > 0 else KV_CACHE_COMPUTE, kv_cache_scale=float(kv_scale),
+        max_train_tokens=max_train_tokens)
 
 
 class MLA:
@@ -146,6 +155,15 @@ class MLA:
             self.ctx, _ptr(x), cu_seqlens.numel() - 1, x.shape[0], _ptr(cu_seqlens), _ptr(prefix_lens),
             max_q_len, max_kv_len, _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
             block_table.shape[1], mask_kind, window, _ptr(row_lo), _ptr(row_hi), _ptr(out), _stream(stream)))
+
+    def backward(self, x, cu_seqlens, max_q_len: int, mask_kind: int, window: int, dout, dx,
+                 grads: Dict[str, "object"], row_lo=None, row_hi=None, stream=None):
+        """Gradient of the expanded layer on training sequences: dx and the
+        weight gradients named in grads (tensors shaped like the weights)."""
+        g = mla_grads(**{n: _ptr(grads.get(n)) for n in WEIGHT_NAMES})
+        _check(self._lib.mla_backward_expanded(
+            self.ctx, _ptr(x), cu_seqlens.numel() - 1, x.shape[0], _ptr(cu_seqlens), max_q_len, mask_kind, window,
+            _ptr(row_lo), _ptr(row_hi), _ptr(dout), _ptr(dx), C.byref(g), _stream(stream)))
 
     def decode(self, x, kv_cache, block_table, seq_lens, max_seq_len: int, mask_kind: int, window: int, out,
                stream=None):

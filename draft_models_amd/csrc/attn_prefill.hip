@@ -246,6 +246,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
     const int t = t0 + qi[qb];
     if (t >= a.total_tokens) continue;
     const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+    if (a.lse && g == 0) a.lse[(int64_t)t * a.H + h] = l[qb] > 0.f ? m[qb] + __log2f(l[qb]) : -INFINITY;
     T* orow = reinterpret_cast<T*>(a.out) + (int64_t)t * a.ldo + (int64_t)h * a.dv;
     const T* grow = a.gate ? reinterpret_cast<const T*>(a.gate) + (int64_t)t * a.ldg + (int64_t)h * a.dv : nullptr;
 #pragma unroll
@@ -598,6 +599,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     const int t = t0 + qi[qb];
     if (t >= a.total_tokens) continue;
     const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
+    if (a.lse && g == 0) a.lse[(int64_t)t * a.H + h] = l[qb] > 0.f ? m[qb] + __log2f(l[qb]) : -INFINITY;
     bf16* orow = reinterpret_cast<bf16*>(a.out) + (int64_t)t * a.ldo + (int64_t)h * a.dv;
     const bf16* grow = a.gate ? reinterpret_cast<const bf16*>(a.gate) + (int64_t)t * a.ldg + (int64_t)h * a.dv : nullptr;
 #pragma unroll

@@ -50,6 +50,8 @@ struct PrefillAttnArgs {
   MaskArgs mask;
   void* out = nullptr; int64_t ldo = 0;             // [T, H * dv]
   const void* gate = nullptr; int64_t ldg = 0;      // raw gate pre-activation [T, H * dv] or null
+  float* lse = nullptr;                             // optional [T, H]: log2-domain log-sum-exp of the
+                                                    // scaled scores (-inf for a row with no visible key)
 };
 hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream_t s);
 const char* prefill_attn_check(const PrefillAttnArgs& a, bool is_bf16);
@@ -120,6 +122,56 @@ struct DecodeAttnArgs {
 hipError_t decode_attn_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 hipError_t decode_merge_launch(const DecodeAttnArgs& a, bool is_bf16, hipStream_t s);
 const char* decode_attn_check(const DecodeAttnArgs& a, bool is_bf16);
+
+// Backward pass of the expanded layer on training sequences (train.hip).
+// Token-packed rows t = cu_seqlens[b] + j unless noted; element type = the
+// compute dtype unless noted.
+struct TrainArgs {
+  const int32_t* cu_seqlens = nullptr;
+  int batch = 0, max_q_len = 0, total_tokens = 0;
+  int Lp = 0;                                   // per-sequence row stride of cache / kvexp
+  int H = 0, n = 0, r = 0, c = 0, dv = 0, q_lora = 0;
+  float scale = 0.f, eps = 0.f;
+  MaskArgs mask;
+  const float* rope_cos = nullptr; const float* rope_sin = nullptr;  // [positions, r/2]
+  int interleaved = 0;
+  const void* q = nullptr; int64_t ldq = 0;     // roped q [T, H (n + r)]
+  const void* cache = nullptr;                  // entries [b Lp + j, c + r]
+  const void* kvexp = nullptr; int64_t ldkv = 0;  // [b Lp + j, H (n + dv)]
+  const void* O = nullptr;                      // attention output (ungated) [T, H dv]
+  void* A = nullptr;                            // gated output [T, H dv]
+  const float* lse = nullptr;                   // [T, H] log2-domain log-sum-exp of the scaled scores
+  const void* buf1 = nullptr; int64_t ldb1 = 0; // fused first projection [T, N1]
+  int off_q = 0, off_kv = 0, off_g = -1;
+  const void* gate = nullptr; int64_t ldg = 0;  // gate input (inside buf1) or null
+  const void* gamma_kv = nullptr; const void* gamma_q = nullptr;
+  float* rho_q = nullptr; float* rho_kv = nullptr;  // [T] RMSNorm scales
+  // backward buffers
+  void* dO = nullptr; int64_t ldo = 0;          // dA in, dO out (in place) [T, H dv]
+  float* D = nullptr;                           // [T, H]
+  void* dkvb = nullptr; int64_t lddkvb = 0;     // [T, H (n + dv)] per head [dk_nope | dv]
+  float* dkr = nullptr;                         // [T, H, r] per-head gradient of the rope key (fp32)
+  void* dQ = nullptr; int64_t lddq = 0;         // [T, H (n + r)]
+  const void* dcn = nullptr;                    // [T, c] gradient of RMSNorm(kv_c)
+  const void* dqn = nullptr;                    // [T, q_lora] gradient of RMSNorm(q_c)
+  void* dbuf1 = nullptr; int64_t lddb1 = 0;     // [T, N1] gradient of the fused first projection output
+};
+const char* train_check(const TrainArgs& a, bool is_bf16);
+hipError_t train_rmsnorm_rows(const void* x, int64_t ldx, const void* gamma, int N, float eps, void* y, int64_t ldy,
+                              float* rho, int rows, bool is_bf16, hipStream_t s);
+hipError_t train_gate_fwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+hipError_t train_gate_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+hipError_t train_attn_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+hipError_t train_kv_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+hipError_t train_q_rope_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+hipError_t train_q_norm_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s);
+// out[j] = sum_t dy[t, j] x[t, j] rho[t]; part: fp32 [ceil(rows / 256), cols]
+hipError_t train_gamma_grad(const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* rho, int rows,
+                            int cols, float* part, void* out, bool is_bf16, hipStream_t s);
+// dst [cols, ldd] = src^T with zero columns from rows to ldd; map_rows: source
+// row of token t is b Lp + (t - cu[b])
+hipError_t train_transpose(const void* src, int64_t lds, int rows, int cols, void* dst, int64_t ldd,
+                           const TrainArgs& a, bool map_rows, bool is_bf16, hipStream_t s);
 
 // Stream-K decode of the 512 + 64 bf16 latent (attn_decode_sk.hip).
 constexpr int kDecodeMaxTiles = 256;   // 32-key tiles per workgroup range

@@ -66,6 +66,40 @@ struct mla_ctx {
   float kv_scale = 1.f;
   void* kv_shadow = nullptr;        // [max_prefill_kv + max_batch page, c + r] bf16
   int32_t* kv_shadow_bt = nullptr;  // [max_batch, ceil(max_seq_len / page)] identity block table
+  // training (mla_backward_expanded): weights in the forms the backward
+  // products read, and its workspaces (max_train_tokens rows)
+  struct Train {
+    int Tm = 0;
+    void* Wqb = nullptr;      // q_b_proj as given [H (n + r), ql]
+    void* gamma_q = nullptr;  // q_a_layernorm [ql]
+    void* WqbT = nullptr;     // [ql, H (n + r)]
+    void* W1T = nullptr;      // fused first projection transposed [hid, N1]
+    void* WkvbT = nullptr;    // [c, H (n + dv)]
+    void* WoT = nullptr;      // [H dv, hid]
+    void* buf1 = nullptr;     // [Tm, N1]
+    void* qn = nullptr;       // [Tm, ql]
+    void* q = nullptr;        // [Tm, H (n + r)]
+    float* rho_q = nullptr;
+    float* rho_kv = nullptr;
+    void* cache = nullptr;    // [max_prefill_kv, E] entries, identity pages
+    int32_t* bt = nullptr;    // identity block table
+    int32_t* zero_prefix = nullptr;  // [max_batch] zeros
+    void* O = nullptr;
+    void* A = nullptr;
+    float* lse = nullptr;
+    void* dA = nullptr;
+    float* D = nullptr;
+    void* dkvb = nullptr;
+    float* dkr = nullptr;
+    void* dQ = nullptr;
+    void* dcn = nullptr;
+    void* dqn = nullptr;
+    void* dbuf1 = nullptr;
+    void* TX = nullptr;       // [hid, Tp] x^T
+    void* TA = nullptr;       // [maxA, Tp] left operands of the weight-gradient products
+    void* TB = nullptr;       // [maxB, Tp] right operands
+    float* part = nullptr;    // column-sum partials
+  } tr;
   std::vector<void*> allocs;
   hipEvent_t done = nullptr;  // recorded on the call's stream when an entry point returns
   // stage timing (mla_profile_*)
@@ -142,6 +176,12 @@ __global__ void block_meta_kernel(const int32_t* prefix_lens, int batch, int q_l
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b <= batch) cu[b] = b * q_len;
   if (b < batch) lens[b] = prefix_lens[b] + q_len;
+}
+
+// training cache: sequence b's page p is block b mbs + p
+__global__ void identity_table_kernel(int32_t* bt, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) bt[i] = i;
 }
 
 // sparse lists: ent[b][j] = the cache entry of listed position idx[b][j] of
@@ -281,10 +321,12 @@ int check_mask(int kind, int window) {
 }
 
 enum Stage { ST_QKV_A = 0, ST_Q_B, ST_ROPE_CACHE, ST_KV_B, ST_PREFILL_ATTN, ST_WUK, ST_DECODE_ATTN,
-             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_EXPAND_ATTN, ST_EXPAND_MERGE, ST_KV_DEQUANT, ST_COUNT };
+             ST_DECODE_MERGE, ST_WUV, ST_O_PROJ, ST_EXPAND_ATTN, ST_EXPAND_MERGE, ST_KV_DEQUANT, ST_BWD_ATTN,
+             ST_BWD_GEMM, ST_BWD_WGRAD, ST_BWD_POINTWISE, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"qkv_a_gemm", "q_b_gemm", "rope_cache", "kv_b_expand", "prefill_attn",
                                      "wuk_absorb", "decode_attn", "decode_merge", "wuv_gemm", "o_proj_gemm",
-                                     "expand_attn", "expand_merge", "kv_dequant"};
+                                     "expand_attn", "expand_merge", "kv_dequant", "attn_bwd", "bwd_gemm",
+                                     "wgrad_gemm", "bwd_pointwise"};
 
 hipEvent_t pool_event(mla_ctx* ctx) {
   if (!ctx->event_pool.empty()) {
@@ -367,6 +409,80 @@ int project(mla_ctx* ctx, const Workspace& ws, const void* x, int T, hipStream_t
     if (int e = run_gemm(ctx, ws, g2, s)) return e;
   }
   query_buffer(ctx, ws, q, ldq);
+  return MLA_OK;
+}
+
+// copies and transposed weights and the workspaces of mla_backward_expanded
+int init_training(mla_ctx* ctx, const mla_weights* w, hipStream_t s) {
+  const mla_config& cfg = ctx->cfg;
+  auto& t = ctx->tr;
+  const int H = ctx->H, esz = ctx->esz;
+  const int64_t hid = ctx->hid, qkh = ctx->qkh, hdv = (int64_t)H * ctx->dv, kvbn = (int64_t)H * (ctx->n + ctx->dv);
+  const int64_t Tm = cfg.max_train_tokens, Tp = (Tm + 63) / 64 * 64;
+  if (cfg.max_prefill_kv <= 0) return fail(MLA_ERR_INVALID_ARG, "max_train_tokens > 0 needs max_prefill_kv > 0");
+  t.Tm = (int)Tm;
+  TrainArgs none;
+  int e;
+  auto alloc = [&](void** p, size_t bytes) { return dev_alloc(ctx, p, bytes); };
+  auto transpose = [&](const void* src, int64_t rows, int64_t cols, void** dst) -> int {
+    if (int e1 = alloc(dst, (size_t)rows * cols * esz)) return e1;
+    if (train_transpose(src, cols, (int)rows, (int)cols, *dst, rows, none, false, ctx->bf16, s) != hipSuccess)
+      return fail(MLA_ERR_HIP, "weight transpose failed");
+    return MLA_OK;
+  };
+  if (ctx->ql > 0) {
+    if ((e = alloc(&t.Wqb, (size_t)H * qkh * ctx->ql * esz))) return e;
+    if ((e = alloc(&t.gamma_q, (size_t)ctx->ql * esz))) return e;
+    if (hipMemcpyAsync(t.Wqb, w->q_b_proj, (size_t)H * qkh * ctx->ql * esz, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(t.gamma_q, w->q_a_layernorm, (size_t)ctx->ql * esz, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return fail(MLA_ERR_HIP, "q_b weight copy failed");
+    if ((e = transpose(t.Wqb, H * qkh, ctx->ql, &t.WqbT))) return e;
+  }
+  if ((e = transpose(ctx->W1, ctx->N1, hid, &t.W1T))) return e;
+  if ((e = transpose(ctx->Wkvb, kvbn, ctx->c, &t.WkvbT))) return e;
+  if ((e = transpose(ctx->Wo, hid, hdv, &t.WoT))) return e;
+  void* p;
+  if ((e = alloc(&t.buf1, (size_t)Tm * ctx->N1 * esz))) return e;
+  if (ctx->ql > 0) {
+    if ((e = alloc(&t.qn, (size_t)Tm * ctx->ql * esz))) return e;
+    if ((e = alloc(&t.q, (size_t)Tm * H * qkh * esz))) return e;
+    if ((e = alloc(&p, (size_t)Tm * sizeof(float)))) return e;
+    t.rho_q = static_cast<float*>(p);
+  }
+  if ((e = alloc(&p, (size_t)Tm * sizeof(float)))) return e;
+  t.rho_kv = static_cast<float*>(p);
+  if ((e = alloc(&t.cache, (size_t)cfg.max_prefill_kv * ctx->E * esz))) return e;
+  const int64_t nbt = (int64_t)cfg.max_batch * ((cfg.max_seq_len + cfg.page_size - 1) / cfg.page_size + 1);
+  if ((e = alloc(&p, (size_t)nbt * sizeof(int32_t)))) return e;
+  t.bt = static_cast<int32_t*>(p);
+  hipLaunchKernelGGL(identity_table_kernel, dim3((unsigned)((nbt + 255) / 256)), dim3(256), 0, s, t.bt, (int)nbt);
+  if ((e = alloc(&p, (size_t)cfg.max_batch * sizeof(int32_t)))) return e;
+  t.zero_prefix = static_cast<int32_t*>(p);
+  if (hipMemsetAsync(t.zero_prefix, 0, (size_t)cfg.max_batch * sizeof(int32_t), s) != hipSuccess)
+    return fail(MLA_ERR_HIP, "zero prefix init failed");
+  if ((e = alloc(&t.O, (size_t)Tm * hdv * esz))) return e;
+  if (ctx->off_g >= 0 && (e = alloc(&t.A, (size_t)Tm * hdv * esz))) return e;
+  if ((e = alloc(&p, (size_t)Tm * H * sizeof(float)))) return e;
+  t.lse = static_cast<float*>(p);
+  if ((e = alloc(&t.dA, (size_t)Tm * hdv * esz))) return e;
+  if ((e = alloc(&p, (size_t)Tm * H * sizeof(float)))) return e;
+  t.D = static_cast<float*>(p);
+  if ((e = alloc(&t.dkvb, (size_t)Tm * kvbn * esz))) return e;
+  if ((e = alloc(&p, (size_t)Tm * H * ctx->r * sizeof(float)))) return e;
+  t.dkr = static_cast<float*>(p);
+  if ((e = alloc(&t.dQ, (size_t)Tm * H * qkh * esz))) return e;
+  if ((e = alloc(&t.dcn, (size_t)Tm * ctx->c * esz))) return e;
+  if (ctx->ql > 0 && (e = alloc(&t.dqn, (size_t)Tm * ctx->ql * esz))) return e;
+  if ((e = alloc(&t.dbuf1, (size_t)Tm * ctx->N1 * esz))) return e;
+  const int64_t maxA = std::max<int64_t>(std::max<int64_t>(hid, ctx->N1), std::max<int64_t>(kvbn, H * qkh));
+  const int64_t maxB = std::max<int64_t>(std::max<int64_t>(hdv, ctx->c), ctx->ql);
+  if ((e = alloc(&t.TX, (size_t)hid * Tp * esz))) return e;
+  if ((e = alloc(&t.TA, (size_t)maxA * Tp * esz))) return e;
+  if ((e = alloc(&t.TB, (size_t)maxB * Tp * esz))) return e;
+  const int64_t cols = std::max<int64_t>(ctx->c, ctx->ql);
+  if ((e = alloc(&p, (size_t)((Tm + 255) / 256) * cols * sizeof(float)))) return e;
+  t.part = static_cast<float*>(p);
+  if (hipGetLastError() != hipSuccess) return fail(MLA_ERR_HIP, "training set-up launch failed");
   return MLA_OK;
 }
 
@@ -533,6 +649,10 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     ctx->kv_shadow_bt = static_cast<int32_t*>(p);
   }
 
+  if (cfg->max_train_tokens > 0) {
+    if (int e2 = init_training(ctx, w, s)) return bail(e2);
+  }
+
   if (hipStreamSynchronize(s) != hipSuccess) return bail(fail(MLA_ERR_HIP, "stream synchronize failed"));
   *out = ctx;
   return MLA_OK;
@@ -692,6 +812,204 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   go.M = total_tokens; go.N = ctx->hid; go.K = ctx->H * ctx->dv;
   StageTimer st(ctx, s, ST_O_PROJ);
   return run_gemm(ctx, ws, go, s);
+}
+
+int mla_backward_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t total_tokens,
+                          const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t mask_kind, int32_t window,
+                          const int32_t* row_lo, const int32_t* row_hi, const void* dout, void* dx,
+                          const mla_grads* grads, void* stream) {
+  if (!ctx) return fail(MLA_ERR_INVALID_ARG, "ctx must not be NULL");
+  if (!x || !cu_seqlens_q || !dout || !dx || !grads)
+    return fail(MLA_ERR_INVALID_ARG, "x, cu_seqlens_q, dout, dx and grads must not be NULL");
+  if (batch <= 0 || total_tokens <= 0 || max_q_len <= 0)
+    return fail(MLA_ERR_INVALID_ARG, "batch, total_tokens and max_q_len must be positive");
+  if ((row_lo == nullptr) != (row_hi == nullptr)) return fail(MLA_ERR_INVALID_ARG, "row_lo and row_hi go together");
+  if (int e = check_mask(mask_kind, window)) return e;
+  const mla_config& c = ctx->cfg;
+  auto& tr = ctx->tr;
+  if (tr.Tm == 0) return fail(MLA_ERR_CAPACITY, "the context was created with max_train_tokens = 0");
+  if (max_q_len > total_tokens) return fail(MLA_ERR_INVALID_ARG, "need max_q_len <= total_tokens");
+  const int Lp = (max_q_len + c.page_size - 1) / c.page_size * c.page_size;
+  if (batch > c.max_batch || total_tokens > tr.Tm || max_q_len > c.max_seq_len ||
+      (int64_t)batch * Lp > c.max_prefill_kv)
+    return fail(MLA_ERR_CAPACITY, "batch, total_tokens, max_q_len or batch * padded max_q_len above the init limits");
+  const int H = ctx->H, esz = ctx->esz;
+  const int64_t hid = ctx->hid, qkh = ctx->qkh, hdv = (int64_t)H * ctx->dv, kvbn = (int64_t)H * (ctx->n + ctx->dv);
+  const int T = total_tokens;
+  const int64_t Tp = ((int64_t)T + 63) / 64 * 64;
+  const int mbs = Lp / c.page_size;
+  const bool bf = ctx->bf16;
+
+  TrainArgs ta;
+  ta.cu_seqlens = cu_seqlens_q; ta.batch = batch; ta.max_q_len = max_q_len; ta.total_tokens = T; ta.Lp = Lp;
+  ta.H = H; ta.n = ctx->n; ta.r = ctx->r; ta.c = ctx->c; ta.dv = ctx->dv; ta.q_lora = ctx->ql;
+  ta.scale = ctx->scale; ta.eps = (float)c.rms_norm_eps;
+  ta.mask.kind = mask_kind; ta.mask.window = window; ta.mask.row_lo = row_lo; ta.mask.row_hi = row_hi;
+  ta.rope_cos = ctx->rope_cos; ta.rope_sin = ctx->rope_sin; ta.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  if (ctx->ql > 0) { ta.q = tr.q; ta.ldq = H * qkh; }
+  else { ta.q = static_cast<char*>(tr.buf1) + (size_t)ctx->off_q * esz; ta.ldq = ctx->N1; }
+  ta.cache = tr.cache; ta.kvexp = ctx->kvexp; ta.ldkv = kvbn;
+  ta.O = tr.O; ta.A = tr.A ? tr.A : tr.O; ta.lse = tr.lse;
+  ta.buf1 = tr.buf1; ta.ldb1 = ctx->N1; ta.off_q = ctx->off_q; ta.off_kv = ctx->off_kv; ta.off_g = ctx->off_g;
+  if (ctx->off_g >= 0) { ta.gate = static_cast<char*>(tr.buf1) + (size_t)ctx->off_g * esz; ta.ldg = ctx->N1; }
+  ta.gamma_kv = ctx->gamma_kv; ta.gamma_q = tr.gamma_q; ta.rho_q = tr.rho_q; ta.rho_kv = tr.rho_kv;
+  ta.dO = tr.dA; ta.ldo = hdv; ta.D = tr.D;
+  ta.dkvb = tr.dkvb; ta.lddkvb = kvbn; ta.dkr = tr.dkr; ta.dQ = tr.dQ; ta.lddq = H * qkh;
+  ta.dcn = tr.dcn; ta.dqn = tr.dqn; ta.dbuf1 = tr.dbuf1; ta.lddb1 = ctx->N1;
+  if (const char* m = train_check(ta, bf)) return fail(MLA_ERR_UNSUPPORTED, m);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  CallDone call_done(ctx, s);
+  const Workspace& ws = ctx->ws;
+  auto gemm = [&](const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int M, int N,
+                  int K) -> int {
+    GemmArgs g;
+    g.A = A; g.lda = lda; g.W = W; g.ldw = ldw; g.C = C; g.ldc = ldc; g.M = M; g.N = N; g.K = K;
+    return run_gemm(ctx, ws, g, s);
+  };
+  auto at = [&](void* base, int64_t off_elems) { return static_cast<void*>(static_cast<char*>(base) + off_elems * esz); };
+
+  // ---- forward, keeping what the backward reads
+  {
+    StageTimer st(ctx, s, ST_QKV_A);
+    if (int e = gemm(x, hid, ctx->W1, hid, tr.buf1, ctx->N1, T, ctx->N1, (int)hid)) return e;
+  }
+  if (ctx->ql > 0) {
+    StageTimer st(ctx, s, ST_Q_B);
+    HIP_TRY(train_rmsnorm_rows(tr.buf1, ctx->N1, tr.gamma_q, ctx->ql, (float)c.rms_norm_eps, tr.qn, ctx->ql,
+                               tr.rho_q, T, bf, s));
+    if (int e = gemm(tr.qn, ctx->ql, tr.Wqb, ctx->ql, tr.q, H * qkh, T, (int)(H * qkh), ctx->ql)) return e;
+  }
+  RopeCacheArgs rc;
+  rc.q = const_cast<void*>(ta.q); rc.ldq = ta.ldq; rc.qk_head = ctx->qkh;
+  rc.kv = at(tr.buf1, ctx->off_kv); rc.ldkv = ctx->N1;
+  rc.gamma_kv = ctx->gamma_kv;
+  rc.cache = tr.cache; rc.block_table = tr.bt;
+  rc.num_blocks = batch * mbs; rc.max_blocks = mbs; rc.page = c.page_size;
+  rc.rope_cos = ctx->rope_cos; rc.rope_sin = ctx->rope_sin;
+  rc.H = H; rc.n = ctx->n; rc.r = ctx->r; rc.c = ctx->c;
+  rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
+  rc.eps = (float)c.rms_norm_eps;
+  rc.decode = 0; rc.cu_seqlens = cu_seqlens_q; rc.prefix_lens = tr.zero_prefix;
+  rc.max_q_len = max_q_len; rc.max_kv_len = Lp; rc.max_seq_len = c.max_seq_len; rc.total_tokens = T;
+  {
+    StageTimer st(ctx, s, ST_ROPE_CACHE);
+    HIP_TRY(rope_cache_launch(rc, bf, max_q_len, batch, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_KV_B);
+    GemmArgs gk;
+    gk.gather = true;
+    gk.ga.cache = tr.cache; gk.ga.block_table = tr.bt; gk.ga.cu_seqlens = cu_seqlens_q;
+    gk.ga.prefix_lens = tr.zero_prefix; gk.ga.batch = batch; gk.ga.max_kv_len = Lp;
+    gk.ga.page = c.page_size; gk.ga.max_blocks = mbs; gk.ga.num_blocks = batch * mbs;
+    gk.ga.entry = ctx->E; gk.ga.max_q_len = max_q_len;
+    gk.A = tr.cache; gk.lda = ctx->E;
+    gk.W = ctx->Wkvb; gk.ldw = ctx->c;
+    gk.C = ctx->kvexp; gk.ldc = kvbn;
+    gk.M = batch * Lp; gk.N = (int)kvbn; gk.K = ctx->c;
+    if (int e = run_gemm(ctx, ws, gk, s)) return e;
+  }
+  {
+    PrefillAttnArgs pa;
+    pa.q = ta.q; pa.ldq = ta.ldq; pa.qk_head = ctx->qkh;
+    pa.kv = ctx->kvexp; pa.ldkv = kvbn;
+    pa.cache = tr.cache; pa.block_table = tr.bt;
+    pa.num_blocks = batch * mbs; pa.max_blocks = mbs; pa.page = c.page_size;
+    pa.cu_seqlens = cu_seqlens_q; pa.prefix_lens = tr.zero_prefix;
+    pa.batch = batch; pa.max_q_len = max_q_len; pa.max_kv_len = Lp; pa.total_tokens = T;
+    pa.H = H; pa.n = ctx->n; pa.r = ctx->r; pa.c = ctx->c; pa.dv = ctx->dv;
+    pa.scale = ctx->scale;
+    pa.mask.kind = mask_kind; pa.mask.window = window; pa.mask.row_lo = row_lo; pa.mask.row_hi = row_hi;
+    pa.out = tr.O; pa.ldo = hdv;
+    pa.lse = tr.lse;
+    if (const char* m = prefill_attn_check(pa, bf)) return fail(MLA_ERR_UNSUPPORTED, m);
+    StageTimer st(ctx, s, ST_PREFILL_ATTN);
+    HIP_TRY(prefill_attn_launch(pa, bf, s));
+  }
+  if (tr.A) {
+    StageTimer st(ctx, s, ST_BWD_POINTWISE);
+    HIP_TRY(train_gate_fwd(ta, bf, s));
+  }
+
+  // ---- backward
+  {
+    StageTimer st(ctx, s, ST_BWD_GEMM);
+    if (int e = gemm(dout, hid, tr.WoT, hid, tr.dA, hdv, T, (int)hdv, (int)hid)) return e;
+  }
+  {
+    StageTimer st(ctx, s, ST_BWD_POINTWISE);
+    HIP_TRY(train_gate_bwd(ta, bf, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_BWD_ATTN);
+    HIP_TRY(train_attn_bwd(ta, bf, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_BWD_GEMM);
+    if (int e = gemm(tr.dkvb, kvbn, tr.WkvbT, kvbn, tr.dcn, ctx->c, T, ctx->c, (int)kvbn)) return e;
+  }
+  {
+    StageTimer st(ctx, s, ST_BWD_POINTWISE);
+    HIP_TRY(train_kv_bwd(ta, bf, s));
+    if (grads->kv_a_layernorm)
+      HIP_TRY(train_gamma_grad(tr.dcn, ctx->c, at(tr.buf1, ctx->off_kv), ctx->N1, tr.rho_kv, T, ctx->c, tr.part,
+                               grads->kv_a_layernorm, bf, s));
+    HIP_TRY(train_q_rope_bwd(ta, bf, s));
+  }
+  if (ctx->ql > 0) {
+    {
+      StageTimer st(ctx, s, ST_BWD_GEMM);
+      if (int e = gemm(tr.dQ, H * qkh, tr.WqbT, H * qkh, tr.dqn, ctx->ql, T, ctx->ql, (int)(H * qkh))) return e;
+    }
+    StageTimer st(ctx, s, ST_BWD_POINTWISE);
+    HIP_TRY(train_q_norm_bwd(ta, bf, s));
+    if (grads->q_a_layernorm)
+      HIP_TRY(train_gamma_grad(tr.dqn, ctx->ql, tr.buf1, ctx->N1, tr.rho_q, T, ctx->ql, tr.part, grads->q_a_layernorm,
+                               bf, s));
+  }
+  {
+    StageTimer st(ctx, s, ST_BWD_GEMM);
+    if (int e = gemm(tr.dbuf1, ctx->N1, tr.W1T, ctx->N1, dx, hid, T, (int)hid, ctx->N1)) return e;
+  }
+  StageTimer st_w(ctx, s, ST_BWD_WGRAD);
+
+  // ---- weight gradients: dW = dY^T X over the token axis, on transposed copies
+  auto tpose = [&](const void* src, int64_t lds, int cols, void* dst, bool map) {
+    return train_transpose(src, lds, T, cols, dst, Tp, ta, map, bf, s);
+  };
+  if (grads->o_proj) {
+    HIP_TRY(tpose(dout, hid, (int)hid, tr.TA, false));
+    HIP_TRY(tpose(ta.A, hdv, (int)hdv, tr.TB, false));
+    if (int e = gemm(tr.TA, Tp, tr.TB, Tp, grads->o_proj, hdv, (int)hid, (int)hdv, (int)Tp)) return e;
+  }
+  if (grads->q_a_proj || grads->q_proj || grads->kv_a_proj_with_mqa || grads->g_proj) {
+    HIP_TRY(tpose(x, hid, (int)hid, tr.TX, false));
+    HIP_TRY(tpose(tr.dbuf1, ctx->N1, ctx->N1, tr.TA, false));
+    void* gq = ctx->ql > 0 ? grads->q_a_proj : grads->q_proj;
+    const int nq = ctx->ql > 0 ? ctx->ql : H * (int)qkh;
+    if (gq)
+      if (int e = gemm(at(tr.TA, (int64_t)ctx->off_q * Tp), Tp, tr.TX, Tp, gq, hid, nq, (int)hid, (int)Tp)) return e;
+    if (grads->kv_a_proj_with_mqa)
+      if (int e = gemm(at(tr.TA, (int64_t)ctx->off_kv * Tp), Tp, tr.TX, Tp, grads->kv_a_proj_with_mqa, hid, ctx->E,
+                       (int)hid, (int)Tp))
+        return e;
+    if (grads->g_proj && ctx->off_g >= 0)
+      if (int e = gemm(at(tr.TA, (int64_t)ctx->off_g * Tp), Tp, tr.TX, Tp, grads->g_proj, hid, (int)hdv, (int)hid,
+                       (int)Tp))
+        return e;
+  }
+  if (grads->kv_b_proj) {
+    HIP_TRY(tpose(tr.dkvb, kvbn, (int)kvbn, tr.TA, false));
+    HIP_TRY(tpose(tr.cache, ctx->E, ctx->c, tr.TB, true));
+    if (int e = gemm(tr.TA, Tp, tr.TB, Tp, grads->kv_b_proj, ctx->c, (int)kvbn, ctx->c, (int)Tp)) return e;
+  }
+  if (ctx->ql > 0 && grads->q_b_proj) {
+    HIP_TRY(tpose(tr.dQ, H * qkh, (int)(H * qkh), tr.TA, false));
+    HIP_TRY(tpose(tr.qn, ctx->ql, ctx->ql, tr.TB, false));
+    if (int e = gemm(tr.TA, Tp, tr.TB, Tp, grads->q_b_proj, ctx->ql, (int)(H * qkh), ctx->ql, (int)Tp)) return e;
+  }
+  return MLA_OK;
 }
 
 }  // extern "C"

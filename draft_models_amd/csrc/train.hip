@@ -1,0 +1,1097 @@
+// Backward pass of the expanded MLA layer on whole training sequences (no
+// cached prefix; token j of a sequence at position j). SpecForge PR "Add
+// config-selectable MLA draft attention" trains MLA as a draft attention and
+// validates it with gradients (Validation); the forward is the expanded form
+// of the MLA blog's wrapper forward and forward_mha listings, and every
+// kernel here is the derivative of one of its steps:
+//   * attention: dV = P^T dO, dP = dO V^T, dS = P (dP - D) with
+//     D = rowsum(dO * O), dQ = scale dS K, dK = scale dS^T Q, recomputing
+//     P = 2^(s log2e scale - lse2) from the forward's log-sum-exp;
+//   * the shared rope key collects the rope part of dK of every head;
+//   * RoPE: the opposite turn; RMSNorm: dx = rho (g - x rho^2 mean(g x)),
+//     g = dy * gamma, and dgamma = sum over tokens of dy * x * rho;
+//   * output gate: dO = dA sigma, d(gate input) = dA O sigma (1 - sigma).
+// The dense products (x W^T, dY W, dY^T X) are the library's GEMMs; the
+// token-axis contractions of the weight gradients run on transposed copies
+// made here (transpose_kernel).
+//
+// Layouts: token-packed rows t = cu_seqlens[b] + j for every per-token buffer
+// except the two the forward kernels address per sequence: the latent cache
+// (identity pages, row b Lp + j) and the expanded keys/values (row b Lp + j),
+// Lp = max_q_len rounded up to the cache page.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void visible_rows(const MaskArgs& m, int t, int p, int L, int& lo, int& hi) {
+  if (m.row_lo != nullptr && m.row_hi != nullptr) {
+    lo = min(max(m.row_lo[t], 0), L);
+    hi = min(max(m.row_hi[t], 0), L);
+    return;
+  }
+  if (m.kind == 0) { lo = 0; hi = L; }
+  else if (m.kind == 1) { lo = 0; hi = min(p + 1, L); }
+  else { lo = max(0, p - m.window + 1); hi = min(p + 1, L); }
+}
+
+// tokens of sequence b, clamped so that every row cu[b] + j stays below total_tokens
+__device__ __forceinline__ int seq_len(const TrainArgs& a, int b) {
+  const int t0 = a.cu_seqlens[b];
+  return min(min(max(a.cu_seqlens[b + 1] - t0, 0), a.max_q_len), max(a.total_tokens - t0, 0));
+}
+
+// sequence of token t (cu_seqlens is nondecreasing; binary search)
+__device__ __forceinline__ int seq_of(const TrainArgs& a, int t) {
+  int lo = 0, hi = a.batch;  // cu[lo] <= t < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu_seqlens[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ void ld_frag(Frag<T>& f, const T* p, bool ok);
+template <>
+__device__ __forceinline__ void ld_frag(Frag<bf16>& f, const bf16* p, bool ok) {
+  f.v = ok ? *reinterpret_cast<const bf16x8*>(p) : bf16x8{};
+}
+template <>
+__device__ __forceinline__ void ld_frag(Frag<float>& f, const float* p, bool ok) {
+  if (ok) {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(p), hi = *reinterpret_cast<const floatx4*>(p + 4);
+    f.v = floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    f.v = floatx8{};
+  }
+}
+
+// element d of head h's key of token (b, j): k_nope from the expansion,
+// k_pe (shared by the heads) from the latent cache
+template <typename T>
+__device__ __forceinline__ T key_elem(const TrainArgs& a, int b, int j, int h, int d) {
+  const int64_t row = (int64_t)b * a.Lp + j;
+  if (d < a.n) return reinterpret_cast<const T*>(a.kvexp)[row * a.ldkv + (int64_t)h * (a.n + a.dv) + d];
+  if (d < a.n + a.r) return reinterpret_cast<const T*>(a.cache)[row * (a.c + a.r) + a.c + (d - a.n)];
+  return T(0.f);
+}
+template <typename T>
+__device__ __forceinline__ T val_elem(const TrainArgs& a, int b, int j, int h, int d) {
+  if (d >= a.dv) return T(0.f);
+  const int64_t row = (int64_t)b * a.Lp + j;
+  return reinterpret_cast<const T*>(a.kvexp)[row * a.ldkv + (int64_t)h * (a.n + a.dv) + a.n + d];
+}
+
+// ---------------------------------------------------------------------------
+// attention backward, keys side: dK and dV of one 64-key tile of one head.
+// Wave w owns keys 16 w .. 16 w + 15 of the tile (MFMA A rows). Per 64-query
+// tile: S^T = K Q^T and dP^T = V dO^T (lane: keys 4 g + i, query lr of each
+// 16-query block), P^T and dS^T go through LDS to become A operands of
+// dV += P^T dO and dK += dS^T Q, whose B operands read transposed copies of
+// the query tile (Qt, dOt).
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(TrainArgs a) {
+  constexpr int BT = 64, KS = DQK / 32, VS = DV / 32;
+  constexpr int DKB = DQK / 16, DVB = DV / 16;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int QROW = DQK + PAD, DOROW = DV + PAD, TROW = BT + PAD;
+  static_assert(DQK % 32 == 0 && DV % 32 == 0, "padded head dims");
+  __shared__ __attribute__((aligned(16))) T Qs[BT * QROW];
+  __shared__ __attribute__((aligned(16))) T Qt[DQK * TROW];
+  __shared__ __attribute__((aligned(16))) T dOs[BT * DOROW];
+  __shared__ __attribute__((aligned(16))) T dOt[DV * TROW];
+  __shared__ __attribute__((aligned(16))) T Pw[4][16 * TROW];
+  __shared__ __attribute__((aligned(16))) T dSw[4][16 * TROW];
+  __shared__ float lse_s[BT], D_s[BT];
+  __shared__ int lo_s[BT], hi_s[BT];
+
+  const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = seq_len(a, b);
+  const int k0 = kt * BT;
+  if (k0 >= S) return;
+  const int t0 = a.cu_seqlens[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const float sl2 = a.scale * kLog2e;
+  const int qk = a.n + a.r;
+
+  // this wave's keys as A operands
+  const int kr = k0 + wave * 16 + lr;
+  const bool krok = kr < S;
+  Frag<T> kf[KS], vf[VS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[ks].v[e] = krok ? key_elem<T>(a, b, kr, h, ks * 32 + g * 8 + e) : T(0.f);
+#pragma unroll
+  for (int vs = 0; vs < VS; ++vs)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vf[vs].v[e] = krok ? val_elem<T>(a, b, kr, h, vs * 32 + g * 8 + e) : T(0.f);
+
+  floatx4 dk[DKB], dv[DVB];
+#pragma unroll
+  for (int i = 0; i < DKB; ++i) dk[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < DVB; ++i) dv[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // queries that can see a key of this tile
+  int qbeg = 0, qend = S;
+  if (a.mask.row_lo == nullptr) {
+    if (a.mask.kind == 1) qbeg = k0;
+    else if (a.mask.kind == 2) { qbeg = k0; qend = min(S, k0 + BT - 1 + max(a.mask.window, 0)); }
+  }
+  qbeg = (qbeg / BT) * BT;
+  const T* Qg = reinterpret_cast<const T*>(a.q);
+  const T* dOg = reinterpret_cast<const T*>(a.dO);
+
+  for (int q0 = qbeg; q0 < qend; q0 += BT) {
+    // ---- stage the query tile: Q, Q^T, dO, dO^T and the per-query statistics
+    for (int v = tid; v < BT * DQK; v += 256) {
+      const int qq = v / DQK, d = v % DQK;
+      const int qi = q0 + qq;
+      T val = T(0.f);
+      if (qi < S && d < qk) val = Qg[(int64_t)(t0 + qi) * a.ldq + (int64_t)h * qk + d];
+      Qs[qq * QROW + d] = val;
+      Qt[d * TROW + qq] = val;
+    }
+    for (int v = tid; v < BT * DV; v += 256) {
+      const int qq = v / DV, d = v % DV;
+      const int qi = q0 + qq;
+      T val = T(0.f);
+      if (qi < S && d < a.dv) val = dOg[(int64_t)(t0 + qi) * a.ldo + (int64_t)h * a.dv + d];
+      dOs[qq * DOROW + d] = val;
+      dOt[d * TROW + qq] = val;
+    }
+    if (tid < BT) {
+      const int qi = q0 + tid;
+      float l2 = -INFINITY, dd = 0.f;
+      int lo = 0, hi = 0;
+      if (qi < S) {
+        const int t = t0 + qi;
+        l2 = a.lse[(int64_t)t * a.H + h];
+        dd = a.D[(int64_t)t * a.H + h];
+        visible_rows(a.mask, t, qi, S, lo, hi);
+      }
+      lse_s[tid] = l2; D_s[tid] = dd; lo_s[tid] = lo; hi_s[tid] = hi;
+    }
+    __syncthreads();
+
+    // ---- S^T, dP^T -> P^T, dS^T (bf16/fp32 in LDS, this wave's 16 keys)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> qf;
+        ld_frag(qf, &Qs[(qb * 16 + lr) * QROW + ks * 32 + g * 8], true);
+        s = mfma16(kf[ks], qf, s);
+      }
+#pragma unroll
+      for (int vs = 0; vs < VS; ++vs) {
+        Frag<T> of;
+        ld_frag(of, &dOs[(qb * 16 + lr) * DOROW + vs * 32 + g * 8], true);
+        dp = mfma16(vf[vs], of, dp);
+      }
+      const int qq = qb * 16 + lr;
+      const float l2 = lse_s[qq], dd = D_s[qq];
+      const int lo = lo_s[qq], hi = hi_s[qq];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + wave * 16 + g * 4 + i;
+        const bool vis = key < S && key >= lo && key < hi;
+        const float p = vis ? fast_exp2(s[i] * sl2 - l2) : 0.f;
+        Pw[wave][(g * 4 + i) * TROW + qq] = from_f32<T>(p);
+        dSw[wave][(g * 4 + i) * TROW + qq] = from_f32<T>(p * (dp[i] - dd));
+      }
+    }
+    __syncthreads();
+
+    // ---- dV += P^T dO, dK += dS^T Q (contraction over the 64 queries)
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+      Frag<T> pf, sf;
+      ld_frag(pf, &Pw[wave][lr * TROW + qs * 32 + g * 8], true);
+      ld_frag(sf, &dSw[wave][lr * TROW + qs * 32 + g * 8], true);
+#pragma unroll
+      for (int db = 0; db < DVB; ++db) {
+        Frag<T> bfr;
+        ld_frag(bfr, &dOt[(db * 16 + lr) * TROW + qs * 32 + g * 8], true);
+        dv[db] = mfma16(pf, bfr, dv[db]);
+      }
+#pragma unroll
+      for (int db = 0; db < DKB; ++db) {
+        Frag<T> bfr;
+        ld_frag(bfr, &Qt[(db * 16 + lr) * TROW + qs * 32 + g * 8], true);
+        dk[db] = mfma16(sf, bfr, dk[db]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds dK / dV of keys 4 g + i, dim 16 db + lr
+  T* dkvb = reinterpret_cast<T*>(a.dkvb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = k0 + wave * 16 + g * 4 + i;
+    if (key >= S) continue;
+    const int64_t t = t0 + key;
+    T* row = dkvb + t * a.lddkvb + (int64_t)h * (a.n + a.dv);
+#pragma unroll
+    for (int db = 0; db < DKB; ++db) {
+      const int d = db * 16 + lr;
+      const float v = dk[db][i] * a.scale;
+      if (d < a.n) row[d] = from_f32<T>(v);
+      else if (d < qk) a.dkr[(t * a.H + h) * a.r + (d - a.n)] = v;
+    }
+#pragma unroll
+    for (int db = 0; db < DVB; ++db) {
+      const int d = db * 16 + lr;
+      if (d < a.dv) row[a.n + d] = from_f32<T>(dv[db][i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention backward, queries side: dQ of one 64-query tile of one head.
+// Wave w owns queries 16 w .. + 15 (A rows of S = Q K^T and dP = dO V^T; lane
+// holds queries 4 g + i, key lr of each 16-key block); dS goes through LDS
+// to become the A operand of dQ += dS K, whose B operand reads K^T.
+// ---------------------------------------------------------------------------
+template <typename T, int DQK, int DV>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(TrainArgs a) {
+  constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16;
+  constexpr int PAD = 16 / sizeof(T);
+  constexpr int KROW = DQK + PAD, VROW = DV + PAD, TROW = BT + PAD;
+  __shared__ __attribute__((aligned(16))) T Ks[BT * KROW];
+  __shared__ __attribute__((aligned(16))) T Kt[DQK * TROW];
+  __shared__ __attribute__((aligned(16))) T Vs[BT * VROW];
+  __shared__ __attribute__((aligned(16))) T dSw[4][16 * TROW];
+
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = seq_len(a, b);
+  const int q0 = qt * BT;
+  if (q0 >= S) return;
+  const int t0 = a.cu_seqlens[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const float sl2 = a.scale * kLog2e;
+  const int qk = a.n + a.r;
+  const T* Qg = reinterpret_cast<const T*>(a.q);
+  const T* dOg = reinterpret_cast<const T*>(a.dO);
+
+  // this wave's queries as A operands (rows lr)
+  const int qa = q0 + wave * 16 + lr;
+  const bool qaok = qa < S;
+  Frag<T> qf[KS], of[VS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int d = ks * 32 + g * 8;
+    ld_frag(qf[ks], Qg + (int64_t)(t0 + (qaok ? qa : 0)) * a.ldq + (int64_t)h * qk + d, qaok && d < qk);
+  }
+#pragma unroll
+  for (int vs = 0; vs < VS; ++vs) {
+    const int d = vs * 32 + g * 8;
+    ld_frag(of[vs], dOg + (int64_t)(t0 + (qaok ? qa : 0)) * a.ldo + (int64_t)h * a.dv + d, qaok && d < a.dv);
+  }
+  // statistics of the 4 output rows of this lane (queries 4 g + i)
+  float l2[4], dd[4];
+  int lo[4], hi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + wave * 16 + g * 4 + i;
+    l2[i] = -INFINITY; dd[i] = 0.f; lo[i] = 0; hi[i] = 0;
+    if (qi < S) {
+      const int t = t0 + qi;
+      l2[i] = a.lse[(int64_t)t * a.H + h];
+      dd[i] = a.D[(int64_t)t * a.H + h];
+      visible_rows(a.mask, t, qi, S, lo[i], hi[i]);
+    }
+  }
+  floatx4 dq[DKB];
+#pragma unroll
+  for (int i = 0; i < DKB; ++i) dq[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // keys some query of this tile can see
+  int kbeg = 0, kend = S;
+  if (a.mask.row_lo == nullptr) {
+    if (a.mask.kind == 1) kend = min(S, q0 + BT);
+    else if (a.mask.kind == 2) { kend = min(S, q0 + BT); kbeg = max(0, q0 - max(a.mask.window, 0) + 1); }
+  }
+  kbeg = (kbeg / BT) * BT;
+
+  for (int k0 = kbeg; k0 < kend; k0 += BT) {
+    for (int v = tid; v < BT * DQK; v += 256) {
+      const int kk = v / DQK, d = v % DQK;
+      const int j = k0 + kk;
+      const T val = (j < S) ? key_elem<T>(a, b, j, h, d) : T(0.f);
+      Ks[kk * KROW + d] = val;
+      Kt[d * TROW + kk] = val;
+    }
+    for (int v = tid; v < BT * DV; v += 256) {
+      const int kk = v / DV, d = v % DV;
+      const int j = k0 + kk;
+      Vs[kk * VROW + d] = (j < S) ? val_elem<T>(a, b, j, h, d) : T(0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<T> kfr;
+        ld_frag(kfr, &Ks[(kb * 16 + lr) * KROW + ks * 32 + g * 8], true);
+        s = mfma16(qf[ks], kfr, s);
+      }
+#pragma unroll
+      for (int vs = 0; vs < VS; ++vs) {
+        Frag<T> vfr;
+        ld_frag(vfr, &Vs[(kb * 16 + lr) * VROW + vs * 32 + g * 8], true);
+        dp = mfma16(of[vs], vfr, dp);
+      }
+      const int key = k0 + kb * 16 + lr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = key < S && key >= lo[i] && key < hi[i];
+        const float p = vis ? fast_exp2(s[i] * sl2 - l2[i]) : 0.f;
+        dSw[wave][(g * 4 + i) * TROW + kb * 16 + lr] = from_f32<T>(p * (dp[i] - dd[i]));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      Frag<T> sf;
+      ld_frag(sf, &dSw[wave][lr * TROW + ks2 * 32 + g * 8], true);
+#pragma unroll
+      for (int db = 0; db < DKB; ++db) {
+        Frag<T> bfr;
+        ld_frag(bfr, &Kt[(db * 16 + lr) * TROW + ks2 * 32 + g * 8], true);
+        dq[db] = mfma16(sf, bfr, dq[db]);
+      }
+    }
+    __syncthreads();
+  }
+
+  T* dQg = reinterpret_cast<T*>(a.dQ);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = q0 + wave * 16 + g * 4 + i;
+    if (qi >= S) continue;
+    T* row = dQg + (int64_t)(t0 + qi) * a.lddq + (int64_t)h * qk;
+#pragma unroll
+    for (int db = 0; db < DKB; ++db) {
+      const int d = db * 16 + lr;
+      if (d < qk) row[d] = from_f32<T>(dq[db][i] * a.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// elementwise and per-token kernels (one workgroup per token)
+// ---------------------------------------------------------------------------
+
+// rows of the q_a projection -> RMSNorm(q_a) * gamma (qn) and rho
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const T* x, int64_t ldx, const T* gamma, int N, float eps,
+                                                           T* y, int64_t ldy, float* rho, int rows) {
+  const int t = blockIdx.x;
+  if (t >= rows) return;
+  __shared__ float red[4];
+  const T* xr = x + (int64_t)t * ldx;
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < N; e += 256) {
+    const float f = to_f32(xr[e]);
+    ss += f * f;
+  }
+  ss = warp_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)N + eps);
+  for (int e = threadIdx.x; e < N; e += 256) y[(int64_t)t * ldy + e] = from_f32<T>(to_f32(xr[e]) * r * to_f32(gamma[e]));
+  if (threadIdx.x == 0) rho[t] = r;
+}
+
+// A = O * sigmoid(gate input)  (or a copy of O without a gate)
+template <typename T>
+__global__ __launch_bounds__(256) void gate_fwd_kernel(TrainArgs a) {
+  const int t = blockIdx.x;
+  const int HD = a.H * a.dv;
+  const T* O = reinterpret_cast<const T*>(a.O) + (int64_t)t * HD;
+  T* A = reinterpret_cast<T*>(a.A) + (int64_t)t * HD;
+  const T* gp = a.gate ? reinterpret_cast<const T*>(a.gate) + (int64_t)t * a.ldg : nullptr;
+  for (int e = threadIdx.x; e < HD; e += 256) {
+    float v = to_f32(O[e]);
+    if (gp) v *= sigmoidf(to_f32(gp[e]));
+    A[e] = from_f32<T>(v);
+  }
+}
+
+// dO = dA * sigma (in place), d(gate input) = dA O sigma (1 - sigma) into
+// dbuf1, D[t, h] = sum_d dO O
+template <typename T>
+__global__ __launch_bounds__(256) void gate_bwd_kernel(TrainArgs a) {
+  const int t = blockIdx.x;
+  const int HD = a.H * a.dv;
+  T* dA = reinterpret_cast<T*>(a.dO) + (int64_t)t * HD;
+  const T* O = reinterpret_cast<const T*>(a.O) + (int64_t)t * HD;
+  const T* gp = a.gate ? reinterpret_cast<const T*>(a.gate) + (int64_t)t * a.ldg : nullptr;
+  T* dgp = a.gate ? reinterpret_cast<T*>(a.dbuf1) + (int64_t)t * a.lddb1 + a.off_g : nullptr;
+  // thread -> (head, 1/64 of its dims): 64 lanes of a wave per head
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int h = wave; h < a.H; h += 4) {
+    float acc = 0.f;
+    for (int d = lane; d < a.dv; d += 64) {
+      const int e = h * a.dv + d;
+      const float da = to_f32(dA[e]), o = to_f32(O[e]);
+      float dov = da;
+      if (gp) {
+        const float s = sigmoidf(to_f32(gp[e]));
+        dov = da * s;
+        dgp[e] = from_f32<T>(da * o * s * (1.f - s));
+      }
+      const T dq = from_f32<T>(dov);
+      dA[e] = dq;
+      acc += to_f32(dq) * o;
+    }
+    acc = warp_sum(acc);
+    if (lane == 0) a.D[(int64_t)t * a.H + h] = acc;
+  }
+}
+
+// rotation of pair j at position p by -angle (the adjoint of RoPE)
+__device__ __forceinline__ void rope_back(const TrainArgs& a, int p, int j, float xa, float xb, float& ya, float& yb) {
+  const float cs = a.rope_cos[(int64_t)p * (a.r / 2) + j], sn = a.rope_sin[(int64_t)p * (a.r / 2) + j];
+  ya = xa * cs + xb * sn;
+  yb = -xa * sn + xb * cs;
+}
+__device__ __forceinline__ void rope_idx(const TrainArgs& a, int j, int& ia, int& ib) {
+  if (a.interleaved) { ia = 2 * j; ib = 2 * j + 1; }
+  else { ia = j; ib = j + a.r / 2; }
+}
+
+// latent side, per token: dkv_c = RMSNorm backward of dcn, dk_pe = the rope
+// gradient summed over heads and turned back; both into dbuf1 (kv block);
+// rho of the latent row into rho_kv
+template <typename T>
+__global__ __launch_bounds__(256) void kv_bwd_kernel(TrainArgs a) {
+  const int t = blockIdx.x;
+  if (t >= a.total_tokens) return;
+  const int b = seq_of(a, t), p = t - a.cu_seqlens[b];
+  __shared__ float red[4], red2[4];
+  const T* x = reinterpret_cast<const T*>(a.buf1) + (int64_t)t * a.ldb1 + a.off_kv;
+  const T* dy = reinterpret_cast<const T*>(a.dcn) + (int64_t)t * a.c;
+  const T* gamma = reinterpret_cast<const T*>(a.gamma_kv);
+  T* out = reinterpret_cast<T*>(a.dbuf1) + (int64_t)t * a.lddb1 + a.off_kv;
+  float ss = 0.f, gx = 0.f;
+  for (int e = threadIdx.x; e < a.c; e += 256) {
+    const float f = to_f32(x[e]);
+    ss += f * f;
+    gx += to_f32(dy[e]) * to_f32(gamma[e]) * f;
+  }
+  ss = warp_sum(ss);
+  gx = warp_sum(gx);
+  if ((threadIdx.x & 63) == 0) { red[threadIdx.x >> 6] = ss; red2[threadIdx.x >> 6] = gx; }
+  __syncthreads();
+  const float rho = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)a.c + a.eps);
+  const float mg = (red2[0] + red2[1] + red2[2] + red2[3]) / (float)a.c;
+  for (int e = threadIdx.x; e < a.c; e += 256) {
+    const float f = to_f32(x[e]);
+    out[e] = from_f32<T>(rho * (to_f32(dy[e]) * to_f32(gamma[e]) - f * rho * rho * mg));
+  }
+  if (threadIdx.x == 0) a.rho_kv[t] = rho;
+  // rope key: sum over heads, then the opposite turn
+  for (int j = threadIdx.x; j < a.r / 2; j += 256) {
+    int ia, ib;
+    rope_idx(a, j, ia, ib);
+    float sa = 0.f, sb = 0.f;
+    for (int h = 0; h < a.H; ++h) {
+      sa += a.dkr[((int64_t)t * a.H + h) * a.r + ia];
+      sb += a.dkr[((int64_t)t * a.H + h) * a.r + ib];
+    }
+    float ya, yb;
+    rope_back(a, p, j, sa, sb, ya, yb);
+    out[a.c + ia] = from_f32<T>(ya);
+    out[a.c + ib] = from_f32<T>(yb);
+  }
+}
+
+// query side, per token: dq = dQ with its rope part turned back (in place in
+// dQ, then also into dbuf1's q block when the query has no low-rank path)
+template <typename T>
+__global__ __launch_bounds__(256) void q_rope_bwd_kernel(TrainArgs a) {
+  const int t = blockIdx.x;
+  if (t >= a.total_tokens) return;
+  const int b = seq_of(a, t), p = t - a.cu_seqlens[b];
+  const int qk = a.n + a.r;
+  T* dq = reinterpret_cast<T*>(a.dQ) + (int64_t)t * a.lddq;
+  for (int v = threadIdx.x; v < a.H * (a.r / 2); v += 256) {
+    const int h = v / (a.r / 2), j = v % (a.r / 2);
+    int ia, ib;
+    rope_idx(a, j, ia, ib);
+    T* row = dq + (int64_t)h * qk + a.n;
+    float ya, yb;
+    rope_back(a, p, j, to_f32(row[ia]), to_f32(row[ib]), ya, yb);
+    row[ia] = from_f32<T>(ya);
+    row[ib] = from_f32<T>(yb);
+  }
+  if (a.q_lora == 0) {
+    __syncthreads();
+    T* out = reinterpret_cast<T*>(a.dbuf1) + (int64_t)t * a.lddb1 + a.off_q;
+    for (int e = threadIdx.x; e < a.H * qk; e += 256) out[e] = dq[e];
+  }
+}
+
+// low-rank query, per token: dq_a = RMSNorm backward of dqn into dbuf1's q block
+template <typename T>
+__global__ __launch_bounds__(256) void q_norm_bwd_kernel(TrainArgs a) {
+  const int t = blockIdx.x;
+  if (t >= a.total_tokens) return;
+  __shared__ float red[4];
+  const int N = a.q_lora;
+  const T* x = reinterpret_cast<const T*>(a.buf1) + (int64_t)t * a.ldb1 + a.off_q;
+  const T* dy = reinterpret_cast<const T*>(a.dqn) + (int64_t)t * N;
+  const T* gamma = reinterpret_cast<const T*>(a.gamma_q);
+  T* out = reinterpret_cast<T*>(a.dbuf1) + (int64_t)t * a.lddb1 + a.off_q;
+  const float rho = a.rho_q[t];
+  float gx = 0.f;
+  for (int e = threadIdx.x; e < N; e += 256) gx += to_f32(dy[e]) * to_f32(gamma[e]) * to_f32(x[e]);
+  gx = warp_sum(gx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = gx;
+  __syncthreads();
+  const float mg = (red[0] + red[1] + red[2] + red[3]) / (float)N;
+  for (int e = threadIdx.x; e < N; e += 256) {
+    const float f = to_f32(x[e]);
+    out[e] = from_f32<T>(rho * (to_f32(dy[e]) * to_f32(gamma[e]) - f * rho * rho * mg));
+  }
+}
+
+// dgamma partial sums: part[blk][j] = sum over rows of block blk of
+// dy[t, j] * x[t, j] * rho[t] (64 columns x 256 rows per workgroup)
+template <typename T>
+__global__ __launch_bounds__(256) void gamma_partial_kernel(const T* dy, int64_t lddy, const T* x, int64_t ldx,
+                                                            const float* rho, int rows, int cols, float* part) {
+  const int cb = blockIdx.x, rb = blockIdx.y;
+  const int col = cb * 64 + (threadIdx.x & 63), r0 = rb * 256 + (threadIdx.x >> 6) * 64;
+  __shared__ float red[4][64];
+  float acc = 0.f;
+  if (col < cols)
+    for (int r = r0; r < min(r0 + 64, rows); ++r)
+      acc += to_f32(dy[(int64_t)r * lddy + col]) * to_f32(x[(int64_t)r * ldx + col]) * rho[r];
+  red[threadIdx.x >> 6][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (threadIdx.x < 64 && col < cols)
+    part[(int64_t)rb * cols + col] = red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gamma_final_kernel(const float* part, int nparts, int cols, T* out) {
+  const int col = blockIdx.x * 256 + threadIdx.x;
+  if (col >= cols) return;
+  float acc = 0.f;
+  for (int i = 0; i < nparts; ++i) acc += part[(int64_t)i * cols + col];
+  out[col] = from_f32<T>(acc);
+}
+
+// dst[c][t] = src[row(t)][c] for t < rows, 0 for rows <= t < rows_pad. With
+// a row map (cache rows of training tokens), row(t) = b Lp + (t - cu[b]).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t lds, int rows, int cols, T* dst,
+                                                        int64_t ldd, TrainArgs a, int map_rows) {
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  for (int v = threadIdx.x; v < 64 * 64; v += 256) {
+    const int rr = v / 64, cc = v % 64;
+    const int r = r0 + rr, c = c0 + cc;
+    T val = T(0.f);
+    if (r < rows && c < cols) {
+      int64_t sr = r;
+      if (map_rows) {
+        const int b = seq_of(a, r);
+        sr = (int64_t)b * a.Lp + (r - a.cu_seqlens[b]);
+      }
+      val = src[sr * lds + c];
+    }
+    tile[rr][cc] = val;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < 64 * 64; v += 256) {
+    const int cc = v / 64, rr = v % 64;
+    const int r = r0 + rr, c = c0 + cc;
+    if (c < cols && r < ldd) dst[(int64_t)c * ldd + r] = tile[rr][cc];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 attention backward with register-resident probabilities. In the
+// keys-side kernel S = Q K^T is computed with the queries as rows, so the
+// accumulator of two 16-query blocks holds, in each lane, the 8 probabilities
+// of one key for queries 16 (e / 4) + 4 g + e % 4 -- the B-operand layout of
+// dV^T = dO^T P and dK^T = Q^T dS over those 32 queries, whose A operands
+// (dO^T, Q^T) come from the row-major query tile through the transposing LDS
+// read (ds_read_b64_tr_b16). The queries-side kernel computes S^T = K Q^T
+// (keys as rows) and dQ^T = K^T dS^T the same way. Tiles are staged with
+// 16-byte loads; no probability or transposed copy goes through LDS.
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// rows r0 .. r0 + 3 (first read) and r0 + 16 .. r0 + 19 (second) of a
+// row-major LDS tile, columns c .. c + 3 of each lane's 16-lane group
+// distributed one column per lane: element e of lane (g, lr) is row
+// 16 (e / 4) + 4 g + e % 4, column 16 D + lr when the lane points at row
+// 4 g + lr / 4, column 16 D + 4 (lr % 4)
+__device__ __forceinline__ bf16x8 tr_pair16(const bf16* p0, const bf16* p1) {
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+  const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+  const v8i16 z = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// 8 elements d .. d + 7 (d a multiple of 8) of head h's key of token (b, j)
+__device__ __forceinline__ bf16x8 key_vec(const TrainArgs& a, int b, int j, int h, int d) {
+  const int64_t row = (int64_t)b * a.Lp + j;
+  if (d < a.n) return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.kvexp) + row * a.ldkv +
+                                                       (int64_t)h * (a.n + a.dv) + d);
+  if (d < a.n + a.r)
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.cache) + row * (a.c + a.r) + a.c + (d - a.n));
+  return bf16x8{};
+}
+__device__ __forceinline__ bf16x8 val_vec(const TrainArgs& a, int b, int j, int h, int d) {
+  if (d >= a.dv) return bf16x8{};
+  const int64_t row = (int64_t)b * a.Lp + j;
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.kvexp) + row * a.ldkv +
+                                          (int64_t)h * (a.n + a.dv) + a.n + d);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a) {
+  constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16, DVB = DV / 16;
+  constexpr int QROW = DQK + 8, OROW = DV + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BT * QROW];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BT * OROW];
+  __shared__ float lse_s[BT], D_s[BT];
+  __shared__ int lo_s[BT], hi_s[BT];
+
+  const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = seq_len(a, b);
+  const int k0 = kt * BT;
+  if (k0 >= S) return;
+  const int t0 = a.cu_seqlens[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int qa = lr >> 2, qb4 = (lr & 3) * 4;
+  const float sl2 = a.scale * kLog2e;
+  const int qk = a.n + a.r;
+
+  // this lane's key (column lr of the wave's 16) as B operands
+  const int key = k0 + wave * 16 + lr;
+  const bool kok = key < S;
+  Frag<bf16> kf[KS], vf[VS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kf[ks].v = kok ? key_vec(a, b, key, h, ks * 32 + g * 8) : bf16x8{};
+#pragma unroll
+  for (int vs = 0; vs < VS; ++vs) vf[vs].v = kok ? val_vec(a, b, key, h, vs * 32 + g * 8) : bf16x8{};
+  floatx4 dkt[DKB], dvt[DVB];
+#pragma unroll
+  for (int i = 0; i < DKB; ++i) dkt[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < DVB; ++i) dvt[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  int qbeg = 0, qend = S;
+  if (a.mask.row_lo == nullptr) {
+    if (a.mask.kind == 1) qbeg = k0;
+    else if (a.mask.kind == 2) { qbeg = k0; qend = min(S, k0 + BT - 1 + max(a.mask.window, 0)); }
+  }
+  qbeg = (qbeg / BT) * BT;
+  const bf16* Qg = reinterpret_cast<const bf16*>(a.q);
+  const bf16* dOg = reinterpret_cast<const bf16*>(a.dO);
+
+  // staging: every load of the tile is issued before the first store (one
+  // memory latency per tile, not one per vector)
+  constexpr int NQV = BT * (DQK / 8) / 256, NOV = BT * (DV / 8) / 256;
+  static_assert(BT * (DQK / 8) % 256 == 0 && BT * (DV / 8) % 256 == 0, "whole staging rounds");
+  for (int q0 = qbeg; q0 < qend; q0 += BT) {
+    bf16x8 qv[NQV], ov[NOV];
+#pragma unroll
+    for (int u = 0; u < NQV; ++u) {
+      const int v = tid + 256 * u;
+      const int qq = v / (DQK / 8), d = (v % (DQK / 8)) * 8;
+      const int qi = q0 + qq;
+      qv[u] = (qi < S && d < qk) ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)(t0 + qi) * a.ldq + (int64_t)h * qk + d)
+                                 : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < NOV; ++u) {
+      const int v = tid + 256 * u;
+      const int qq = v / (DV / 8), d = (v % (DV / 8)) * 8;
+      const int qi = q0 + qq;
+      ov[u] = (qi < S && d < a.dv)
+                  ? *reinterpret_cast<const bf16x8*>(dOg + (int64_t)(t0 + qi) * a.ldo + (int64_t)h * a.dv + d)
+                  : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < NQV; ++u) {
+      const int v = tid + 256 * u;
+      *reinterpret_cast<bf16x8*>(&Qs[(v / (DQK / 8)) * QROW + (v % (DQK / 8)) * 8]) = qv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NOV; ++u) {
+      const int v = tid + 256 * u;
+      *reinterpret_cast<bf16x8*>(&dOs[(v / (DV / 8)) * OROW + (v % (DV / 8)) * 8]) = ov[u];
+    }
+    if (tid < BT) {
+      const int qi = q0 + tid;
+      float l2 = -INFINITY, dd = 0.f;
+      int lo = 0, hi = 0;
+      if (qi < S) {
+        const int t = t0 + qi;
+        l2 = a.lse[(int64_t)t * a.H + h];
+        dd = a.D[(int64_t)t * a.H + h];
+        visible_rows(a.mask, t, qi, S, lo, hi);
+      }
+      lse_s[tid] = l2; D_s[tid] = dd; lo_s[tid] = lo; hi_s[tid] = hi;
+    }
+    __syncthreads();
+
+    // S and dP: s[qb][i] is query 16 qb + 4 g + i, key lr of the wave
+    floatx4 pr[4], ds[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<bf16> af;
+        af.v = *reinterpret_cast<const bf16x8*>(&Qs[(qb * 16 + lr) * QROW + ks * 32 + g * 8]);
+        sv = mfma16(af, kf[ks], sv);
+      }
+#pragma unroll
+      for (int vs = 0; vs < VS; ++vs) {
+        Frag<bf16> af;
+        af.v = *reinterpret_cast<const bf16x8*>(&dOs[(qb * 16 + lr) * OROW + vs * 32 + g * 8]);
+        dp = mfma16(af, vf[vs], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qq = qb * 16 + g * 4 + i;
+        const bool vis = kok && key >= lo_s[qq] && key < hi_s[qq];
+        const float p = vis ? fast_exp2(sv[i] * sl2 - lse_s[qq]) : 0.f;
+        pr[qb][i] = p;
+        ds[qb][i] = p * (dp[i] - D_s[qq]);
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over 32 queries at a time
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      Frag<bf16> pf, sf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf.v[e] = (bf16)pr[2 * j][e];
+        pf.v[4 + e] = (bf16)pr[2 * j + 1][e];
+        sf.v[e] = (bf16)ds[2 * j][e];
+        sf.v[4 + e] = (bf16)ds[2 * j + 1][e];
+      }
+      const int r0 = 32 * j + 4 * g + qa;
+#pragma unroll
+      for (int D = 0; D < DVB; ++D) {
+        Frag<bf16> af;
+        af.v = tr_pair16(&dOs[r0 * OROW + 16 * D + qb4], &dOs[(r0 + 16) * OROW + 16 * D + qb4]);
+        dvt[D] = mfma16(af, pf, dvt[D]);
+      }
+#pragma unroll
+      for (int D = 0; D < DKB; ++D) {
+        Frag<bf16> af;
+        af.v = tr_pair16(&Qs[r0 * QROW + 16 * D + qb4], &Qs[(r0 + 16) * QROW + 16 * D + qb4]);
+        dkt[D] = mfma16(af, sf, dkt[D]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // dkt[D][i]: dK of key lr, dim 16 D + 4 g + i (dvt likewise)
+  if (!kok) return;
+  const int64_t t = t0 + key;
+  bf16* row = reinterpret_cast<bf16*>(a.dkvb) + t * a.lddkvb + (int64_t)h * (a.n + a.dv);
+#pragma unroll
+  for (int D = 0; D < DKB; ++D)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * D + 4 * g + i;
+      const float v = dkt[D][i] * a.scale;
+      if (d < a.n) row[d] = (bf16)v;
+      else if (d < qk) a.dkr[(t * a.H + h) * a.r + (d - a.n)] = v;
+    }
+#pragma unroll
+  for (int D = 0; D < DVB; ++D)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * D + 4 * g + i;
+      if (d < a.dv) row[a.n + d] = (bf16)dvt[D][i];
+    }
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
+  constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16;
+  constexpr int KROW = DQK + 8, VROW = DV + 8;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BT * KROW];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BT * VROW];
+
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = seq_len(a, b);
+  const int q0 = qt * BT;
+  if (q0 >= S) return;
+  const int t0 = a.cu_seqlens[b];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+  const int qa = lr >> 2, qb4 = (lr & 3) * 4;
+  const float sl2 = a.scale * kLog2e;
+  const int qk = a.n + a.r;
+  const bf16* Qg = reinterpret_cast<const bf16*>(a.q);
+  const bf16* dOg = reinterpret_cast<const bf16*>(a.dO);
+
+  // this lane's query (column lr of the wave's 16) as B operands
+  const int qi = q0 + wave * 16 + lr;
+  const bool qok = qi < S;
+  const int t = t0 + (qok ? qi : 0);
+  Frag<bf16> qf[KS], of[VS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int d = ks * 32 + g * 8;
+    qf[ks].v = (qok && d < qk) ? *reinterpret_cast<const bf16x8*>(Qg + (int64_t)t * a.ldq + (int64_t)h * qk + d)
+                               : bf16x8{};
+  }
+#pragma unroll
+  for (int vs = 0; vs < VS; ++vs) {
+    const int d = vs * 32 + g * 8;
+    of[vs].v = (qok && d < a.dv) ? *reinterpret_cast<const bf16x8*>(dOg + (int64_t)t * a.ldo + (int64_t)h * a.dv + d)
+                                 : bf16x8{};
+  }
+  float l2 = -INFINITY, dd = 0.f;
+  int lo = 0, hi = 0;
+  if (qok) {
+    l2 = a.lse[(int64_t)t * a.H + h];
+    dd = a.D[(int64_t)t * a.H + h];
+    visible_rows(a.mask, t, qi, S, lo, hi);
+  }
+  floatx4 dqt[DKB];
+#pragma unroll
+  for (int i = 0; i < DKB; ++i) dqt[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  int kbeg = 0, kend = S;
+  if (a.mask.row_lo == nullptr) {
+    if (a.mask.kind == 1) kend = min(S, q0 + BT);
+    else if (a.mask.kind == 2) { kend = min(S, q0 + BT); kbeg = max(0, q0 - max(a.mask.window, 0) + 1); }
+  }
+  kbeg = (kbeg / BT) * BT;
+
+  // staging: every load of the tile is issued before the first store
+  constexpr int NKV = BT * (DQK / 8) / 256, NVV = BT * (DV / 8) / 256;
+  static_assert(BT * (DQK / 8) % 256 == 0 && BT * (DV / 8) % 256 == 0, "whole staging rounds");
+  for (int k0 = kbeg; k0 < kend; k0 += BT) {
+    bf16x8 kv[NKV], vv[NVV];
+#pragma unroll
+    for (int u = 0; u < NKV; ++u) {
+      const int v = tid + 256 * u;
+      const int j = k0 + v / (DQK / 8);
+      kv[u] = j < S ? key_vec(a, b, j, h, (v % (DQK / 8)) * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int v = tid + 256 * u;
+      const int j = k0 + v / (DV / 8);
+      vv[u] = j < S ? val_vec(a, b, j, h, (v % (DV / 8)) * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int u = 0; u < NKV; ++u) {
+      const int v = tid + 256 * u;
+      *reinterpret_cast<bf16x8*>(&Ks[(v / (DQK / 8)) * KROW + (v % (DQK / 8)) * 8]) = kv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+      const int v = tid + 256 * u;
+      *reinterpret_cast<bf16x8*>(&Vs[(v / (DV / 8)) * VROW + (v % (DV / 8)) * 8]) = vv[u];
+    }
+    __syncthreads();
+    // S^T and dP^T: st[kb][i] is key 16 kb + 4 g + i, query lr of the wave
+    floatx4 dst[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        Frag<bf16> af;
+        af.v = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + lr) * KROW + ks * 32 + g * 8]);
+        sv = mfma16(af, qf[ks], sv);
+      }
+#pragma unroll
+      for (int vs = 0; vs < VS; ++vs) {
+        Frag<bf16> af;
+        af.v = *reinterpret_cast<const bf16x8*>(&Vs[(kb * 16 + lr) * VROW + vs * 32 + g * 8]);
+        dp = mfma16(af, of[vs], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kb * 16 + g * 4 + i;
+        const bool vis = qok && key < S && key >= lo && key < hi;
+        const float p = vis ? fast_exp2(sv[i] * sl2 - l2) : 0.f;
+        dst[kb][i] = p * (dp[i] - dd);
+      }
+    }
+    // dQ^T += K^T dS^T over 32 keys at a time
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      Frag<bf16> sf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sf.v[e] = (bf16)dst[2 * j][e];
+        sf.v[4 + e] = (bf16)dst[2 * j + 1][e];
+      }
+      const int r0 = 32 * j + 4 * g + qa;
+#pragma unroll
+      for (int D = 0; D < DKB; ++D) {
+        Frag<bf16> af;
+        af.v = tr_pair16(&Ks[r0 * KROW + 16 * D + qb4], &Ks[(r0 + 16) * KROW + 16 * D + qb4]);
+        dqt[D] = mfma16(af, sf, dqt[D]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!qok) return;
+  bf16* row = reinterpret_cast<bf16*>(a.dQ) + (int64_t)t * a.lddq + (int64_t)h * qk;
+#pragma unroll
+  for (int D = 0; D < DKB; ++D)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * D + 4 * g + i;
+      if (d < qk) row[d] = (bf16)(dqt[D][i] * a.scale);
+    }
+}
+
+template <typename T, int DQK, int DV>
+hipError_t launch_attn_bwd(const TrainArgs& a, hipStream_t s) {
+  const int tiles = (a.max_q_len + 63) / 64;
+  dim3 grid(tiles, a.H, a.batch);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, DQK, DV>), grid, dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, DQK, DV>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DQK, int DV>
+hipError_t launch_attn_bwd_bf16(const TrainArgs& a, hipStream_t s) {
+  const int tiles = (a.max_q_len + 63) / 64;
+  dim3 grid(tiles, a.H, a.batch);
+  hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t attn_bwd_t(const TrainArgs& a, hipStream_t s) {
+  const int qk = a.n + a.r;
+  if constexpr (sizeof(T) == 2) {
+    // 16-byte staging: every 8-element vector of a key lies in one source
+    if (a.n % 8 == 0 && a.r % 8 == 0 && a.dv % 8 == 0) {
+      if (qk <= 64 && a.dv <= 64) return launch_attn_bwd_bf16<64, 64>(a, s);
+      if (qk <= 192 && a.dv <= 128) return launch_attn_bwd_bf16<192, 128>(a, s);
+    }
+  }
+  if (qk <= 32 && a.dv <= 32) return launch_attn_bwd<T, 32, 32>(a, s);
+  if (qk <= 64 && a.dv <= 64) return launch_attn_bwd<T, 64, 64>(a, s);
+  if constexpr (sizeof(T) == 2) {
+    if (qk <= 192 && a.dv <= 128) return launch_attn_bwd<T, 192, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t launch_all(void (*k)(TrainArgs), int grid, const TrainArgs& a, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+const char* train_check(const TrainArgs& a, bool is_bf16) {
+  const int qk = a.n + a.r;
+  if (qk > 192 || a.dv > 128) return "backward: head dims above 192 (q/k) or 128 (v) are not supported";
+  if (!is_bf16 && (qk > 64 || a.dv > 64)) return "backward: fp32 supports q/k head dims up to 64 and v up to 64";
+  if (a.r % 2) return "backward: odd rope dim";
+  return nullptr;
+}
+
+hipError_t train_rmsnorm_rows(const void* x, int64_t ldx, const void* gamma, int N, float eps, void* y, int64_t ldy,
+                              float* rho, int rows, bool is_bf16, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (is_bf16)
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<bf16>, dim3(rows), dim3(256), 0, s, static_cast<const bf16*>(x), ldx,
+                       static_cast<const bf16*>(gamma), N, eps, static_cast<bf16*>(y), ldy, rho, rows);
+  else
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<float>, dim3(rows), dim3(256), 0, s, static_cast<const float*>(x), ldx,
+                       static_cast<const float*>(gamma), N, eps, static_cast<float*>(y), ldy, rho, rows);
+  return hipGetLastError();
+}
+
+hipError_t train_gate_fwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_all<bf16>(gate_fwd_kernel<bf16>, a.total_tokens, a, s)
+                 : launch_all<float>(gate_fwd_kernel<float>, a.total_tokens, a, s);
+}
+hipError_t train_gate_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_all<bf16>(gate_bwd_kernel<bf16>, a.total_tokens, a, s)
+                 : launch_all<float>(gate_bwd_kernel<float>, a.total_tokens, a, s);
+}
+hipError_t train_attn_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  if (a.batch <= 0 || a.max_q_len <= 0) return hipSuccess;
+  return is_bf16 ? attn_bwd_t<bf16>(a, s) : attn_bwd_t<float>(a, s);
+}
+hipError_t train_kv_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_all<bf16>(kv_bwd_kernel<bf16>, a.total_tokens, a, s)
+                 : launch_all<float>(kv_bwd_kernel<float>, a.total_tokens, a, s);
+}
+hipError_t train_q_rope_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_all<bf16>(q_rope_bwd_kernel<bf16>, a.total_tokens, a, s)
+                 : launch_all<float>(q_rope_bwd_kernel<float>, a.total_tokens, a, s);
+}
+hipError_t train_q_norm_bwd(const TrainArgs& a, bool is_bf16, hipStream_t s) {
+  return is_bf16 ? launch_all<bf16>(q_norm_bwd_kernel<bf16>, a.total_tokens, a, s)
+                 : launch_all<float>(q_norm_bwd_kernel<float>, a.total_tokens, a, s);
+}
+
+hipError_t train_gamma_grad(const void* dy, int64_t lddy, const void* x, int64_t ldx, const float* rho, int rows,
+                            int cols, float* part, void* out, bool is_bf16, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int nparts = (rows + 255) / 256;
+  dim3 g1((cols + 63) / 64, nparts);
+  if (is_bf16) {
+    hipLaunchKernelGGL(gamma_partial_kernel<bf16>, g1, dim3(256), 0, s, static_cast<const bf16*>(dy), lddy,
+                       static_cast<const bf16*>(x), ldx, rho, rows, cols, part);
+    hipLaunchKernelGGL(gamma_final_kernel<bf16>, dim3((cols + 255) / 256), dim3(256), 0, s, part, nparts, cols,
+                       static_cast<bf16*>(out));
+  } else {
+    hipLaunchKernelGGL(gamma_partial_kernel<float>, g1, dim3(256), 0, s, static_cast<const float*>(dy), lddy,
+                       static_cast<const float*>(x), ldx, rho, rows, cols, part);
+    hipLaunchKernelGGL(gamma_final_kernel<float>, dim3((cols + 255) / 256), dim3(256), 0, s, part, nparts, cols,
+                       static_cast<float*>(out));
+  }
+  return hipGetLastError();
+}
+
+hipError_t train_transpose(const void* src, int64_t lds, int rows, int cols, void* dst, int64_t ldd,
+                           const TrainArgs& a, bool map_rows, bool is_bf16, hipStream_t s) {
+  if (cols <= 0 || ldd <= 0) return hipSuccess;
+  dim3 grid((cols + 63) / 64, (int)((ldd + 63) / 64));
+  if (is_bf16)
+    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(src), lds, rows, cols,
+                       static_cast<bf16*>(dst), ldd, a, (int)map_rows);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(src), lds, rows,
+                       cols, static_cast<float*>(dst), ldd, a, (int)map_rows);
+  return hipGetLastError();
+}
+
+}  // namespace mla

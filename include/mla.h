@@ -118,6 +118,7 @@ typedef struct mla_config {
   int32_t kv_cache_dtype;   /* mla_kv_cache_dtype; FP8_E4M3 needs dtype BF16, c = 512, r = 64 */
   float kv_cache_scale;     /* FP8_E4M3: value = code * scale (> 0, finite); a power of two keeps the
                                prefill's bf16 copy of the entries exact */
+  int32_t max_train_tokens; /* mla_backward_expanded: tokens per call; 0 = not used */
 } mla_config;
 
 /* Layer weights, device pointers in nn.Linear [out, in] row-major layout with
@@ -133,6 +134,21 @@ typedef struct mla_weights {
   const void* o_proj;             /* [hidden, H * dv] */
   const void* g_proj;             /* [H * dv, hidden]             (use_output_gate) */
 } mla_weights;
+
+/* Gradients of the layer weights (mla_backward_expanded): device pointers
+ * with the shapes and element type of the mla_weights entries of the same
+ * name. A NULL entry is not computed. */
+typedef struct mla_grads {
+  void* q_a_proj;
+  void* q_a_layernorm;
+  void* q_b_proj;
+  void* q_proj;
+  void* kv_a_proj_with_mqa;
+  void* kv_a_layernorm;
+  void* kv_b_proj;
+  void* o_proj;
+  void* g_proj;
+} mla_grads;
 
 typedef struct mla_ctx mla_ctx;
 
@@ -184,6 +200,39 @@ MLA_API int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int
                          int32_t max_blocks, int32_t mask_kind, int32_t window,
                          const int32_t* row_lo, const int32_t* row_hi,
                          void* out, void* stream);
+
+/*
+ * mla_backward_expanded — gradient of the expanded MLA layer on whole training
+ * sequences (no cached prefix; token j of a sequence is at position j). The
+ * SpecForge PR "Add config-selectable MLA draft attention" trains MLA as a
+ * draft attention and validates it with gradients (Validation); the PR
+ * "extract GQA/MLA attention into reusable layers" checks outputs and
+ * gradients (Accuracy Test). The forward is mla_prefill_expanded's (MLA blog,
+ * wrapper forward and forward_mha listings) with prefix_lens = 0; given
+ * dout = dL/dout, the call writes dx = dL/dx and dL/dW of every weight named
+ * in grads, each by the chain rule through that forward: o_proj, the output
+ * gate, softmax attention (recomputed from the saved log-sum-exp), the
+ * kv_b_proj expansion, the rope key shared by the heads, RoPE, both RMSNorms
+ * and the first projections. The forward is recomputed inside the call.
+ *   x            device [total_tokens, hidden]; sequence b owns rows
+ *                cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   cu_seqlens_q device int32 [batch + 1] (as mla_prefill_expanded)
+ *   max_q_len    host: >= every sequence length
+ *   mask_kind, window, row_lo, row_hi: as mla_prefill_expanded
+ *   dout         device [total_tokens, hidden]
+ *   dx           device [total_tokens, hidden] (written)
+ *   grads        host struct of device outputs (overwritten, not accumulated)
+ * Every array is in the context's dtype. Limits: total_tokens <=
+ * max_train_tokens and <= max_tokens, batch <= max_batch, max_q_len <=
+ * max_seq_len, and batch * (max_q_len rounded up to page_size) <=
+ * max_prefill_kv (else MLA_ERR_CAPACITY). Supports q/k head dims n + r <= 192
+ * and v_head_dim <= 128 in bf16, <= 64 and <= 64 in fp32 (else
+ * MLA_ERR_UNSUPPORTED). Asynchronous; the context's workspaces are used.
+ */
+MLA_API int mla_backward_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t total_tokens,
+                         const int32_t* cu_seqlens_q, int32_t max_q_len, int32_t mask_kind, int32_t window,
+                         const int32_t* row_lo, const int32_t* row_hi, const void* dout, void* dx,
+                         const mla_grads* grads, void* stream);
 
 /*
  * mla_decode_absorbed — one new token per sequence in absorbed form (MLA blog,
@@ -298,9 +347,14 @@ MLA_API int mla_decode_absorbed_noalloc(mla_ctx* ctx, const void* x, int32_t bat
  *                  one kernel (stages 3 and 4 do not run then)
  *  11 expand_merge log-sum-exp merge of those chunks (+ output gate)
  *  12 kv_dequant   8-bit cache, prefill: bf16 copy of the visible entries
+ *  13 attn_bwd     backward: attention gradient kernels (dK/dV and dQ)
+ *  14 bwd_gemm     backward: dA, dcn, dqn and dx products
+ *  15 wgrad_gemm   backward: weight gradients (with their transposed copies)
+ *  16 bwd_pointwise backward: gate, RMSNorm, RoPE and RMSNorm-gain kernels
+ * The backward's forward recomputation is timed under stages 0-4.
  * A stage may be more than one kernel (a split-K GEMM adds its reduction).
  */
-#define MLA_NUM_STAGES 13
+#define MLA_NUM_STAGES 17
 MLA_API int mla_profile_enable(mla_ctx* ctx, int32_t enable);
 /* ms[i]: total elapsed milliseconds of stage i; count[i]: times it ran. Both
  * host arrays of MLA_NUM_STAGES entries (count may be NULL). Synchronises. */

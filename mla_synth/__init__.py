@@ -23,7 +23,9 @@ is then rounded to the storage dtype, round-to-nearest-even for bf16):
 The five named workloads are the shapes of the MLA configurations this library
 is measured on (a tiny fp32 model, a draft block over a latent prefix, a
 DeepSeek-V3-shaped absorbed decode, a long causal prefill and a long-context
-sliding-window decode with an output gate).
+sliding-window decode with an output gate); train_bf16 is four causal
+training sequences of 2048 tokens at the draft-block model dims, for the
+backward pass (with dL/dout from draw_dout).
 """
 from __future__ import annotations
 
@@ -156,6 +158,8 @@ DIMS: Dict[str, ModelDims] = {
                                   rope_style=ROPE_INTERLEAVED, use_output_gate=True,
                                   **_DEEPSEEK_HEAD),
 }
+# training sequences at the draft-block model dims (the backward pass)
+DIMS["train_bf16"] = DIMS["draft_block_bf16"]
 
 # Full-size batch shapes of each workload.
 SHAPES = {
@@ -168,6 +172,7 @@ SHAPES = {
                          mask_kind=MASK_CAUSAL),
     "long_decode_bf16": dict(mode="decode", seed=4, batch=16, len_range=(16384, 32768),
                              mask_kind=MASK_SLIDING, window=1024),
+    "train_bf16": dict(mode="prefill", seed=5, q_lens=[2048] * 4, prefix_lens=[0] * 4, mask_kind=MASK_CAUSAL),
 }
 
 
@@ -287,6 +292,18 @@ def make_workload(name: str, *, seed: Optional[int] = None, batch: Optional[int]
                     num_blocks=total, mask_kind=mask_kind, window=window,
                     row_lo=row_lo, row_hi=row_hi, kv_scale=float(kv_scale), prefix_codes=prefix_codes)
 
+
+def draw_dout(w: Workload, seed: int) -> np.ndarray:
+    """dL/dout of a training workload [total_tokens, hidden]: N(0, 1) from a
+    generator of its own, rounded to the workload's dtype (an input of the
+    backward pass, like x)."""
+    rng = np.random.default_rng(seed)
+    return round_to_dtype(rng.standard_normal((w.total_tokens, w.dims.hidden_size), dtype=np.float32),
+                          w.dims.dtype)
+
+
+# seed of dL/dout of the training workload
+TRAIN_DOUT_SEED = 8
 
 # seed of the sparse decode workload's lists (decode_bf16 shapes, 2048 per sequence)
 SPARSE_TOPK_SEED = 7

@@ -14,6 +14,18 @@ from oracle import mla as om
 
 TOL_BF16 = dict(max_abs=2e-2, rel_l2=5e-3)
 TOL_F32 = dict(max_abs=1e-4, rel_l2=None)
+# Gradients (mla_backward_expanded). The forward's bf16 bar covers one chain
+# of bf16 storage points (q_c, q, cache entries, expanded K/V, probabilities,
+# attention output), observed 3-4.5e-3 rel-L2. A gradient recomputes that
+# forward and adds its own chain (dA, dO, P and dS of the attention backward,
+# dQ / dK / dV, dcn or dqn, the first projection's gradient, the output),
+# about 8 more roundings of 2^-9 / sqrt(3) relative each: sqrt(8) * 1.1e-3 =
+# 3.2e-3 in quadrature with the forward's 4e-3 gives 5.1e-3; the bar is twice
+# the forward's. Max error relative to the tensor's scale (max(1, max |ref|)):
+# a weight gradient sums over every token, so an element that cancels to a
+# small value keeps the absolute error of its large terms.
+TOL_BF16_GRAD = dict(max_abs=2e-2, rel_l2=1e-2)
+TOL_F32_GRAD = dict(max_abs=1e-4, rel_l2=None)
 
 
 def say(msg: str):
@@ -87,7 +99,8 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def assert_close(got, ref, dtype: str, what: str, magnitude_scaled: bool = False):
+def assert_close(got, ref, dtype: str, what: str, magnitude_scaled: bool = False, tol=None,
+                 tensor_scaled: bool = False):
     """max |got - ref| <= max_abs and ||got - ref|| / ||ref|| <= rel_l2.
 
     magnitude_scaled: the max-abs bar is applied to |got - ref| / max(1, |ref|).
@@ -95,11 +108,13 @@ def assert_close(got, ref, dtype: str, what: str, magnitude_scaled: bool = False
     2^-9 |v| (0.0156 at |v| = 8, above 2e-2 beyond), and the unnormalised rope
     key reaches |v| of about 8, so an absolute bar cannot hold for any bf16
     storage of it; the relative L2 bar is unchanged."""
-    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    tol = tol or (TOL_BF16 if dtype == "bf16" else TOL_F32)
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
     max_abs, rel = errors(got, ref)
     worst = max_abs
-    if magnitude_scaled and got.size:
+    if tensor_scaled and got.size:
+        worst = max_abs / max(1.0, float(np.max(np.abs(np.asarray(ref, np.float64)))))
+    elif magnitude_scaled and got.size:
         d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
         worst = float(np.max(d / np.maximum(1.0, np.abs(np.asarray(ref, np.float64)))))
     say(f"  {what}: max_abs={max_abs:.3e} scaled_max={worst:.3e} rel_l2={rel:.3e}")
@@ -205,3 +220,56 @@ def check(w: ms.Workload, out, cache, res, rows_per_seq=None):
         assert_close(np.concatenate(got_e), np.concatenate(ref_e), w.dims.dtype, "cache entries",
                      magnitude_scaled=True)
     assert_close(np.concatenate(got_o), np.concatenate(ref_o), w.dims.dtype, "out")
+
+
+# ------------------------------------------------------------ backward pass
+
+draw_dout = ms.draw_dout
+
+
+def run_backward(w: ms.Workload, dout: np.ndarray):
+    """One mla_backward_expanded call on a training workload (no prefix).
+    Returns (dx [T, hidden], {weight name: dW}) as float32 numpy."""
+    from mla_synth.device import to_torch
+    say(f"[gpu-bwd] {w.name} B={w.batch} T={w.total_tokens} max_q={int(w.q_lens.max())} mask={w.mask_kind} "
+        f"window={w.window} seed={w.seed} heads={w.dims.num_heads} dtype={w.dims.dtype}")
+    assert int(w.prefix_lens.max()) == 0
+    t = upload(w)
+    d = w.dims
+    max_q = int(w.q_lens.max())
+    lp = -(-max_q // d.page_size) * d.page_size
+    cfg = B.make_config(d, max_batch=w.batch, max_tokens=w.total_tokens, max_seq_len=max_q,
+                        max_prefill_kv=w.batch * lp, max_train_tokens=w.total_tokens)
+    m = B.MLA(cfg, t["weights"])
+    dt = torch.bfloat16 if d.dtype == "bf16" else torch.float32
+    g = {k: torch.full_like(v, float("nan")) for k, v in t["weights"].items()}
+    dx = torch.full((w.total_tokens, d.hidden_size), float("nan"), dtype=dt, device="cuda")
+    m.backward(t["x"], t["cu_seqlens"], max_q, w.mask_kind, w.window, to_torch(dout, d.dtype, "cuda"), dx, g,
+               row_lo=t.get("row_lo"), row_hi=t.get("row_hi"))
+    torch.cuda.synchronize()
+    m.close()
+    return from_torch(dx), {k: from_torch(v) for k, v in g.items()}
+
+
+def check_backward(w: ms.Workload, dout, dx, grads, seqs=None, tol=None):
+    """dx rows and every weight gradient against oracle.backward (the weight
+    gradients are compared only when every sequence is evaluated), to the
+    gradient bars TOL_BF16_GRAD / TOL_F32_GRAD with the max error taken
+    relative to each tensor's scale."""
+    from oracle import backward as ob
+    dxs, dW, _ = ob.backward(w.dims, w.weights, w.x, w.q_lens, w.mask_kind, dout, w.window, w.row_lo, w.row_hi,
+                             seqs=seqs)
+    cu = w.cu_seqlens
+    got = np.concatenate([dx[cu[b]:cu[b + 1]] for b in dxs])
+    ref = np.concatenate([dxs[b] for b in dxs])
+    pairs = [("dx", got, ref)]
+    if seqs is None:
+        pairs += [(f"d{k}", grads[k], dW[k]) for k in sorted(dW)]
+    failures = []
+    tol = tol or (TOL_BF16_GRAD if w.dims.dtype == "bf16" else TOL_F32_GRAD)
+    for what, gv, rv in pairs:  # every comparison is printed before the first failure is raised
+        try:
+            assert_close(gv, rv, w.dims.dtype, what, tol=tol, tensor_scaled=True)
+        except AssertionError as e:
+            failures.append(str(e))
+    assert not failures, "; ".join(failures)

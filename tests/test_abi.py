@@ -116,4 +116,7 @@ def test_calls_reject_null_context():
                                     None, None, None, None) == 1
     assert "ctx" in B.last_error()
     assert lib.mla_decode_absorbed(None, None, 1, None, 1, None, 1, None, 1, 0, 0, None, None) == 1
+    assert lib.mla_backward_expanded(None, None, 1, 1, None, 1, 0, 0, None, None, None, None, None, None) == 1
+    assert "ctx" in B.last_error()
+    assert lib.mla_decode_absorbed_noalloc(None, None, 1, None, 1, None, 1, None, 1, 0, 0, None, None) == 1
     lib.mla_free(None)  # no-op

@@ -1,0 +1,72 @@
+"""GPU parity of mla_backward_expanded (the gradient of the expanded MLA layer
+on training sequences) against the fp64 oracle's analytic gradient
+(oracle.backward, pinned by finite differences and torch.autograd on the
+CPU): dx and every weight gradient, same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import mla_synth as ms
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts only with -m gpu
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _check(w, seed, **kw):
+    dout = U.draw_dout(w, seed)
+    dx, g = U.run_backward(w, dout)
+    U.check_backward(w, dout, dx, g, **kw)
+
+
+def test_backward_tiny_f32():
+    """The tiny fp32 model: two causal sequences (16 and 9 tokens)."""
+    w = ms.make_workload("tiny_f32", q_lens=[16, 9], prefix_lens=[0, 0], seed=70)
+    _check(w, 170)
+
+
+@pytest.mark.parametrize("variant", [
+    dict(q_lora_rank=64, rope_style=ms.ROPE_INTERLEAVED, use_output_gate=True),
+    dict(use_output_gate=True),
+])
+@pytest.mark.parametrize("mask,window", [(ms.MASK_FULL, 0), (ms.MASK_SLIDING, 7), (ms.MASK_CAUSAL, 0)])
+def test_backward_tiny_f32_variants(variant, mask, window):
+    """Low-rank query, gate, both RoPE styles, every mask; lengths across
+    the 64-token tiles (70, 1, 130)."""
+    w = ms.make_workload("tiny_f32", dims_override=variant, q_lens=[70, 1, 130], prefix_lens=[0, 0, 0],
+                         mask_kind=mask, window=window, seed=71, gamma_noise=True)
+    _check(w, 171)
+
+
+def test_backward_tiny_f32_dropped_rows():
+    """Explicit visible intervals: dropped rows (no visible key) pass no
+    gradient; an interval that ends before the row's own position."""
+    q_lens = [20, 12]
+    T = sum(q_lens)
+    lo = np.zeros(T, np.int32)
+    hi = np.array([i + 1 for q in q_lens for i in range(q)], np.int32)
+    hi[3:6] = 0
+    lo[25:27], hi[25:27] = 2, 4
+    w = ms.make_workload("tiny_f32", q_lens=q_lens, prefix_lens=[0, 0], row_interval=(lo, hi), seed=72,
+                         dims_override=dict(q_lora_rank=64))
+    _check(w, 172)
+
+
+def test_backward_draft_block_dims_bf16():
+    """bf16 at the draft-block model dims (hidden 4096, 32 heads, q_lora
+    1536, kv_lora 512, nope 128, rope 64, v 128, interleaved RoPE): two
+    causal training sequences of 200 and 77 tokens."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[200, 77], prefix_lens=[0, 0], mask_kind=ms.MASK_CAUSAL,
+                         seed=73)
+    _check(w, 173)
+
+
+def test_backward_gate_neox_bf16():
+    """bf16, 16 heads, output gate, NeoX RoPE, sliding window 50, lengths 130,
+    64 and 1."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[130, 64, 1], prefix_lens=[0, 0, 0], mask_kind=ms.MASK_SLIDING,
+                         window=50, seed=74,
+                         dims_override={"num_heads": 16, "use_output_gate": True, "rope_style": ms.ROPE_NEOX})
+    _check(w, 174)
