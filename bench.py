@@ -211,6 +211,7 @@ STAGE_SOURCES = {
     "expand_attn": ["attn_mha_fused.hip", "kernels.h", "common.h"],
     "expand_merge": ["attn_mha_fused.hip", "kernels.h", "common.h"],
     "kv_dequant": ["mla_api.hip", "kernels.h", "common.h"],
+    "attn_bwd": ["train.hip", "kernels.h", "common.h"],
 }
 # kernel that carries a stage (the one whose counters are summarised); a
 # stage whose kernel name also runs other stages of the workload (a GEMM
@@ -221,6 +222,8 @@ STAGE_KERNEL = {
     "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
     "rope_cache": "rope_cache_kernel", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
     "kv_dequant": "kv_shadow_kernel",
+    # a stage of two kernels: its traffic is the sum of both per-dispatch averages
+    "attn_bwd": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd_dq_bf16_kernel"),
 }
 COPY_KERNEL = "neg_kernel"  # torch's elementwise negation kernel of the copy calibration (not the flush fill)
 
@@ -264,20 +267,28 @@ def traffic_summary(fetch_dir, write_dir, workload, copy_mib, commands, out_dir=
         fac = [known_kib / v for g, v in cp.values() if g == gmax and v > 0]
         res[counter] = (rows, sum(fac) / len(fac), (min(fac), max(fac)), len(fac))
     written = []
-    for stage, pat in STAGE_KERNEL.items():
+    for stage, pats in STAGE_KERNEL.items():
+        pats = (pats,) if isinstance(pats, str) else pats
         per = {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             rows, factor, spread, ncal = res[counter]
-            disp = _per_dispatch(rows, counter, pat)
-            if not disp or len({g for g, _ in disp.values()}) != 1:
+            tot, nd = 0.0, None
+            for pat in pats:
+                disp = _per_dispatch(rows, counter, pat)
+                if not disp or len({g for g, _ in disp.values()}) != 1:
+                    nd = None
+                    break
+                tot += sum(v for _, v in disp.values()) / len(disp)
+                nd = len(disp)
+            if nd is None:
                 per = None
                 break
-            per[counter] = (sum(v for _, v in disp.values()) / len(disp), factor, len(disp), spread, ncal)
+            per[counter] = (tot, factor, nd, spread, ncal)
         if not per:
             continue
         fk, ff, n, fs, fn = per["FETCH_SIZE"]
         wk, wf, _, ws, wn = per["WRITE_SIZE"]
-        rec = {"stage": stage, "workload": workload, "kernel": pat, "dispatches": n,
+        rec = {"stage": stage, "workload": workload, "kernel": " + ".join(pats), "dispatches": n,
                "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
                "copy_calibration_mib": copy_mib, "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
                "fetch_factor_spread": [round(fs[0], 4), round(fs[1], 4)],
@@ -297,7 +308,9 @@ def trace_summary(stats_csv, workload, command, bench_line, out_dir=None):
     table of a bench.py run, with the bench line of the same run and the
     hash of the kernel sources it was taken on."""
     import csv
-    rows = list(csv.DictReader(open(stats_csv)))
+    # torch's spin kernel is the measuring harness's own (it holds the GPU while
+    # the profiled pass's launches are queued), not part of the workload
+    rows = [r for r in csv.DictReader(open(stats_csv)) if "spin_kernel" not in r["Name"]]
     line = json.loads(bench_line)
     rf = line.get("roofline") or {}
     stage = rf.get("kernel", "step")
@@ -307,7 +320,8 @@ def trace_summary(stats_csv, workload, command, bench_line, out_dir=None):
            f" dominant-stage sources: `{kernel_source_sha(STAGE_SOURCES.get(stage, srcs))}`.", "",
            "Command (`<repo>` is the repository root, `<out>` any output directory):", "",
            f"    {command}", "", f"Workload: {DESCR.get(workload, workload)}.", "",
-           "## rocprofv3 kernel statistics (all calls, including warmup and context setup)", "",
+           "## rocprofv3 kernel statistics (all calls, including warmup and context setup; the",
+           "harness's GPU spin before the profiled pass left out)", "",
            "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows[:12]:
         name = r["Name"][:90]
@@ -677,6 +691,7 @@ def main():
     ap.add_argument("--mfma-summary", metavar="PMC_DIR",
                     help="write profiles/mfma_<workload>.json from one rocprofv3 --pmc run of --workload "
                          "with the MFMA counters; no GPU work")
+    ap.add_argument("--out-dir", default=None, help="directory of the summary files (default: profiles/)")
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="write profiles/<stage>_<workload>.md from the kernel_stats.csv of a rocprofv3 "
                          "--kernel-trace --stats run of --workload and that run's bench line; no GPU work")
@@ -688,14 +703,14 @@ def main():
         cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) +
                f" --output-format csv -d <out> -o run -- python3 <repo>/bench.py --workload {args.workload} "
                f"--steps {args.steps} --warmup {args.warmup} --cpu-seconds 0 --no-peaks")
-        print("wrote", mfma_summary(args.mfma_summary, args.workload, cmd))
+        print("wrote", mfma_summary(args.mfma_summary, args.workload, cmd, args.out_dir))
         return
     if args.traffic_summary:
         cmd = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --output-format csv -d <out> -o run -- "
                f"python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} --warmup {args.warmup} "
                f"--cpu-seconds 0 --no-peaks --copy-calibrate {args.copy_calibrate}")
         for p in traffic_summary(*args.traffic_summary, args.workload, args.copy_calibrate,
-                                 [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")]):
+                                 [cmd.format(c="FETCH_SIZE"), cmd.format(c="WRITE_SIZE")], args.out_dir):
             print("wrote", p)
         return
     if args.trace_summary:
@@ -703,7 +718,7 @@ def main():
                f"-o run -- python3 <repo>/bench.py --workload {args.workload} --steps {args.steps} "
                f"--warmup {args.warmup} --cpu-seconds 0 --no-peaks")
         line = next(ln for ln in open(args.trace_summary[1]) if ln.startswith("{"))
-        print("wrote", trace_summary(args.trace_summary[0], args.workload, cmd, line))
+        print("wrote", trace_summary(args.trace_summary[0], args.workload, cmd, line, args.out_dir))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
