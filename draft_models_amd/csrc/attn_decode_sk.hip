@@ -55,13 +55,20 @@ static_assert(HB == 8, "the rescale flags of the head blocks are read as one 8-b
 constexpr int ROWB = ECH * 16;      // bytes per tile row
 constexpr float kLog2e = 1.4426950408889634f;
 static_assert(SLOTS % 256 == 0 && (SLOTS % NT) % 256 == 0, "tile slots: whole 64-lane DMA instructions");
-// 8-bit cache: a tile is copied as 36 chunks of 16 codes per row into a
-// staging area, then widened to bf16 into the ring by the wavefront that
-// copied each chunk
+// 8-bit cache: a tile is copied as 36 chunks of 16 codes per row into a ring
+// of staging buffers, where both products read the codes and widen them to
+// bf16 in registers
 constexpr int ECH8 = 36;
 constexpr int SLOTS8 = KT * ECH8;
 constexpr int DMA_N8 = (SLOTS8 + NT - 1) / NT;
 static_assert(SLOTS8 % 64 == 0 && ECH8 * 16 == ROWB / 2, "8-bit tile: whole 64-lane copy instructions");
+
+// Staged 8-bit tile: chunk c (16 codes) of row `row` sits in slot
+// 36 row + (c ^ swz8(row)) (the XOR stays inside an aligned group of 4 chunks).
+// Rows are 576 bytes (16 row mod 64 banks), so the 16 rows that one 16-byte
+// read serves at a time land on distinct banks, as do the 8 rows x 2 halves
+// of a chunk that 16 lanes of an 8-byte transposing read take.
+__device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
 
 // Chunk c (16 bytes) of tile row `row` sits at chunk (c & ~7) + ((c & 7) ^ swz(row))
 // of the row (rows are 72 chunks = 1152 bytes, so rows r and r + 2 start on
@@ -70,6 +77,7 @@ static_assert(SLOTS8 % 64 == 0 && ECH8 * 16 == ROWB / 2, "8-bit tile: whole 64-l
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 // Two transposing LDS reads (4 keys each) concatenated into one 8-element
@@ -132,10 +140,14 @@ template <> struct Blocks<false> {
 
 // GATHER: sparse lists (a.gather_ent), compiled separately so that the
 // contiguous-range kernel carries none of its registers
+// FP8: 8-bit cache. The codes of tile t stay in staging buffer t % 3, where
+// both products read them (16-byte reads for the scores, 8-bit transposing
+// reads for the values) and widen them to bf16 in registers; no bf16 ring.
 template <int NBUF, bool GATHER, bool FP8>
 __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16x8 tile[NBUF][SLOTS];
-  __shared__ __attribute__((aligned(16))) uint4 stage8[FP8 ? SLOTS8 : 1];  // 8-bit tile being copied
+  constexpr int NSTAGE = FP8 ? 3 : 1;
+  __shared__ __attribute__((aligned(16))) bf16x8 tile[FP8 ? 1 : NBUF][FP8 ? 1 : SLOTS];
+  __shared__ __attribute__((aligned(16))) uint4 stage8[NSTAGE][FP8 ? SLOTS8 : 1];
   __shared__ int t_ent[kDecodeMaxTiles];  // first cache entry of the tile, -1: unmapped page
   __shared__ int t_k0[kDecodeMaxTiles];   // key of the tile's row 0
   __shared__ int t_seq[kDecodeMaxTiles];
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   // ---- tile list: prefix sum of the per-sequence tile counts (in tile 0's
   // memory, before any copy into it), then this range's tiles
   constexpr int SPT = kDecodeMaxBatch / NT;  // sequences per thread in the scan
-  int* tstart = reinterpret_cast<int*>(&tile[0][0]);
+  int* tstart = FP8 ? reinterpret_cast<int*>(&stage8[0][0]) : reinterpret_cast<int*>(&tile[0][0]);
   {
     int cnt[SPT], loc = 0;
 #pragma unroll
@@ -257,11 +269,12 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     return e;
   };
 
-  // 8-bit cache: instruction j of this wavefront copies chunks
-  // [(NW j + wave) 64, +64) of the tile (row p / 36, codes 16 (p % 36) ..)
+  // 8-bit cache: instruction j of this wavefront fills staging slots
+  // [(NW j + wave) 64, +64) of buffer `buf`; slot p holds chunk
+  // (p % 36) ^ swz8(p / 36) of row p / 36
   const bool last_dma8 = (DMA_N8 - 1) * NW * 64 + wave * 64 < SLOTS8;
-  const uint32_t stage_lds = lds_addr(&stage8[0]);
-  auto issue8 = [&](int ent, int k0, int lo, int hi, int ev) {
+  const uint32_t stage_lds = lds_addr(&stage8[0][0]);
+  auto issue8 = [&](int buf, int ent, int k0, int lo, int hi, int ev) {
     const uint8_t* cache8 = reinterpret_cast<const uint8_t*>(a.cache);
     uint32_t z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -271,59 +284,39 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       if (j == DMA_N8 - 1 && !last_dma8) continue;
       const int pidx = (j * NW + wave) * 64 + lane + (int)z;
       const int row = pidx / ECH8;
+      const int c = (pidx - row * ECH8) ^ swz8(row);  // source chunk of the slot
       const void* src;
       if (gather) {
         const int e = __shfl(ev, row);
-        src = e >= 0 ? (const void*)(cache8 + (int64_t)e * (ECH8 * 16) + (pidx - row * ECH8) * 16) : (const void*)a.zeros;
+        src = e >= 0 ? (const void*)(cache8 + (int64_t)e * (ECH8 * 16) + c * 16) : (const void*)a.zeros;
       } else {
         const int key = k0 + row;
         const bool ok = inner || (ent >= 0 && key >= lo && key < hi);
-        src = ok ? (const void*)(cache8 + (int64_t)ent * (ECH8 * 16) + pidx * 16) : (const void*)a.zeros;
+        src = ok ? (const void*)(cache8 + ((int64_t)ent + row) * (ECH8 * 16) + c * 16) : (const void*)a.zeros;
       }
-      dma16_v(src, stage_lds + (uint32_t)(j * NW + wave) * 1024u);
+      dma16_v(src, stage_lds + (uint32_t)buf * (SLOTS8 * 16) + (uint32_t)(j * NW + wave) * 1024u);
     }
   };
-  // widen this wavefront's chunks of the staged 8-bit tile into ring buffer
-  // `buf` (after its copies landed): codes 16 m .. 16 m + 15 of a row are
-  // bf16 chunks 2 m and 2 m + 1 (exact: every E4M3 value is a bf16 value)
-  auto widen8 = [&](int buf) {
-    char* T = reinterpret_cast<char*>(&tile[buf][0]);
-#pragma unroll
-    for (int j = 0; j < DMA_N8; ++j) {
-      if (j == DMA_N8 - 1 && !last_dma8) continue;
-      const int pidx = (j * NW + wave) * 64 + lane;
-      const uint4 w = stage8[pidx];
-      const int row = pidx / ECH8, m = pidx - row * ECH8;
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      bf16x8 o[2];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q] >> (16 * h), 1.0f, false);
-          o[q >> 1][4 * (q & 1) + 2 * h] = d[0];
-          o[q >> 1][4 * (q & 1) + 2 * h + 1] = d[1];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = 2 * m + u;
-        const int pos = (c & ~7) | ((c & 7) ^ swz(row));
-        *reinterpret_cast<bf16x8*>(T + row * ROWB + pos * 16) = o[u];
-      }
-    }
+  // 8 codes (two dwords) -> one bf16 operand (exact: every E4M3 value is a
+  // bf16 value)
+  auto widen8x8 = [](uint32_t x, uint32_t y) __attribute__((always_inline)) {
+    const auto d0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false);
+    const auto d1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true);
+    const auto d2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, false);
+    const auto d3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(y, 1.0f, true);
+    return bf16x8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
   };
-
   // ev: the gathered entries of tile i (sparse lists only)
-  auto issue = [&](int i, int buf, int ev) {
+  auto issue = [&](int i, int ev) {
     const int ent = __builtin_amdgcn_readfirstlane(t_ent[i]);
     const int k0 = __builtin_amdgcn_readfirstlane(t_k0[i]);
     const int lo = __builtin_amdgcn_readfirstlane(t_lo[i]);
     const int hi = __builtin_amdgcn_readfirstlane(t_hi[i]);
     if constexpr (FP8) {
-      issue8(ent, k0, lo, hi, ev);
+      issue8(i % NSTAGE, ent, k0, lo, hi, ev);
       return;
     }
+    const int buf = i % NBUF;
     const uint32_t dst = tile_lds + (uint32_t)buf * (SLOTS * 16) + (uint32_t)wave * 1024u;
     uint32_t z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -383,23 +376,40 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) kb[u] = row * ROWB + (((2 * u) | hl) ^ swz(row)) * 16;
   }
+  // 8-bit cache: steps 2 u and 2 u + 1 take the codes of chunk 2 u + l / 32
+  // (codes 0-7, then 8-15) from one 16-byte read of the staged tile: lane l
+  // reads row l % 32, slot 36 row + 4 (u / 2) + ((2 (u % 2) + l / 32) ^ swz8(row));
+  // kb8[u % 2] is the byte offset without the 64 (u / 2). The queries follow
+  // the same order of the 576 dims (step t, half h: dims 16 (2 (t / 2) + h) +
+  // 8 (t % 2) .. + 7).
+  int kb8[2];
+  {
+    const int row = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kb8[u] = row * (ECH8 * 16) + (((2 * u) | hl) ^ swz8(row)) * 16;
+  }
   // value operand A (16 dims x 32 keys, transposing reads): lane k = 4 qa + qb
   // of 16-lane group g points at rows 4 g + qa (and 16 + 4 g + qa), dims
-  // 16 D + 4 qb .. + 3 = chunk 2 D + qb / 2, byte (qb & 1) * 8 of the chunk
+  // 16 D + 4 qb .. + 3 = chunk 2 D + qb / 2, byte (qb & 1) * 8 of the chunk.
+  // 8-bit cache (ds_read_b64_tr_b8: element r of lane t of a 16-lane group
+  // is byte t % 8 of the 8 read by lane 2 r + t / 8): lane s of group g points
+  // at key row 8 g + s / 2, codes 16 D + 8 (s % 2) .. + 7, so that lane t
+  // receives dim 16 D + t of keys 8 g .. 8 g + 7
   int vrow, vx;
   {
     const int qa = lr >> 2, qb = lr & 3;
-    const int row = 4 * g + qa;
-    vrow = row * ROWB + (qb & 1) * 8;
-    vx = (qb >> 1) ^ swz(row);
+    const int row = FP8 ? 8 * g + (lr >> 1) : 4 * g + qa;
+    vrow = FP8 ? row * (ECH8 * 16) + (lr & 1) * 8 : row * ROWB + (qb & 1) * 8;
+    vx = FP8 ? swz8(row) : (qb >> 1) ^ swz(row);
   }
 
   // O^T (this wavefront's blocks) += C^T P^T for tile t; operand element e of
-  // lane (g, lr) is key 16 (e / 4) + 4 g + e % 4
+  // lane (g, lr) is key 16 (e / 4) + 4 g + e % 4 (8-bit cache: key 8 g + e)
   auto value = [&](floatx4* RG, auto rolec, int t) __attribute__((always_inline)) {
     using BK = Blocks<decltype(rolec)::value>;
     const int wl = wave & 3;
-    const char* Tb = reinterpret_cast<const char*>(&tile[t % NBUF][0]);
+    const char* Tb = FP8 ? reinterpret_cast<const char*>(&stage8[t % NSTAGE][0])
+                         : reinterpret_cast<const char*>(&tile[t % NBUF][0]);
     const int pb = t & 1;
     // one 8-byte read of all the rescale flags (rare: lazy rescaling)
     const uint64_t flags = *reinterpret_cast<const uint64_t*>(&aflag[pb][0]);
@@ -420,8 +430,14 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
 #pragma unroll
       for (int j = BK::first(ps); j < BK::last(ps); ++j) {
         const int D = BK::D(j, wl);
-        const char* p = Tb + vrow + (D >> 2) * 128 + ((2 * (D & 3)) ^ vx) * 16;
-        vf[j - BK::first(ps)].v = tr_pair(p, p + 16 * ROWB);
+        if constexpr (FP8) {
+          const v2i32 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) v2i32*)(Tb + vrow + (D ^ vx) * 16));
+          vf[j - BK::first(ps)].v = widen8x8((uint32_t)w[0], (uint32_t)w[1]);
+        } else {
+          const char* p = Tb + vrow + (D >> 2) * 128 + ((2 * (D & 3)) ^ vx) * 16;
+          vf[j - BK::first(ps)].v = tr_pair(p, p + 16 * ROWB);
+        }
       }
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
@@ -438,7 +454,9 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   };
 
   // ---- ring of NBUF tiles: tile t is read in steps t (scores) and t + 1
-  // (values), so step t refills the buffer of tile t - 2 with tile t + NBUF - 2
+  // (values), so step t refills the buffer of tile t - 2 with tile t + NBUF - 2.
+  // 8-bit cache: likewise, step t copies tile t + 1 into the staging buffer of
+  // tile t - 2.
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 tiles");
   auto wait_tiles = [&](int later) {  // all but the copies of the `later` tiles issued last have landed
     if (later <= 0) MLA_WAIT_VMCNT(0);
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
   static_assert(NBUF == 3, "the sparse-list entries run one tile ahead of the copies");
   int ev = gather_load(0);                              // entries of the next tile to copy
   uint32_t gm = gather ? (uint32_t)__ballot(ev >= 0) : 0u;  // row mask of the next tile to score
-  issue(0, 0, ev);
+  issue(0, ev);
   ev = gather_load(1);
 
   // the piece loop, compiled once per role: each copy has its own register
@@ -482,8 +500,8 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       const bf16* qp = reinterpret_cast<const bf16*>(a.q) + qt * a.ldq + qh * a.qk_head + a.n;
 #pragma unroll
       for (int t = 0; t < KS2; ++t) {
-        const int e = t * 16 + (lane >> 5) * 8;
-        const bf16* src = !hok ? a.zeros : (t < 32 ? ql + e : qp + (e - 512));
+        const int e = FP8 ? (2 * (t >> 1) + (lane >> 5)) * 16 + (t & 1) * 8 : t * 16 + (lane >> 5) * 8;
+        const bf16* src = !hok ? a.zeros : (e < 512 ? ql + e : qp + (e - 512));
         RG[t] = __builtin_bit_cast(floatx4, *reinterpret_cast<const bf16x8*>(src));
       }
 #pragma unroll
@@ -495,10 +513,6 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
     // the queries, the tiles in flight and the outputs stored by the previous
     // piece (stores may complete out of order with loads): wait for everything
     MLA_WAIT_VMCNT(0);
-    // (8-bit cache: tile 0 was copied before the loop; later pieces' first
-    // tiles were widened at the end of the previous piece)
-    if constexpr (FP8)
-      if (i == 0) widen8(0);
     // ... for every wavefront; the previous piece's normalisers are no longer read
     lds_barrier();
     m = -INFINITY;
@@ -512,7 +526,7 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
       // last in step it - 1)
       const uint32_t gm_cur = gm;  // row mask of tile it (sparse lists)
       if (it < iend && it + 1 < n) {
-        issue(it + 1, (it + 1) % NBUF, ev);
+        issue(it + 1, ev);
         if (gather) {
           gm = (uint32_t)__ballot(ev >= 0);
           ev = gather_load(it + 2);
@@ -525,22 +539,41 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         if (scoring) {
           // ---- S^T (32 keys x 32 heads) = C q^T over the 576 dims
           const int k0 = __builtin_amdgcn_readfirstlane(t_k0[it]);
-          const char* Tb = reinterpret_cast<const char*>(&tile[it % NBUF][0]);
-          // key fragments are read KLA steps ahead of their MFMA (one wavefront
-          // per SIMD scores, so its own reads must cover the LDS latency)
-          constexpr int KLA = GATHER ? 3 : 4;  // (the sparse lists hold more registers)
           floatx16 sc = {};
-          bf16x8 kf[KLA];
+          if constexpr (FP8) {
+            // 16-byte code reads PLA step pairs ahead, widened just before
+            // their two MFMAs
+            const char* Sb = reinterpret_cast<const char*>(&stage8[it % NSTAGE][0]);
+            constexpr int NP = KS2 / 2, PLA = 2;
+            uint4 kw[PLA];
 #pragma unroll
-          for (int t = 0; t < KLA; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(Tb + kb[t & 3] + (t >> 2) * 128);
-          // hard scheduling fences keep each read KLA steps ahead (the
-          // scheduler would otherwise sink it to its MFMA)
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int t = 0; t < KS2; ++t) {
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KLA], __builtin_bit_cast(bf16x8, RG[t]), sc, 0, 0, 0);
-            if (t + KLA < KS2) kf[t % KLA] = *reinterpret_cast<const bf16x8*>(Tb + kb[(t + KLA) & 3] + ((t + KLA) >> 2) * 128);
+            for (int u = 0; u < PLA; ++u) kw[u] = *reinterpret_cast<const uint4*>(Sb + kb8[u & 1] + (u >> 1) * 64);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+              const uint4 w = kw[u % PLA];
+              if (u + PLA < NP) kw[u % PLA] = *reinterpret_cast<const uint4*>(Sb + kb8[(u + PLA) & 1] + ((u + PLA) >> 1) * 64);
+              sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8x8(w.x, w.y), __builtin_bit_cast(bf16x8, RG[2 * u]), sc, 0, 0, 0);
+              sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(widen8x8(w.z, w.w), __builtin_bit_cast(bf16x8, RG[2 * u + 1]), sc, 0, 0, 0);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            const char* Tb = reinterpret_cast<const char*>(&tile[it % NBUF][0]);
+            // key fragments are read KLA steps ahead of their MFMA (one wavefront
+            // per SIMD scores, so its own reads must cover the LDS latency)
+            constexpr int KLA = GATHER ? 3 : 4;  // (the sparse lists hold more registers)
+            bf16x8 kf[KLA];
+#pragma unroll
+            for (int t = 0; t < KLA; ++t) kf[t] = *reinterpret_cast<const bf16x8*>(Tb + kb[t & 3] + (t >> 2) * 128);
+            // hard scheduling fences keep each read KLA steps ahead (the
+            // scheduler would otherwise sink it to its MFMA)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < KS2; ++t) {
+              sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KLA], __builtin_bit_cast(bf16x8, RG[t]), sc, 0, 0, 0);
+              if (t + KLA < KS2) kf[t % KLA] = *reinterpret_cast<const bf16x8*>(Tb + kb[(t + KLA) & 3] + ((t + KLA) >> 2) * 128);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
           // ---- online softmax of head hs (log2 domain); element e of lane l
           // is key 8 (e / 4) + 4 (l / 32) + e % 4; lanes l and l ^ 32 hold the
@@ -579,12 +612,14 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         if (scoring) {
           // probabilities: key group kg = 2 q + l / 32 (keys 4 kg .. 4 kg + 3)
           // goes to lane 16 (kg % 4) + lr of head block hb, half kg / 4
+          // (8-bit cache: lane 16 (kg / 2) + lr, half kg % 2)
           const int hb = 2 * wave + ((lane >> 4) & 1);
           char* pbase = reinterpret_cast<char*>(&pbuf[it & 1][hb][0]);
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int kg = 2 * q4 + (lane >> 5);
-            *reinterpret_cast<bf16x4*>(pbase + (16 * (kg & 3) + lr) * 16 + (kg >> 2) * 8) = pq[q4];
+            const int off = FP8 ? (16 * (kg >> 1) + lr) * 16 + (kg & 1) * 8 : (16 * (kg & 3) + lr) * 16 + (kg >> 2) * 8;
+            *reinterpret_cast<bf16x4*>(pbase + off) = pq[q4];
           }
           const uint64_t rm = __ballot(alpha != 1.f);
           if (lane < 32) abuf[it & 1][hs] = alpha;
@@ -610,8 +645,6 @@ __global__ __launch_bounds__(NT, 1) void decode_sk_kernel(DecodeAttnArgs a) {
         value(RG, rolec, it - 1);
       }
       if (it < iend) wait_tiles(min(NBUF - 3, n - 2 - it));  // tile it + 1 landed
-      if constexpr (FP8)
-        if (it < iend && it + 1 < n) widen8((it + 1) % NBUF);
       // tile it + 1 is in LDS for every wavefront; the probabilities of tile
       // it are shared; tile it - 1 and the probabilities of tile it - 1 are no
       // longer read
