@@ -129,25 +129,27 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   const bool rowstat = rownorm && wn == 0;
   const int NK = g.K / BK;
 
-  // one k step: fragments from buffer kt % NBUF; with `copies`, the copies of
-  // steps kt + 2 and kt + 3 spread over its 32 MFMAs (one per 4)
-  auto step = [&](int kt, bool copies) {
+  // two k steps (one barrier interval): fragments of step kt from buffer
+  // kt % NBUF are read before its MFMAs, those of step kt + 1 in between them
+  // (both steps' tiles are in LDS), so that only the first step's reads wait
+  // on the LDS latency; the copies of steps kt + 2 and kt + 3 spread over the
+  // 32 MFMAs of step kt (one per 4)
+  auto frags = [&](int kt, Frag<bf16>* af, Frag<bf16>* wf, int x) __attribute__((always_inline)) {
     const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
     const bf16x8* TA = TW + SLOTS;
-    Frag<bf16> af[4], wf[8];
+    // x < 0: all twelve fragments; else the ones read during MFMA group x
+    if (x < 0) {
 #pragma unroll
-    for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wm * 64 + y * 16 + lr, g4)];
+      for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wm * 64 + y * 16 + lr, g4)];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) wf[x].v = TW[swz(wn * 128 + x * 16 + lr, g4)];
-    const bool c0 = copies && kt + 2 < NK, c1 = copies && kt + 3 < NK;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (x < 4 ? c0 : c1) copy(x < 4 ? kt + 2 : kt + 3, x & 3);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = mfma16(wf[x], af[y], acc[x][y]);
+      for (int xx = 0; xx < 8; ++xx) wf[xx].v = TW[swz(wn * 128 + xx * 16 + lr, g4)];
+    } else if (x < 4) {
+      af[x].v = TA[swz(wm * 64 + x * 16 + lr, g4)];
+      wf[2 * x].v = TW[swz(wn * 128 + 2 * x * 16 + lr, g4)];
+      wf[2 * x + 1].v = TW[swz(wn * 128 + (2 * x + 1) * 16 + lr, g4)];
     }
+  };
+  auto rstat = [&](const Frag<bf16>* af) __attribute__((always_inline)) {
     if (rowstat) {
 #pragma unroll
       for (int y = 0; y < 4; ++y)
@@ -157,6 +159,26 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
           sq[y] += f * f;
         }
     }
+  };
+  auto pair = [&](int kt) __attribute__((always_inline)) {
+    Frag<bf16> af0[4], wf0[8], af1[4], wf1[8];
+    frags(kt, af0, wf0, -1);
+    const bool c0 = kt + 2 < NK, c1 = kt + 3 < NK;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (x < 4 ? c0 : c1) copy(x < 4 ? kt + 2 : kt + 3, x & 3);
+      frags(kt + 1, af1, wf1, x);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = mfma16(wf0[x], af0[y], acc[x][y]);
+    }
+    rstat(af0);
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = mfma16(wf1[x], af1[y], acc[x][y]);
+    rstat(af1);
   };
 
 #pragma unroll
@@ -168,8 +190,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
     // are done; no newer ones exist yet
     MLA_WAIT_VMCNT(0);
     lds_barrier();  // every wavefront's copies of kt, kt + 1 landed; kt - 2, kt - 1 read by all
-    step(kt, true);
-    step(kt + 1, false);
+    pair(kt);
   }
   lds_barrier();  // the ring is read by all before it stages the output
 
