@@ -46,7 +46,12 @@ hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_el
 
 // The 256 x 256 LDS-streaming kernel (gemm_big.hip) and when it applies.
 bool gemm_big_eligible(const GemmArgs& g, bool is_bf16);
-hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s);
+// Split-K count (>= 2) for a product the kernel fits except for having too
+// few output tiles, with splits * M * N fp32 partials within ws_elems; else 0.
+int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems);
+// splits == 1: C directly; else fp32 partials part[split][M][N] (summed by
+// the caller)
+hipError_t gemm_big_launch(const GemmArgs& g, float* part, int splits, hipStream_t s);
 
 // Validation of the alignment and size assumptions of gemm_launch; returns
 // nullptr when fine, else a static message.

@@ -566,7 +566,17 @@ const char* gemm_check(const GemmArgs& g, bool is_bf16) {
 
 hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_elems, hipStream_t s) {
   if (g.M == 0) return hipSuccess;
-  if (g.zeros != nullptr && gemm_big_eligible(g, is_bf16)) return gemm_big_launch(g, g.zeros, s);
+  if (g.zeros != nullptr && gemm_big_eligible(g, is_bf16)) return gemm_big_launch(g, nullptr, 1, s);
+  if (g.zeros != nullptr && ws != nullptr) {
+    if (const int sp = gemm_big_splits(g, is_bf16, ws_elems); sp > 1) {
+      if (hipError_t e = gemm_big_launch(g, ws, sp, s); e != hipSuccess) return e;
+      const int64_t total = (int64_t)g.M * g.N;
+      const int blocks = (int)((total / 4 + 255) / 256 + 1);
+      hipLaunchKernelGGL(splitk_reduce<bf16>, dim3(blocks), dim3(256), 0, s, ws, sp, g.M, g.N,
+                         reinterpret_cast<bf16*>(g.C), g.ldc, false, g.K, 0.f);
+      return hipGetLastError();
+    }
+  }
   int ci = 0, splits = 1;
   if (is_bf16 && stream_pick(g, ws, ws_elems, 256, &ci, &splits)) return launch_stream_cfg(g, ws, ci, splits, s);
   return is_bf16 ? launch_t<bf16>(g, ws, ws_elems, s) : launch_t<float>(g, ws, ws_elems, s);

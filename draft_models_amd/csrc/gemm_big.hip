@@ -13,7 +13,10 @@
 // at a time, and those rows then hit distinct banks. Rows that do not exist
 // (past M or N, or absent gathered rows) re-read an existing row and are not
 // stored. Tiles are placed on XCDs in 2-D blocks (see TileMap) so that each
-// XCD's L2 keeps its band of weight rows.
+// XCD's L2 keeps its band of weight rows. Products with too few output tiles
+// to fill the CUs (weight gradients: K = tokens) split K: split z
+// (blockIdx.y) runs its k range and writes an fp32 partial tile, summed by a
+// reduce kernel.
 #include <algorithm>
 
 #include "common.h"
@@ -42,7 +45,7 @@ struct TileMap {
   int mtiles, ntiles, xm, xn;
 };
 
-__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, TileMap tm) {
+__global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, TileMap tm, float* part, int kper) {
   // operand ring (buffer i: weight rows, then activation rows); after the k
   // loop the same 128 KB stage the output tile for coalesced stores
   __shared__ __attribute__((aligned(16))) bf16x8 lds[NBUF * 2 * SLOTS];
@@ -63,8 +66,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address math
   const int wm = wave & 3, wn = wave >> 2;
   const int lr = lane & 15, g4 = lane >> 4;
-  const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A);
-  const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W);
+  // split-K: steps [kt0, kt0 + NK) of this split (kper steps per split, even)
+  const int kt0 = part ? (int)blockIdx.y * kper : 0;
+  const bf16* __restrict__ A = reinterpret_cast<const bf16*>(g.A) + (int64_t)kt0 * BK;
+  const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W) + (int64_t)kt0 * BK;
 
   // per-lane copy geometry (k-independent): slot s = (j * 8 + wave) * 64 +
   // lane of a tile holds chunk (row s / 4, c), its source at byte offset
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   // the RMSNorm row statistic: only the wavefronts that publish it (wn == 0)
   const bool rownorm = g.epi == EPI_ROWNORM;
   const bool rowstat = rownorm && wn == 0;
-  const int NK = g.K / BK;
+  const int NK = part ? min(kper, g.K / BK - kt0) : g.K / BK;
 
   // two k steps (one barrier interval): fragments of step kt from buffer
   // kt % NBUF are read before its MFMAs, those of step kt + 1 in between them
@@ -192,6 +197,25 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
     lds_barrier();  // every wavefront's copies of kt, kt + 1 landed; kt - 2, kt - 1 read by all
     pair(kt);
   }
+  if (part) {
+    // fp32 partial tile of split blockIdx.y: lane holds C[m][n .. n + 3]
+    float* P = part + (int64_t)blockIdx.y * g.M * g.N;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int m = m0 + wm * 64 + y * 16 + lr;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int n = n0 + wn * 128 + x * 16 + 4 * g4;
+        if (n + 3 < g.N) {
+          *reinterpret_cast<floatx4*>(P + (int64_t)m * g.N + n) = acc[x][y];
+        } else {
+          for (int e = 0; e < 4 && n + e < g.N; ++e) P[(int64_t)m * g.N + n + e] = acc[x][y][e];
+        }
+      }
+    }
+    return;
+  }
   lds_barrier();  // the ring is read by all before it stages the output
 
   if (rownorm) {
@@ -253,7 +277,9 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
 
 }  // namespace
 
-bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) {
+namespace {
+// every condition of the kernel except the number of output tiles
+bool big_shape_ok(const GemmArgs& g, bool is_bf16) {
   if (!is_bf16 || g.batch != 1 || g.K % (2 * BK) != 0 || g.M < 512 || g.N < 256) return false;  // two steps per barrier
   // 16-byte output stores (and gate loads)
   if (g.ldc % 8 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
@@ -263,11 +289,28 @@ bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) {
   if ((int64_t)g.N * g.ldw >= lim) return false;
   if (!g.gather && (int64_t)g.M * g.lda >= lim) return false;
   if (g.gather && (int64_t)g.ga.num_blocks * g.ga.page * g.ga.entry >= lim) return false;
-  return (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) >= 256;
+  return true;
+}
+int64_t big_tiles(const GemmArgs& g) { return (int64_t)((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN); }
+}  // namespace
+
+bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) { return big_shape_ok(g, is_bf16) && big_tiles(g) >= 256; }
+
+int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems) {
+  if (!big_shape_ok(g, is_bf16) || g.gather || g.epi != EPI_STORE) return 0;
+  const int64_t tiles = big_tiles(g);
+  if (tiles >= 256) return 0;
+  // one round of the 256 CUs, at most 8 splits, at least 512 of K per split
+  int sp = (int)std::min<int64_t>(8, (256 + tiles - 1) / tiles);
+  sp = std::min(sp, g.K / 512);
+  while (sp > 1 && (int64_t)sp * g.M * g.N > ws_elems) --sp;
+  if (sp < 2) return 0;
+  // even step counts per split; drop splits left empty by the rounding
+  const int nk = g.K / BK, kper = ((nk + sp - 1) / sp + 1) / 2 * 2;
+  return (nk + kper - 1) / kper;
 }
 
-hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s) {
-  (void)zeros;
+hipError_t gemm_big_launch(const GemmArgs& g, float* part, int splits, hipStream_t s) {
   TileMap tm;
   tm.mtiles = (g.M + BM - 1) / BM;
   tm.ntiles = (g.N + BN - 1) / BN;
@@ -292,7 +335,12 @@ hipError_t gemm_big_launch(const GemmArgs& g, const void* zeros, hipStream_t s) 
     const int nb = (xj + 1) * tm.ntiles / tm.xn - xj * tm.ntiles / tm.xn;
     per = std::max(per, mb * nb);
   }
-  hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8), dim3(NWAVE * 64), 0, s, g, tm);
+  if (splits > 1) {
+    const int nk = g.K / BK, kper = ((nk + splits - 1) / splits + 1) / 2 * 2;
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8, splits), dim3(NWAVE * 64), 0, s, g, tm, part, kper);
+  } else {
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(per * 8), dim3(NWAVE * 64), 0, s, g, tm, (float*)nullptr, 0);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,16 @@ def test_backward_draft_block_dims_bf16():
     _check(w, 173)
 
 
+def test_backward_split_k_bf16():
+    """bf16 at the draft-block model dims with 2 x 512 causal tokens: enough
+    rows for the 256 x 256 GEMM kernel, too few output tiles to fill the
+    GPU, so the weight gradients (K = 1024 tokens), the data gradients and
+    the recomputed first projection run split-K with fp32 partials."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[512, 512], prefix_lens=[0, 0], mask_kind=ms.MASK_CAUSAL,
+                         seed=75)
+    _check(w, 175)
+
+
 def test_backward_gate_neox_bf16():
     """bf16, 16 heads, output gate, NeoX RoPE, sliding window 50, lengths 130,
     64 and 1."""
