@@ -625,6 +625,49 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t ld
   }
 }
 
+// The same for bf16 with 16-byte accesses (rows of src and dst, and both
+// pointers, 16-byte aligned): a 64 x 64 tile is loaded as 8-element row
+// chunks, and every output chunk gathers 8 tokens of one column from LDS.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* src, int64_t lds, int rows, int cols,
+                                                             bf16* dst, int64_t ldd, TrainArgs a, int map_rows) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][64 + 8];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  for (int v = threadIdx.x; v < 64 * 8; v += 256) {
+    const int rr = v >> 3, ch = v & 7;
+    const int r = r0 + rr, c = c0 + ch * 8;
+    bf16x8 val = {};
+    if (r < rows && c < cols) {
+      int64_t sr = r;
+      if (map_rows) {
+        const int b = seq_of(a, r);
+        sr = (int64_t)b * a.Lp + (r - a.cu_seqlens[b]);
+      }
+      const bf16* p = src + sr * lds + c;
+      if (c + 8 <= cols) {
+        val = *reinterpret_cast<const bf16x8*>(p);
+      } else {
+        for (int e = 0; e < 8 && c + e < cols; ++e) val[e] = p[e];
+      }
+    }
+    *reinterpret_cast<bf16x8*>(&tile[rr][ch * 8]) = val;
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < 64 * 8; v += 256) {
+    const int cc = v >> 3, ch = v & 7;
+    const int c = c0 + cc, r = r0 + ch * 8;
+    if (c >= cols || r >= ldd) continue;
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = tile[ch * 8 + e][cc];
+    bf16* q = dst + (int64_t)c * ldd + r;
+    if (r + 8 <= ldd) {
+      *reinterpret_cast<bf16x8*>(q) = o;
+    } else {
+      for (int e = 0; e < 8 && r + e < ldd; ++e) q[e] = o[e];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 attention backward with register-resident probabilities. In the
 // keys-side kernel S = Q K^T is computed with the queries as rows, so the
@@ -1085,7 +1128,11 @@ hipError_t train_transpose(const void* src, int64_t lds, int rows, int cols, voi
                            const TrainArgs& a, bool map_rows, bool is_bf16, hipStream_t s) {
   if (cols <= 0 || ldd <= 0) return hipSuccess;
   dim3 grid((cols + 63) / 64, (int)((ldd + 63) / 64));
-  if (is_bf16)
+  const bool vec = lds % 8 == 0 && ldd % 8 == 0 && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+  if (is_bf16 && vec)
+    hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, s, static_cast<const bf16*>(src), lds, rows, cols,
+                       static_cast<bf16*>(dst), ldd, a, (int)map_rows);
+  else if (is_bf16)
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(src), lds, rows, cols,
                        static_cast<bf16*>(dst), ldd, a, (int)map_rows);
   else
