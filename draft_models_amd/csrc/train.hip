@@ -710,6 +710,23 @@ __device__ __forceinline__ bf16x8 val_vec(const TrainArgs& a, int b, int j, int 
                                           (int64_t)h * (a.n + a.dv) + a.n + d);
 }
 
+// Workgroup id -> (64-row tile, head, sequence) of the bf16 backward kernels.
+// The (sequence, head) pairs go to the 8 XCDs round-robin (a workgroup runs
+// on XCD id mod 8): pair p on XCD p mod 8, whose workgroups take all tiles of
+// one pair before the next, so that the pair's rows are fetched into one L2
+// and re-read from there by every tile. desc: tiles in descending order
+// (causal query tiles: the last sees the most keys), else ascending (key
+// tiles: the first sees the most queries), heaviest first.
+__device__ __forceinline__ bool bwd_tile(const TrainArgs& a, int tiles, bool desc, int& t, int& h, int& b) {
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int p = (slot / tiles) * 8 + xcd, ti = slot % tiles;
+  if (p >= a.H * a.batch) return false;
+  h = p % a.H;
+  b = p / a.H;
+  t = desc ? tiles - 1 - ti : ti;
+  return true;
+}
+
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a) {
   constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16, DVB = DV / 16;
@@ -719,7 +736,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
   __shared__ float lse_s[BT], D_s[BT];
   __shared__ int lo_s[BT], hi_s[BT];
 
-  const int kt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int kt, h, b;
+  if (!bwd_tile(a, (a.max_q_len + BT - 1) / BT, false, kt, h, b)) return;
   const int S = seq_len(a, b);
   const int k0 = kt * BT;
   if (k0 >= S) return;
@@ -882,7 +900,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[BT * KROW];
   __shared__ __attribute__((aligned(16))) bf16 Vs[BT * VROW];
 
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int qt, h, b;
+  if (!bwd_tile(a, (a.max_q_len + BT - 1) / BT, true, qt, h, b)) return;
   const int S = seq_len(a, b);
   const int q0 = qt * BT;
   if (q0 >= S) return;
@@ -1026,7 +1045,8 @@ hipError_t launch_attn_bwd(const TrainArgs& a, hipStream_t s) {
 template <int DQK, int DV>
 hipError_t launch_attn_bwd_bf16(const TrainArgs& a, hipStream_t s) {
   const int tiles = (a.max_q_len + 63) / 64;
-  dim3 grid(tiles, a.H, a.batch);
+  const int npx = (a.H * a.batch + 7) / 8;  // (sequence, head) pairs per XCD
+  dim3 grid((unsigned)(8 * npx * tiles));
   hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
