@@ -6,9 +6,9 @@
 // through a 4-buffer LDS ring, two steps per barrier: while steps kt and
 // kt + 1 are multiplied, both operand tiles of steps kt + 2 and kt + 3 (256
 // rows x 64 bytes each) stream from HBM straight into LDS with
-// global_load_lds_dwordx4, each wavefront's copies spread between the MFMAs
-// of the first step, so that one wavefront's copy-issue stall is covered by
-// the other wavefront of its SIMD. The 16-byte chunks of a 64-byte row are
+// global_load_lds_dwordx4, issued right after the barrier (the copy-issue
+// stall of one wavefront is covered by the other wavefront of its SIMD, and
+// the copies get the whole interval to land). The 16-byte chunks of a 64-byte row are
 // XOR-ed with (row >> 1) & 3: the LDS serves a 16-byte read 8 lanes (8 rows)
 // at a time, and those rows then hit distinct banks. Rows that do not exist
 // (past M or N, or absent gathered rows) re-read an existing row and are not
@@ -137,8 +137,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   // two k steps (one barrier interval): fragments of step kt from buffer
   // kt % NBUF are read before its MFMAs, those of step kt + 1 in between them
   // (both steps' tiles are in LDS), so that only the first step's reads wait
-  // on the LDS latency; the copies of steps kt + 2 and kt + 3 spread over the
-  // 32 MFMAs of step kt (one per 4)
+  // on the LDS latency; the copies of steps kt + 2 and kt + 3 are issued first
   auto frags = [&](int kt, Frag<bf16>* af, Frag<bf16>* wf, int x) __attribute__((always_inline)) {
     const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
     const bf16x8* TA = TW + SLOTS;
@@ -168,11 +167,17 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   auto pair = [&](int kt) __attribute__((always_inline)) {
     Frag<bf16> af0[4], wf0[8], af1[4], wf1[8];
     frags(kt, af0, wf0, -1);
-    const bool c0 = kt + 2 < NK, c1 = kt + 3 < NK;
+    // the copies of steps kt + 2 and kt + 3 all go out first: the earlier they
+    // are issued, the less the next barrier interval waits for them
+    if (kt + 2 < NK)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) copy(kt + 2, q);
+    if (kt + 3 < NK)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) copy(kt + 3, q);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       __builtin_amdgcn_sched_barrier(0);
-      if (x < 4 ? c0 : c1) copy(x < 4 ? kt + 2 : kt + 3, x & 3);
       frags(kt + 1, af1, wf1, x);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
