@@ -105,7 +105,8 @@ __device__ __forceinline__ void visible(const DecodeAttnArgs& a, int b, int& lo,
     hi = a.gather_k;
     return;
   }
-  const int L = min(max(a.seq_lens[b / a.seq_div], 0), a.max_seq_len);
+  const int64_t len = (int64_t)a.seq_lens[b / a.seq_div] + a.len_add;
+  const int L = (int)min(max(len, (int64_t)0), (int64_t)a.max_seq_len);
   lo = a.mask.kind == 2 ? max(0, L - a.mask.window) : 0;
   hi = L;
 }

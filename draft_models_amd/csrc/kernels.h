@@ -22,7 +22,7 @@ struct RopeCacheArgs {
   // token -> (sequence, position)
   int decode = 0;
   const int32_t* seq_lens = nullptr;     // decode
-  const int32_t* cu_seqlens = nullptr;   // prefill
+  const int32_t* cu_seqlens = nullptr;   // prefill; null: blocks of max_q_len tokens, block b at b max_q_len
   const int32_t* prefix_lens = nullptr;  // prefill
   int max_q_len = 0, max_kv_len = 0, max_seq_len = 0, total_tokens = 0;
   // 8-bit cache (OCP E4M3 codes of value / scale), else the compute dtype
@@ -90,6 +90,7 @@ struct DecodeAttnArgs {
   const int32_t* block_table = nullptr;
   int num_blocks = 0, max_blocks = 0, page = 0;
   const int32_t* seq_lens = nullptr;
+  int len_add = 0;                                  // added to every seq_lens entry (stream-K only)
   int max_seq_len = 0, batch = 0;
   int H = 0, n = 0, r = 0, c = 0;
   float scale = 0.f;

@@ -53,8 +53,6 @@ struct mla_ctx {
   // workspaces of the calls (allocated at init from the capacity fields)
   Workspace ws;
   void* kvexp = nullptr;   // [max_prefill_kv, H (n + dv)]
-  int32_t* blk_cu = nullptr;    // query blocks: [max_batch + 1] token offsets b q_len
-  int32_t* blk_lens = nullptr;  // query blocks: [max_batch] cache lengths prefix + q_len
   int max_splits = 32;
   int cus = 256;            // compute units of the device
   bool sk_shape = false;    // bf16 512 + 64 latent: stream-K decode
@@ -171,13 +169,6 @@ __global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst,
 }
 
 // Wuk_t[h][cc][nn] = kv_b_proj[h (n + dv) + nn][cc]
-// query blocks: cu[b] = b q_len (b <= batch), lens[b] = prefix_lens[b] + q_len
-__global__ void block_meta_kernel(const int32_t* prefix_lens, int batch, int q_len, int32_t* cu, int32_t* lens) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b <= batch) cu[b] = b * q_len;
-  if (b < batch) lens[b] = prefix_lens[b] + q_len;
-}
-
 // training cache: sequence b's page p is block b mbs + p
 __global__ void identity_table_kernel(int32_t* bt, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -600,10 +591,6 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   if ((e = dev_alloc(ctx, &ctx->ws.qlat, (size_t)QR * H * ctx->c * esz))) return bail(e);
   if ((e = dev_alloc(ctx, &ctx->ws.olat, (size_t)QR * H * ctx->c * esz))) return bail(e);
   void* p;
-  if ((e = dev_alloc(ctx, &p, (size_t)(B + 1) * sizeof(int32_t)))) return bail(e);
-  ctx->blk_cu = static_cast<int32_t*>(p);
-  if ((e = dev_alloc(ctx, &p, (size_t)B * sizeof(int32_t)))) return bail(e);
-  ctx->blk_lens = static_cast<int32_t*>(p);
   if (cfg->max_topk > 0) {
     if ((e = dev_alloc(ctx, &p, (size_t)B * cfg->max_topk * sizeof(int32_t)))) return bail(e);
     ctx->ws.sp_ent = static_cast<int32_t*>(p);
@@ -1275,7 +1262,7 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   da.q = q; da.ldq = ldq; da.qk_head = ctx->qkh;
   da.cache = kv_cache; da.block_table = block_table;
   da.num_blocks = num_blocks; da.max_blocks = max_blocks; da.page = c.page_size;
-  da.seq_lens = ctx->blk_lens; da.max_seq_len = max_kv_len; da.batch = (int)V;
+  da.seq_lens = prefix_lens; da.len_add = q_len; da.max_seq_len = max_kv_len; da.batch = (int)V;
   da.H = 128; da.Hr = H; da.seq_div = (int)(V / batch);
   da.n = ctx->n; da.r = ctx->r; da.c = ctx->c;
   da.scale = ctx->scale;
@@ -1288,10 +1275,6 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   da.tstart = ws.sk_tstart;
   if (da.ranges > ctx->sk_max_ranges) return fail(MLA_ERR_CAPACITY, "decode ranges above the init sizing");
   if (const char* m = decode_sk_check(da)) return fail(MLA_ERR_UNSUPPORTED, m);
-
-  hipLaunchKernelGGL(block_meta_kernel, dim3((batch + 256) / 256), dim3(256), 0, s, prefix_lens, batch, q_len,
-                     ctx->blk_cu, ctx->blk_lens);
-  HIP_TRY(hipGetLastError());
 
   if (int e = project(ctx, ws, x, (int)T, s, &q, &ldq)) return e;
 
@@ -1306,7 +1289,7 @@ int mla_decode_absorbed_block(mla_ctx* ctx, const void* x, int32_t batch, int32_
   rc.interleaved = c.rope_style == MLA_ROPE_INTERLEAVED;
   rc.eps = (float)c.rms_norm_eps;
   rc.kv_fp8 = ctx->kv_fp8; rc.kv_scale = ctx->kv_scale;
-  rc.decode = 0; rc.cu_seqlens = ctx->blk_cu; rc.prefix_lens = prefix_lens;
+  rc.decode = 0; rc.cu_seqlens = nullptr; rc.prefix_lens = prefix_lens;  // blocks of q_len tokens
   rc.max_q_len = q_len; rc.max_kv_len = max_kv_len; rc.max_seq_len = c.max_seq_len;
   rc.total_tokens = (int)T;
   {

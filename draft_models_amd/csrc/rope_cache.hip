@@ -25,10 +25,11 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
     t = b;
     pos = min(L, a.max_seq_len) - 1;
   } else {
-    int ql = a.cu_seqlens[b + 1] - a.cu_seqlens[b];
+    const int cb = a.cu_seqlens ? a.cu_seqlens[b] : b * a.max_q_len;
+    int ql = a.cu_seqlens ? a.cu_seqlens[b + 1] - cb : a.max_q_len;
     ql = min(max(ql, 0), a.max_q_len);
     if (i >= ql) return;
-    t = a.cu_seqlens[b] + i;
+    t = cb + i;
     if (t < 0 || t >= a.total_tokens) return;
     const int pl = min(max(a.prefix_lens[b], 0), a.max_kv_len - ql);
     pos = pl + i;
