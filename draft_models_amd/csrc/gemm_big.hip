@@ -2,13 +2,15 @@
 //
 // A 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD:
 // wavefront w computes rows 64 (w & 3) .. + 63 and columns 128 (w >> 2) ..
-// + 127 (32 accumulator blocks of 16 x 16). The k axis moves in 32-wide steps
-// through a 4-buffer LDS ring, two steps per barrier: while steps kt and
-// kt + 1 are multiplied, both operand tiles of steps kt + 2 and kt + 3 (256
-// rows x 64 bytes each) stream from HBM straight into LDS with
-// global_load_lds_dwordx4, issued right after the barrier (the copy-issue
-// stall of one wavefront is covered by the other wavefront of its SIMD, and
-// the copies get the whole interval to land). The 16-byte chunks of a 64-byte row are
+// + 127 (32 accumulator blocks of 16 x 16). The k axis moves in 32-wide steps,
+// two per barrier interval, through two LDS buffers that each hold the 64 k
+// of one interval as 128-byte rows: while steps kt and kt + 1 are multiplied,
+// both operand tiles of steps kt + 2 and kt + 3 (256 rows x 128 bytes each)
+// stream from HBM straight into LDS with global_load_lds_dwordx4, issued right
+// after the barrier (the copy-issue stall of one wavefront is covered by the
+// other wavefront of its SIMD, and the copies get the whole interval to land).
+// One copy instruction moves 8 whole 128-byte rows: each source cache line is
+// requested once, not once per 32-wide step. The 16-byte chunks of a row are
 // XOR-ed with (row >> 1) & 3: the LDS serves a 16-byte read 8 lanes (8 rows)
 // at a time, and those rows then hit distinct banks. Rows that do not exist
 // (past M or N, or absent gathered rows) re-read an existing row and are not
@@ -27,12 +29,12 @@ namespace mla {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int ROWCH = BK / 8;                    // 16-byte chunks per 64-byte tile row
-constexpr int SLOTS = 256 * ROWCH;               // 16-byte slots per operand tile (16 KB)
-constexpr int NBUF = 4;                          // ring buffers (two steps multiplied, two copied)
+constexpr int ROWCH = 2 * BK / 8;                // 16-byte chunks per 128-byte tile row (two k steps)
+constexpr int SLOTS = 256 * ROWCH;               // 16-byte slots per operand tile (32 KB)
+constexpr int NBUF = 2;                          // buffers (one interval multiplied, one copied)
 constexpr int NWAVE = 8;
-constexpr int DPW = SLOTS / (NWAVE * 64);        // copies per wavefront per operand per step
-static_assert(DPW == 2, "copy schedule assumes 2 copies per operand and wavefront");
+constexpr int DPW = SLOTS / (NWAVE * 64);        // copies per wavefront per operand per interval
+static_assert(DPW == 4, "copy schedule assumes 4 copies per operand and wavefront");
 
 __device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 3)); }
 
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   const bf16* __restrict__ W = reinterpret_cast<const bf16*>(g.W) + (int64_t)kt0 * BK;
 
   // per-lane copy geometry (k-independent): slot s = (j * 8 + wave) * 64 +
-  // lane of a tile holds chunk (row s / 4, c), its source at byte offset
+  // lane of a tile holds chunk (row s / 8, c), its source at byte offset
   // row_base + 16 (c ^ ((row >> 1) & 3)), the base (advanced by k) in scalar
   // registers. Offsets fit 32 bits (host check).
   uint32_t woff[DPW], aoff[DPW];
@@ -115,12 +117,13 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
     rowok[tid] = ok;
   }
   const uint32_t lds0 = lds_addr(&lds[0]);
-  // copy q (0, 1: weight rows; 2, 3: activation rows) of step kt into its buffer
+  // copy q (0..3: weight rows; 4..7: activation rows) of the interval of
+  // steps kt, kt + 1 (kt even) into its buffer
   auto copy = [&](int kt, int q) {
-    const uint32_t dst = lds0 + (uint32_t)((kt % NBUF) * 2 * SLOTS + (q >> 1) * SLOTS) * 16u +
-                         (uint32_t)(((q & 1) * NWAVE + wave) * 1024);
-    if (q < 2) dma16_sbase(woff[q & 1], W + kt * BK, dst);
-    else dma16_sbase(aoff[q & 1], A + kt * BK, dst);
+    const uint32_t dst = lds0 + (uint32_t)(((kt >> 1) % NBUF) * 2 * SLOTS + (q >> 2) * SLOTS) * 16u +
+                         (uint32_t)(((q & 3) * NWAVE + wave) * 1024);
+    if (q < 4) dma16_sbase(woff[q & 3], W + kt * BK, dst);
+    else dma16_sbase(aoff[q & 3], A + kt * BK, dst);
   };
 
   floatx4 acc[8][4];  // [n block][m block]: C[m 64 wm + 16 y + lr][n 128 wn + 16 x + 4 g4 + i]
@@ -139,18 +142,19 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   // (both steps' tiles are in LDS), so that only the first step's reads wait
   // on the LDS latency; the copies of steps kt + 2 and kt + 3 are issued first
   auto frags = [&](int kt, Frag<bf16>* af, Frag<bf16>* wf, int x) __attribute__((always_inline)) {
-    const bf16x8* TW = &lds[(kt % NBUF) * 2 * SLOTS];
+    const bf16x8* TW = &lds[((kt >> 1) % NBUF) * 2 * SLOTS];
     const bf16x8* TA = TW + SLOTS;
+    const int c = (kt & 1) * 4 + g4;  // chunk of step kt in the interval's 128-byte rows
     // x < 0: all twelve fragments; else the ones read during MFMA group x
     if (x < 0) {
 #pragma unroll
-      for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wm * 64 + y * 16 + lr, g4)];
+      for (int y = 0; y < 4; ++y) af[y].v = TA[swz(wm * 64 + y * 16 + lr, c)];
 #pragma unroll
-      for (int xx = 0; xx < 8; ++xx) wf[xx].v = TW[swz(wn * 128 + xx * 16 + lr, g4)];
+      for (int xx = 0; xx < 8; ++xx) wf[xx].v = TW[swz(wn * 128 + xx * 16 + lr, c)];
     } else if (x < 4) {
-      af[x].v = TA[swz(wm * 64 + x * 16 + lr, g4)];
-      wf[2 * x].v = TW[swz(wn * 128 + 2 * x * 16 + lr, g4)];
-      wf[2 * x + 1].v = TW[swz(wn * 128 + (2 * x + 1) * 16 + lr, g4)];
+      af[x].v = TA[swz(wm * 64 + x * 16 + lr, c)];
+      wf[2 * x].v = TW[swz(wn * 128 + 2 * x * 16 + lr, c)];
+      wf[2 * x + 1].v = TW[swz(wn * 128 + (2 * x + 1) * 16 + lr, c)];
     }
   };
   auto rstat = [&](const Frag<bf16>* af) __attribute__((always_inline)) {
@@ -171,10 +175,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
     // are issued, the less the next barrier interval waits for them
     if (kt + 2 < NK)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) copy(kt + 2, q);
-    if (kt + 3 < NK)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) copy(kt + 3, q);
+      for (int q = 0; q < 8; ++q) copy(kt + 2, q);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       __builtin_amdgcn_sched_barrier(0);
@@ -192,9 +193,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
   };
 
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) copy(kt, q);
+  for (int q = 0; q < 8; ++q) copy(0, q);
   for (int kt = 0; kt < NK; kt += 2) {
     // this wavefront's copies of steps kt, kt + 1 (issued during step kt - 2)
     // are done; no newer ones exist yet
