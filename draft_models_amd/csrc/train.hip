@@ -681,6 +681,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* src, in
 // ---------------------------------------------------------------------------
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 // rows r0 .. r0 + 3 (first read) and r0 + 16 .. r0 + 19 (second) of a
 // row-major LDS tile, columns c .. c + 3 of each lane's 16-lane group
@@ -733,8 +734,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
   constexpr int QROW = DQK + 8, OROW = DV + 8;
   __shared__ __attribute__((aligned(16))) bf16 Qs[BT * QROW];
   __shared__ __attribute__((aligned(16))) bf16 dOs[BT * OROW];
-  __shared__ float lse_s[BT], D_s[BT];
-  __shared__ int lo_s[BT], hi_s[BT];
+  __shared__ __attribute__((aligned(16))) float lse_s[BT], D_s[BT];
+  __shared__ __attribute__((aligned(16))) int lo_s[BT], hi_s[BT];
 
   int kt, h, b;
   if (!bwd_tile(a, (a.max_q_len + BT - 1) / BT, false, kt, h, b)) return;
@@ -817,55 +818,74 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
     }
     __syncthreads();
 
-    // S and dP: s[qb][i] is query 16 qb + 4 g + i, key lr of the wave
-    floatx4 pr[4], ds[4];
+    // S and dP of the four 16-query blocks: sv[qb][i] is query 16 qb + 4 g + i,
+    // key lr of the wave. The four blocks' chains are interleaved (k step
+    // outer), and every A fragment is read two MFMAs ahead of its use; the
+    // fences keep the compiler from moving a read back next to its MFMA.
+    constexpr int NSF = 4 * (KS + VS);  // fragment j: Q (ks = j / 4) or dO (vs = j / 4 - KS) of block j % 4
+    auto sfrag = [&](int j) -> bf16x8 {
+      const int qb = j & 3, st = j >> 2;
+      return st < KS ? *reinterpret_cast<const bf16x8*>(&Qs[(qb * 16 + lr) * QROW + st * 32 + g * 8])
+                     : *reinterpret_cast<const bf16x8*>(&dOs[(qb * 16 + lr) * OROW + (st - KS) * 32 + g * 8]);
+    };
+    floatx4 sv[4], dp[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int qb = 0; qb < 4; ++qb) sv[qb] = dp[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      Frag<bf16> fr[3];
+      fr[0].v = sfrag(0);
+      fr[1].v = sfrag(1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        Frag<bf16> af;
-        af.v = *reinterpret_cast<const bf16x8*>(&Qs[(qb * 16 + lr) * QROW + ks * 32 + g * 8]);
-        sv = mfma16(af, kf[ks], sv);
-      }
-#pragma unroll
-      for (int vs = 0; vs < VS; ++vs) {
-        Frag<bf16> af;
-        af.v = *reinterpret_cast<const bf16x8*>(&dOs[(qb * 16 + lr) * OROW + vs * 32 + g * 8]);
-        dp = mfma16(af, vf[vs], dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qq = qb * 16 + g * 4 + i;
-        const bool vis = kok && key >= lo_s[qq] && key < hi_s[qq];
-        const float p = vis ? fast_exp2(sv[i] * sl2 - lse_s[qq]) : 0.f;
-        pr[qb][i] = p;
-        ds[qb][i] = p * (dp[i] - D_s[qq]);
+      for (int j = 0; j < NSF; ++j) {
+        if (j + 2 < NSF) fr[(j + 2) % 3].v = sfrag(j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int qb = j & 3, st = j >> 2;
+        if (st < KS) sv[qb] = mfma16(fr[j % 3], kf[st], sv[qb]);
+        else dp[qb] = mfma16(fr[j % 3], vf[st - KS], dp[qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS over 32 queries at a time
+    // probabilities and dS; a lane's four rows 16 qb + 4 g .. + 3 of every
+    // row value come in one 16-byte read (branch-free visibility test)
+    Frag<bf16> pf[2], sf[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      Frag<bf16> pf, sf;
+    for (int qb = 0; qb < 4; ++qb) {
+      const int q4 = qb * 16 + g * 4;
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(&lse_s[q4]);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(&D_s[q4]);
+      const intx4 lo4 = *reinterpret_cast<const intx4*>(&lo_s[q4]);
+      const intx4 hi4 = *reinterpret_cast<const intx4*>(&hi_s[q4]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf.v[e] = (bf16)pr[2 * j][e];
-        pf.v[4 + e] = (bf16)pr[2 * j + 1][e];
-        sf.v[e] = (bf16)ds[2 * j][e];
-        sf.v[4 + e] = (bf16)ds[2 * j + 1][e];
+      for (int i = 0; i < 4; ++i) {
+        const bool vis = kok & (key >= lo4[i]) & (key < hi4[i]);
+        const float p = vis ? fast_exp2(sv[qb][i] * sl2 - l4[i]) : 0.f;
+        // B operands of the 32-query halves: element e of lane (g, lr) is
+        // query 16 (e / 4) + 4 g + e % 4 of half qb / 2
+        pf[qb >> 1].v[(qb & 1) * 4 + i] = (bf16)p;
+        sf[qb >> 1].v[(qb & 1) * 4 + i] = (bf16)(p * (dp[qb][i] - d4[i]));
       }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the two 32-query halves: 40
+    // transposed A fragments, each read two MFMAs ahead
+    constexpr int NTF = 2 * (DVB + DKB);  // fragment x: half x / (DVB + DKB), dO^T block or Q^T block
+    auto tfrag = [&](int x) -> bf16x8 {
+      const int j = x / (DVB + DKB), d = x % (DVB + DKB);
       const int r0 = 32 * j + 4 * g + qa;
+      return d < DVB ? tr_pair16(&dOs[r0 * OROW + 16 * d + qb4], &dOs[(r0 + 16) * OROW + 16 * d + qb4])
+                     : tr_pair16(&Qs[r0 * QROW + 16 * (d - DVB) + qb4], &Qs[(r0 + 16) * QROW + 16 * (d - DVB) + qb4]);
+    };
+    {
+      Frag<bf16> fr[3];
+      fr[0].v = tfrag(0);
+      fr[1].v = tfrag(1);
 #pragma unroll
-      for (int D = 0; D < DVB; ++D) {
-        Frag<bf16> af;
-        af.v = tr_pair16(&dOs[r0 * OROW + 16 * D + qb4], &dOs[(r0 + 16) * OROW + 16 * D + qb4]);
-        dvt[D] = mfma16(af, pf, dvt[D]);
-      }
-#pragma unroll
-      for (int D = 0; D < DKB; ++D) {
-        Frag<bf16> af;
-        af.v = tr_pair16(&Qs[r0 * QROW + 16 * D + qb4], &Qs[(r0 + 16) * QROW + 16 * D + qb4]);
-        dkt[D] = mfma16(af, sf, dkt[D]);
+      for (int x = 0; x < NTF; ++x) {
+        if (x + 2 < NTF) fr[(x + 2) % 3].v = tfrag(x + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int j = x / (DVB + DKB), d = x % (DVB + DKB);
+        if (d < DVB) dvt[d] = mfma16(fr[x % 3], pf[j], dvt[d]);
+        else dkt[d - DVB] = mfma16(fr[x % 3], sf[j], dkt[d - DVB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
@@ -976,46 +996,64 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
       *reinterpret_cast<bf16x8*>(&Vs[(v / (DV / 8)) * VROW + (v % (DV / 8)) * 8]) = vv[u];
     }
     __syncthreads();
-    // S^T and dP^T: st[kb][i] is key 16 kb + 4 g + i, query lr of the wave
-    floatx4 dst[4];
+    // S^T and dP^T of the four 16-key blocks: sv[kb][i] is key 16 kb + 4 g +
+    // i, query lr of the wave. The four blocks' chains are interleaved (k step
+    // outer), and every A fragment is read two MFMAs ahead of its use; the
+    // fences keep the compiler from moving a read back next to its MFMA.
+    constexpr int NSF = 4 * (KS + VS);  // fragment j: K (ks = j / 4) or V (vs = j / 4 - KS) of block j % 4
+    auto sfrag = [&](int j) -> bf16x8 {
+      const int kb = j & 3, st = j >> 2;
+      return st < KS ? *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + lr) * KROW + st * 32 + g * 8])
+                     : *reinterpret_cast<const bf16x8*>(&Vs[(kb * 16 + lr) * VROW + (st - KS) * 32 + g * 8]);
+    };
+    floatx4 sv[4], dp[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      floatx4 sv = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 4; ++kb) sv[kb] = dp[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      Frag<bf16> fr[3];
+      fr[0].v = sfrag(0);
+      fr[1].v = sfrag(1);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        Frag<bf16> af;
-        af.v = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + lr) * KROW + ks * 32 + g * 8]);
-        sv = mfma16(af, qf[ks], sv);
+      for (int j = 0; j < NSF; ++j) {
+        if (j + 2 < NSF) fr[(j + 2) % 3].v = sfrag(j + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = j & 3, st = j >> 2;
+        if (st < KS) sv[kb] = mfma16(fr[j % 3], qf[st], sv[kb]);
+        else dp[kb] = mfma16(fr[j % 3], of[st - KS], dp[kb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // dS^T as the B operands of the two 32-key halves: element e of lane
+    // (g, lr) is key 16 (e / 4) + 4 g + e % 4 of half kb / 2 (branch-free
+    // visibility test)
+    Frag<bf16> sf[2];
 #pragma unroll
-      for (int vs = 0; vs < VS; ++vs) {
-        Frag<bf16> af;
-        af.v = *reinterpret_cast<const bf16x8*>(&Vs[(kb * 16 + lr) * VROW + vs * 32 + g * 8]);
-        dp = mfma16(af, of[vs], dp);
-      }
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + kb * 16 + g * 4 + i;
-        const bool vis = qok && key < S && key >= lo && key < hi;
-        const float p = vis ? fast_exp2(sv[i] * sl2 - l2) : 0.f;
-        dst[kb][i] = p * (dp[i] - dd);
+        const bool vis = qok & (key < S) & (key >= lo) & (key < hi);
+        const float p = vis ? fast_exp2(sv[kb][i] * sl2 - l2) : 0.f;
+        sf[kb >> 1].v[(kb & 1) * 4 + i] = (bf16)(p * (dp[kb][i] - dd));
       }
-    }
-    // dQ^T += K^T dS^T over 32 keys at a time
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      Frag<bf16> sf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sf.v[e] = (bf16)dst[2 * j][e];
-        sf.v[4 + e] = (bf16)dst[2 * j + 1][e];
-      }
+    // dQ^T += K^T dS^T over the two 32-key halves: 2 DKB transposed A
+    // fragments, each read two MFMAs ahead
+    constexpr int NTF = 2 * DKB;
+    auto tfrag = [&](int x) -> bf16x8 {
+      const int j = x / DKB, d = x % DKB;
       const int r0 = 32 * j + 4 * g + qa;
+      return tr_pair16(&Ks[r0 * KROW + 16 * d + qb4], &Ks[(r0 + 16) * KROW + 16 * d + qb4]);
+    };
+    {
+      Frag<bf16> fr[3];
+      fr[0].v = tfrag(0);
+      fr[1].v = tfrag(1);
 #pragma unroll
-      for (int D = 0; D < DKB; ++D) {
-        Frag<bf16> af;
-        af.v = tr_pair16(&Ks[r0 * KROW + 16 * D + qb4], &Ks[(r0 + 16) * KROW + 16 * D + qb4]);
-        dqt[D] = mfma16(af, sf, dqt[D]);
+      for (int x = 0; x < NTF; ++x) {
+        if (x + 2 < NTF) fr[(x + 2) % 3].v = tfrag(x + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        dqt[x % DKB] = mfma16(fr[x % 3], sf[x / DKB], dqt[x % DKB]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
