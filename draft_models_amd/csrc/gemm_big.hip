@@ -11,8 +11,10 @@
 // other wavefront of its SIMD, and the copies get the whole interval to land).
 // One copy instruction moves 8 whole 128-byte rows: each source cache line is
 // requested once, not once per 32-wide step. The 16-byte chunks of a row are
-// XOR-ed with (row >> 1) & 3: the LDS serves a 16-byte read 8 lanes (8 rows)
-// at a time, and those rows then hit distinct banks. Rows that do not exist
+// XOR-ed with (row >> 1) & 7: the LDS serves a 16-byte read 16 lanes (16 rows
+// of one fragment) at a time, and those rows then hit distinct banks (rows
+// r and r + 8 shared banks with (row >> 1) & 3: half the LDS cycles were
+// conflicts). Rows that do not exist
 // (past M or N, or absent gathered rows) re-read an existing row and are not
 // stored. Tiles are placed on XCDs in 2-D blocks (see TileMap) so that each
 // XCD's L2 keeps its band of weight rows. Products with too few output tiles
@@ -36,7 +38,7 @@ constexpr int NWAVE = 8;
 constexpr int DPW = SLOTS / (NWAVE * 64);        // copies per wavefront per operand per interval
 static_assert(DPW == 4, "copy schedule assumes 4 copies per operand and wavefront");
 
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 3)); }
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWCH + (c ^ ((row >> 1) & 7)); }
 
 // Tile placement: the 8 XCDs (workgroup id mod 8) form an xm x xn grid; XCD
 // (xi, xj) owns the block of M-tile band xi and N-tile band xj and walks it
@@ -75,14 +77,14 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
 
   // per-lane copy geometry (k-independent): slot s = (j * 8 + wave) * 64 +
   // lane of a tile holds chunk (row s / 8, c), its source at byte offset
-  // row_base + 16 (c ^ ((row >> 1) & 3)), the base (advanced by k) in scalar
+  // row_base + 16 (c ^ ((row >> 1) & 7)), the base (advanced by k) in scalar
   // registers. Offsets fit 32 bits (host check).
   uint32_t woff[DPW], aoff[DPW];
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int s = (j * NWAVE + wave) * 64 + lane;
     const int row = s / ROWCH, cs = s % ROWCH;
-    const uint32_t colb = (uint32_t)(cs ^ ((row >> 1) & 3)) * 16u;
+    const uint32_t colb = (uint32_t)(cs ^ ((row >> 1) & 7)) * 16u;
     const int n = min(n0 + row, g.N - 1);
     woff[j] = (uint32_t)((int64_t)n * g.ldw * 2) + colb;
     const int m = min(m0 + row, g.M - 1);
