@@ -695,6 +695,18 @@ __device__ __forceinline__ bf16x8 tr_pair16(const bf16* p0, const bf16* p1) {
   return __builtin_bit_cast(bf16x8, z);
 }
 
+// Element index of element e of row r in a bf16 tile with NCH 16-byte
+// chunks of data per row, padded by 16 elements, chunk bit 0 XOR-ed with row
+// bit 3. The LDS serves a 16-byte read 16 lanes at a time and an 8-byte
+// (transposing) read 32 lanes at a time; with this layout the 16 rows of a
+// fragment read and the 8 rows x 4 column groups of a transposing read both
+// land on distinct banks (rows padded by 8 left the transposing reads 2-way
+// conflicted), and each read pattern needs one per-lane base address.
+template <int NCH>
+__device__ __forceinline__ int swz_el(int r, int e) {
+  return r * (NCH * 8 + 16) + (((e >> 3) ^ ((r >> 3) & 1)) << 3) + (e & 7);
+}
+
 // 8 elements d .. d + 7 (d a multiple of 8) of head h's key of token (b, j)
 __device__ __forceinline__ bf16x8 key_vec(const TrainArgs& a, int b, int j, int h, int d) {
   const int64_t row = (int64_t)b * a.Lp + j;
@@ -731,9 +743,10 @@ __device__ __forceinline__ bool bwd_tile(const TrainArgs& a, int tiles, bool des
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a) {
   constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16, DVB = DV / 16;
-  constexpr int QROW = DQK + 8, OROW = DV + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BT * QROW];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BT * OROW];
+  constexpr int QCH = DQK / 8, OCH = DV / 8;  // 16-byte chunks per row
+  static_assert(QCH % 2 == 0 && OCH % 2 == 0, "even chunk counts (chunk bit 0 is swizzled)");
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BT * (DQK + 16)];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BT * (DV + 16)];
   __shared__ __attribute__((aligned(16))) float lse_s[BT], D_s[BT];
   __shared__ __attribute__((aligned(16))) int lo_s[BT], hi_s[BT];
 
@@ -797,12 +810,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
 #pragma unroll
     for (int u = 0; u < NQV; ++u) {
       const int v = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&Qs[(v / (DQK / 8)) * QROW + (v % (DQK / 8)) * 8]) = qv[u];
+      *reinterpret_cast<bf16x8*>(&Qs[swz_el<QCH>(v / QCH, (v % QCH) * 8)]) = qv[u];
     }
 #pragma unroll
     for (int u = 0; u < NOV; ++u) {
       const int v = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&dOs[(v / (DV / 8)) * OROW + (v % (DV / 8)) * 8]) = ov[u];
+      *reinterpret_cast<bf16x8*>(&dOs[swz_el<OCH>(v / OCH, (v % OCH) * 8)]) = ov[u];
     }
     if (tid < BT) {
       const int qi = q0 + tid;
@@ -825,8 +838,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
     constexpr int NSF = 4 * (KS + VS);  // fragment j: Q (ks = j / 4) or dO (vs = j / 4 - KS) of block j % 4
     auto sfrag = [&](int j) -> bf16x8 {
       const int qb = j & 3, st = j >> 2;
-      return st < KS ? *reinterpret_cast<const bf16x8*>(&Qs[(qb * 16 + lr) * QROW + st * 32 + g * 8])
-                     : *reinterpret_cast<const bf16x8*>(&dOs[(qb * 16 + lr) * OROW + (st - KS) * 32 + g * 8]);
+      return st < KS ? *reinterpret_cast<const bf16x8*>(&Qs[swz_el<QCH>(qb * 16 + lr, st * 32 + g * 8)])
+                     : *reinterpret_cast<const bf16x8*>(&dOs[swz_el<OCH>(qb * 16 + lr, (st - KS) * 32 + g * 8)]);
     };
     floatx4 sv[4], dp[4];
 #pragma unroll
@@ -871,8 +884,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
     auto tfrag = [&](int x) -> bf16x8 {
       const int j = x / (DVB + DKB), d = x % (DVB + DKB);
       const int r0 = 32 * j + 4 * g + qa;
-      return d < DVB ? tr_pair16(&dOs[r0 * OROW + 16 * d + qb4], &dOs[(r0 + 16) * OROW + 16 * d + qb4])
-                     : tr_pair16(&Qs[r0 * QROW + 16 * (d - DVB) + qb4], &Qs[(r0 + 16) * QROW + 16 * (d - DVB) + qb4]);
+      return d < DVB ? tr_pair16(&dOs[swz_el<OCH>(r0, 16 * d + qb4)], &dOs[swz_el<OCH>(r0 + 16, 16 * d + qb4)])
+                     : tr_pair16(&Qs[swz_el<QCH>(r0, 16 * (d - DVB) + qb4)],
+                                 &Qs[swz_el<QCH>(r0 + 16, 16 * (d - DVB) + qb4)]);
     };
     {
       Frag<bf16> fr[3];
@@ -916,9 +930,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_bf16_kernel(TrainArgs a)
 template <int DQK, int DV>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
   constexpr int BT = 64, KS = DQK / 32, VS = DV / 32, DKB = DQK / 16;
-  constexpr int KROW = DQK + 8, VROW = DV + 8;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BT * KROW];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[BT * VROW];
+  constexpr int KCH = DQK / 8, VCH = DV / 8;  // 16-byte chunks per row
+  static_assert(KCH % 2 == 0 && VCH % 2 == 0, "even chunk counts (chunk bit 0 is swizzled)");
+  __shared__ __attribute__((aligned(16))) bf16 Ks[BT * (DQK + 16)];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[BT * (DV + 16)];
 
   int qt, h, b;
   if (!bwd_tile(a, (a.max_q_len + BT - 1) / BT, true, qt, h, b)) return;
@@ -988,12 +1003,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
 #pragma unroll
     for (int u = 0; u < NKV; ++u) {
       const int v = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&Ks[(v / (DQK / 8)) * KROW + (v % (DQK / 8)) * 8]) = kv[u];
+      *reinterpret_cast<bf16x8*>(&Ks[swz_el<KCH>(v / KCH, (v % KCH) * 8)]) = kv[u];
     }
 #pragma unroll
     for (int u = 0; u < NVV; ++u) {
       const int v = tid + 256 * u;
-      *reinterpret_cast<bf16x8*>(&Vs[(v / (DV / 8)) * VROW + (v % (DV / 8)) * 8]) = vv[u];
+      *reinterpret_cast<bf16x8*>(&Vs[swz_el<VCH>(v / VCH, (v % VCH) * 8)]) = vv[u];
     }
     __syncthreads();
     // S^T and dP^T of the four 16-key blocks: sv[kb][i] is key 16 kb + 4 g +
@@ -1003,8 +1018,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
     constexpr int NSF = 4 * (KS + VS);  // fragment j: K (ks = j / 4) or V (vs = j / 4 - KS) of block j % 4
     auto sfrag = [&](int j) -> bf16x8 {
       const int kb = j & 3, st = j >> 2;
-      return st < KS ? *reinterpret_cast<const bf16x8*>(&Ks[(kb * 16 + lr) * KROW + st * 32 + g * 8])
-                     : *reinterpret_cast<const bf16x8*>(&Vs[(kb * 16 + lr) * VROW + (st - KS) * 32 + g * 8]);
+      return st < KS ? *reinterpret_cast<const bf16x8*>(&Ks[swz_el<KCH>(kb * 16 + lr, st * 32 + g * 8)])
+                     : *reinterpret_cast<const bf16x8*>(&Vs[swz_el<VCH>(kb * 16 + lr, (st - KS) * 32 + g * 8)]);
     };
     floatx4 sv[4], dp[4];
 #pragma unroll
@@ -1042,7 +1057,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
     auto tfrag = [&](int x) -> bf16x8 {
       const int j = x / DKB, d = x % DKB;
       const int r0 = 32 * j + 4 * g + qa;
-      return tr_pair16(&Ks[r0 * KROW + 16 * d + qb4], &Ks[(r0 + 16) * KROW + 16 * d + qb4]);
+      return tr_pair16(&Ks[swz_el<KCH>(r0, 16 * d + qb4)], &Ks[swz_el<KCH>(r0 + 16, 16 * d + qb4)]);
     };
     {
       Frag<bf16> fr[3];
