@@ -48,7 +48,10 @@ hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_el
 bool gemm_big_eligible(const GemmArgs& g, bool is_bf16);
 // Split-K count (>= 2) for a product the kernel fits except for having too
 // few output tiles, with splits * M * N fp32 partials within ws_elems; else 0.
-int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems);
+// narrow: also products narrower than one 256-wide tile (the narrow last
+// columns of a wider product, whose tiles are mostly idle columns but whose
+// k range is split over the CUs).
+int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems, bool narrow = false);
 // splits == 1: C directly; else fp32 partials part[split][M][N] (summed by
 // the caller)
 hipError_t gemm_big_launch(const GemmArgs& g, float* part, int splits, hipStream_t s);

@@ -564,9 +564,42 @@ const char* gemm_check(const GemmArgs& g, bool is_bf16) {
   return nullptr;
 }
 
+constexpr int kMaxReduceSplitsBig = 8;  // gemm_big_splits never returns more
+
 hipError_t gemm_launch(const GemmArgs& g, bool is_bf16, float* ws, int64_t ws_elems, hipStream_t s) {
   if (g.M == 0) return hipSuccess;
-  if (g.zeros != nullptr && gemm_big_eligible(g, is_bf16)) return gemm_big_launch(g, nullptr, 1, s);
+  if (g.zeros != nullptr && gemm_big_eligible(g, is_bf16)) {
+    // a narrow last column of 256-wide tiles (N mod 256 <= 128, e.g. the
+    // 2112-wide first projection) still costs full tiles; when it adds a
+    // round of workgroups, the 256-multiple part runs alone and the narrow
+    // columns run as a product of their own
+    const int tail = g.N % 256;
+    if (tail > 0 && tail <= 128 && g.epi == EPI_STORE && !g.gather && g.batch == 1) {
+      GemmArgs head = g;
+      head.N = g.N - tail;
+      const int64_t mt = (g.M + 255) / 256;
+      const int64_t rounds_all = (mt * ((g.N + 255) / 256) + 255) / 256, rounds_head = (mt * (head.N / 256) + 255) / 256;
+      if (rounds_head < rounds_all && gemm_big_eligible(head, is_bf16)) {
+        if (hipError_t e = gemm_big_launch(head, nullptr, 1, s); e != hipSuccess) return e;
+        GemmArgs t = g;
+        t.N = tail;
+        t.W = reinterpret_cast<const char*>(g.W) + (size_t)head.N * g.ldw * 2;
+        t.C = reinterpret_cast<char*>(g.C) + (size_t)head.N * 2;
+        // the narrow columns on the same kernel, k split over the CUs
+        if (const int sp = ws != nullptr ? gemm_big_splits(t, is_bf16, ws_elems, true) : 0;
+            sp > 1 && sp <= kMaxReduceSplitsBig) {
+          if (hipError_t e = gemm_big_launch(t, ws, sp, s); e != hipSuccess) return e;
+          const int64_t total = (int64_t)t.M * t.N;
+          const int blocks = (int)((total / 4 + 255) / 256 + 1);
+          hipLaunchKernelGGL(splitk_reduce<bf16>, dim3(blocks), dim3(256), 0, s, ws, sp, t.M, t.N,
+                             reinterpret_cast<bf16*>(t.C), t.ldc, false, t.K, 0.f);
+          return hipGetLastError();
+        }
+        return gemm_launch(t, is_bf16, ws, ws_elems, s);
+      }
+    }
+    return gemm_big_launch(g, nullptr, 1, s);
+  }
   if (g.zeros != nullptr && ws != nullptr) {
     if (const int sp = gemm_big_splits(g, is_bf16, ws_elems); sp > 1) {
       if (hipError_t e = gemm_big_launch(g, ws, sp, s); e != hipSuccess) return e;

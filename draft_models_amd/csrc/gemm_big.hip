@@ -284,9 +284,10 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void gemm_big_kernel(GemmArgs g, Til
 }  // namespace
 
 namespace {
-// every condition of the kernel except the number of output tiles
-bool big_shape_ok(const GemmArgs& g, bool is_bf16) {
-  if (!is_bf16 || g.batch != 1 || g.K % (2 * BK) != 0 || g.M < 512 || g.N < 256) return false;  // two steps per barrier
+// every condition of the kernel except the number of output tiles (min_n:
+// the narrowest product worth 256-wide tiles)
+bool big_shape_ok(const GemmArgs& g, bool is_bf16, int min_n = 256) {
+  if (!is_bf16 || g.batch != 1 || g.K % (2 * BK) != 0 || g.M < 512 || g.N < min_n) return false;  // two steps per barrier
   // 16-byte output stores (and gate loads)
   if (g.ldc % 8 || (reinterpret_cast<uintptr_t>(g.C) & 15)) return false;
   if (g.epi == EPI_GATE && (g.ldg % 8 || (reinterpret_cast<uintptr_t>(g.G) & 15))) return false;
@@ -302,8 +303,8 @@ int64_t big_tiles(const GemmArgs& g) { return (int64_t)((g.M + BM - 1) / BM) * (
 
 bool gemm_big_eligible(const GemmArgs& g, bool is_bf16) { return big_shape_ok(g, is_bf16) && big_tiles(g) >= 256; }
 
-int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems) {
-  if (!big_shape_ok(g, is_bf16) || g.gather || g.epi != EPI_STORE) return 0;
+int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems, bool narrow) {
+  if (!big_shape_ok(g, is_bf16, narrow ? 8 : 256) || g.gather || g.epi != EPI_STORE) return 0;
   const int64_t tiles = big_tiles(g);
   if (tiles >= 256) return 0;
   // one round of the 256 CUs, at most 8 splits, at least 512 of K per split
