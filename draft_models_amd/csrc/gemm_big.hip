@@ -307,14 +307,22 @@ int gemm_big_splits(const GemmArgs& g, bool is_bf16, int64_t ws_elems, bool narr
   if (!big_shape_ok(g, is_bf16, narrow ? 8 : 256) || g.gather || g.epi != EPI_STORE) return 0;
   const int64_t tiles = big_tiles(g);
   if (tiles >= 256) return 0;
-  // one round of the 256 CUs, at most 8 splits, at least 512 of K per split
-  int sp = (int)std::min<int64_t>(8, (256 + tiles - 1) / tiles);
-  sp = std::min(sp, g.K / 512);
-  while (sp > 1 && (int64_t)sp * g.M * g.N > ws_elems) --sp;
-  if (sp < 2) return 0;
-  // even step counts per split; drop splits left empty by the rounding
-  const int nk = g.K / BK, kper = ((nk + sp - 1) / sp + 1) / 2 * 2;
-  return (nk + kper - 1) / kper;
+  // 2..8 splits of at least 512 of K, even step counts per split: the count
+  // with the least estimated time = rounds of the 256 CUs x steps per split x
+  // ~0.95 us per 32-wide step of a 256 x 256 tile, plus the fp32 partials the
+  // reduce reads and the output it writes at ~4 TB/s
+  const int nk = g.K / BK;
+  int best = 0;
+  double best_us = 1e300;
+  for (int sp = 2; sp <= std::min(8, g.K / 512); ++sp) {
+    if ((int64_t)sp * g.M * g.N > ws_elems) break;
+    const int kper = ((nk + sp - 1) / sp + 1) / 2 * 2;
+    const int used = (nk + kper - 1) / kper;  // splits left non-empty by the rounding
+    const double rounds = (double)((tiles * used + 255) / 256);
+    const double us = rounds * kper * 0.95 + (double)g.M * g.N * (4.0 * used + 2.0) / 4.0e6;
+    if (us < best_us - 1e-9) { best_us = us; best = used; }
+  }
+  return best >= 2 ? best : 0;
 }
 
 hipError_t gemm_big_launch(const GemmArgs& g, float* part, int splits, hipStream_t s) {

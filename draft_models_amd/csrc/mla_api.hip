@@ -620,9 +620,9 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
   ctx->ws.part_o = static_cast<float*>(p);
   if ((e = dev_alloc(ctx, &p, (size_t)part_rows * part_heads * sizeof(float)))) return bail(e);
   ctx->ws.part_lse = static_cast<float*>(p);
-  // (training: the weight gradients' split-K partials, up to 8 x 576 x 4096
-  // or 3 x 1536 x 4096 floats at the DeepSeek dims)
-  ctx->ws.gemm_ws_elems = cfg->max_train_tokens > 0 ? (int64_t)24 << 20 : (int64_t)16 << 20;
+  // (training: the split-K partials of the weight and data gradients, e.g.
+  // 3 x 6144 x 1536 or 4 x 8192 x 1536 floats at the draft-block dims)
+  ctx->ws.gemm_ws_elems = cfg->max_train_tokens > 0 ? (int64_t)56 << 20 : (int64_t)16 << 20;
   if ((e = dev_alloc(ctx, &p, (size_t)ctx->ws.gemm_ws_elems * sizeof(float)))) return bail(e);
   ctx->ws.gemm_ws = static_cast<float*>(p);
   if ((e = dev_alloc(ctx, &ctx->zeros, 256))) return bail(e);
