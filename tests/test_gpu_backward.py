@@ -73,6 +73,16 @@ def test_backward_split_k_bf16():
     _check(w, 175)
 
 
+def test_backward_split_k3_bf16():
+    """bf16 at the draft-block model dims with 2 x 1024 causal tokens: the
+    q_b and first-projection weight gradients (144 output tiles, K = 2048
+    tokens) split K three ways (22, 22 and 20 of the 64 32-wide steps), the
+    split count chosen by estimated time."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[1024, 1024], prefix_lens=[0, 0], mask_kind=ms.MASK_CAUSAL,
+                         seed=76)
+    _check(w, 176)
+
+
 def test_backward_gate_neox_bf16():
     """bf16, 16 heads, output gate, NeoX RoPE, sliding window 50, lengths 130,
     64 and 1."""
