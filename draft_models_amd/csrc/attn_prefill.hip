@@ -549,9 +549,9 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   };
 
   // ---- software pipeline over the key tiles: step t computes the scores of
-  // tile t + 1 (MFMA) in the same basic block as the softmax of tile t (VALU),
-  // so that the two units overlap, then P V of tile t; tile t + 2 streams in
-  // meanwhile. Two score arrays alternate (the loop is unrolled by two).
+  // tile t + 1 (MFMA), the softmax of tile t (VALU), then P V of tile t (MFMA);
+  // tile t + 2 streams in meanwhile. Two score arrays alternate (the loop is
+  // unrolled by two).
   const int ntl = kbeg < kend ? (kend - kbeg + KT - 1) / KT : 0;
   MLA_WAIT_VMCNT(0);  // query fragments landed: in the loop only tile copies are outstanding
   if (ntl > 0) issue(kbeg, 0);
@@ -568,22 +568,26 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     if (t + 2 < ntl) issue(k0 + 2 * KT, (t + 2) % NBUF);
     if (!active) return;  // no query of this wavefront exists: it only helps stream tiles
     if (!(k0 >= in_lo && k0 + KT <= in_hi)) mask(cur, k0);
+    // the wave raises its priority over its MFMA blocks and drops it for
+    // the softmax: of the two waves of a SIMD, the one in an MFMA block
+    // issues first, so the two drift half a phase apart and one's softmax
+    // VALU runs beside the other's MFMAs (the fences keep each block whole)
+    __builtin_amdgcn_s_setprio(3);
     scores((t + 1) % NBUF, nxt);  // after the last tile: a stale buffer, unused
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
     const bool rescale = softmax(cur);
-    // interleave the two: per group one LDS read, two MFMAs, six VALU
-#pragma unroll
-    for (int gi = 0; gi < 24; ++gi) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-    }
+    __builtin_amdgcn_sched_barrier(0);
     if (__any(rescale)) {
 #pragma unroll
       for (int d = 0; d < 8; ++d)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) o[d][qb] *= alpha[qb];
     }
+    __builtin_amdgcn_s_setprio(3);
     pv(t % NBUF, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   int t = 0;
   for (; t + 1 < ntl; t += 2) {
