@@ -456,16 +456,22 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // fragment j = 4 ks + kb, read two fragments ahead of its MFMAs (the
+    // fences keep the compiler from moving a read back next to its use)
+    auto kfr = [&](int j) -> bf16x8 {
+      const int ks = j >> 2, kb = j & 3, row = kb * 16 + lr;
+      return ks < 4 ? KN[kslot(row, ks * 4 + g, NOPE_CH)] : KP[kslot(row, (ks - 4) * 4 + g, PE_CH)];
+    };
+    Frag<bf16> fr[3];
+    fr[0].v = kfr(0);
+    fr[1].v = kfr(1);
 #pragma unroll
-    for (int ks = 0; ks < 6; ++ks) {
+    for (int j = 0; j < 24; ++j) {
+      if (j + 2 < 24) fr[(j + 2) % 3].v = kfr(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        Frag<bf16> kf;
-        const int row = kb * 16 + lr;
-        kf.v = ks < 4 ? KN[kslot(row, ks * 4 + g, NOPE_CH)] : KP[kslot(row, (ks - 4) * 4 + g, PE_CH)];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = mfma16(kf, qf[qb][ks], sc[kb][qb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) sc[j & 3][qb] = mfma16(fr[j % 3], qf[qb][j >> 2], sc[j & 3][qb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // ---- online softmax (log2 domain) with lazy rescaling of the tile at key
