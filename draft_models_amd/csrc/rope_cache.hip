@@ -145,12 +145,143 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(RopeCacheArgs a) {
   }
 }
 
+// bf16 form for a 512 + 64 latent with 16-byte aligned rows: the three parts
+// of a token run side by side, every access 16 bytes wide. Wavefronts 0-1
+// rotate the rope dims of the query heads (a lane holds two 16-byte vectors
+// of one head: NeoX pairs (j, j + 32) are the same element of both,
+// interleaved pairs neighbours in one), wavefront 2 normalises the latent (8
+// dims per lane, one wavefront reduction) and writes it, wavefront 3 rotates
+// k_pe and writes it. Same arithmetic per value as the general kernel.
+__global__ __launch_bounds__(256) void rope_cache_bf16_kernel(RopeCacheArgs a) {
+  const int b = blockIdx.y, i = blockIdx.x;
+  int t, pos;
+  if (a.decode) {
+    if (i != 0) return;
+    const int L = a.seq_lens[b];
+    if (L < 1) return;
+    t = b;
+    pos = min(L, a.max_seq_len) - 1;
+  } else {
+    const int cb = a.cu_seqlens ? a.cu_seqlens[b] : b * a.max_q_len;
+    int ql = a.cu_seqlens ? a.cu_seqlens[b + 1] - cb : a.max_q_len;
+    ql = min(max(ql, 0), a.max_q_len);
+    if (i >= ql) return;
+    t = cb + i;
+    if (t < 0 || t >= a.total_tokens) return;
+    const int pl = min(max(a.prefix_lens[b], 0), a.max_kv_len - ql);
+    pos = pl + i;
+  }
+  constexpr int C = 512, HALF = 32;
+  const float* cs = a.rope_cos + (int64_t)pos * HALF;
+  const float* sn = a.rope_sin + (int64_t)pos * HALF;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // rotation of the two 16-byte vectors x0 (dims 8 v ..) and x1 (dims 32 + 8 v ..)
+  auto rotate = [&](bf16x8& x0, bf16x8& x1, int v) {
+    if (a.interleaved) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j0 = 4 * v + e, j1 = 16 + 4 * v + e;
+        const float a0 = (float)x0[2 * e], b0 = (float)x0[2 * e + 1];
+        const float a1 = (float)x1[2 * e], b1 = (float)x1[2 * e + 1];
+        x0[2 * e] = (bf16)(a0 * cs[j0] - b0 * sn[j0]);
+        x0[2 * e + 1] = (bf16)(a0 * sn[j0] + b0 * cs[j0]);
+        x1[2 * e] = (bf16)(a1 * cs[j1] - b1 * sn[j1]);
+        x1[2 * e + 1] = (bf16)(a1 * sn[j1] + b1 * cs[j1]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 8 * v + e;
+        const float xa = (float)x0[e], xb = (float)x1[e];
+        x0[e] = (bf16)(xa * cs[j] - xb * sn[j]);
+        x1[e] = (bf16)(xa * sn[j] + xb * cs[j]);
+      }
+    }
+  };
+  if (wave < 2) {
+    bf16* q = reinterpret_cast<bf16*>(a.q) + (int64_t)t * a.ldq;
+    for (int p = threadIdx.x; p < a.H * 4; p += 128) {
+      const int h = p >> 2, v = p & 3;
+      bf16x8* qh = reinterpret_cast<bf16x8*>(q + (int64_t)h * a.qk_head + a.n);
+      bf16x8 x0 = qh[v], x1 = qh[v + 4];
+      rotate(x0, x1, v);
+      qh[v] = x0;
+      qh[v + 4] = x1;
+    }
+    return;
+  }
+  if (pos / a.page >= a.max_blocks) return;
+  const int blk = a.block_table[(int64_t)b * a.max_blocks + pos / a.page];
+  if (blk < 0 || blk >= a.num_blocks) return;
+  const int64_t ent = ((int64_t)blk * a.page + pos % a.page) * (C + 2 * HALF);
+  const bf16* kv = reinterpret_cast<const bf16*>(a.kv) + (int64_t)t * a.ldkv;
+  // 8-bit entry: as in the general kernel, each value rounded to bf16 first,
+  // then the E4M3 code of value / scale
+  auto codes = [&](const float (&v)[8]) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = fminf(fmaxf((float)(bf16)v[e] / a.kv_scale, -448.f), 448.f);
+      const uint32_t cd = (uint32_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
+      if (e < 4) w0 |= cd << (8 * e);
+      else w1 |= cd << (8 * (e - 4));
+    }
+    return uint2{w0, w1};
+  };
+  if (wave == 2) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(kv + 8 * lane);
+    float f[8], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[e] = (float)x[e];
+      ss += f[e] * f[e];
+    }
+    ss = warp_sum(ss);
+    const float scale = rsqrtf(ss / (float)C + a.eps);
+    const bf16x8 gm = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.gamma_kv) + 8 * lane);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = f[e] * scale * (float)gm[e];
+    if (a.kv_fp8) {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(a.cache) + ent + 8 * lane) = codes(f);
+    } else {
+      bf16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (bf16)f[e];
+      *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.cache) + ent + 8 * lane) = y;
+    }
+    return;
+  }
+  if (lane >= 4) return;
+  const bf16x8* kp = reinterpret_cast<const bf16x8*>(kv + C);
+  bf16x8 x0 = kp[lane], x1 = kp[lane + 4];
+  rotate(x0, x1, lane);
+  if (a.kv_fp8) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(a.cache) + ent + C;
+    float f0[8], f1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f0[e] = (float)x0[e];
+      f1[e] = (float)x1[e];
+    }
+    *reinterpret_cast<uint2*>(dst + 8 * lane) = codes(f0);
+    *reinterpret_cast<uint2*>(dst + 8 * (lane + 4)) = codes(f1);
+  } else {
+    bf16x8* dst = reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.cache) + ent + C);
+    dst[lane] = x0;
+    dst[lane + 4] = x1;
+  }
+}
+
 }  // namespace
 
 hipError_t rope_cache_launch(const RopeCacheArgs& a, bool is_bf16, int grid_x, int batch, hipStream_t s) {
   if (grid_x <= 0 || batch <= 0) return hipSuccess;
   dim3 grid(grid_x, batch);
-  if (is_bf16) hipLaunchKernelGGL(rope_cache_kernel<bf16>, grid, dim3(256), 0, s, a);
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool fast = is_bf16 && a.c == 512 && a.r == 64 && a.ldq % 8 == 0 && a.qk_head % 8 == 0 && a.n % 8 == 0 &&
+                    a.ldkv % 8 == 0 && al16(a.q) && al16(a.kv) && al16(a.gamma_kv) && al16(a.cache);
+  if (fast) hipLaunchKernelGGL(rope_cache_bf16_kernel, grid, dim3(256), 0, s, a);
+  else if (is_bf16) hipLaunchKernelGGL(rope_cache_kernel<bf16>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(rope_cache_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
