@@ -348,6 +348,25 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   __syncthreads();
   const int kbeg = (iv[0] / KT) * KT, kend = iv[1];
   const int in_lo = iv[2], in_hi = iv[3];  // tiles inside [in_lo, in_hi) need no mask
+  // the union of this wavefront's visible intervals: a tile outside it is
+  // masked for every row of the wavefront (its probabilities are all 0), so
+  // the wavefront skips its products (under a causal mask: the tiles past
+  // its own diagonal, which the workgroup streams for its later queries)
+  int wlo = 0x7fffffff, whi = 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    if (lo[qb] < hi[qb]) {
+      wlo = min(wlo, lo[qb]);
+      whi = max(whi, hi[qb]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    wlo = min(wlo, __shfl_xor(wlo, o));
+    whi = max(whi, __shfl_xor(whi, o));
+  }
+  wlo = __builtin_amdgcn_readfirstlane(wlo);
+  whi = __builtin_amdgcn_readfirstlane(whi);
+  auto live = [&](int k0) { return k0 < whi && k0 + KT > wlo; };
 
   // queries in registers (B operand: column = query, 8 contraction elements)
   Frag<bf16> qf[QB][6];
@@ -566,22 +585,24 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   else MLA_WAIT_VMCNT(0);
   lds_barrier();
   floatx4 s0[4][QB], s1[4][QB];
-  if (active && ntl > 0) scores(0, s0);
+  if (active && ntl > 0 && live(kbeg)) scores(0, s0);
   auto step = [&](int t, floatx4 (&cur)[4][QB], floatx4 (&nxt)[4][QB]) {
     const int k0 = kbeg + t * KT;
     MLA_WAIT_VMCNT(0);  // tile t + 1 landed (the only copies in flight)
     lds_barrier();      // ... for every wavefront; P V of tile t - 1 is done everywhere
     if (t + 2 < ntl) issue(k0 + 2 * KT, (t + 2) % NBUF);
     if (!active) return;  // no query of this wavefront exists: it only helps stream tiles
-    if (!(k0 >= in_lo && k0 + KT <= in_hi)) mask(cur, k0);
+    const bool cur_live = live(k0), nxt_live = live(k0 + KT);
+    if (cur_live && !(k0 >= in_lo && k0 + KT <= in_hi)) mask(cur, k0);
     // the wave raises its priority over its MFMA blocks and drops it for
     // the softmax: of the two waves of a SIMD, the one in an MFMA block
     // issues first, so the two drift half a phase apart and one's softmax
     // VALU runs beside the other's MFMAs (the fences keep each block whole)
     __builtin_amdgcn_s_setprio(3);
-    scores((t + 1) % NBUF, nxt);  // after the last tile: a stale buffer, unused
+    if (nxt_live) scores((t + 1) % NBUF, nxt);  // after the last tile: a stale buffer, unused
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
+    if (!cur_live) return;
     const bool rescale = softmax(cur);
     __builtin_amdgcn_sched_barrier(0);
     if (__any(rescale)) {
