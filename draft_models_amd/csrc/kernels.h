@@ -25,6 +25,7 @@ struct RopeCacheArgs {
   const int32_t* cu_seqlens = nullptr;   // prefill; null: blocks of max_q_len tokens, block b at b max_q_len
   const int32_t* prefix_lens = nullptr;  // prefill
   int max_q_len = 0, max_kv_len = 0, max_seq_len = 0, total_tokens = 0;
+  int batch = 0;  // sequences (rope_cache_launch sets it from its argument)
   // 8-bit cache (OCP E4M3 codes of value / scale), else the compute dtype
   int kv_fp8 = 0;
   float kv_scale = 1.f;

@@ -223,6 +223,14 @@ def test_prefill_big_tiles():
     _run_and_check(w)
 
 
+def test_prefill_big_tiles_interleaved():
+    """Interleaved RoPE through the 256 x 256 tiles: the query rotation in the
+    q_b projection's epilogue (token positions found from the sequence
+    offsets, a one-token sequence between two long ones, cached prefixes)."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[520, 1, 390], prefix_lens=[0, 11, 3], seed=81)
+    _run_and_check(w)
+
+
 def test_prefill_chunked_sliding():
     """Causal prefill of a chunk after a cached prefix under a sliding window."""
     w = ms.make_workload("prefill_bf16", q_lens=[77, 200], prefix_lens=[300, 5], mask_kind=ms.MASK_SLIDING,
