@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NWAVE * 64, 1) void mha_fused_kernel(MhaFusedArgs a
     }
   }
 
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.q_log2 ? 1.f : a.scale * kLog2e;  // q_log2: the products are the scaled scores
   const int key_b = k0 + eb * 64;  // first entry of this block
   const int qblocks = (sg.ql + 15) >> 4;
   // expanded keys (k_nope wavefronts) or values (v wavefronts) in bf16, the

@@ -297,6 +297,12 @@ __device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch +
 __device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 7) << 1)); }
 }  // namespace big
 
+// LOG2Q: the queries were multiplied by scale * log2(e), so the products are
+// the scaled scores in log2 units; each tile's score accumulators then start
+// at minus the row's reference max and the probabilities are exp2 of the
+// products as they come out of the MFMAs (a rare reference move shifts the
+// current and the next tile's scores)
+template <bool LOG2Q>
 __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnArgs a) {
   using namespace big;
   __shared__ __attribute__((aligned(16))) bf16x8 knope[NBUF][KT * NOPE_CH];
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, g = lane >> 4;
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = LOG2Q ? 1.f : a.scale * kLog2e;
 
   if (tid == 0) { iv[0] = 0x7fffffff; iv[1] = 0; iv[2] = 0; iv[3] = 0x7fffffff; }
   __syncthreads();
@@ -472,9 +478,12 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     const bf16x8* KN = knope[bf];
     const bf16x8* KP = kpe[bf];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      // LOG2Q: start at minus the reference max (0 while the row has none)
+      const float z = LOG2Q && m[qb] != -INFINITY ? -m[qb] : 0.f;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) sc[kb][qb] = floatx4{z, z, z, z};
+    }
     // fragment j = 4 ks + kb, read two fragments ahead of its MFMAs (the
     // fences keep the compiler from moving a read back next to its use)
     auto kfr = [&](int j) -> bf16x8 {
@@ -510,8 +519,57 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
           if (key < lo[qb] || key >= hi[qb]) sc[kb][qb][i] = -INFINITY;
         }
   };
-  auto softmax = [&](floatx4 (&sc)[4][QB]) -> bool {
+  auto softmax = [&](floatx4 (&sc)[4][QB], floatx4 (&nx)[4][QB]) -> bool {
     bool rescale = false;
+    if constexpr (LOG2Q) {
+      // sc = score - ref, ref = m (0 while m = -inf); the tile's max
+      // relative to ref moves the reference when the row has none yet or
+      // when it exceeds it by more than 8; both tiles in registers (this one
+      // and the next, already computed against the old reference) then
+      // shift by the move d
+      float d[QB];
+      bool shift = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
+        mx = red4_max(mx);
+        const bool none = m[qb] == -INFINITY;
+        const float mnew = none ? mx : (mx > 8.f ? m[qb] + mx : m[qb]);
+        d[qb] = mnew == -INFINITY ? 0.f : mnew - (none ? 0.f : m[qb]);
+        alpha[qb] = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
+        rescale |= mnew != m[qb];
+        shift |= d[qb] != 0.f;
+        m[qb] = mnew;
+      }
+      if (__any(shift)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            sc[kb][qb] -= d[qb];
+            nx[kb][qb] -= d[qb];
+          }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float sum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = fast_exp2(sc[kb][qb][i]);  // masked -> 0
+            sc[kb][qb][i] = p;
+            sum += p;
+          }
+        sum = red4_sum(sum);
+        l[qb] = l[qb] * alpha[qb] + sum;
+      }
+      return rescale;
+    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -603,7 +661,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     if (!cur_live) return;
-    const bool rescale = softmax(cur);
+    const bool rescale = softmax(cur, nxt);
     __builtin_amdgcn_sched_barrier(0);
     if (__any(rescale)) {
 #pragma unroll
@@ -682,9 +740,11 @@ hipError_t prefill_attn_launch(const PrefillAttnArgs& a, bool is_bf16, hipStream
   if (is_bf16 && a.n == 128 && a.r == 64 && a.dv == 128 && a.c % 8 == 0 && a.page % big::KT == 0) {
     const int64_t nqt = (a.max_q_len + big::BQ - 1) / big::BQ, npx = ((int64_t)a.H * a.batch + 7) / 8;
     if (8 * npx * nqt > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_attn_bf16_kernel, dim3((unsigned)(8 * npx * nqt)), dim3(64 * big::NW), 0, s, a);
+    if (a.q_log2) hipLaunchKernelGGL(prefill_attn_bf16_kernel<true>, dim3((unsigned)(8 * npx * nqt)), dim3(64 * big::NW), 0, s, a);
+    else hipLaunchKernelGGL(prefill_attn_bf16_kernel<false>, dim3((unsigned)(8 * npx * nqt)), dim3(64 * big::NW), 0, s, a);
     return hipGetLastError();
   }
+  if (a.q_log2) return hipErrorInvalidValue;  // only the kernel above takes log2-scaled queries
   return is_bf16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
 }
 

@@ -48,6 +48,7 @@ struct PrefillAttnArgs {
   int batch = 0, max_q_len = 0, max_kv_len = 0, total_tokens = 0;
   int H = 0, n = 0, r = 0, c = 0, dv = 0;
   float scale = 0.f;
+  int q_log2 = 0;  // q was multiplied by scale * log2(e) (bf16 DeepSeek-head kernel only)
   MaskArgs mask;
   void* out = nullptr; int64_t ldo = 0;             // [T, H * dv]
   const void* gate = nullptr; int64_t ldg = 0;      // raw gate pre-activation [T, H * dv] or null
@@ -70,6 +71,7 @@ struct MhaFusedArgs {
   int batch = 0, max_q_len = 0, max_kv_len = 0, total_tokens = 0;
   int H = 0;
   float scale = 0.f;
+  int q_log2 = 0;  // q was multiplied by scale * log2(e)
   MaskArgs mask;
   int nchunks = 0;                                  // ceil(max_kv_len / 256)
   int qblocks = 0;                                  // ceil(max_q_len / 16)

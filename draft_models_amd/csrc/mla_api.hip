@@ -44,6 +44,7 @@ struct mla_ctx {
   void* W1 = nullptr;  // fused first projection [N1, hid] = [q_a | q ; kv_a ; g]
   int N1 = 0, off_q = 0, off_kv = 0, off_g = -1;
   void* Wqb = nullptr;     // q_b_proj with the q_a_layernorm gain folded into its columns
+  void* Wqb_l2 = nullptr;  // the same times scale * log2(e): queries for the bf16 prefill attention
   void* Wkvb = nullptr;    // kv_b_proj [H (n + dv), c]
   void* Wuk_t = nullptr;   // per head W_UK^T [H][c][n]
   void* Wo = nullptr;      // o_proj [hid, H dv]
@@ -153,18 +154,19 @@ void* scratch_ptr(int device) {
   return g_scratch_ptr[device];
 }
 
-__global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst, int64_t rows, int cols, int bf) {
+__global__ void scale_cols_kernel(const void* src, const void* gamma, void* dst, int64_t rows, int cols, int bf,
+                                  float mul) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= rows * cols) return;
   const int col = (int)(i % cols);
   if (bf) {
     const bf16* s = reinterpret_cast<const bf16*>(src);
     const bf16* g = reinterpret_cast<const bf16*>(gamma);
-    reinterpret_cast<bf16*>(dst)[i] = (bf16)((float)s[i] * (float)g[col]);
+    reinterpret_cast<bf16*>(dst)[i] = (bf16)((float)s[i] * (float)g[col] * mul);
   } else {
     const float* s = reinterpret_cast<const float*>(src);
     const float* g = reinterpret_cast<const float*>(gamma);
-    reinterpret_cast<float*>(dst)[i] = s[i] * g[col];
+    reinterpret_cast<float*>(dst)[i] = s[i] * g[col] * mul;
   }
 }
 
@@ -379,7 +381,8 @@ void query_buffer(mla_ctx* ctx, const Workspace& ws, void** q, int64_t* ldq) {
 
 // fused first projection and (low-rank path) the q_b projection with the
 // q_a RMSNorm folded into its epilogue; fills q / ldq
-int project(mla_ctx* ctx, const Workspace& ws, const void* x, int T, hipStream_t s, void** q, int64_t* ldq) {
+int project(mla_ctx* ctx, const Workspace& ws, const void* x, int T, hipStream_t s, void** q, int64_t* ldq,
+            bool log2_q = false) {
   GemmArgs g1;
   g1.A = x; g1.lda = ctx->hid;
   g1.W = ctx->W1; g1.ldw = ctx->hid;
@@ -392,7 +395,7 @@ int project(mla_ctx* ctx, const Workspace& ws, const void* x, int T, hipStream_t
   if (ctx->ql > 0) {
     GemmArgs g2;
     g2.A = ws.buf1; g2.lda = ctx->N1;
-    g2.W = ctx->Wqb; g2.ldw = ctx->ql;
+    g2.W = log2_q ? ctx->Wqb_l2 : ctx->Wqb; g2.ldw = ctx->ql;
     g2.C = ws.qbuf; g2.ldc = (int64_t)ctx->H * ctx->qkh;
     g2.M = T; g2.N = ctx->H * ctx->qkh; g2.K = ctx->ql;
     g2.epi = EPI_ROWNORM; g2.eps = (float)ctx->cfg.rms_norm_eps;
@@ -539,8 +542,17 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     if ((e = dev_alloc(ctx, &ctx->Wqb, (size_t)rows * ctx->ql * esz))) return bail(e);
     const int64_t tot = rows * ctx->ql;
     hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->q_b_proj,
-                       w->q_a_layernorm, ctx->Wqb, rows, ctx->ql, (int)ctx->bf16);
+                       w->q_a_layernorm, ctx->Wqb, rows, ctx->ql, (int)ctx->bf16, 1.f);
     if (hipGetLastError() != hipSuccess) return bail(fail(MLA_ERR_HIP, "q_b_proj repack failed"));
+    // the bf16 prefill attention kernels take queries already multiplied by
+    // scale * log2(e) (one rounding, as for the folded gain): the q_b
+    // projection of the prefill uses this copy
+    if (ctx->bf16 && ctx->n == 128 && ctx->r == 64 && ctx->dv == 128 && cfg->page_size % 64 == 0) {
+      if ((e = dev_alloc(ctx, &ctx->Wqb_l2, (size_t)rows * ctx->ql * esz))) return bail(e);
+      hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->q_b_proj,
+                         w->q_a_layernorm, ctx->Wqb_l2, rows, ctx->ql, (int)ctx->bf16, ctx->scale * 1.4426950408889634f);
+      if (hipGetLastError() != hipSuccess) return bail(fail(MLA_ERR_HIP, "q_b_proj repack failed"));
+    }
   }
   const int64_t kvb_rows = (int64_t)H * (ctx->n + ctx->dv);
   if ((e = dev_alloc(ctx, &ctx->Wkvb, (size_t)kvb_rows * ctx->c * esz))) return bail(e);
@@ -674,7 +686,9 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
 
   void* q;
   int64_t ldq;
-  if (int e = project(ctx, ws, x, total_tokens, s, &q, &ldq)) return e;
+  // queries multiplied by scale * log2(e) when the bf16 attention kernels run
+  const bool log2_q = ctx->Wqb_l2 != nullptr;
+  if (int e = project(ctx, ws, x, total_tokens, s, &q, &ldq, log2_q)) return e;
 
   RopeCacheArgs rc;
   rc.q = q; rc.ldq = ldq; rc.qk_head = ctx->qkh;
@@ -720,7 +734,7 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   fa.wkvb = ctx->Wkvb;
   fa.cu_seqlens = cu_seqlens_q; fa.prefix_lens = prefix_lens;
   fa.batch = batch; fa.max_q_len = max_q_len; fa.max_kv_len = max_kv_len; fa.total_tokens = total_tokens;
-  fa.H = ctx->H; fa.scale = ctx->scale;
+  fa.H = ctx->H; fa.scale = ctx->scale; fa.q_log2 = log2_q;
   fa.mask.kind = mask_kind; fa.mask.window = window; fa.mask.row_lo = row_lo; fa.mask.row_hi = row_hi;
   fa.nchunks = (max_kv_len + 255) / 256;
   fa.qblocks = (max_q_len + 15) / 16;
@@ -781,7 +795,7 @@ int mla_prefill_expanded(mla_ctx* ctx, const void* x, int32_t batch, int32_t tot
   pa.cu_seqlens = cu_seqlens_q; pa.prefix_lens = prefix_lens;
   pa.batch = batch; pa.max_q_len = max_q_len; pa.max_kv_len = max_kv_len; pa.total_tokens = total_tokens;
   pa.H = ctx->H; pa.n = ctx->n; pa.r = ctx->r; pa.c = ctx->c; pa.dv = ctx->dv;
-  pa.scale = ctx->scale;
+  pa.scale = ctx->scale; pa.q_log2 = log2_q;
   pa.mask.kind = mask_kind; pa.mask.window = window; pa.mask.row_lo = row_lo; pa.mask.row_hi = row_hi;
   pa.out = ws.attn; pa.ldo = (int64_t)ctx->H * ctx->dv;
   if (ctx->off_g >= 0) {
