@@ -265,6 +265,22 @@ def test_softmax_scale_override():
     U.check(w, out, cache, U.oracle(w, softmax_scale=0.05))
 
 
+def test_prefill_large_scale_bf16():
+    """bf16 prefill with a softmax scale 3x the default: peaked rows whose
+    running maximum moves by more than the lazy-rescale margin after the
+    first tile, so the reference moves of the attention kernels (both tiles
+    in registers shifted) are exercised, with cached prefixes and a ragged
+    last tile."""
+    w = ms.make_workload("prefill_bf16", q_lens=[300, 700], prefix_lens=[0, 100], seed=82)
+    scale = 0.22
+    out, cache = U.run_gpu(w, softmax_scale=scale)
+    # the bf16 storage errors of q and of the keys enter the logits times the
+    # scale: the output bar grows with it (default 1 / sqrt(192))
+    grow = scale * np.sqrt(192.0)
+    tol = dict(max_abs=U.TOL_BF16["max_abs"] * grow, rel_l2=U.TOL_BF16["rel_l2"] * grow)
+    U.check(w, out, cache, U.oracle(w, softmax_scale=scale), out_tol=tol)
+
+
 def test_capacity_above_call():
     """Context limits larger than the call (workspace rows beyond the batch)."""
     w = ms.make_workload("decode_bf16", seq_lens=[100, 3000], seed=17)
