@@ -220,7 +220,7 @@ STAGE_SOURCES = {
 STAGE_KERNEL = {
     "decode_attn": "decode_sk_kernel", "decode_merge": "decode_sk_merge_kernel",
     "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
-    "rope_cache": "rope_cache_kernel", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
+    "rope_cache": "rope_cache", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
     "kv_dequant": "kv_shadow_kernel",
     # a stage of two kernels: its traffic is the sum of both per-dispatch averages
     "attn_bwd": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd_dq_bf16_kernel"),
