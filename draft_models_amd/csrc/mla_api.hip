@@ -544,10 +544,11 @@ int mla_init_weights(const mla_config* cfg, const mla_weights* w, void* stream, 
     hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->q_b_proj,
                        w->q_a_layernorm, ctx->Wqb, rows, ctx->ql, (int)ctx->bf16, 1.f);
     if (hipGetLastError() != hipSuccess) return bail(fail(MLA_ERR_HIP, "q_b_proj repack failed"));
-    // the bf16 prefill attention kernels take queries already multiplied by
-    // scale * log2(e) (one rounding, as for the folded gain): the q_b
-    // projection of the prefill uses this copy
-    if (ctx->bf16 && ctx->n == 128 && ctx->r == 64 && ctx->dv == 128 && cfg->page_size % 64 == 0) {
+    // the bf16 prefill attention kernels (the conditions under which
+    // prefill_attn_launch and the fused kernel take them) get queries already
+    // multiplied by scale * log2(e) (one rounding, as for the folded gain):
+    // the q_b projection of the prefill uses this copy
+    if (ctx->bf16 && ctx->n == 128 && ctx->r == 64 && ctx->dv == 128 && ctx->c % 8 == 0 && cfg->page_size % 64 == 0) {
       if ((e = dev_alloc(ctx, &ctx->Wqb_l2, (size_t)rows * ctx->ql * esz))) return bail(e);
       hipLaunchKernelGGL(scale_cols_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, w->q_b_proj,
                          w->q_a_layernorm, ctx->Wqb_l2, rows, ctx->ql, (int)ctx->bf16, ctx->scale * 1.4426950408889634f);
