@@ -615,19 +615,26 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
           pf[qb][k2].v[e] = (bf16)sc[2 * k2][qb][e];
           pf[qb][k2].v[4 + e] = (bf16)sc[2 * k2 + 1][qb][e];
         }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    // V fragment j = 2 d + k2, read two fragments ahead of its MFMAs (the
+    // fences keep the compiler from moving a read back next to its use)
+    auto vfr = [&](int j) -> bf16x8 {
+      const int d = j >> 1, k2 = j & 1;
       const int el = d * 16 + rb * 4;
       const int c = el >> 3, half = (el >> 2) & 1;
+      const int r0 = k2 * 32 + g * 4 + ra;
+      return tr_pair(reinterpret_cast<const bf16*>(&VT[vslot(r0, c)]) + half * 4,
+                     reinterpret_cast<const bf16*>(&VT[vslot(r0 + 16, c)]) + half * 4);
+    };
+    Frag<bf16> vr[3];
+    vr[0].v = vfr(0);
+    vr[1].v = vfr(1);
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const int r0 = k2 * 32 + g * 4 + ra;
-        Frag<bf16> vf;
-        vf.v = tr_pair(reinterpret_cast<const bf16*>(&VT[vslot(r0, c)]) + half * 4,
-                       reinterpret_cast<const bf16*>(&VT[vslot(r0 + 16, c)]) + half * 4);
+    for (int j = 0; j < 16; ++j) {
+      if (j + 2 < 16) vr[(j + 2) % 3].v = vfr(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[d][qb] = mfma16(vf, pf[qb][k2], o[d][qb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) o[j >> 1][qb] = mfma16(vr[j % 3], pf[qb][j & 1], o[j >> 1][qb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
