@@ -7,7 +7,7 @@
 // prefix and to the new tokens separately and merging the two results by
 // their log-sum-exp (the listing's merge_attn_states step).
 //
-// Work split: one workgroup = 4 wavefronts x (16 * QB) queries of one head of
+// Work split (generic kernel): one workgroup = 4 wavefronts x (16 * QB) queries of one head of
 // one sequence. Scores are computed transposed (S^T = K Q^T) so that each
 // lane ends up holding the probabilities of one query for 8 keys -- exactly
 // the B-operand layout of the P V product -- and no LDS round trip of P is
@@ -265,15 +265,16 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel for the DeepSeek head shape (n = 128, r = 64, dv = 128). One
-// workgroup = 8 wavefronts x 32 queries (two 16-query MFMA blocks each, so
-// every LDS fragment feeds two MFMAs) of one head. 64-key tiles stream from
-// HBM straight into LDS (global_load_lds_dwordx4), double-buffered: k_nope
-// and v rows of the expanded buffer through the scalar-base form, the shared
-// rope key from the paged cache. Rows are unpadded with XOR-swizzled 16-byte
-// chunks: by the row's low bits for the key tiles (row & 15 for the 16-chunk
-// k_nope rows, row & 7 for the 8-chunk rope rows: the 16 rows of a 16-byte
-// score operand read hit distinct banks) and by 2 (row & 7) for the value tile (chunk pairs stay adjacent;
-// the 8 rows read together by 32 lanes of transposing reads hit distinct banks). Tiles inside every query's visible interval skip the masking.
+// workgroup = 8 wavefronts (two per SIMD) x 32 queries of one head, on the
+// 32x32x16 MFMA. 64-key tiles stream from HBM straight into LDS
+// (global_load_lds_dwordx4) through a 3-tile ring: k_nope and v rows of the
+// expanded buffer through the scalar-base form, the shared rope key from the
+// paged cache. Rows are unpadded with XOR-swizzled 16-byte chunks: by the
+// row's low bits for the key tiles (row & 15 for the 16-chunk k_nope rows,
+// row & 7 for the 8-chunk rope rows: the rows of a 16-byte score operand read
+// hit distinct banks) and by 4 (row & 3) for the value tile (the 4 rows x 64
+// bytes that 32 lanes of transposing reads take in one pass hit distinct
+// banks). Tiles inside every query's visible interval skip the masking.
 // ---------------------------------------------------------------------------
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -288,20 +289,33 @@ __device__ __forceinline__ bf16x8 tr_pair(const bf16* p0, const bf16* p1) {
 
 namespace big {
 constexpr int KT = 64;                  // keys per tile
-constexpr int QB = 2;                   // 16-query blocks per wavefront
 constexpr int NW = 8;                   // wavefronts per workgroup (two per SIMD)
-constexpr int BQ = NW * 16 * QB;        // queries per workgroup
+constexpr int BQ = NW * 32;             // queries per workgroup
 constexpr int NOPE_CH = 16, PE_CH = 8, V_CH = 16;   // 16-byte chunks per key row
 constexpr int NBUF = 3;                 // tile ring: t (values), t + 1 (scores), t + 2 (in flight)
 __device__ __forceinline__ int kslot(int row, int c, int ch) { return row * ch + (c ^ (row & (ch - 1))); }
-__device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 7) << 1)); }
+__device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ ((row & 3) << 2)); }
 }  // namespace big
 
+// S^T = K Q^T per 32-key block: element e of lane l is key
+// 32 kb + 8 (e / 4) + 4 (l / 32) + e % 4 of query l % 32 (lanes l and l ^ 32
+// hold the same query), so a row reduction is one in-lane pass plus one
+// permlane32_swap, and the accumulator's 8 consecutive elements of a 16-key
+// step are exactly the B operand of O^T = V^T P^T in the same key order. The
+// V^T operand comes from two transposing reads per fragment (keys
+// 16 s + 4 (l / 32) + 0..3 and + 8). Software pipeline: step t computes the
+// scores of tile t + 1, the softmax of tile t, then P V of tile t, as fenced
+// blocks; the wavefront runs at priority 3 over its MFMA blocks and 0 over
+// the softmax, so that the two wavefronts of a SIMD drift half a phase apart
+// and one's softmax VALU runs beside the other's MFMAs. K and V fragments are
+// read two ahead of their MFMAs.
+//
 // LOG2Q: the queries were multiplied by scale * log2(e), so the products are
 // the scaled scores in log2 units; each tile's score accumulators then start
 // at minus the row's reference max and the probabilities are exp2 of the
 // products as they come out of the MFMAs (a rare reference move shifts the
 // current and the next tile's scores)
+
 template <bool LOG2Q>
 __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnArgs a) {
   using namespace big;
@@ -330,41 +344,27 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;  // query of the lane, half of the key group
   const int lr = lane & 15, g = lane >> 4;
   const float sl2 = LOG2Q ? 1.f : a.scale * kLog2e;
 
   if (tid == 0) { iv[0] = 0x7fffffff; iv[1] = 0; iv[2] = 0; iv[3] = 0x7fffffff; }
   __syncthreads();
-  int lo[QB], hi[QB], qi[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qi[qb] = qt * BQ + wave * 16 * QB + qb * 16 + lr;
-    lo[qb] = 0; hi[qb] = 0;
-    if (qi[qb] < ql && t0 + qi[qb] < a.total_tokens) visible(a.mask, t0 + qi[qb], pl + qi[qb], L, lo[qb], hi[qb]);
-    if (g == 0 && lo[qb] < hi[qb]) {
-      atomicMin(&iv[0], lo[qb]);
-      atomicMax(&iv[1], hi[qb]);
-      atomicMax(&iv[2], lo[qb]);
-      atomicMin(&iv[3], hi[qb]);
-    }
-    if (g == 0 && qi[qb] < ql && lo[qb] >= hi[qb]) {  // an empty row: no tile is unmasked for it
-      atomicMax(&iv[2], 0x7fffffff);
-    }
+  const int qi = qt * BQ + wave * 32 + lq;
+  int lo = 0, hi = 0;
+  if (qi < ql && t0 + qi < a.total_tokens) visible(a.mask, t0 + qi, pl + qi, L, lo, hi);
+  if (hf == 0 && lo < hi) {
+    atomicMin(&iv[0], lo);
+    atomicMax(&iv[1], hi);
+    atomicMax(&iv[2], lo);
+    atomicMin(&iv[3], hi);
   }
+  if (hf == 0 && qi < ql && lo >= hi) atomicMax(&iv[2], 0x7fffffff);  // an empty row: no tile is unmasked for it
   __syncthreads();
   const int kbeg = (iv[0] / KT) * KT, kend = iv[1];
   const int in_lo = iv[2], in_hi = iv[3];  // tiles inside [in_lo, in_hi) need no mask
-  // the union of this wavefront's visible intervals: a tile outside it is
-  // masked for every row of the wavefront (its probabilities are all 0), so
-  // the wavefront skips its products (under a causal mask: the tiles past
-  // its own diagonal, which the workgroup streams for its later queries)
-  int wlo = 0x7fffffff, whi = 0;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-    if (lo[qb] < hi[qb]) {
-      wlo = min(wlo, lo[qb]);
-      whi = max(whi, hi[qb]);
-    }
+  // the union of this wavefront's visible intervals (tiles outside it are skipped)
+  int wlo = lo < hi ? lo : 0x7fffffff, whi = lo < hi ? hi : 0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     wlo = min(wlo, __shfl_xor(wlo, o));
@@ -374,25 +374,24 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   whi = __builtin_amdgcn_readfirstlane(whi);
   auto live = [&](int k0) { return k0 < whi && k0 + KT > wlo; };
 
-  // queries in registers (B operand: column = query, 8 contraction elements)
-  Frag<bf16> qf[QB][6];
+  // queries in registers (B operand of step ks: dims 16 ks + 8 hf .. + 7 of query lq)
+  bf16x8 qf[12];
+  {
+    const bool qok = qi < ql && t0 + qi < a.total_tokens;
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + (int64_t)(t0 + (qok ? qi : 0)) * a.ldq + (int64_t)h * a.qk_head;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bool qok = qi[qb] < ql && t0 + qi[qb] < a.total_tokens;
-    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + (int64_t)(t0 + (qok ? qi[qb] : 0)) * a.ldq +
-                       (int64_t)h * a.qk_head;
-#pragma unroll
-    for (int ks = 0; ks < 6; ++ks) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g * 8);
-      qf[qb][ks].v = qok ? v : bf16x8{};
+    for (int ks = 0; ks < 12; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hf * 8);
+      qf[ks] = qok ? v : bf16x8{};
     }
   }
 
-  // DMA geometry. k_nope / v: 16 chunks per key row, 4 instructions per wave
-  // each (rows 4 (4 j + wave) .. + 3); byte offsets relative to the tile's
-  // first key row of this head in the expanded buffer. k_pe: 8 chunks per row,
-  // 2 instructions per wave, per-lane 64-bit addresses (the rows of one tile
-  // may lie in two pages).
+  // DMA geometry. k_nope / v: 16 chunks per key row, 2 instructions per wave
+  // each; byte offsets relative to the tile's first key row of this head in
+  // the expanded buffer. k_pe: 8 chunks per row, 1 instruction per wave, byte
+  // offsets relative to the tile's first entry in its cache page (tiles never
+  // cross a page: they start at multiples of 64 keys and the page size is a
+  // multiple of 64)
   const bf16* kvb = reinterpret_cast<const bf16*>(a.kv) + (int64_t)b * a.max_kv_len * a.ldkv + (int64_t)h * (a.n + a.dv);
   const int64_t row_bytes = a.ldkv * 2;
   uint32_t noff[2], voff[2];
@@ -401,24 +400,19 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     const int sl = (j * NW + wave) * 64 + lane;
     const int row = sl / NOPE_CH, cs = sl % NOPE_CH;
     noff[j] = (uint32_t)(row * row_bytes) + (uint32_t)((cs ^ (row & (NOPE_CH - 1))) * 16);
-    const int cv = cs ^ ((row & 7) << 1);
+    const int cv = cs ^ ((row & 3) << 2);
     voff[j] = (uint32_t)(row * row_bytes) + 256u + (uint32_t)(cv * 16);
   }
   const bf16* cache = reinterpret_cast<const bf16*>(a.cache);
   const int E = a.c + a.r;
   const int32_t* __restrict__ btab = a.block_table + (int64_t)b * a.max_blocks;
   const uint32_t knope_lds = lds_addr(&knope[0][0]), vt_lds = lds_addr(&vt[0][0]), kpe_lds = lds_addr(&kpe[0][0]);
-  // k_pe: 8 chunks per row, 2 instructions per wave; byte offsets relative to
-  // the tile's first entry in its cache page (tiles never cross a page: they
-  // start at multiples of 64 keys and the page size is a multiple of 64)
-  uint32_t poff[1];
-#pragma unroll
-  for (int j = 0; j < 1; ++j) {
-    const int sl = (j * NW + wave) * 64 + lane;
+  uint32_t poff;
+  {
+    const int sl = wave * 64 + lane;
     const int row = sl / PE_CH, cs = sl % PE_CH;
-    poff[j] = (uint32_t)(row * E * 2) + (uint32_t)(a.c * 2) + (uint32_t)((cs ^ (row & 7)) * 16);
+    poff = (uint32_t)(row * E * 2) + (uint32_t)(a.c * 2) + (uint32_t)((cs ^ (row & 7)) * 16);
   }
-  // block-table entries of the key range live in a register, one page per lane
   int pbase = kbeg / a.page;
   int btreg = (pbase + lane < a.max_blocks) ? btab[pbase + lane] : -1;
 
@@ -444,7 +438,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
         dma16_sbase(noff[j], base, nb + (uint32_t)(j * NW + wave) * 1024u);
         dma16_sbase(voff[j], base, vb + (uint32_t)(j * NW + wave) * 1024u);
       }
-      dma16_sbase(poff[0], pbase_ptr, pb + (uint32_t)wave * 1024u);
+      dma16_sbase(poff, pbase_ptr, pb + (uint32_t)wave * 1024u);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -457,191 +451,148 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
       {
         const int row = (wave * 64 + lane) / PE_CH;
         const uint32_t back = row >= rows_valid ? (uint32_t)((row - rows_valid + 1) * E * 2) : 0u;
-        dma16_sbase(poff[0] - back, pbase_ptr, pb + (uint32_t)wave * 1024u);
+        dma16_sbase(poff - back, pbase_ptr, pb + (uint32_t)wave * 1024u);
       }
     }
   };
 
-  floatx4 o[8][QB];
-  float m[QB], l[QB];
+  // O^T block db: element e of lane l is dim 32 db + 8 (e / 4) + 4 hf + e % 4 of query lq
+  floatx16 o[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY; l[qb] = 0.f;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  const int ra = lr >> 2, rb = lr & 3;
-  const bool active = qt * BQ + wave * 16 * QB < ql;
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m = -INFINITY, l = 0.f, alpha = 1.f;
+  const bool active = qt * BQ + wave * 32 < ql;
 
-  // ---- S^T = K Q^T of the tile in buffer `bf`: sc[kb][qb][i] = key 16 kb + 4 g + i, query lr of block qb
-  auto scores = [&](int bf, floatx4 (&sc)[4][QB]) {
+  // ---- S^T = K Q^T of the tile in buffer bf: sc[kb] = keys 32 kb .. + 31
+  auto scores = [&](int bf, floatx16 (&sc)[2]) {
     const bf16x8* KN = knope[bf];
     const bf16x8* KP = kpe[bf];
+    // LOG2Q: start at minus the reference max (0 while the row has none)
+    const float z = LOG2Q && m != -INFINITY ? -m : 0.f;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // LOG2Q: start at minus the reference max (0 while the row has none)
-      const float z = LOG2Q && m[qb] != -INFINITY ? -m[qb] : 0.f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sc[kb][qb] = floatx4{z, z, z, z};
-    }
-    // fragment j = 4 ks + kb, read two fragments ahead of its MFMAs (the
-    // fences keep the compiler from moving a read back next to its use)
+      for (int e = 0; e < 16; ++e) sc[kb][e] = z;
+    // fragment j = 2 ks + kb: key 32 kb + lq, dims 16 ks + 8 hf .. + 7; read
+    // two fragments ahead of its MFMA behind fences
     auto kfr = [&](int j) -> bf16x8 {
-      const int ks = j >> 2, kb = j & 3, row = kb * 16 + lr;
-      return ks < 4 ? KN[kslot(row, ks * 4 + g, NOPE_CH)] : KP[kslot(row, (ks - 4) * 4 + g, PE_CH)];
+      const int ks = j >> 1, kb = j & 1, row = kb * 32 + lq;
+      return ks < 8 ? KN[kslot(row, ks * 2 + hf, NOPE_CH)] : KP[kslot(row, (ks - 8) * 2 + hf, PE_CH)];
     };
-    Frag<bf16> fr[3];
-    fr[0].v = kfr(0);
-    fr[1].v = kfr(1);
+    bf16x8 fr[3];
+    fr[0] = kfr(0);
+    fr[1] = kfr(1);
 #pragma unroll
     for (int j = 0; j < 24; ++j) {
-      if (j + 2 < 24) fr[(j + 2) % 3].v = kfr(j + 2);
+      if (j + 2 < 24) fr[(j + 2) % 3] = kfr(j + 2);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sc[j & 3][qb] = mfma16(fr[j % 3], qf[qb][j >> 2], sc[j & 3][qb]);
+      sc[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % 3], qf[j >> 1], sc[j & 1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // ---- online softmax (log2 domain) with lazy rescaling of the tile at key
-  // k0; the probabilities replace the scores in place (fp32)
-  float alpha[QB];
-  // keys outside a row's visible interval (only on tiles that cross an
-  // interval end) score -inf: exp2(-inf) = 0, also for rows that have seen no
-  // visible key yet (their reference max stays -inf and is replaced by 0)
-  auto mask = [&](floatx4 (&sc)[4][QB], int k0) {
+  auto mask = [&](floatx16 (&sc)[2], int k0) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + kb * 16 + g * 4 + i;
-          if (key < lo[qb] || key >= hi[qb]) sc[kb][qb][i] = -INFINITY;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (key < lo || key >= hi) sc[kb][e] = -INFINITY;
+      }
   };
-  auto softmax = [&](floatx4 (&sc)[4][QB], floatx4 (&nx)[4][QB]) -> bool {
-    bool rescale = false;
+  // online softmax (log2 domain) with lazy rescaling; probabilities replace the scores
+  auto softmax = [&](floatx16 (&sc)[2], floatx16 (&nx)[2]) -> bool {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
+    mx = red2_max(mx);
     if constexpr (LOG2Q) {
-      // sc = score - ref, ref = m (0 while m = -inf); the tile's max
-      // relative to ref moves the reference when the row has none yet or
-      // when it exceeds it by more than 8; both tiles in registers (this one
-      // and the next, already computed against the old reference) then
-      // shift by the move d
-      float d[QB];
-      bool shift = false;
+      // sc = score - ref (ref = m, 0 while m = -inf); a reference move d
+      // shifts this tile and the next one (computed against the old ref)
+      const bool none = m == -INFINITY;
+      const float mnew = none ? mx : (mx > 8.f ? m + mx : m);
+      const float d = mnew == -INFINITY ? 0.f : mnew - (none ? 0.f : m);
+      alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+      const bool rescale = mnew != m;
+      m = mnew;
+      if (__any(d != 0.f)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
-        mx = red4_max(mx);
-        const bool none = m[qb] == -INFINITY;
-        const float mnew = none ? mx : (mx > 8.f ? m[qb] + mx : m[qb]);
-        d[qb] = mnew == -INFINITY ? 0.f : mnew - (none ? 0.f : m[qb]);
-        alpha[qb] = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
-        rescale |= mnew != m[qb];
-        shift |= d[qb] != 0.f;
-        m[qb] = mnew;
+        for (int kb = 0; kb < 2; ++kb) {
+          sc[kb] -= d;
+          nx[kb] -= d;
+        }
       }
-      if (__any(shift)) {
+      float sum = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            sc[kb][qb] -= d[qb];
-            nx[kb][qb] -= d[qb];
-          }
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float sum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = fast_exp2(sc[kb][qb][i]);  // masked -> 0
-            sc[kb][qb][i] = p;
-            sum += p;
-          }
-        sum = red4_sum(sum);
-        l[qb] = l[qb] * alpha[qb] + sum;
-      }
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(sc[kb][e]);  // masked -> 0
+          sc[kb][e] = p;
+          sum += p;
+        }
+      l = l * alpha + red2_sum(sum);
       return rescale;
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][qb][i]);
-      mx = red4_max(mx);
+    } else {
       mx *= sl2;  // the scale is positive: the max of the scaled scores
-      const float mnew = (mx > m[qb] + 8.f) ? mx : m[qb];
-      alpha[qb] = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
-      rescale |= mnew != m[qb];
+      const float mnew = (mx > m + 8.f) ? mx : m;
+      alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+      const bool rescale = mnew != m;
       const float nm = (mnew == -INFINITY) ? 0.f : -mnew;
       float sum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sc[kb][qb][i], sl2, nm));
-          sc[kb][qb][i] = p;
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][e], sl2, nm));
+          sc[kb][e] = p;
           sum += p;
         }
-      sum = red4_sum(sum);
-      l[qb] = l[qb] * alpha[qb] + sum;
-      m[qb] = mnew;
+      l = l * alpha + red2_sum(sum);
+      m = mnew;
+      return rescale;
     }
-    return rescale;
   };
-  // ---- O^T += V^T P^T; transposed V operand from the row-major tile: lane
-  // k = 4 a + b' of a 16-lane group points at key row 32 k2 + 4 g + a [+16],
-  // dims 16 d + 4 b' .. + 3, and receives keys 32 k2 + 4 g + {0..3} [+16] of dim 16 d + lr
-  auto pv = [&](int bf, const floatx4 (&sc)[4][QB]) {
+  // ---- O^T += V^T P^T: k step s = keys 16 s .. + 15 of the tile; the B
+  // operand is accumulator elements 8 (s & 1) .. + 7 of block s / 2 (keys
+  // 16 s + 4 hf + (0..3), 16 s + 8 + 4 hf + (0..3)); the A operand of dim
+  // block db is read in the same key order: group G = lane / 16 of 16 lanes
+  // covers dims 32 db + 16 (G & 1) .., lane 4 a + b' points at key row
+  // 16 s + 4 hf + a (+ 8), dims + 4 b' .. + 3
+  auto pv = [&](int bf, const floatx16 (&sc)[2]) {
     const bf16x8* VT = vt[bf];
-    // probabilities as the B operand: element e of lane (g, lr) is key
-    // 32 k2 + 4 g + (e < 4 ? e : 16 + e - 4)
-    Frag<bf16> pf[QB][2];
+    bf16x8 pf[4];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pf[qb][k2].v[e] = (bf16)sc[2 * k2][qb][e];
-          pf[qb][k2].v[4 + e] = (bf16)sc[2 * k2 + 1][qb][e];
-        }
-    // V fragment j = 2 d + k2, read two fragments ahead of its MFMAs (the
-    // fences keep the compiler from moving a read back next to its use)
+      for (int e = 0; e < 8; ++e) pf[st][e] = (bf16)sc[st >> 1][8 * (st & 1) + e];
+    const int ra = lr >> 2, rb = lr & 3;
+    // fragment j = 4 s + db, read two ahead of its MFMA behind fences
     auto vfr = [&](int j) -> bf16x8 {
-      const int d = j >> 1, k2 = j & 1;
-      const int el = d * 16 + rb * 4;
+      const int st = j >> 2, db = j & 3;
+      const int el = db * 32 + (g & 1) * 16 + rb * 4;
       const int c = el >> 3, half = (el >> 2) & 1;
-      const int r0 = k2 * 32 + g * 4 + ra;
+      const int r0 = st * 16 + hf * 4 + ra;
       return tr_pair(reinterpret_cast<const bf16*>(&VT[vslot(r0, c)]) + half * 4,
-                     reinterpret_cast<const bf16*>(&VT[vslot(r0 + 16, c)]) + half * 4);
+                     reinterpret_cast<const bf16*>(&VT[vslot(r0 + 8, c)]) + half * 4);
     };
-    Frag<bf16> vr[3];
-    vr[0].v = vfr(0);
-    vr[1].v = vfr(1);
+    bf16x8 vr[3];
+    vr[0] = vfr(0);
+    vr[1] = vfr(1);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      if (j + 2 < 16) vr[(j + 2) % 3].v = vfr(j + 2);
+      if (j + 2 < 16) vr[(j + 2) % 3] = vfr(j + 2);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) o[j >> 1][qb] = mfma16(vr[j % 3], pf[qb][j & 1], o[j >> 1][qb]);
+      o[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[j % 3], pf[j >> 2], o[j & 3], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- software pipeline over the key tiles: step t computes the scores of
-  // tile t + 1 (MFMA), the softmax of tile t (VALU), then P V of tile t (MFMA);
-  // tile t + 2 streams in meanwhile. Two score arrays alternate (the loop is
-  // unrolled by two).
+  // ---- software pipeline over the key tiles; tile t + 2 streams in meanwhile.
+  // Two score arrays alternate (the loop is unrolled by two).
   const int ntl = kbeg < kend ? (kend - kbeg + KT - 1) / KT : 0;
   MLA_WAIT_VMCNT(0);  // query fragments landed: in the loop only tile copies are outstanding
   if (ntl > 0) issue(kbeg, 0);
@@ -649,9 +600,9 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   if (ntl > 1) MLA_WAIT_VMCNT(5);  // the copies of tile 1 may stay in flight
   else MLA_WAIT_VMCNT(0);
   lds_barrier();
-  floatx4 s0[4][QB], s1[4][QB];
+  floatx16 s0[2], s1[2];
   if (active && ntl > 0 && live(kbeg)) scores(0, s0);
-  auto step = [&](int t, floatx4 (&cur)[4][QB], floatx4 (&nxt)[4][QB]) {
+  auto step = [&](int t, floatx16 (&cur)[2], floatx16 (&nxt)[2]) {
     const int k0 = kbeg + t * KT;
     MLA_WAIT_VMCNT(0);  // tile t + 1 landed (the only copies in flight)
     lds_barrier();      // ... for every wavefront; P V of tile t - 1 is done everywhere
@@ -659,10 +610,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     if (!active) return;  // no query of this wavefront exists: it only helps stream tiles
     const bool cur_live = live(k0), nxt_live = live(k0 + KT);
     if (cur_live && !(k0 >= in_lo && k0 + KT <= in_hi)) mask(cur, k0);
-    // the wave raises its priority over its MFMA blocks and drops it for
-    // the softmax: of the two waves of a SIMD, the one in an MFMA block
-    // issues first, so the two drift half a phase apart and one's softmax
-    // VALU runs beside the other's MFMAs (the fences keep each block whole)
+    // priority 3 over the MFMA blocks, 0 over the softmax (the fences keep each block whole)
     __builtin_amdgcn_s_setprio(3);
     if (nxt_live) scores((t + 1) % NBUF, nxt);  // after the last tile: a stale buffer, unused
     __builtin_amdgcn_sched_barrier(0);
@@ -672,9 +620,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
     __builtin_amdgcn_sched_barrier(0);
     if (__any(rescale)) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[d][qb] *= alpha[qb];
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     __builtin_amdgcn_s_setprio(3);
     pv(t % NBUF, cur);
@@ -688,27 +634,28 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_bf16_kernel(PrefillAttnAr
   }
   if (t < ntl) step(t, s0, s1);
 
-  // ---- epilogue: lane holds O[query lr][d .. d+3], d = 16 db + 4 g
+  // ---- epilogue: lane holds O[query lq][32 db + 8 i + 4 hf + (0..3)]
+  if (qi >= ql) return;
+  const int tt = t0 + qi;
+  if (tt >= a.total_tokens) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (a.lse && hf == 0) a.lse[(int64_t)tt * a.H + h] = l > 0.f ? m + __log2f(l) : -INFINITY;
+  bf16* orow = reinterpret_cast<bf16*>(a.out) + (int64_t)tt * a.ldo + (int64_t)h * a.dv;
+  const bf16* grow = a.gate ? reinterpret_cast<const bf16*>(a.gate) + (int64_t)tt * a.ldg + (int64_t)h * a.dv : nullptr;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    if (qi[qb] >= ql) continue;
-    const int t = t0 + qi[qb];
-    if (t >= a.total_tokens) continue;
-    const float inv = l[qb] > 0.f ? 1.f / l[qb] : 0.f;
-    if (a.lse && g == 0) a.lse[(int64_t)t * a.H + h] = l[qb] > 0.f ? m[qb] + __log2f(l[qb]) : -INFINITY;
-    bf16* orow = reinterpret_cast<bf16*>(a.out) + (int64_t)t * a.ldo + (int64_t)h * a.dv;
-    const bf16* grow = a.gate ? reinterpret_cast<const bf16*>(a.gate) + (int64_t)t * a.ldg + (int64_t)h * a.dv : nullptr;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int d0 = d * 16 + g * 4;
-      floatx4 v = o[d][qb] * inv;
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = db * 32 + i * 8 + hf * 4;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = o[db][4 * i + j] * inv;
       if (grow) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] *= sigmoidf((float)grow[d0 + i]);
+        for (int j = 0; j < 4; ++j) v[j] *= sigmoidf((float)grow[d0 + j]);
       }
       *reinterpret_cast<bf16x4*>(orow + d0) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
     }
-  }
 }
 
 template <typename T, int DQK, int DV>
