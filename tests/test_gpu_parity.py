@@ -253,6 +253,49 @@ def test_dropped_rows_are_exact_zero():
     assert np.all(out[3:9] == 0) and np.all(out[20:24] == 0)
 
 
+def test_prefill_full_mask_bf16():
+    """FULL mask through the bf16 flash kernel (more than 64 new tokens, so
+    not the fused path): every query sees its whole sequence, keys after its
+    own position included, over ragged last tiles and a cached prefix."""
+    w = ms.make_workload("prefill_bf16", q_lens=[150, 90], prefix_lens=[20, 0], mask_kind=ms.MASK_FULL, seed=83)
+    _run_and_check(w)
+
+
+def test_prefill_explicit_intervals_bf16():
+    """Explicit visible intervals through the bf16 flash kernel: a wave's
+    32 rows all dropped, empty intervals away from key 0, single-key rows,
+    rows that see keys after their own position, and random intervals whose
+    ends are not tile multiples; dropped rows are exactly zero."""
+    q_lens, prefix = [300, 170], [37, 0]
+    kv = [p + q for p, q in zip(prefix, q_lens)]
+    T = sum(q_lens)
+    seq = np.repeat(np.arange(2), q_lens)
+    pos = np.concatenate([p + np.arange(q) for p, q in zip(prefix, q_lens)])
+    kvr = np.asarray(kv)[seq]
+    lo = np.zeros(T, np.int64)
+    hi = pos + 1
+    rng = np.random.default_rng(84)
+    r = np.arange(150, 300)
+    lo[r] = rng.integers(0, pos[r] + 1)
+    hi[r] = rng.integers(lo[r], kvr[r] + 1)
+    r = np.arange(380, 470)
+    lo[r] = rng.integers(0, kvr[r])
+    hi[r] = rng.integers(lo[r], kvr[r] + 1)
+    hi[0:32] = 0
+    lo[40:48], hi[40:48] = 100, 100
+    lo[60:91] = 65 + np.arange(31) % 7
+    hi[60:91] = kv[0]
+    lo[100:104], hi[100:104] = 200, 201
+    lo[300:364], hi[300:364] = 0, 0
+    lo[364:380], hi[364:380] = 0, kv[1]
+    dropped = lo >= hi
+    w = ms.make_workload("prefill_bf16", q_lens=q_lens, prefix_lens=prefix,
+                         row_interval=(lo.astype(np.int32), hi.astype(np.int32)), seed=85)
+    out = _run_and_check(w)
+    assert dropped.sum() >= 100
+    assert np.all(out[dropped] == 0)
+
+
 def test_window_zero_gives_zero_output():
     w = ms.make_workload("tiny_f32", mask_kind=ms.MASK_SLIDING, window=0, q_lens=[9], prefix_lens=[4], seed=15)
     out, _ = U.run_gpu(w)
