@@ -1085,6 +1085,258 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(TrainArgs a) {
     }
 }
 
+// dQ of the bf16 backward at n 128, r 64, dv 128 on the 32x32x16 MFMA: a
+// workgroup is 8 wavefronts x 32 queries of one (sequence, head) pair (two
+// wavefronts per SIMD); 64-key tiles (k_nope and v rows of the expanded
+// buffer, the rope key from the cache) stream HBM -> LDS by
+// global_load_lds_dwordx4 through a 3-tile ring. Per 32-key block: S^T = K Q^T
+// (12 MFMAs, the wavefront's queries as B operands in registers), dP^T = V dO^T
+// (8, dO in registers), dS^T = P^T (dP^T - D) in registers, whose accumulator
+// elements are, lane for lane, the B operand of dQ^T += K^T dS^T (12, K^T from
+// transposing reads). Rows are unpadded with XOR-swizzled 16-byte chunks: the
+// 16 rows of a row read and the 4 rows x 32 bytes of a transposing-read pass
+// hit distinct banks (k_nope: chunk ^ ((row & 3) << 2 | (row >> 2) & 3), rope
+// rows of 8 chunks: chunk ^ (((row >> 1) & 1) << 2 | (row >> 2) & 3), value
+// rows, read by rows only: chunk ^ (row & 15)).
+namespace bwdq {
+constexpr int KT = 64, NW = 8, BQ = NW * 32, NOPE_CH = 16, PE_CH = 8, V_CH = 16, NBUF = 3;
+__device__ __forceinline__ int nsw(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int psw(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int nslot(int row, int c) { return row * NOPE_CH + (c ^ nsw(row)); }
+__device__ __forceinline__ int pslot(int row, int c) { return row * PE_CH + (c ^ psw(row)); }
+__device__ __forceinline__ int vslot(int row, int c) { return row * V_CH + (c ^ (row & 15)); }
+}  // namespace bwdq
+
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_big_kernel(TrainArgs a) {
+  using namespace bwdq;
+  __shared__ __attribute__((aligned(16))) bf16x8 kn[NBUF][KT * NOPE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 kp[NBUF][KT * PE_CH];
+  __shared__ __attribute__((aligned(16))) bf16x8 vr[NBUF][KT * V_CH];
+  __shared__ int iv[4];  // union lo, union hi, intersection lo, intersection hi
+
+  // workgroup id -> (query tile, head, sequence): the pairs go to the XCDs
+  // round-robin, heaviest (latest) query tiles first
+  const int np = a.H * a.batch, npx = (np + 7) / 8;
+  const int id = blockIdx.x, xcd = id & 7, slot = id >> 3;
+  const int nqt = (a.max_q_len + BQ - 1) / BQ;
+  const int pr = (slot % npx) * 8 + xcd;
+  const int qt = nqt - 1 - slot / npx;
+  if (pr >= np || qt < 0) return;
+  const int h = pr % a.H, b = pr / a.H;
+  const int S = seq_len(a, b);
+  if (qt * BQ >= S) return;
+  const int t0 = a.cu_seqlens[b];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 31, hf = lane >> 5;  // query of the lane, half of the key group
+  const int lr = lane & 15, g = lane >> 4, ra = lr >> 2, rb = lr & 3;
+  const float sl2 = a.scale * kLog2e;
+  const int qk = a.n + a.r;
+
+  if (tid == 0) { iv[0] = 0x7fffffff; iv[1] = 0; iv[2] = 0; iv[3] = 0x7fffffff; }
+  __syncthreads();
+  const int qi = qt * BQ + wave * 32 + lq;
+  const bool qok = qi < S;
+  const int tq = t0 + (qok ? qi : 0);
+  int lo = 0, hi = 0;
+  if (qok) visible_rows(a.mask, tq, qi, S, lo, hi);
+  if (hf == 0 && lo < hi) {
+    atomicMin(&iv[0], lo);
+    atomicMax(&iv[1], hi);
+    atomicMax(&iv[2], lo);
+    atomicMin(&iv[3], hi);
+  }
+  if (hf == 0 && qok && lo >= hi) atomicMax(&iv[2], 0x7fffffff);  // an empty row: every tile is masked for it
+  __syncthreads();
+  const int kbeg = (iv[0] / KT) * KT, kend = iv[1];
+  const int in_lo = iv[2], in_hi = iv[3];  // tiles inside [in_lo, in_hi) need no mask
+  // the union of this wavefront's visible intervals (tiles outside it are skipped)
+  int wlo = lo < hi ? lo : 0x7fffffff, whi = lo < hi ? hi : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    wlo = min(wlo, __shfl_xor(wlo, o));
+    whi = max(whi, __shfl_xor(whi, o));
+  }
+  wlo = __builtin_amdgcn_readfirstlane(wlo);
+  whi = __builtin_amdgcn_readfirstlane(whi);
+  auto live = [&](int k0) { return k0 < whi && k0 + KT > wlo; };
+
+  // B operands: q of step ks = dims 16 ks + 8 hf .. + 7, dO of step s likewise
+  bf16x8 qf[12], of[8];
+  {
+    const bf16* qrow = reinterpret_cast<const bf16*>(a.q) + (int64_t)tq * a.ldq + (int64_t)h * qk;
+    const bf16* orow = reinterpret_cast<const bf16*>(a.dO) + (int64_t)tq * a.ldo + (int64_t)h * a.dv;
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + hf * 8);
+      qf[ks] = qok ? v : bf16x8{};
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(orow + s * 16 + hf * 8);
+      of[s] = qok ? v : bf16x8{};
+    }
+  }
+  const float l2 = qok ? a.lse[(int64_t)tq * a.H + h] : 0.f;
+  const float dd = qok ? a.D[(int64_t)tq * a.H + h] : 0.f;
+
+  // copy geometry (as in the forward prefill kernel): 2 k_nope and 2 v
+  // instructions of 1 KB per wavefront, 1 rope instruction
+  const bf16* kvb = reinterpret_cast<const bf16*>(a.kvexp) + (int64_t)b * a.Lp * a.ldkv + (int64_t)h * (a.n + a.dv);
+  const int64_t row_bytes = a.ldkv * 2;
+  const int E = a.c + a.r;
+  const bf16* crow = reinterpret_cast<const bf16*>(a.cache) + (int64_t)b * a.Lp * E;
+  uint32_t noff[2], voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sl = (j * NW + wave) * 64 + lane;
+    const int row = sl / NOPE_CH, cs = sl % NOPE_CH;
+    noff[j] = (uint32_t)(row * row_bytes) + (uint32_t)((cs ^ nsw(row)) * 16);
+    voff[j] = (uint32_t)(row * row_bytes) + (uint32_t)(a.n * 2) + (uint32_t)((cs ^ (row & 15)) * 16);
+  }
+  uint32_t poff;
+  {
+    const int sl = wave * 64 + lane;
+    const int row = sl / PE_CH, cs = sl % PE_CH;
+    poff = (uint32_t)(row * E * 2) + (uint32_t)(a.c * 2) + (uint32_t)((cs ^ psw(row)) * 16);
+  }
+  const uint32_t kn_lds = lds_addr(&kn[0][0]), vr_lds = lds_addr(&vr[0][0]), kp_lds = lds_addr(&kp[0][0]);
+  auto issue = [&](int k0, int buf) {
+    // rows past the last key re-read the last key (their probabilities are masked)
+    const int rows_valid = min(kend, S) - k0;
+    const bf16* base = kvb + (int64_t)k0 * a.ldkv;
+    const bf16* pbase = crow + (int64_t)k0 * E;
+    const uint32_t nb = kn_lds + (uint32_t)(buf * KT * NOPE_CH * 16);
+    const uint32_t vb = vr_lds + (uint32_t)(buf * KT * V_CH * 16);
+    const uint32_t pb = kp_lds + (uint32_t)(buf * KT * PE_CH * 16);
+    if (rows_valid >= KT) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dma16_sbase(noff[j], base, nb + (uint32_t)(j * NW + wave) * 1024u);
+        dma16_sbase(voff[j], base, vb + (uint32_t)(j * NW + wave) * 1024u);
+      }
+      dma16_sbase(poff, pbase, pb + (uint32_t)wave * 1024u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = ((j * NW + wave) * 64 + lane) / NOPE_CH;
+        const uint32_t back = row >= rows_valid ? (uint32_t)((row - rows_valid + 1) * row_bytes) : 0u;
+        dma16_sbase(noff[j] - back, base, nb + (uint32_t)(j * NW + wave) * 1024u);
+        dma16_sbase(voff[j] - back, base, vb + (uint32_t)(j * NW + wave) * 1024u);
+      }
+      const int row = (wave * 64 + lane) / PE_CH;
+      const uint32_t back = row >= rows_valid ? (uint32_t)((row - rows_valid + 1) * E * 2) : 0u;
+      dma16_sbase(poff - back, pbase, pb + (uint32_t)wave * 1024u);
+    }
+  };
+
+  // dQ^T block db: element e of lane l is dim 32 db + 8 (e / 4) + 4 hf + e % 4 of query lq
+  floatx16 dq[6];
+#pragma unroll
+  for (int db = 0; db < 6; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dq[db][e] = 0.f;
+  const bool active = qt * BQ + wave * 32 < S;
+
+  // keys 32 kb .. + 31 of the tile in buffer bf (first key k0)
+  auto block = [&](int bf, int kb, int k0, bool edge) {
+    const bf16x8* KN = kn[bf];
+    const bf16x8* KP = kp[bf];
+    const bf16x8* VR = vr[bf];
+    // the lane coordinates made opaque here, so that the fragment addresses
+    // are computed next to their reads instead of held across the tile loop
+    int lq = lane & 31, hf = lane >> 5, g = lane >> 4, ra = (lane & 15) >> 2, rb = lane & 3;
+    asm volatile("" : "+v"(lq), "+v"(hf), "+v"(g), "+v"(ra), "+v"(rb));
+    floatx16 sc, dp;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.f;
+    // S^T (fragments 0..11: key 32 kb + lq, dims 16 j + 8 hf) and dP^T
+    // (12..19: value dims 16 (j - 12) + 8 hf), each read two MFMAs ahead
+    const int row = kb * 32 + lq;
+    auto sfr = [&](int j) -> bf16x8 {
+      return j < 8 ? KN[nslot(row, 2 * j + hf)] : (j < 12 ? KP[pslot(row, 2 * (j - 8) + hf)] : VR[vslot(row, 2 * (j - 12) + hf)]);
+    };
+    bf16x8 fr[3];
+    fr[0] = sfr(0);
+    fr[1] = sfr(1);
+#pragma unroll
+    for (int j = 0; j < 20; ++j) {
+      if (j + 2 < 20) fr[(j + 2) % 3] = sfr(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j < 12) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % 3], qf[j], sc, 0, 0, 0);
+      else dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % 3], of[j - 12], dp, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dS^T = P^T (dP^T - D); element e is key k0 + 32 kb + 8 (e / 4) + 4 hf + e % 4
+    bf16x8 dsf[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * hf + (e & 3);
+      const bool vis = !edge || (qok & (key >= lo) & (key < hi));
+      const float p = vis ? fast_exp2(__builtin_fmaf(sc[e], sl2, -l2)) : 0.f;
+      dsf[e >> 3][e & 7] = (bf16)(p * (dp[e] - dd));
+    }
+    // dQ^T += K^T dS^T: fragment x = (half sp = x / 6, dim block db = x % 6);
+    // the A operand is read in the key order of the B operand (keys 16 st +
+    // 4 hf + (0..3) and + 8): group G of 16 lanes covers dims 32 db + 16 (G &
+    // 1) .., lane 4 ra + rb points at key row 16 st + 4 hf + ra (+ 8), dims
+    // + 4 rb .. + 3
+    auto tfr = [&](int x) -> bf16x8 {
+      const int sp = x / 6, db = x % 6, st = 2 * kb + sp;
+      const int r0 = st * 16 + hf * 4 + ra;
+      int el = db * 32 + (g & 1) * 16 + rb * 4;
+      if (db < 4) {
+        const int c = el >> 3, half = (el >> 2) & 1;
+        return tr_pair16(reinterpret_cast<const bf16*>(&KN[nslot(r0, c)]) + half * 4,
+                         reinterpret_cast<const bf16*>(&KN[nslot(r0 + 8, c)]) + half * 4);
+      }
+      el -= 128;
+      const int c = el >> 3, half = (el >> 2) & 1;
+      return tr_pair16(reinterpret_cast<const bf16*>(&KP[pslot(r0, c)]) + half * 4,
+                       reinterpret_cast<const bf16*>(&KP[pslot(r0 + 8, c)]) + half * 4);
+    };
+    fr[0] = tfr(0);
+    fr[1] = tfr(1);
+#pragma unroll
+    for (int x = 0; x < 12; ++x) {
+      if (x + 2 < 12) fr[(x + 2) % 3] = tfr(x + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      dq[x % 6] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[x % 3], dsf[x / 6], dq[x % 6], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int ntl = kbeg < kend ? (kend - kbeg + KT - 1) / KT : 0;
+  MLA_WAIT_VMCNT(0);  // queries and dO landed: in the loop only tile copies are outstanding
+  if (ntl > 0) issue(kbeg, 0);
+  if (ntl > 1) issue(kbeg + KT, 1);
+  for (int t = 0; t < ntl; ++t) {
+    const int k0 = kbeg + t * KT;
+    if (t + 1 < ntl) MLA_WAIT_VMCNT(5);  // tile t landed; the copies of tile t + 1 may stay in flight
+    else MLA_WAIT_VMCNT(0);
+    lds_barrier();  // ... for every wavefront; tile t - 1 is no longer read
+    if (t + 2 < ntl) issue(k0 + 2 * KT, (t + 2) % NBUF);
+    if (!active || !live(k0)) continue;
+    const bool edge = !(k0 >= in_lo && k0 + KT <= in_hi);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) block(t % NBUF, kb, k0, edge);
+  }
+
+  // epilogue: lane holds dQ[query lq][32 db + 8 i + 4 hf + (0..3)], times the scale
+  if (!qok) return;
+  bf16* out = reinterpret_cast<bf16*>(a.dQ) + (int64_t)tq * a.lddq + (int64_t)h * qk;
+#pragma unroll
+  for (int db = 0; db < 6; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = db * 32 + i * 8 + hf * 4;
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = dq[db][4 * i + j] * a.scale;
+      *reinterpret_cast<bf16x4*>(out + d0) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    }
+}
+
 template <typename T, int DQK, int DV>
 hipError_t launch_attn_bwd(const TrainArgs& a, hipStream_t s) {
   const int tiles = (a.max_q_len + 63) / 64;
@@ -1102,6 +1354,12 @@ hipError_t launch_attn_bwd_bf16(const TrainArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(8 * npx * tiles));
   hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (DQK == 192 && a.n == 128 && a.r == 64 && a.dv == 128 && a.c % 8 == 0) {
+    const int64_t nqt = (a.max_q_len + bwdq::BQ - 1) / bwdq::BQ;
+    if (8 * (int64_t)npx * nqt > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_bwd_dq_big_kernel, dim3((unsigned)(8 * npx * nqt)), dim3(64 * bwdq::NW), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DQK, DV>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

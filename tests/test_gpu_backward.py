@@ -90,3 +90,35 @@ def test_backward_gate_neox_bf16():
                          window=50, seed=74,
                          dims_override={"num_heads": 16, "use_output_gate": True, "rope_style": ms.ROPE_NEOX})
     _check(w, 174)
+
+
+def test_backward_full_mask_bf16():
+    """bf16 at the draft-block model dims under the FULL mask (every query
+    sees its whole sequence, keys after it included): 300 and 40 tokens,
+    over a 256-query tile boundary and ragged 64-key tiles."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[300, 40], prefix_lens=[0, 0], mask_kind=ms.MASK_FULL, seed=77)
+    _check(w, 177)
+
+
+def test_backward_intervals_bf16():
+    """bf16 at the draft-block model dims with explicit visible intervals:
+    a wavefront's 32 rows dropped, empty intervals away from key 0, rows
+    that see keys after their own position, a one-key row and random
+    intervals whose ends are not tile multiples."""
+    q_lens = [290, 50]
+    T = sum(q_lens)
+    rng = np.random.default_rng(78)
+    pos = np.concatenate([np.arange(q) for q in q_lens])
+    kv = np.concatenate([[q] * q for q in q_lens])
+    lo = np.zeros(T, np.int64)
+    hi = pos + 1
+    r = np.arange(100, 250)
+    lo[r] = rng.integers(0, pos[r] + 1)
+    hi[r] = rng.integers(lo[r], kv[r] + 1)
+    hi[32:64] = 0
+    lo[70:80], hi[70:80] = 40, 40
+    lo[80:90], hi[80:90] = 13, kv[80]
+    lo[260:264], hi[260:264] = 5, 6
+    w = ms.make_workload("draft_block_bf16", q_lens=q_lens, prefix_lens=[0, 0],
+                         row_interval=(lo.astype(np.int32), hi.astype(np.int32)), seed=78)
+    _check(w, 178)
