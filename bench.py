@@ -222,8 +222,9 @@ STAGE_KERNEL = {
     "prefill_attn": "prefill_attn_bf16_kernel", "kv_b_expand": "gemm_big_kernel",
     "rope_cache": "rope_cache", "expand_attn": "mha_fused_kernel", "expand_merge": "mha_fused_merge_kernel",
     "kv_dequant": "kv_shadow_kernel",
-    # a stage of two kernels: its traffic is the sum of both per-dispatch averages
-    "attn_bwd": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd_dq_bf16_kernel"),
+    # a stage of two kernels (the dQ pattern names both dQ kernels): its traffic is
+    # the sum of both per-dispatch averages
+    "attn_bwd": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd_dq_"),
 }
 COPY_KERNEL = "neg_kernel"  # torch's elementwise negation kernel of the copy calibration (not the flush fill)
 
