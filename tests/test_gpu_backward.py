@@ -122,3 +122,12 @@ def test_backward_intervals_bf16():
     w = ms.make_workload("draft_block_bf16", q_lens=q_lens, prefix_lens=[0, 0],
                          row_interval=(lo.astype(np.int32), hi.astype(np.int32)), seed=78)
     _check(w, 178)
+
+
+def test_backward_sliding_multi_tile_bf16():
+    """bf16 at the draft-block model dims under a sliding window of 300 over
+    sequences of 600 and 257 tokens: several 256-query tiles whose first
+    visible key is past key 0 and not a tile multiple."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[600, 257], prefix_lens=[0, 0], mask_kind=ms.MASK_SLIDING,
+                         window=300, seed=79)
+    _check(w, 179)
