@@ -131,3 +131,14 @@ def test_backward_sliding_multi_tile_bf16():
     w = ms.make_workload("draft_block_bf16", q_lens=[600, 257], prefix_lens=[0, 0], mask_kind=ms.MASK_SLIDING,
                          window=300, seed=79)
     _check(w, 179)
+
+
+def test_backward_small_heads_bf16():
+    """bf16 with 8 heads of nope 64, rope 32, v 64 (q/k head 96): the
+    general bf16 attention-gradient kernels (16 keys or queries per
+    wavefront, staged tiles) that shapes other than nope 128 / rope 64 /
+    v 128 take."""
+    w = ms.make_workload("draft_block_bf16", q_lens=[150, 70], prefix_lens=[0, 0], mask_kind=ms.MASK_CAUSAL, seed=80,
+                         dims_override={"num_heads": 8, "qk_nope_head_dim": 64, "qk_rope_head_dim": 32,
+                                        "v_head_dim": 64})
+    _check(w, 180)
